@@ -1,0 +1,200 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) FusedBitLinear library.
+ *
+ * One FusedBitLinear projection (in_features K -> out_features N, no bias)
+ * computes, for every token row x[m, :]:
+ *
+ *   RMSNorm   r_m  = 1 / sqrt(mean_k x[m,k]^2 + eps),  xn = (x * r_m) * g
+ *   act-quant s_m  = 127 / max(max_k |xn[m,k]|, 1e-5),
+ *             xq   = clamp(round_half_even(xn * s_m), -128, 127)      (int8)
+ *   weights   beta = max(mean |W|, 1e-5) over the whole matrix,
+ *             Wq   = clamp(round_half_even(W / beta), -1, +1)         (ternary)
+ *   contract  acc[m,n] = sum_k xq[m,k] * Wq[n,k]                      (int32)
+ *   rescale   y[m,n]   = acc[m,n] / s_m * beta
+ *
+ * Where each step comes from (page titles and sections):
+ *   - FusedBitLinear(in, out, bias=False) carrying its own RMSNorm with
+ *     eps = 1e-08, the norm fused with the ternary projection and applied
+ *     right before quantization: hysenlabs ja review "matmulfreellm 評価 ...",
+ *     section "HGRNBit という層構成を読む"; hysenlabs fr review "MatMul-Free
+ *     LM : un modèle de langage sans multiplication matricielle ...", section
+ *     "HGRNBit : ce que la structure du modèle révèle"; hysenlabs de review
+ *     "MatMul-Free LM: Ternary-Gewichte statt Matrixmultiplikation im
+ *     Transformer", section "HGRNBit: was in einem Block tatsächlich passiert".
+ *   - absmean ternary weights, and products by -1/0/+1 reduced to negate /
+ *     zero / keep: datacamp "MatMul-freie LLMs: Zentrale Konzepte erklärt",
+ *     section "MatMul durch ternäre Operationen ersetzen".
+ *   - RMSNorm before quantization and the scaled ternary accumulation:
+ *     same datacamp page, section "Kernkomponenten: MLGRU und GLU", figure
+ *     panels 5 and 4.
+ *   - y = W x orientation of a linear layer (W stored [out, in]): aidev
+ *     bluegarage "量子化とは何か？MatMulというAIの計算やモデルサイズの最大の
+ *     ネック", section "ニューラルネットにおける実態".
+ *   The activation format (8-bit, one absmax scale per token), round half to
+ *   even, the 1e-5 floors and eps inside the square root are the readings
+ *   this library fixes where the pages are silent.
+ *
+ * Precision.  The sums of x^2 and |W| are accumulated in fp64; every other
+ * step before an integer is decided runs in IEEE fp32 with correctly rounded
+ * division and square root; the contraction is exact int32; the rescale is
+ * fp32 (acc * (beta / s_m)), rounded to nearest-even into the output dtype.
+ *
+ * ---------------------------------------------------------------- layout
+ * Packed ternary weights (bitlinear_pack_weights output) use N*K/4 bytes:
+ *   - 2-bit code per weight: code = Wq + 1 (0 = -1, 1 = 0, 2 = +1; 3 unused).
+ *   - The [N, K] matrix is cut into tiles of 32 rows x 128 columns (K index),
+ *     1024 bytes each, stored row-tile-major: tile (nt, kb) starts at byte
+ *     1024 * (nt * (K/128) + kb).
+ *   - In a tile, row n = 32*nt + 16*h + c (h in {0,1}, c in 0..15) and the
+ *     16-column group j (k = 128*kb + 16*j + e, j in 0..7, e in 0..15) form
+ *     one little-endian 32-bit word at tile byte offset
+ *     16 * (16 * (j / 2) + c) + 4 * (2 * h + j % 2).
+ *   - In that word the code of element e sits at bits 8*(e%4) + 2*(e/4)
+ *     (and the next bit), so (word >> 2q) & 0x03030303 yields the codes of
+ *     elements 4q .. 4q+3 as four bytes.
+ * With this layout one 16-byte load by lane L of a 64-lane wave returns
+ * exactly the four B operands (rows 16h + L%16, k-groups 2*(L/16) + s) that
+ * lane feeds to four v_mfma_i32_16x16x64_i8 instructions, and a wave reads a
+ * tile as one contiguous 1 KiB.
+ * beta is a separate fp32 in device memory.
+ *
+ * ------------------------------------------------------------ conventions
+ * - All pointers to data are DEVICE pointers, caller-allocated and owned; the
+ *   library allocates nothing and keeps no per-call state.  Every data
+ *   pointer must be 16-byte aligned.
+ * - Matrices are dense row-major: x [M, K], gain [K], W [N, K], y [M, N].
+ * - Shapes: K % 128 == 0, N % 32 == 0, 128 <= K <= 65536, 32 <= N <= 2^20,
+ *   0 <= M <= 2^24.  M == 0 is a no-op that returns BL_OK.
+ * - dtypes: BL_F32, BL_F16, BL_BF16 for x / gain (same dtype) and for y.
+ * - Calls are asynchronous on `stream` (0 = the null stream); errors from a
+ *   kernel surface at the caller's next synchronization.  Every argument is
+ *   validated on the host before anything is launched; a rejected call
+ *   launches nothing and touches no memory.
+ * - Calls that share a workspace must be ordered (same stream).
+ * - Inputs must be finite; NaN / Inf give unspecified codes.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype codes */
+enum { BL_F32 = 0, BL_F16 = 1, BL_BF16 = 2 };
+
+/* status codes (0 = success) */
+enum {
+    BL_OK = 0,
+    BL_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    BL_ERR_DTYPE = -2,       /* unknown dtype code                          */
+    BL_ERR_SHAPE = -3,       /* M, N or K outside the supported set         */
+    BL_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned            */
+    BL_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required  */
+    BL_ERR_EPS = -6,         /* eps not finite or not > 0                   */
+    BL_ERR_HIP = -7,         /* a HIP launch or query failed                */
+    BL_ERR_UNSUPPORTED = -8, /* valid request this build does not implement */
+    BL_ERR_PATH = -9         /* unknown execution path code                 */
+};
+
+/* execution paths for bitlinear_forward_path / bitlinear_gemm_i32 */
+enum {
+    BL_PATH_AUTO = 0,    /* choose by M (what bitlinear_forward does)        */
+    BL_PATH_FUSED = 1,   /* one kernel: norm + quant + skinny contraction    */
+    BL_PATH_SKINNY = 2,  /* act-quant kernel, then skinny contraction (M<=16)*/
+    BL_PATH_MFMA = 3     /* act-quant kernel, then tiled MFMA contraction    */
+};
+
+/* Bytes of packed weights for an [N, K] matrix: N*K/4 (0 for a bad shape). */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_pack_weights needs (0 for a bad shape). */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/* Offline weight packing (absmean ternarization + 2-bit tile layout).
+ *   W       device fp32 [N, K] latent weights (read only)
+ *   packed  device, bitlinear_packed_bytes(N, K) bytes (written)
+ *   beta    device fp32 scalar: the per-tensor scale (written)
+ *   ws      device scratch of >= bitlinear_pack_workspace_bytes(N, K)
+ * beta stays on the device; no host synchronization is needed before a
+ * forward call on the same stream. */
+int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, void *packed,
+                           float *beta, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Workspace bytes bitlinear_forward needs for (M, K, N), covering every
+ * path (0 for a bad shape). */
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* One FusedBitLinear forward: y = rescale(contract(quant(rmsnorm(x)), Wq)).
+ *   x       device [M, K], dtype x_dtype (read only)
+ *   gain    device [K], dtype x_dtype: the RMSNorm weight (read only)
+ *   packed  device packed weights of an [N, K] matrix (read only)
+ *   beta    device fp32 scalar written by bitlinear_pack_weights
+ *   y       device [M, N], dtype y_dtype (written)
+ *   eps     RMSNorm epsilon (the layer uses 1e-8)
+ *   ws      device scratch of >= bitlinear_workspace_bytes(M, K, N) bytes;
+ *           its contents on entry do not matter; it holds the int8
+ *           activations, per-row scales and row sums between the stages.
+ * Returns BL_OK or a negative BL_ERR_* code (nothing launched on error). */
+int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
+                      const void *gain, const void *packed, const float *beta,
+                      int64_t N, void *y, int y_dtype, float eps, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Same as bitlinear_forward with an explicit execution path (BL_PATH_*).
+ * BL_PATH_FUSED requires M <= 16, K <= 8192 and M * (K + 16) <= 57216 (its
+ * int8 activations live in LDS); BL_PATH_SKINNY requires M <= 16 (else
+ * BL_ERR_SHAPE).  Every path computes the same function: the integer codes
+ * and accumulators are identical, y may differ only where a pre-rounding
+ * activation value lies within a few fp32 ulps of a .5 boundary (the fp64
+ * sum of squares is added in a different order). */
+int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
+                           const void *gain, const void *packed,
+                           const float *beta, int64_t N, void *y, int y_dtype,
+                           float eps, void *ws, size_t ws_bytes, int path,
+                           hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *bitlinear_status_string(int status);
+
+/* ------------------------------------------------ stage-level entry points
+ * These expose the stages of the path one at a time so each can be checked
+ * on its own (bit-exact integer outputs). */
+
+/* RMSNorm + per-token int8 quantization.
+ *   xq [M, K] int8, s [M] fp32, rowsum [M] int32 = sum_k xq[m, k]
+ *   (all device, written). */
+int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
+                        int64_t M, int64_t K, float eps, int8_t *xq, float *s,
+                        int32_t *rowsum, hipStream_t stream);
+
+/* Exact contraction acc[m, n] = sum_k xq[m, k] * Wq[n, k] from int8
+ * activations and packed weights (datacamp page above, section "MatMul
+ * durch ternäre Operationen ersetzen").
+ *   xq      device int8 [M, K] (read only)
+ *   rowsum  device int32 [M] = sum_k xq[m, k] (as written by
+ *           bitlinear_act_quant); the kernels use it to turn the sum over
+ *           the stored codes (Wq + 1) back into the signed sum, so a wrong
+ *           rowsum gives a wrong acc.
+ *   acc     device int32 [M, N] (written)
+ *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 16) or BL_PATH_MFMA;
+ *           BL_PATH_FUSED is BL_ERR_PATH here. */
+int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
+                       int64_t K, const void *packed, int64_t N, int32_t *acc,
+                       int path, hipStream_t stream);
+
+/* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device). */
+int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
+                             int8_t *Wq, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,51 @@
+"""MI355X (gfx950) FusedBitLinear: RMSNorm + per-token int8 activations +
+absmean ternary weights packed at 2 bits + exact integer contraction +
+rescale, in HIP kernels behind the C ABI of include/bitlinear.h.
+
+The functions named bitlinear_* mirror the C entry points one to one.
+pack() and forward() below only allocate outputs and workspaces with torch
+and call them.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (  # noqa: F401
+    BL_BF16, BL_F16, BL_F32, BL_PATH_AUTO, BL_PATH_FUSED, BL_PATH_MFMA,
+    BL_PATH_SKINNY, CODE_DTYPE, DTYPE_CODE, BitLinearError, lib,
+    bitlinear_act_quant, bitlinear_forward, bitlinear_forward_path,
+    bitlinear_gemm_i32, bitlinear_pack_weights, bitlinear_pack_workspace_bytes,
+    bitlinear_packed_bytes, bitlinear_status_string, bitlinear_unpack_weights,
+    bitlinear_workspace_bytes,
+)
+
+
+def _bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def pack(W: torch.Tensor):
+    """Pack latent fp32 weights [N, K] (on the GPU).  Returns
+    (packed uint8 [N*K/4], beta fp32 [1])."""
+    N, K = W.shape
+    packed = torch.empty(bitlinear_packed_bytes(N, K), dtype=torch.uint8, device=W.device)
+    beta = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = _bytes(bitlinear_pack_workspace_bytes(N, K), W.device)
+    bitlinear_pack_weights(W, packed, beta, ws)
+    return packed, beta
+
+
+def forward(x: torch.Tensor, gain: torch.Tensor, packed: torch.Tensor,
+            beta: torch.Tensor, N: int, eps: float = 1e-8, out_dtype=None,
+            path: int = BL_PATH_AUTO, ws: torch.Tensor | None = None):
+    """y [M, N] = FusedBitLinear(x [M, K]) with the packed weights."""
+    M, K = x.shape
+    y = torch.empty(M, N, dtype=out_dtype or x.dtype, device=x.device)
+    if ws is None:
+        ws = _bytes(bitlinear_workspace_bytes(M, K, N), x.device)
+    bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=eps)
+    return y
+
+
+def workspace(M: int, K: int, N: int, device="cuda") -> torch.Tensor:
+    return _bytes(bitlinear_workspace_bytes(M, K, N), device)

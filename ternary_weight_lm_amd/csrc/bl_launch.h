@@ -1,0 +1,61 @@
+// bl_launch.h -- host-side launchers of the gfx950 kernels.  Each returns
+// the hipError_t of its launches; argument checking is done once, in the C
+// ABI layer (capi.cpp), before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Output kinds of the contraction kernels: a BL_* dtype code, or kOutI32 for
+// the exact int32 accumulator (stage-level entry point).
+constexpr int kOutI32 = 3;
+
+// Workspace bytes of the weight packer (partial sums of |W|).
+size_t pack_workspace_bytes();
+
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, void *packed,
+                       float *beta, void *ws, hipStream_t stream);
+
+hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *Wq,
+                         hipStream_t stream);
+
+hipError_t launch_act_quant(const void *x, int x_dtype, const void *gain,
+                            int64_t M, int64_t K, float eps, int8_t *xq,
+                            float *s, int32_t *rowsum, hipStream_t stream);
+
+// Tiled MFMA contraction of pre-quantized activations (any M).
+// out_kind = BL_* writes y = (acc) * beta / s; kOutI32 writes acc.
+hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
+                            const float *s, const void *packed,
+                            const float *beta, int64_t M, int64_t N,
+                            int64_t K, void *out, int out_kind,
+                            hipStream_t stream);
+
+// Skinny contraction for M <= 16: one workgroup per 32 output rows.
+// fused = true: x / gain / eps are read and normalized + quantized inside;
+// fused = false: xq / s / rowsum come from a previous act-quant launch.
+struct SkinnyArgs {
+  bool fused;
+  const void *x;
+  int x_dtype;
+  const void *gain;
+  float eps;
+  const int8_t *xq;
+  const float *s;
+  const int32_t *rowsum;
+  const void *packed;
+  const float *beta;
+  int64_t M, N, K;
+  void *out;
+  int out_kind;
+};
+hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream);
+
+// Largest M and K the fused skinny kernel accepts.
+constexpr int64_t kFusedMaxM = 16;
+constexpr int64_t kFusedMaxK = 8192;
+constexpr int64_t kSkinnyMaxM = 16;
+
+}  // namespace bl

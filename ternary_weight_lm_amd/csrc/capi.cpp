@@ -1,0 +1,231 @@
+// capi.cpp -- the extern "C" boundary of libbitlinear.so.
+//
+// Every entry point validates all of its arguments on the host before it
+// launches anything (so a rejected call touches no memory and needs no GPU),
+// then dispatches to the kernel launchers in bl_launch.h.  No exception
+// crosses the boundary; every failure is a negative status code.
+#include <cmath>
+#include <cstdint>
+
+#include "bitlinear.h"
+#include "bl_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;
+constexpr int64_t kMaxN = int64_t(1) << 20;
+constexpr int64_t kMaxM = int64_t(1) << 24;
+// dynamic LDS the fused skinny kernel may use: 64 KiB minus its static part
+constexpr int64_t kFusedLdsBytes = 65536 - 8320;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == BL_F32 || dt == BL_F16 || dt == BL_BF16; }
+
+bool nk_ok(int64_t N, int64_t K) {
+  return K >= 128 && K <= kMaxK && K % 128 == 0 && N >= 32 && N <= kMaxN && N % 32 == 0;
+}
+
+bool m_ok(int64_t M) { return M >= 0 && M <= kMaxM; }
+
+bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+// Forward workspace: xq [M, K] int8 | s [M] fp32 | rowsum [M] int32.
+struct FwdWs {
+  int8_t *xq;
+  float *s;
+  int32_t *rowsum;
+};
+
+size_t fwd_ws_bytes(int64_t M, int64_t K) {
+  return align256((size_t)(M * K)) + 2 * align256((size_t)M * 4);
+}
+
+FwdWs carve(void *ws, int64_t M, int64_t K) {
+  char *b = static_cast<char *>(ws);
+  FwdWs w;
+  w.xq = reinterpret_cast<int8_t *>(b);
+  b += align256((size_t)(M * K));
+  w.s = reinterpret_cast<float *>(b);
+  b += align256((size_t)M * 4);
+  w.rowsum = reinterpret_cast<int32_t *>(b);
+  return w;
+}
+
+bool fused_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= bl::kFusedMaxM && K <= bl::kFusedMaxK && M * (K + 16) <= kFusedLdsBytes;
+}
+
+// Default path by token count.
+int auto_path(int64_t M, int64_t K) {
+  if (M <= 4 && fused_fits(M, K)) return BL_PATH_FUSED;
+  if (M <= bl::kSkinnyMaxM) return BL_PATH_SKINNY;
+  return BL_PATH_MFMA;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bitlinear_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "null pointer";
+    case BL_ERR_DTYPE: return "unsupported dtype";
+    case BL_ERR_SHAPE: return "unsupported shape";
+    case BL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case BL_ERR_WORKSPACE: return "workspace missing or too small";
+    case BL_ERR_EPS: return "eps must be finite and > 0";
+    case BL_ERR_HIP: return "HIP launch failed";
+    case BL_ERR_UNSUPPORTED: return "unsupported request";
+    case BL_ERR_PATH: return "unknown or inapplicable execution path";
+    default: return "unknown status";
+  }
+}
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  return nk_ok(N, K) ? (size_t)(N * K / 4) : 0;
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+  return nk_ok(N, K) ? bl::pack_workspace_bytes() : 0;
+}
+
+int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, void *packed,
+                           float *beta, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!nk_ok(N, K)) return BL_ERR_SHAPE;
+  if (!W || !packed || !beta) return BL_ERR_NULL;
+  if (!ws || ws_bytes < bl::pack_workspace_bytes()) return BL_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  return hip_status(bl::launch_pack(W, N, K, packed, beta, ws, stream));
+}
+
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (!nk_ok(N, K) || !m_ok(M)) return 0;
+  return fwd_ws_bytes(M, K);
+}
+
+int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
+                           const void *gain, const void *packed,
+                           const float *beta, int64_t N, void *y, int y_dtype,
+                           float eps, void *ws, size_t ws_bytes, int path,
+                           hipStream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (path < BL_PATH_AUTO || path > BL_PATH_MFMA) return BL_ERR_PATH;
+  if (M == 0) return BL_OK;
+  if (!x || !gain || !packed || !beta || !y) return BL_ERR_NULL;
+  if (!ws || ws_bytes < fwd_ws_bytes(M, K)) return BL_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(packed) || !aligned16(y) ||
+      !aligned16(ws) || (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  if (path == BL_PATH_AUTO) path = auto_path(M, K);
+  if (path == BL_PATH_FUSED && !fused_fits(M, K)) return BL_ERR_SHAPE;
+  if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
+
+  if (path == BL_PATH_FUSED) {
+    bl::SkinnyArgs a{};
+    a.fused = true;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    a.gain = gain;
+    a.eps = eps;
+    a.packed = packed;
+    a.beta = beta;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.out = y;
+    a.out_kind = y_dtype;
+    return hip_status(bl::launch_skinny(a, stream));
+  }
+  const FwdWs w = carve(ws, M, K);
+  hipError_t e = bl::launch_act_quant(x, x_dtype, gain, M, K, eps, w.xq, w.s, w.rowsum, stream);
+  if (e != hipSuccess) return BL_ERR_HIP;
+  if (path == BL_PATH_SKINNY) {
+    bl::SkinnyArgs a{};
+    a.fused = false;
+    a.xq = w.xq;
+    a.s = w.s;
+    a.rowsum = w.rowsum;
+    a.packed = packed;
+    a.beta = beta;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.out = y;
+    a.out_kind = y_dtype;
+    return hip_status(bl::launch_skinny(a, stream));
+  }
+  return hip_status(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
+                                         y_dtype, stream));
+}
+
+int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
+                      const void *gain, const void *packed, const float *beta,
+                      int64_t N, void *y, int y_dtype, float eps, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return bitlinear_forward_path(x, x_dtype, M, K, gain, packed, beta, N, y, y_dtype, eps, ws,
+                                ws_bytes, BL_PATH_AUTO, stream);
+}
+
+int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
+                        int64_t M, int64_t K, float eps, int8_t *xq, float *s,
+                        int32_t *rowsum, hipStream_t stream) {
+  if (!dtype_ok(x_dtype)) return BL_ERR_DTYPE;
+  if (!m_ok(M) || K < 128 || K > kMaxK || K % 128 != 0) return BL_ERR_SHAPE;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (M == 0) return BL_OK;
+  if (!x || !gain || !xq || !s || !rowsum) return BL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(xq) ||
+      (reinterpret_cast<uintptr_t>(s) & 3u) || (reinterpret_cast<uintptr_t>(rowsum) & 3u))
+    return BL_ERR_ALIGN;
+  return hip_status(bl::launch_act_quant(x, x_dtype, gain, M, K, eps, xq, s, rowsum, stream));
+}
+
+int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
+                       int64_t K, const void *packed, int64_t N, int32_t *acc,
+                       int path, hipStream_t stream) {
+  if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (path != BL_PATH_AUTO && path != BL_PATH_SKINNY && path != BL_PATH_MFMA) return BL_ERR_PATH;
+  if (M == 0) return BL_OK;
+  if (!xq || !rowsum || !packed || !acc) return BL_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(packed) || !aligned16(acc) ||
+      (reinterpret_cast<uintptr_t>(rowsum) & 3u))
+    return BL_ERR_ALIGN;
+  if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
+  if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
+  if (path == BL_PATH_SKINNY) {
+    bl::SkinnyArgs a{};
+    a.fused = false;
+    a.xq = xq;
+    a.rowsum = rowsum;
+    a.packed = packed;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.out = acc;
+    a.out_kind = bl::kOutI32;
+    return hip_status(bl::launch_skinny(a, stream));
+  }
+  return hip_status(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
+                                         bl::kOutI32, stream));
+}
+
+int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
+                             int8_t *Wq, hipStream_t stream) {
+  if (!nk_ok(N, K)) return BL_ERR_SHAPE;
+  if (!packed || !Wq) return BL_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(Wq)) return BL_ERR_ALIGN;
+  return hip_status(bl::launch_unpack(packed, N, K, Wq, stream));
+}
+
+}  // extern "C"

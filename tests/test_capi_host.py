@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point include/bitlinear.h declares, answers the size queries with
+their closed forms, and rejects every malformed call with the documented
+status before launching anything (so made-up pointers are never touched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_lm_amd as tw
+from ternary_weight_lm_amd import _lib
+
+OK, NULL, DTYPE, SHAPE, ALIGN, WS, EPS, HIP, UNSUP, PATH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+# made-up, 16-byte aligned device addresses: validation fails before any use
+A = 0x7F0000001000
+B = 0x7F0000002000
+C = 0x7F0000003000
+D = 0x7F0000004000
+E = 0x7F0000005000
+Y = 0x7F0000006000
+WSP = 0x7F0000100000
+
+
+def declared_functions():
+    text = open(_lib.HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tw.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_size_queries_closed_forms():
+    L = tw.lib()
+    for N, K in [(32, 128), (1024, 1024), (11264, 2048), (2048, 5632), (2560, 7040)]:
+        assert L.bitlinear_packed_bytes(N, K) == N * K // 4
+        assert L.bitlinear_pack_workspace_bytes(N, K) > 0
+    for bad in [(16, 128), (32, 64), (33, 128), (32, 130), (0, 128), (32, 0),
+                (32, 65536 + 128), ((1 << 20) + 32, 128)]:
+        assert L.bitlinear_packed_bytes(*bad) == 0
+        assert L.bitlinear_pack_workspace_bytes(*bad) == 0
+
+    def al(v):
+        return (v + 255) // 256 * 256
+    for M, K, N in [(1, 1024, 1024), (16, 1024, 1024), (4096, 2048, 11264), (3, 7040, 2560)]:
+        assert L.bitlinear_workspace_bytes(M, K, N) == al(M * K) + 2 * al(4 * M)
+    assert L.bitlinear_workspace_bytes(-1, 128, 32) == 0
+    assert L.bitlinear_workspace_bytes((1 << 24) + 1, 128, 32) == 0
+    assert L.bitlinear_workspace_bytes(0, 128, 32) == 2 * 0 + 0
+
+
+def test_status_strings():
+    L = tw.lib()
+    for code in (OK, NULL, DTYPE, SHAPE, ALIGN, WS, EPS, HIP, UNSUP, PATH, 12345):
+        s = L.bitlinear_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def fwd(x=A, xdt=1, M=4, K=1024, g=B, pk=C, beta=D, N=1024, y=Y, ydt=1, eps=1e-8,
+        ws=WSP, wsb=None, path=0):
+    L = tw.lib()
+    if wsb is None:
+        wsb = L.bitlinear_workspace_bytes(M, K, N) if M >= 0 else 0
+    return L.bitlinear_forward_path(x, xdt, M, K, g, pk, beta, N, y, ydt, eps, ws, wsb, path, None)
+
+
+def test_forward_validation_order_and_codes():
+    assert fwd(xdt=3) == DTYPE
+    assert fwd(ydt=-1) == DTYPE
+    assert fwd(K=1000) == SHAPE
+    assert fwd(K=0) == SHAPE
+    assert fwd(N=48) == SHAPE
+    assert fwd(M=-1) == SHAPE
+    assert fwd(M=(1 << 24) + 1) == SHAPE
+    assert fwd(K=65536 + 128) == SHAPE
+    assert fwd(eps=0.0) == EPS
+    assert fwd(eps=-1e-8) == EPS
+    assert fwd(eps=float("nan")) == EPS
+    assert fwd(eps=float("inf")) == EPS
+    assert fwd(path=7) == PATH
+    assert fwd(path=-1) == PATH
+    # empty batch: a valid no-op, even with no buffers at all
+    assert fwd(M=0, x=None, y=None, ws=None, wsb=0) == OK
+    for kw in ("x", "g", "pk", "beta", "y"):
+        assert fwd(**{kw: None}) == NULL, kw
+    assert fwd(ws=None) == WS
+    assert fwd(wsb=100) == WS
+    for kw in ("x", "g", "pk", "y", "ws"):
+        assert fwd(**{kw: {"x": A, "g": B, "pk": C, "y": Y, "ws": WSP}[kw] + 8}) == ALIGN, kw
+    assert fwd(beta=D + 2) == ALIGN
+    # path limits
+    assert fwd(M=17, path=1) == SHAPE
+    assert fwd(M=17, path=2) == SHAPE
+    assert fwd(M=16, K=8192, path=1) == SHAPE   # fused LDS budget exceeded
+    assert fwd(M=1, K=8320, path=1) == SHAPE    # fused K limit
+
+
+def test_forward_default_entry_point_validates_the_same_way():
+    L = tw.lib()
+    ws = L.bitlinear_workspace_bytes(4, 1024, 1024)
+    assert L.bitlinear_forward(A, 1, 4, 1000, B, C, D, 1024, Y, 1, 1e-8, WSP, ws, None) == SHAPE
+    assert L.bitlinear_forward(A, 1, 4, 1024, B, C, D, 1024, Y, 1, 0.0, WSP, ws, None) == EPS
+    assert L.bitlinear_forward(None, 1, 4, 1024, B, C, D, 1024, Y, 1, 1e-8, WSP, ws, None) == NULL
+    assert L.bitlinear_forward(A, 1, 0, 1024, B, C, D, 1024, Y, 1, 1e-8, None, 0, None) == OK
+
+
+def test_pack_validation():
+    L = tw.lib()
+    wsb = L.bitlinear_pack_workspace_bytes(64, 256)
+    assert L.bitlinear_pack_weights(A, 48, 256, C, D, WSP, wsb, None) == SHAPE
+    assert L.bitlinear_pack_weights(A, 64, 200, C, D, WSP, wsb, None) == SHAPE
+    assert L.bitlinear_pack_weights(None, 64, 256, C, D, WSP, wsb, None) == NULL
+    assert L.bitlinear_pack_weights(A, 64, 256, None, D, WSP, wsb, None) == NULL
+    assert L.bitlinear_pack_weights(A, 64, 256, C, None, WSP, wsb, None) == NULL
+    assert L.bitlinear_pack_weights(A, 64, 256, C, D, None, wsb, None) == WS
+    assert L.bitlinear_pack_weights(A, 64, 256, C, D, WSP, wsb - 1, None) == WS
+    assert L.bitlinear_pack_weights(A + 4, 64, 256, C, D, WSP, wsb, None) == ALIGN
+    assert L.bitlinear_pack_weights(A, 64, 256, C + 4, D, WSP, wsb, None) == ALIGN
+    assert L.bitlinear_pack_weights(A, 64, 256, C, D + 1, WSP, wsb, None) == ALIGN
+
+
+def test_stage_entry_points_validation():
+    L = tw.lib()
+    assert L.bitlinear_act_quant(A, 5, B, 4, 1024, 1e-8, C, D, E, None) == DTYPE
+    assert L.bitlinear_act_quant(A, 1, B, 4, 1000, 1e-8, C, D, E, None) == SHAPE
+    assert L.bitlinear_act_quant(A, 1, B, 4, 1024, 0.0, C, D, E, None) == EPS
+    assert L.bitlinear_act_quant(A, 1, B, 4, 1024, 1e-8, None, D, E, None) == NULL
+    assert L.bitlinear_act_quant(A, 1, B, 4, 1024, 1e-8, C + 8, D, E, None) == ALIGN
+    assert L.bitlinear_act_quant(A, 1, B, 0, 1024, 1e-8, None, None, None, None) == OK
+    assert L.bitlinear_gemm_i32(A, B, 4, 1024, C, 1000, D, 0, None) == SHAPE
+    assert L.bitlinear_gemm_i32(A, B, 4, 1024, C, 1024, D, 1, None) == PATH
+    assert L.bitlinear_gemm_i32(A, B, 17, 1024, C, 1024, D, 2, None) == SHAPE
+    assert L.bitlinear_gemm_i32(None, B, 4, 1024, C, 1024, D, 0, None) == NULL
+    assert L.bitlinear_gemm_i32(A, B + 2, 4, 1024, C, 1024, D, 0, None) == ALIGN
+    assert L.bitlinear_unpack_weights(C, 32, 100, D, None) == SHAPE
+    assert L.bitlinear_unpack_weights(None, 32, 128, D, None) == NULL
+    assert L.bitlinear_unpack_weights(C, 32, 128, D + 8, None) == ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        _lib._ptr(x)
+
+
+def test_missing_library_is_an_error(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError):
+        _lib.lib()

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, on
+seeded inputs at sizes the oracle finishes in seconds, spanning several
+tiles, ragged token counts, partial 128-wide output tiles and K-block counts
+that do not divide evenly among the waves."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ternary_weight_lm_amd as tw
+from ternary_weight_lm_amd import synth
+from tests.parity import (DEV, check_pack, check_xq, check_y, gpu_act_quant,
+                          run_forward, say, y_to_np)
+
+pytestmark = pytest.mark.gpu
+
+PACK_SHAPES = [(32, 128), (64, 384), (96, 1024), (1024, 1024), (160, 1280), (2048, 5632)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_pack_bit_exact(N, K):
+    say(f"pack N={N} K={K}")
+    W = synth.make_w(101, 0, N, N, K, zero_row_frac=0.05 if N >= 64 else 0.0)
+    (o_packed, o_beta, o_Wq), (d_packed, d_beta) = check_pack(W)
+    # decoding the device bytes gives the oracle's ternary matrix
+    Wq = torch.empty(N, K, dtype=torch.int8, device=DEV)
+    tw.bitlinear_unpack_weights(d_packed, N, K, Wq)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wq.cpu().numpy(), o_Wq)
+
+
+def test_pack_exact_ties_and_extremes():
+    """A matrix whose mean |W| is exactly 2^-6 and that holds entries at
+    exactly beta/2 (round half to even -> 0) and one ulp above (-> +-1)."""
+    say("pack ties")
+    N, K = 64, 256
+    r = np.random.default_rng(5)
+    c = np.float32(2.0 ** -6)
+    W = (np.where(r.random((N, K)) < 0.5, -1.0, 1.0) * c).astype(np.float32)
+    half = np.float32(2.0 ** -7)
+    up = np.nextafter(half, np.float32(1))
+    W[0, :6] = [half, -half, up, -up, np.float32(2.0 ** -5),
+                np.nextafter(np.float32(2.0 ** -5), np.float32(0))]
+    assert np.abs(W.astype(np.float64)).sum() == 256.0      # mean exactly 2^-6
+    (o_packed, o_beta, o_Wq), _ = check_pack(torch.from_numpy(W))
+    assert o_beta == c
+    np.testing.assert_array_equal(o_Wq[0, :6], [0, 0, 1, -1, 1, 1])
+    # all-zero matrix: the scale floor, every code zero
+    (_, zb, zq), _ = check_pack(torch.zeros(N, K))
+    assert zb == np.float32(1e-5) and not zq.any()
+    # huge magnitudes: the scale follows them, the largest saturate at +-1
+    Wx = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wx[5, :4] = [1e30, -1e30, 3e38, -3e38]
+    (_, _, xq_), _ = check_pack(torch.from_numpy(Wx))
+    np.testing.assert_array_equal(xq_[5, :4], [0, 0, 1, -1])
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (33, 1280), (64, 2048), (7, 7040)])
+def test_act_quant(dtype, M, K):
+    say(f"act_quant {dtype} M={M} K={K}")
+    x = synth.make_x(7, 0, 0, M, K, dtype, outlier_p=0.01)
+    g = synth.make_gain(7, 0, 0, K, dtype)
+    if M >= 5:
+        x[3] = 0        # all-zero row
+        x[4] = x[4] * 1e-4
+    xq, s, rs = gpu_act_quant(x.to(DEV), g.to(DEV))
+    xn, _ = oracle.rmsnorm(synth.widen(x), synth.widen(g))
+    oq, os_, ov = oracle.act_quant(xn)
+    ref = {"xq": oq, "s": os_, "v": ov}
+    check_xq(xq, s, ref)
+    np.testing.assert_array_equal(rs, xq.astype(np.int64).sum(1))
+
+
+def _random_codes(M, K, seed):
+    r = np.random.default_rng(seed)
+    xq = r.integers(-128, 128, size=(M, K)).astype(np.int8)
+    xq[0, :] = 127
+    if M > 1:
+        xq[1, :] = -128
+    return xq
+
+
+@pytest.mark.parametrize("path", [tw.BL_PATH_SKINNY, tw.BL_PATH_MFMA])
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (3, 96, 384), (16, 160, 1280),
+                                   (17, 160, 1280), (33, 1024, 1024), (130, 96, 640),
+                                   (16, 64, 7040), (200, 256, 2048)])
+def test_gemm_i32_bit_exact(path, M, N, K):
+    if path == tw.BL_PATH_SKINNY and M > 16:
+        pytest.skip("skinny path is for M <= 16")
+    say(f"gemm_i32 path={path} M={M} N={N} K={K}")
+    xq = _random_codes(M, K, M * 7 + K)
+    r = np.random.default_rng(N + K)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wq[N // 3] = 0
+    Wq[N // 2] = 1
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc, path=path)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
+
+
+FWD_CASES = [
+    # path, M, N, K, x dtype, y dtype
+    (tw.BL_PATH_FUSED, 1, 1024, 1024, "fp16", "fp16"),
+    (tw.BL_PATH_FUSED, 3, 160, 1280, "bf16", "bf16"),
+    (tw.BL_PATH_FUSED, 16, 96, 384, "fp32", "fp32"),
+    (tw.BL_PATH_FUSED, 2, 64, 7040, "bf16", "fp32"),
+    (tw.BL_PATH_SKINNY, 1, 160, 1280, "fp16", "fp16"),
+    (tw.BL_PATH_SKINNY, 11, 1024, 1024, "bf16", "bf16"),
+    (tw.BL_PATH_SKINNY, 16, 64, 2048, "fp32", "fp16"),
+    (tw.BL_PATH_MFMA, 1, 96, 384, "fp16", "fp16"),
+    (tw.BL_PATH_MFMA, 17, 160, 1280, "bf16", "bf16"),
+    (tw.BL_PATH_MFMA, 33, 1024, 1024, "fp32", "fp32"),
+    (tw.BL_PATH_MFMA, 130, 256, 640, "fp16", "bf16"),
+    (tw.BL_PATH_MFMA, 257, 128, 2048, "bf16", "bf16"),
+    (tw.BL_PATH_AUTO, 1, 1024, 1024, "fp16", "fp16"),
+    (tw.BL_PATH_AUTO, 8, 256, 2560, "bf16", "bf16"),
+    (tw.BL_PATH_AUTO, 64, 256, 2560, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("path,M,N,K,xdt,ydt", FWD_CASES)
+def test_forward_matches_oracle(path, M, N, K, xdt, ydt):
+    say(f"forward path={path} M={M} N={N} K={K} x={xdt} y={ydt}")
+    seed = 1000 + M * 13 + N + K
+    x = synth.make_x(seed, 0, 0, M, K, xdt, outlier_p=0.01)
+    g = synth.make_gain(seed, 0, 0, K, xdt)
+    if M >= 3:
+        x[2] = 0
+    W = synth.make_w(seed, 0, 0, N, K, zero_row_frac=0.05)
+    (o_packed, o_beta, o_Wq), (d_packed, d_beta) = check_pack(W)
+    y, x_dev, g_dev = run_forward(x, g, d_packed, d_beta, N, ydt, path=path)
+    ref = oracle.forward(synth.widen(x), synth.widen(g), o_Wq, o_beta)
+    xq_gpu, s_gpu, _ = gpu_act_quant(x_dev, g_dev)
+    check_xq(xq_gpu, s_gpu, ref)
+    check_y(y, ref, ydt, Wq=o_Wq, beta=o_beta, xq_gpu=xq_gpu, s_gpu=s_gpu)
+    # zeroed weight rows give exact zeros
+    zero_rows = np.nonzero(~o_Wq.any(axis=1))[0]
+    assert np.all(y[:, zero_rows] == 0.0)
+    if M >= 3:
+        assert np.all(y[2] == 0.0)
+
+
+def test_paths_agree_and_repeat_bitwise():
+    say("paths agree")
+    M, N, K = 4, 512, 2048
+    x = synth.make_x(77, 0, 0, M, K, "fp16")
+    g = synth.make_gain(77, 0, 0, K, "fp16")
+    W = synth.make_w(77, 0, 0, N, K)
+    packed, beta = tw.pack(W.to(DEV))
+    xd, gd = x.to(DEV), g.to(DEV)
+    outs = [tw.forward(xd, gd, packed, beta, N, path=p)
+            for p in (tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY, tw.BL_PATH_MFMA, tw.BL_PATH_FUSED)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_empty_batch_is_noop():
+    say("empty batch")
+    N, K = 64, 256
+    packed, beta = tw.pack(synth.make_w(3, 0, 0, N, K).to(DEV))
+    x = torch.empty(0, K, dtype=torch.float16, device=DEV)
+    g = torch.ones(K, dtype=torch.float16, device=DEV)
+    y = tw.forward(x, g, packed, beta, N)
+    torch.cuda.synchronize()
+    assert y.shape == (0, N)
