@@ -1,0 +1,451 @@
+#!/usr/bin/env python3
+"""FusedBitLinear benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the whole hot path -- RMSNorm, per-token int8
+quantization, ternary contraction against pre-packed 2-bit weights and the
+rescale -- over every projection of the workload, on seeded synthetic inputs
+already resident in HBM.  Default workload: the 370M-shaped attention
+projections at decode (M = 1 token, four 1024 -> 1024 FusedBitLinear layers,
+fp16 activations).  Other workloads (--workload c1 | c3 | c4 | c5-M<M>) are
+the parity configurations, measurable the same way.
+
+Method
+  * Weights come from a rotating pool of distinct packed copies of at least
+    --pool-mib MiB (default 1024 MiB, four times the 256 MiB Infinity Cache),
+    so every step streams its weights from HBM.
+  * Steps are captured into HIP graphs (chunks of at most 512 steps);
+    W warm-up steps are replayed untimed, then exactly K steps are timed
+    with events on the replay stream, bracketed by device synchronization.
+  * Roofline of the dominant kernel: a second graph holding only that
+    kernel's launches is timed the same way, giving its average duration
+    (this matches rocprofv3's per-kernel average); algorithmic bytes (packed
+    weights + x + gain + y + beta) or ops (2 M N K) per launch over it give
+    `achieved`.
+  * cpu_baseline: the plain C oracle, single-threaded, on the same inputs,
+    timed for about --cpu-seconds on the host.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FusedBitLinear tokens/s; decode HBM GB/s & prefill int8 TOPS as % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA
+GRAPH_CHUNK = 512             # at most this many steps per captured graph
+GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c2",
+                    help="c1 | c2 | c3 | c4 | c5-M1 | c5-M8 | c5-M64 | c5-M512 | c5-M8192")
+    ap.add_argument("--pool-mib", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-reps", type=int, default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy three times "
+                         "(reference for the HBM byte counters) and exit")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+    the scale between counter units and bytes."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 3}), flush=True)
+
+
+# ---------------------------------------------------------------- workload
+
+class Workload:
+    def __init__(self, key: str):
+        from ternary_weight_lm_amd import synth
+        if key.startswith("c5"):
+            cfg = synth.CONFIGS["c5"]
+            M = int(key.split("-M")[1]) if "-M" in key else 1
+            assert M in cfg.M_list, f"c5 runs at M in {cfg.M_list}"
+            layers = cfg.layers
+        else:
+            cfg = synth.CONFIGS[key]
+            M = cfg.M_list[0]
+            layers = cfg.layers
+        self.key, self.cfg, self.M, self.layers = key, cfg, M, layers
+        # (layer, projection index) for every call of a step
+        self.calls = [(l, i) for l in range(layers) for i in range(len(cfg.projs))]
+
+    def groups(self):
+        """Launch groups of a step: the i/f/g projections of one layer read
+        the same block input in HGRNBit, so when they all take the fused
+        decode path they go out as one grouped launch; every other projection
+        (o_proj after the recurrence, the MLP pair) is launched on its own."""
+        import ternary_weight_lm_amd as tw
+        out, cur = [], []
+        for j, (layer, pi) in enumerate(self.calls):
+            name = self.cfg.projs[pi].name
+            fused = tw.bitlinear_select_path(self.M, self.cfg.projs[pi].K) == tw.BL_PATH_FUSED
+            if fused and name in ("i_proj", "f_proj", "g_proj") and (
+                    not cur or self.calls[cur[0]][0] == layer):
+                cur.append(j)
+                continue
+            if cur:
+                out.append(cur)
+                cur = []
+            if fused and name in ("i_proj", "f_proj", "g_proj"):
+                cur = [j]
+            else:
+                out.append([j])
+        if cur:
+            out.append(cur)
+        return out
+
+    def shape(self, call):
+        p = self.cfg.projs[call[1]]
+        return p.K, p.N
+
+    def describe(self):
+        projs = [f"{p.name} {p.K}->{p.N}" for p in self.cfg.projs]
+        return {"workload": self.cfg.name + ("" if not self.key.startswith("c5") else f"_M{self.M}"),
+                "tokens_per_step": self.M, "layers": self.layers, "projections": projs,
+                "x_dtype": self.cfg.dtype, "y_dtype": self.cfg.y_dtype}
+
+
+def build_inputs(wl: Workload, pool_bytes: int, dev):
+    """Device inputs: x and gain per (layer-shared) projection, a pool of
+    packed weight copies, per-call beta, outputs and workspaces."""
+    import torch
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+
+    cfg, M = wl.cfg, wl.M
+    xs, gs, host = {}, {}, {}
+    packed, betas = [], []
+    for call in wl.calls:
+        layer, pi = call
+        x, g, W = synth.config_inputs(cfg, M, layer, pi)
+        key = (0 if wl.layers > 1 else layer, pi)
+        if key not in xs:
+            xs[key] = x.to(dev)
+        gs[call] = g.to(dev)
+        pk, beta = tw.pack(W.to(dev))
+        packed.append(pk)
+        betas.append(beta)
+        if wl.layers == 1 or layer in (0, wl.layers - 1):
+            host[("W",) + call] = (x, g, W)       # oracle sample
+        del W
+    set_bytes = sum(p.numel() for p in packed)
+    copies = max(1, math.ceil(pool_bytes / set_bytes))
+    pool = []
+    for c in range(copies):
+        pool.append([p if c == 0 else p.clone() for p in packed])
+    # outputs and workspaces are shared by the layers of a projection type:
+    # each layer's output is consumed before the next layer runs
+    ydt = synth.DTYPES[cfg.y_dtype]
+    per_type_y = {pi: torch.empty(M, p.N, dtype=ydt, device=dev) for pi, p in enumerate(cfg.projs)}
+    per_type_ws = {pi: tw.workspace(M, p.K, p.N, device=dev) for pi, p in enumerate(cfg.projs)}
+    ys = [per_type_y[c[1]] for c in wl.calls]
+    wss = [per_type_ws[c[1]] for c in wl.calls]
+    torch.cuda.synchronize()
+    return {"xs": xs, "gs": gs, "pool": pool, "betas": betas, "ys": ys, "wss": wss,
+            "set_bytes": set_bytes, "copies": copies, "host": host, "groups": wl.groups()}
+
+
+def step_fn(wl, inp, s, keep):
+    """Enqueue one step (weights from pool copy s).  `keep` collects the
+    ctypes descriptor arrays so they outlive graph capture."""
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+    pool = inp["pool"][s % inp["copies"]]
+    for grp in inp["groups"]:
+        if len(grp) > 1:
+            items = []
+            for j in grp:
+                call = wl.calls[j]
+                x = inp["xs"][(0 if wl.layers > 1 else call[0], call[1])]
+                items.append((x, inp["gs"][call], pool[j], inp["betas"][j], inp["ys"][j]))
+            arr = tw.make_calls(items)
+            keep.append(arr)
+            tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
+                                         synth.DTYPES[wl.cfg.y_dtype])
+            continue
+        j = grp[0]
+        call = wl.calls[j]
+        K, N = wl.shape(call)
+        x = inp["xs"][(0 if wl.layers > 1 else call[0], call[1])]
+        tw.bitlinear_forward(x, inp["gs"][call], pool[j], inp["betas"][j], N, inp["ys"][j],
+                             inp["wss"][j])
+
+
+def capture(wl, inp, first, count):
+    import torch
+    graphs = []
+    s = first
+    per_step = sum(1 if len(grp) > 1 else 2 for grp in inp["groups"])  # upper bound
+    chunk = max(1, min(GRAPH_CHUNK, GRAPH_MAX_LAUNCHES // per_step))
+    while count > 0:
+        n = min(count, chunk)
+        g = torch.cuda.CUDAGraph()
+        keep = []
+        with torch.cuda.graph(g):
+            for k in range(n):
+                step_fn(wl, inp, s + k, keep)
+        graphs.append((g, n))
+        s += n
+        count -= n
+    return graphs
+
+
+# ---------------------------------------------------------------- roofline
+
+def algorithmic(wl, call):
+    """Bytes (packed W + x + gain + y + beta) and ops (2 M N K) of one call."""
+    from ternary_weight_lm_amd import synth
+    import torch
+    K, N = wl.shape(call)
+    xb = torch.tensor([], dtype=synth.DTYPES[wl.cfg.dtype]).element_size()
+    yb = torch.tensor([], dtype=synth.DTYPES[wl.cfg.y_dtype]).element_size()
+    M = wl.M
+    byt = N * K // 4 + M * K * xb + K * xb + M * N * yb + 4
+    return byt, 2 * M * N * K
+
+
+def roofline_from_steps(wl, inp, steps, ms):
+    """Fused decode path: every launch of a step is the dominant kernel, so
+    the timed steps themselves give its average duration."""
+    import ternary_weight_lm_amd as tw
+    launches = steps * len(inp["groups"])
+    sec = ms / 1e3
+    byt = sum(algorithmic(wl, c)[0] for c in wl.calls) * steps
+    ops = sum(algorithmic(wl, c)[1] for c in wl.calls) * steps
+    ach = byt / sec / 1e9
+    grouped = any(len(g) > 1 for g in inp["groups"])
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 5), "traffic": None,
+            "kernel": "bl::skinny_kernel<fused=true> (norm+quant+contract+rescale)"
+                      + (", i/f/g grouped per launch" if grouped else ""),
+            "launches": launches, "avg_kernel_us": round(sec * 1e6 / launches, 3),
+            "algorithmic_bytes_per_launch": round(byt / launches, 1),
+            "ops_per_launch": round(ops / launches, 1),
+            "timed_region": "the benchmark steps themselves (one kernel per launch)"}
+
+
+def roofline(wl, inp, reps):
+    """Average duration of the dominant kernel: a HIP graph holding only its
+    launches (reps passes over every call, weights rotating through the
+    pool) is timed with events on the replay stream.  For the two-kernel
+    paths the activations are quantized once beforehand, so the graph holds
+    nothing but contraction launches."""
+    import torch
+    import ternary_weight_lm_amd as tw
+    path = tw.bitlinear_select_path(wl.M, wl.shape(wl.calls[0])[0])
+    bound = "hbm" if path in (tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY) else "mfma"
+    ncalls = len(wl.calls)
+    stage = {}
+    if path != tw.BL_PATH_FUSED:
+        for j, call in enumerate(wl.calls):
+            K, N = wl.shape(call)
+            xkey = (0 if wl.layers > 1 else call[0], call[1])
+            if xkey not in stage:
+                xq = torch.empty(wl.M, K, dtype=torch.int8, device="cuda")
+                sc = torch.empty(wl.M, dtype=torch.float32, device="cuda")
+                rs = torch.empty(wl.M, dtype=torch.int32, device="cuda")
+                tw.bitlinear_act_quant(inp["xs"][xkey], inp["gs"][call], xq, sc, rs)
+                stage[xkey] = (xq, sc, rs)
+
+    def launch(r):
+        s, j = divmod(r, ncalls)
+        call = wl.calls[j]
+        K, N = wl.shape(call)
+        pk = inp["pool"][(s + 7) % inp["copies"]][j]
+        xkey = (0 if wl.layers > 1 else call[0], call[1])
+        if path == tw.BL_PATH_FUSED:
+            tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j], N,
+                                      inp["ys"][j], inp["wss"][j], path)
+        else:
+            xq, sc, rs = stage[xkey]
+            tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
+
+    total = reps * ncalls
+    graphs = []
+    r = 0
+    while r < total:
+        n = min(total - r, GRAPH_MAX_LAUNCHES)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for q in range(r, r + n):
+                launch(q)
+        graphs.append(g)
+        r += n
+    graphs[0].replay()                      # warm the replay path
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for g in graphs:
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3
+    byt = ops = 0
+    for call in wl.calls:
+        cb, co = algorithmic(wl, call)
+        byt += cb * reps
+        ops += co * reps
+    kernel = {tw.BL_PATH_FUSED: "bl::skinny_kernel<fused=true> (norm+quant+contract+rescale)",
+              tw.BL_PATH_SKINNY: "bl::skinny_kernel<fused=false> (contract+rescale)",
+              tw.BL_PATH_MFMA: "bl::gemm_mfma_kernel (contract+rescale)"}[path]
+    if bound == "hbm":
+        ach = byt / sec / 1e9
+        out = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(ach / HBM_PEAK_GBS, 5)}
+    else:
+        ach = ops / sec / 1e12
+        out = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+               "frac": round(ach / I8_PEAK_TOPS, 5)}
+    out["traffic"] = None
+    out["kernel"] = kernel
+    out["launches"] = total
+    out["avg_kernel_us"] = round(sec * 1e6 / total, 3)
+    out["algorithmic_bytes_per_launch"] = round(byt / total, 1)
+    out["ops_per_launch"] = round(ops / total, 1)
+    return out
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, inp, seconds):
+    """The oracle, as it stands, on one host core: full steps for the small
+    workloads, a fixed row sample for the large ones (tokens/s scaled by the
+    sampled row count; every row costs the same in the oracle)."""
+    import numpy as np
+    import oracle
+    from ternary_weight_lm_amd import synth
+
+    host = inp["host"]
+    rows = wl.M if wl.M <= 32 else 8
+    sample_calls = [c for c in wl.calls if ("W",) + c in host]
+    prepared = []
+    for call in sample_calls:
+        x, g, W = host[("W",) + call]
+        W = W.numpy()
+        _, beta, Wq = oracle.pack_weights(W)
+        xw = synth.widen(x)
+        sel = np.linspace(0, wl.M - 1, rows).round().astype(int)
+        prepared.append((xw[sel], synth.widen(g), Wq, beta))
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for xw, gw, Wq, beta in prepared:
+            oracle.forward(xw, gw, Wq, beta)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_pass = el / n                               # seconds for `rows` rows of sample_calls
+    per_token_all_calls = per_pass / rows * (len(wl.calls) / len(sample_calls))
+    return {"value": round(1.0 / per_token_all_calls, 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{n} passes of {rows} of {wl.M} token rows through "
+                       f"{len(sample_calls)} of {len(wl.calls)} projections "
+                       f"({el:.1f} s single-threaded on {platform.processor() or 'host'}; "
+                       f"scaled to every projection of a step)")}
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} / WORLD_SIZE {world} "
+              "is not supported (the FusedBitLinear hot path is measured per GPU; the "
+              "multi-GPU sharding design is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_weight_lm_amd as tw
+    tw.lib()                                  # fail loudly without the HIP library
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    dev = torch.device("cuda:0")
+
+    wl = Workload(args.workload)
+    big = wl.M >= 512 or wl.key == "c5-M64"
+    stack = wl.layers > 1
+    steps = args.steps if args.steps is not None else (20 if big else (100 if stack else 2000))
+    warmup = args.warmup if args.warmup is not None else (3 if big else (10 if stack else 100))
+    reps = args.roofline_reps if args.roofline_reps is not None else (
+        2 if big else (10 if stack else 200))
+
+    inp = build_inputs(wl, args.pool_mib << 20, dev)
+
+    warm_graphs = capture(wl, inp, 0, warmup) if warmup > 0 else []
+    timed_graphs = capture(wl, inp, warmup, steps)
+    for g, _ in warm_graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for g, _ in timed_graphs:
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / steps
+    tokens_per_s = wl.M * steps / (ms / 1e3)
+
+    import ternary_weight_lm_amd as tw
+    path = tw.bitlinear_select_path(wl.M, wl.shape(wl.calls[0])[0])
+    if path == tw.BL_PATH_FUSED:
+        roof = roofline_from_steps(wl, inp, steps, ms)
+    else:
+        roof = roofline(wl, inp, reps)
+        roof["timed_region"] = "a graph of the dominant kernel's launches only"
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": dict(wl.describe(), weight_pool_MiB=round(inp["set_bytes"] * inp["copies"] / 2**20, 1),
+                       weight_copies=inp["copies"],
+                       launch=f"hipGraph; {len(inp['groups'])} launches per step "
+                              f"({'i/f/g grouped' if any(len(g) > 1 for g in inp['groups']) else 'one per projection'})",
+                       parallelism="single GPU"),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

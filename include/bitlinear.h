@@ -148,7 +148,7 @@ int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
                       size_t ws_bytes, hipStream_t stream);
 
 /* Same as bitlinear_forward with an explicit execution path (BL_PATH_*).
- * BL_PATH_FUSED requires M <= 16, K <= 8192 and M * (K + 16) <= 57216 (its
+ * BL_PATH_FUSED requires M <= 16, K <= 8192 and M * (K + 16) <= 56320 (its
  * int8 activations live in LDS); BL_PATH_SKINNY requires M <= 16 (else
  * BL_ERR_SHAPE).  Every path computes the same function: the integer codes
  * and accumulators are identical, y may differ only where a pre-rounding
@@ -159,6 +159,35 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
                            const float *beta, int64_t N, void *y, int y_dtype,
                            float eps, void *ws, size_t ws_bytes, int path,
                            hipStream_t stream);
+
+/* The BL_PATH_FUSED / _SKINNY / _MFMA path bitlinear_forward takes for a
+ * token count M and in_features K (BL_ERR_SHAPE for an invalid M or K). */
+int bitlinear_select_path(int64_t M, int64_t K);
+
+/* One projection of a grouped forward (all pointers device, as in
+ * bitlinear_forward). */
+typedef struct bl_call {
+    const void *x;        /* [M, K], dtype x_dtype                       */
+    const void *gain;     /* [K], dtype x_dtype                          */
+    const void *packed;   /* packed weights of an [N, K] matrix          */
+    const float *beta;    /* per-tensor weight scale                     */
+    void *y;              /* [M, N], dtype y_dtype (written)             */
+    int64_t M, K, N;
+} bl_call;
+
+/* Several independent FusedBitLinear forwards in as few launches as
+ * possible (one launch per 16 calls), for decode steps where each call is
+ * too small to fill the GPU on its own -- e.g. the i/f/g/o projections of an
+ * HGRNBit block (hysenlabs ja review, section "HGRNBit という層構成を読む").
+ *   calls   HOST array of ncalls descriptors (read during the call only)
+ *   Every call must satisfy the BL_PATH_FUSED limits (M <= 16, K <= 8192,
+ *   M * (K + 16) <= 56320) and the usual shape / alignment rules, and all
+ *   share x_dtype, y_dtype and eps; calls with M == 0 are skipped.  No
+ *   workspace is needed.  Results equal bitlinear_forward on each call.
+ *   0 <= ncalls <= 4096; any invalid call rejects the whole group before
+ *   anything is launched. */
+int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
+                              int y_dtype, float eps, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(int status);
@@ -187,6 +216,18 @@ int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
  *           BL_PATH_FUSED is BL_ERR_PATH here. */
 int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                        int64_t K, const void *packed, int64_t N, int32_t *acc,
+                       int path, hipStream_t stream);
+
+/* Contraction + rescale from already quantized activations:
+ *   y[m, n] = (sum_k xq[m, k] * Wq[n, k]) * beta / s[m]
+ * (datacamp page above, section "MatMul durch ternäre Operationen
+ * ersetzen" and figure panel 4).  xq, s and rowsum are what
+ * bitlinear_act_quant writes; with them this is the second half of
+ * bitlinear_forward, so one quantized input can feed several projections.
+ *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 16) or BL_PATH_MFMA. */
+int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
+                       int64_t M, int64_t K, const void *packed,
+                       const float *beta, int64_t N, void *y, int y_dtype,
                        int path, hipStream_t stream);
 
 /* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device). */

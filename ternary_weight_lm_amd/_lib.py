@@ -37,6 +37,16 @@ class BitLinearError(RuntimeError):
 _lib = None
 
 P = ctypes.c_void_p
+
+
+class BlCall(ctypes.Structure):
+    """struct bl_call of bitlinear.h"""
+    _fields_ = [("x", ctypes.c_void_p), ("gain", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64)]
+
+
 I64 = ctypes.c_int64
 SZ = ctypes.c_size_t
 I = ctypes.c_int
@@ -49,9 +59,12 @@ SIGNATURES = {
     "bitlinear_workspace_bytes": ([I64, I64, I64], SZ),
     "bitlinear_forward": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, P], I),
     "bitlinear_forward_path": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
+    "bitlinear_forward_grouped": ([P, I, I, I, F, P], I),
     "bitlinear_status_string": ([I], ctypes.c_char_p),
+    "bitlinear_select_path": ([I64, I64], I),
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
+    "bitlinear_contract": ([P, P, P, I64, I64, P, P, I64, P, I, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
 }
 
@@ -109,6 +122,12 @@ def bitlinear_workspace_bytes(M: int, K: int, N: int) -> int:
     return int(lib().bitlinear_workspace_bytes(M, K, N))
 
 
+def bitlinear_select_path(M: int, K: int) -> int:
+    p = int(lib().bitlinear_select_path(M, K))
+    _check("bitlinear_select_path", min(p, 0))
+    return p
+
+
 def bitlinear_status_string(status: int) -> str:
     return lib().bitlinear_status_string(status).decode()
 
@@ -136,6 +155,26 @@ def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stre
         path, _stream(stream)))
 
 
+def make_calls(items):
+    """ctypes array of bl_call from (x, gain, packed, beta, y) tensor tuples."""
+    arr = (BlCall * len(items))()
+    for i, (x, gain, packed, beta, y) in enumerate(items):
+        M, K = x.shape
+        arr[i] = BlCall(_ptr(x), _ptr(gain), _ptr(packed), _ptr(beta), _ptr(y), M, K,
+                        y.shape[1])
+    return arr
+
+
+def bitlinear_forward_grouped(calls, x_dtype, y_dtype, eps=1e-8, stream=None):
+    """calls: a make_calls() array (kept by the caller, e.g. for graph capture)
+    or a list of (x, gain, packed, beta, y) tuples."""
+    if not isinstance(calls, ctypes.Array):
+        calls = make_calls(calls)
+    _check("bitlinear_forward_grouped", lib().bitlinear_forward_grouped(
+        ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[x_dtype],
+        DTYPE_CODE[y_dtype], eps, _stream(stream)))
+
+
 def bitlinear_act_quant(x, gain, xq, s, rowsum, eps=1e-8, stream=None):
     M, K = x.shape
     _check("bitlinear_act_quant", lib().bitlinear_act_quant(
@@ -147,6 +186,13 @@ def bitlinear_gemm_i32(xq, rowsum, packed, N, acc, path=BL_PATH_AUTO, stream=Non
     M, K = xq.shape
     _check("bitlinear_gemm_i32", lib().bitlinear_gemm_i32(
         _ptr(xq), _ptr(rowsum), M, K, _ptr(packed), N, _ptr(acc), path, _stream(stream)))
+
+
+def bitlinear_contract(xq, s, rowsum, packed, beta, N, y, path=BL_PATH_AUTO, stream=None):
+    M, K = xq.shape
+    _check("bitlinear_contract", lib().bitlinear_contract(
+        _ptr(xq), _ptr(s), _ptr(rowsum), M, K, _ptr(packed), _ptr(beta), N, _ptr(y),
+        DTYPE_CODE[y.dtype], path, _stream(stream)))
 
 
 def bitlinear_unpack_weights(packed, N, K, Wq, stream=None):

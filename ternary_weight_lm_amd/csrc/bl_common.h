@@ -17,16 +17,17 @@ constexpr int kWave = 64;
 // -------------------------------------------------------------- elements
 
 // 8 consecutive elements of dtype DT kept as raw bits in registers: one
-// 16-byte load for fp16 / bf16, two for fp32.
+// 16-byte load for fp16 / bf16, two for fp32.  (Native int vectors: copies of
+// HIP's uint4 struct can be lowered to memcpy through private memory.)
 template <int DT> struct Chunk8 {
-  uint4 u[DT == BL_F32 ? 2 : 1];
+  v4i u[DT == BL_F32 ? 2 : 1];
 };
 
 // p must be 16-byte aligned.
 template <int DT>
 __device__ __forceinline__ Chunk8<DT> load_chunk(const void *p) {
   Chunk8<DT> c;
-  const uint4 *q = reinterpret_cast<const uint4 *>(p);
+  const v4i *q = reinterpret_cast<const v4i *>(p);
   c.u[0] = q[0];
   if constexpr (DT == BL_F32) c.u[1] = q[1];
   return c;
@@ -36,15 +37,16 @@ __device__ __forceinline__ Chunk8<DT> load_chunk(const void *p) {
 template <int DT>
 __device__ __forceinline__ void widen(const Chunk8<DT> &c, float f[8]) {
   if constexpr (DT == BL_F32) {
-    f[0] = __uint_as_float(c.u[0].x); f[1] = __uint_as_float(c.u[0].y);
-    f[2] = __uint_as_float(c.u[0].z); f[3] = __uint_as_float(c.u[0].w);
-    f[4] = __uint_as_float(c.u[1].x); f[5] = __uint_as_float(c.u[1].y);
-    f[6] = __uint_as_float(c.u[1].z); f[7] = __uint_as_float(c.u[1].w);
-  } else {
-    const uint32_t w[4] = {c.u[0].x, c.u[0].y, c.u[0].z, c.u[0].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+      f[i] = __int_as_float(c.u[0][i]);
+      f[4 + i] = __int_as_float(c.u[1][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wd = (uint32_t)c.u[0][i];
+      const uint32_t lo = wd & 0xFFFFu, hi = wd >> 16;
       if constexpr (DT == BL_BF16) {
         f[2 * i] = __uint_as_float(lo << 16);
         f[2 * i + 1] = __uint_as_float(hi << 16);
@@ -64,15 +66,6 @@ __device__ __forceinline__ void load8(const void *p, float f[8]) {
 // Bytes per element of a dtype code.
 __host__ __device__ constexpr int dtype_bytes(int dt) { return dt == BL_F32 ? 4 : 2; }
 
-// Round-to-nearest-even conversion of fp32 to the output dtype bits.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u)           // Inf / NaN: truncate,
-    return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));  // keep NaN quiet
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
@@ -84,48 +77,95 @@ __device__ __forceinline__ void store1(void *base, int64_t idx, float v) {
   } else if constexpr (DT == BL_F16) {
     reinterpret_cast<uint16_t *>(base)[idx] = f32_to_f16_bits(v);
   } else {
-    reinterpret_cast<uint16_t *>(base)[idx] = f32_to_bf16_bits(v);
+    // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
+    reinterpret_cast<__bf16 *>(base)[idx] = (__bf16)v;
   }
 }
 
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row: conflict-free for
+// 16-byte accesses by 8 consecutive rows (32 banks) and by 16 consecutive
+// rows (64 banks), the two ways gfx9 LDS serves ds_read/write_b128.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+}
+
 // ------------------------------------------------------- wave reductions
+// All-lane reductions of a 64-lane wave: a DPP butterfly inside each row of
+// 16 lanes (quad_perm xor 1, quad_perm xor 2, half-row mirror, row mirror;
+// after each step every lane of the group holds the same partial), then the
+// four row results are read out of lanes 0, 16, 32, 48 and combined in a
+// fixed order ((r0 + r1) + (r2 + r3)).  DPP moves are plain VALU ops, far
+// cheaper in latency than LDS-routed shuffles.  The result is identical in
+// every lane and the association order is fixed, so every kernel that uses
+// these gets bit-identical sums.
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int2 u = __builtin_bit_cast(int2, v);
+  return __builtin_bit_cast(double, make_int2(dpp_i32<CTRL>(u.x), dpp_i32<CTRL>(u.y)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside 16 lanes
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  const int2 u = __builtin_bit_cast(int2, v);
+  auto lane_val = [&](int l) {
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(u.x, l),
+                                                __builtin_amdgcn_readlane(u.y, l)));
+  };
+  return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_i32<kDppXor1>(v);
+  v += dpp_i32<kDppXor2>(v);
+  v += dpp_i32<kDppHalfMirror>(v);
+  v += dpp_i32<kDppMirror>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return fmaxf(fmaxf(lane_val(0), lane_val(16)), fmaxf(lane_val(32), lane_val(48)));
 }
 
 // ------------------------------------------------------------ quantizers
 
-// Correctly rounded fp32 division: the fp64 quotient is correctly rounded
-// (IEEE division on the f64 unit) and rounding it again to fp32 cannot
-// change the result, since 53 >= 2*24 + 2.
-__device__ __forceinline__ float div_rn(float a, float b) {
-  return (float)((double)a / (double)b);
-}
+// Correctly rounded fp32 division: the library is compiled with
+// -fhip-fp32-correctly-rounded-divide-sqrt, under which fp32 '/' lowers to
+// the IEEE division sequence (div_scale / rcp / fma / div_fixup).
+__device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
 
-// Correctly rounded fp32 square root of a positive finite t.  The fp64
-// root gives a candidate within one fp32 ulp; it is then corrected exactly:
-// the midpoints between neighbouring floats have at most 25 significant
-// bits, so their squares are exact in fp64 and can be compared with t (a
-// tie is impossible: t has 24 significant bits, a midpoint square 49-50).
-// HIP's __fsqrt_rn is not used because it lowers to the native,
-// not correctly rounded, instruction.
+// Correctly rounded fp32 square root of a positive finite t.  The fp32 root
+// is a candidate within one ulp; it is then corrected exactly: the midpoints
+// between neighbouring floats have at most 25 significant bits, so their
+// squares are exact in fp64 and can be compared with t (a tie is
+// impossible: t has 24 significant bits, a midpoint square 49-50).  HIP's
+// __fsqrt_rn is not used because it lowers to the native instruction.
 __device__ __forceinline__ float sqrt_rn(float t) {
-  float q = (float)__builtin_sqrt((double)t);
+  float q = __builtin_sqrtf(t);
   const uint32_t u = __float_as_uint(q);
   const double qd = q;
   const double hi = 0.5 * (qd + (double)__uint_as_float(u + 1));

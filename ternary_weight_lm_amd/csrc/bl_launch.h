@@ -53,6 +53,11 @@ struct SkinnyArgs {
 };
 hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream);
 
+// Up to kGroupMax fused skinny calls per launch (more are split into several
+// launches).  Every call must be fused-eligible and share x / out dtypes.
+constexpr int kGroupMax = 16;
+hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream);
+
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;
 constexpr int64_t kFusedMaxK = 8192;

@@ -6,6 +6,7 @@
 // crosses the boundary; every failure is a negative status code.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "bitlinear.h"
 #include "bl_launch.h"
@@ -16,7 +17,8 @@ constexpr int64_t kMaxK = 65536;
 constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int64_t kMaxM = int64_t(1) << 24;
 // dynamic LDS the fused skinny kernel may use: 64 KiB minus its static part
-constexpr int64_t kFusedLdsBytes = 65536 - 8320;
+// (8320 bytes) and some slack
+constexpr int64_t kFusedLdsBytes = 65536 - 9216;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -85,6 +87,11 @@ const char *bitlinear_status_string(int status) {
     case BL_ERR_PATH: return "unknown or inapplicable execution path";
     default: return "unknown status";
   }
+}
+
+int bitlinear_select_path(int64_t M, int64_t K) {
+  if (!m_ok(M) || M == 0 || K < 128 || K > kMaxK || K % 128 != 0) return BL_ERR_SHAPE;
+  return auto_path(M, K);
 }
 
 size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
@@ -177,6 +184,43 @@ int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
                                 ws_bytes, BL_PATH_AUTO, stream);
 }
 
+int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
+                              int y_dtype, float eps, hipStream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (ncalls < 0 || ncalls > 4096) return BL_ERR_SHAPE;
+  if (ncalls == 0) return BL_OK;
+  if (!calls) return BL_ERR_NULL;
+  std::vector<bl::SkinnyArgs> args;
+  args.reserve((size_t)ncalls);
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_call &c = calls[i];
+    if (!nk_ok(c.N, c.K) || !m_ok(c.M)) return BL_ERR_SHAPE;
+    if (c.M == 0) continue;
+    if (!fused_fits(c.M, c.K)) return BL_ERR_SHAPE;
+    if (!c.x || !c.gain || !c.packed || !c.beta || !c.y) return BL_ERR_NULL;
+    if (!aligned16(c.x) || !aligned16(c.gain) || !aligned16(c.packed) || !aligned16(c.y) ||
+        (reinterpret_cast<uintptr_t>(c.beta) & 3u))
+      return BL_ERR_ALIGN;
+    bl::SkinnyArgs a{};
+    a.fused = true;
+    a.x = c.x;
+    a.x_dtype = x_dtype;
+    a.gain = c.gain;
+    a.eps = eps;
+    a.packed = c.packed;
+    a.beta = c.beta;
+    a.M = c.M;
+    a.N = c.N;
+    a.K = c.K;
+    a.out = c.y;
+    a.out_kind = y_dtype;
+    args.push_back(a);
+  }
+  if (args.empty()) return BL_OK;
+  return hip_status(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream));
+}
+
 int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
                         int64_t M, int64_t K, float eps, int8_t *xq, float *s,
                         int32_t *rowsum, hipStream_t stream) {
@@ -218,6 +262,39 @@ int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
   }
   return hip_status(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
                                          bl::kOutI32, stream));
+}
+
+int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
+                       int64_t M, int64_t K, const void *packed,
+                       const float *beta, int64_t N, void *y, int y_dtype,
+                       int path, hipStream_t stream) {
+  if (!dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (path != BL_PATH_AUTO && path != BL_PATH_SKINNY && path != BL_PATH_MFMA) return BL_ERR_PATH;
+  if (M == 0) return BL_OK;
+  if (!xq || !s || !rowsum || !packed || !beta || !y) return BL_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(packed) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(s) & 3u) || (reinterpret_cast<uintptr_t>(rowsum) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
+  if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
+  if (path == BL_PATH_SKINNY) {
+    bl::SkinnyArgs a{};
+    a.fused = false;
+    a.xq = xq;
+    a.s = s;
+    a.rowsum = rowsum;
+    a.packed = packed;
+    a.beta = beta;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.out = y;
+    a.out_kind = y_dtype;
+    return hip_status(bl::launch_skinny(a, stream));
+  }
+  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, stream));
 }
 
 int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,

@@ -13,12 +13,13 @@
 // of 128 (one packed tile column).  4 waves as 2 x 2; wave (wm, wn) owns
 // 16*MI rows x 64 outputs = MI x 4 MFMA blocks of 16 x 16.
 //   A (xq): global -> registers -> LDS, double-buffered, 16-byte chunks of a
-//           128-byte row XOR-swizzled with (row & 7) so the 16 lanes that read
-//           one column of chunks hit distinct banks.
+//           128-byte row XOR-swizzled (swz) so the lanes that read one column
+//           of chunks hit distinct banks.
 //   B (packed codes): each wave loads its two 1 KiB tiles per k-block
 //           straight into registers (one 16-byte load per lane per tile, the
 //           layout was built for exactly this) and unpacks them with
 //           shift + mask; no LDS traffic for weights.
+//   Loads run two k-blocks ahead of the MFMAs.
 // Epilogue: subtract rowsum, multiply by beta / s_m, round to the output
 // dtype (or store the exact int32 accumulator).
 // Workgroup ids are remapped so each of the 8 XCDs (which receive ids
@@ -30,6 +31,60 @@
 #include "bl_launch.h"
 
 namespace bl {
+
+// One k-block of 128: multiply the A tile in `cur` (LDS) by the B codes in
+// b0/b1, request k-block kb+2 (A into a_load, B into b0/b1 once they are
+// consumed) and stage k-block kb+1 (a_store) into `next`.  Called twice per
+// loop trip with the register sets swapped, so no register is ever copied
+// (a copy would have to wait for its load and serialize the pipeline).
+template <int MI>
+__device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, uint8_t *next,
+                                            v4i (&acc)[MI][4], v4i (&a_store)[MI],
+                                            v4i (&a_load)[MI], v4i &b0, v4i &b1,
+                                            const int8_t *const (&a_src)[MI],
+                                            const int (&a_dst)[MI], const v4i *b_src0,
+                                            const v4i *b_src1, int arow0, int lane) {
+  const int k2 = min(kb + 2, KB - 1);  // the tail re-reads the last block (unused)
+  // scheduling fences keep each k-block's work in its own slot: without
+  // them the scheduler pulls the next block's unpack (and so its wait for
+  // the B loads) forward, shortening the prefetch distance
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < MI; ++j)
+    a_load[j] = *reinterpret_cast<const v4i *>(a_src[j] + (int64_t)k2 * 128);
+  __builtin_amdgcn_sched_barrier(0);
+  v4i a[MI][2];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = arow0 + 16 * mi;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ch = 2 * (lane >> 4) + s2;
+      a[mi][s2] = *reinterpret_cast<const v4i *>(cur + row * 128 + (swz(row, ch) << 4));
+    }
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    // word (h, s2) of a lane slot sits at dword 2h + s2
+    const v4i w00 = unpack_codes(s2 ? b0.y : b0.x);
+    const v4i w01 = unpack_codes(s2 ? b0.w : b0.z);
+    const v4i w10 = unpack_codes(s2 ? b1.y : b1.x);
+    const v4i w11 = unpack_codes(s2 ? b1.w : b1.z);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      acc[mi][0] = mfma16x16x64(a[mi][s2], w00, acc[mi][0]);
+      acc[mi][1] = mfma16x16x64(a[mi][s2], w01, acc[mi][1]);
+      acc[mi][2] = mfma16x16x64(a[mi][s2], w10, acc[mi][2]);
+      acc[mi][3] = mfma16x16x64(a[mi][s2], w11, acc[mi][3]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  b0 = b_src0[k2 * 64];
+  b1 = b_src1[k2 * 64];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(next + a_dst[j]) = a_store[j];
+  __syncthreads();
+}
 
 template <int MI, int OUT>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
@@ -65,13 +120,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
     const int c = tid + 256 * j;
     const int row = c >> 3, ch = c & 7;
     a_src[j] = xq + (int64_t)min(m0 + row, M - 1) * K + ch * 16;
-    a_dst[j] = row * 128 + ((ch ^ (row & 7)) << 4);
+    a_dst[j] = row * 128 + (swz(row, ch) << 4);
   }
-  // ---- B: the wave's two packed 32-row tiles; missing tiles read as zero.
+  // ---- B: the wave's two packed 32-row tiles.  Tiles past N (partial last
+  // output tile) re-read the last real tile: their columns are never stored.
   const int nt0 = (n0 >> 5) + 2 * wn;
-  const uint4 *b_src0 = packed + (int64_t)nt0 * KB * 64 + lane;
-  const uint4 *b_src1 = b_src0 + (int64_t)KB * 64;
-  const bool b_ok0 = nt0 < NT, b_ok1 = nt0 + 1 < NT;
+  const v4i *b_src0 = reinterpret_cast<const v4i *>(packed) + (int64_t)min(nt0, NT - 1) * KB * 64 + lane;
+  const v4i *b_src1 = reinterpret_cast<const v4i *>(packed) + (int64_t)min(nt0 + 1, NT - 1) * KB * 64 + lane;
 
   v4i acc[MI][4];
 #pragma unroll
@@ -79,70 +134,59 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
 
-  uint4 areg[MI];
+  // Prefetch distance 2: the A chunks and B tiles of k-block kb+2 are
+  // requested while k-block kb is multiplied, so each load has about two
+  // iterations of MFMA work to arrive; A goes through a double-buffered LDS
+  // stage one iteration before use.  (Native int vectors, not uint4: struct
+  // copies are lowered to memcpy through private memory.)
+  v4i P[MI], Q[MI];   // A staging sets
+  v4i X0, X1, Y0, Y1; // B of even / odd k-blocks
+  {
+    const int k1 = min(1, KB - 1);
 #pragma unroll
-  for (int j = 0; j < MI; ++j) areg[j] = *reinterpret_cast<const uint4 *>(a_src[j]);
-  uint4 b0 = b_ok0 ? b_src0[0] : make_uint4(0, 0, 0, 0);
-  uint4 b1 = b_ok1 ? b_src1[0] : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < MI; ++j) Q[j] = *reinterpret_cast<const v4i *>(a_src[j]);
 #pragma unroll
-  for (int j = 0; j < MI; ++j) *reinterpret_cast<uint4 *>(&lds[0][a_dst[j]]) = areg[j];
+    for (int j = 0; j < MI; ++j)
+      P[j] = *reinterpret_cast<const v4i *>(a_src[j] + (int64_t)k1 * 128);
+    X0 = b_src0[0];
+    X1 = b_src1[0];
+    Y0 = b_src0[k1 * 64];
+    Y1 = b_src1[k1 * 64];
+#pragma unroll
+    for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(&lds[0][a_dst[j]]) = Q[j];
+  }
   __syncthreads();
 
   const int arow0 = wm * 16 * MI + (lane & 15);
-  for (int kb = 0; kb < KB; ++kb) {
-    const uint4 c0 = b0, c1 = b1;
-    // prefetch the next k-block (the last iteration re-reads block KB-1; the
-    // copy it leaves in the idle LDS buffer is never read)
-    const int kn = min(kb + 1, KB - 1);
-    {
-      const int64_t ko = (int64_t)kn * 128;
-#pragma unroll
-      for (int j = 0; j < MI; ++j) areg[j] = *reinterpret_cast<const uint4 *>(a_src[j] + ko);
-      if (b_ok0) b0 = b_src0[kn * 64];
-      if (b_ok1) b1 = b_src1[kn * 64];
-    }
-    const uint8_t *As = lds[kb & 1];
-    v4i a[MI][2];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int row = arow0 + 16 * mi;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int ch = 2 * (lane >> 4) + s2;
-        a[mi][s2] = *reinterpret_cast<const v4i *>(As + row * 128 + ((ch ^ (row & 7)) << 4));
-      }
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      // word (h, s2) of a lane slot sits at dword 2h + s2
-      const v4i w00 = unpack_codes(s2 ? c0.y : c0.x);
-      const v4i w01 = unpack_codes(s2 ? c0.w : c0.z);
-      const v4i w10 = unpack_codes(s2 ? c1.y : c1.x);
-      const v4i w11 = unpack_codes(s2 ? c1.w : c1.z);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        acc[mi][0] = mfma16x16x64(a[mi][s2], w00, acc[mi][0]);
-        acc[mi][1] = mfma16x16x64(a[mi][s2], w01, acc[mi][1]);
-        acc[mi][2] = mfma16x16x64(a[mi][s2], w10, acc[mi][2]);
-        acc[mi][3] = mfma16x16x64(a[mi][s2], w11, acc[mi][3]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < MI; ++j)
-      *reinterpret_cast<uint4 *>(&lds[(kb + 1) & 1][a_dst[j]]) = areg[j];
-    __syncthreads();
+  // Both halves of a trip are unconditional: a conditional second half would
+  // let the compiler sink the first half's prefetch loads into it.
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
+    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, a_src, a_dst, b_src0, b_src1,
+                    arow0, lane);
+    gemm_kblock<MI>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y0, Y1, a_src, a_dst, b_src0,
+                    b_src1, arow0, lane);
   }
+  if (kb < KB)
+    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, a_src, a_dst, b_src0, b_src1,
+                    arow0, lane);
 
-  // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.
-  const float bt = OUT == kOutI32 ? 0.0f : *beta;
+  // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  Lane
+  // l < 16*MI first fetches row sum and rescale factor of the wave's row l
+  // (one division per lane); the others get them by cross-lane shuffles.
+  const int mrow = min(m0 + wm * 16 * MI + lane, M - 1);
+  const int my_rs = lane < 16 * MI ? rowsum[mrow] : 0;
+  float my_scale = 0.0f;
+  if constexpr (OUT != kOutI32) my_scale = lane < 16 * MI ? div_rn(*beta, s[mrow]) : 0.0f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 16 * MI + 16 * mi + 4 * (lane >> 4) + i;
+      const int r = 16 * mi + 4 * (lane >> 4) + i;
+      const int m = m0 + wm * 16 * MI + r;
+      const int rs = __shfl(my_rs, r, kWave);
+      const float scale = __shfl(my_scale, r, kWave);
       if (m >= M) continue;
-      const int rs = rowsum[m];
-      const float scale = OUT == kOutI32 ? 0.0f : div_rn(bt, s[m]);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int n = n0 + 64 * wn + 16 * nb + (lane & 15);

@@ -1,0 +1,166 @@
+// rowquant.h -- RMSNorm + per-token absmax int8 quantization of one token
+// row by one 64-lane wave.  Used by the act-quant kernel (a wave per row)
+// and by the fused decode prologue, so both paths produce bit-identical
+// codes and scales.
+//
+// Lane L owns the 8-element chunks k = 8L + 512c (c = 0, 1, ...), read with
+// 16-byte loads.  Up to K = 8192 the chunks are loaded once, all in flight
+// together, and kept in registers (widened when K <= 4096, raw above);
+// longer rows are re-read for each pass, four chunks in flight.  Either way
+// a lane adds its x^2 terms in the same order (chunk-major; fma with an exact
+// fp64 square is the plain product-then-add) and the cross-lane reductions
+// are the same fixed xor-shuffle trees, so the result does not depend on
+// which variant ran.  No LDS, no barriers.
+//   pass 1: sum of x^2 (fp64)            -> r = 1/sqrt(fp32(sum/K) + eps)
+//   pass 2: max |(x * r) * g|            -> s = 127 / max(., 1e-5)
+//   pass 3: xq = clamp(rne(xn * s)), handed to the sink 8 at a time; the
+//           row sum of the codes is reduced exactly in int32.
+#pragma once
+
+#include "bl_common.h"
+
+namespace bl {
+
+constexpr int kRowCache = 8;  // cached chunks per lane: K <= 4096
+
+// Four int32 codes in [-128, 127] -> one dword of int8 (byte i = code i),
+// three byte permutes.
+__device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
+  const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u);
+  const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
+// How a lane holds its chunks of the row between the three passes.
+enum RowMode {
+  kRowFloat = 0,  // widened once, xn kept in registers: K <= 512 * kRowCache
+  kRowRaw = 1,    // raw 16-byte chunks kept, widened per pass: K <= 512 * kRowRawCache
+  kRowReload = 2  // re-read from memory every pass, 4 chunks in flight
+};
+constexpr int kRowRawCache = 16;  // K <= 8192
+
+__host__ __device__ constexpr int row_mode(int K) {
+  return K <= 512 * kRowCache ? kRowFloat : (K <= 512 * kRowRawCache ? kRowRaw : kRowReload);
+}
+
+// Quantizes one row with the calling wave.  `sink(k, codes)` receives the 8
+// codes of elements k..k+7 as two dwords.  On return every lane holds s and
+// the row sum.  The three modes run the same operations in the same order.
+template <int DT, int MODE, class Sink>
+__device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
+                                             const char *__restrict__ gr, int K,
+                                             float eps, Sink sink, float &s_out,
+                                             int &rowsum_out) {
+  constexpr int EB = dtype_bytes(DT);
+  const int lane = threadIdx.x & 63;
+  const int nch = (K + 511) >> 9;  // chunk rounds (some lanes idle in the last)
+  const auto kof = [&](int c) { return 8 * lane + 512 * c; };
+  // c < nch is uniform across the wave; lanes past K in the last round load
+  // a valid chunk and never use it
+  const auto ld = [&](int c) { return load_chunk<DT>(xr + (int64_t)min(kof(c), K - 8) * EB); };
+
+  auto emit = [&](int k, const float *xn, float sc, int &rs) {
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = quant8(xn[e], sc);
+    const uint2 codes = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+    rs = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs, false);
+    rs = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs, false);
+    sink(k, codes);
+  };
+
+  if constexpr (MODE == kRowFloat) {
+    // x widened once; after pass 2 the same registers hold xn
+    float v[kRowCache][8];
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c)
+      if (c < nch) widen<DT>(ld(c), v[c]);
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c)
+      if (c < nch && kof(c) < K) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)v[c][e], (double)v[c][e], ss);
+      }
+    const float r = rms_inv(wave_sum(ss), K, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c)
+      if (c < nch && kof(c) < K) {
+        float g[8];
+        load8<DT>(gr + (int64_t)kof(c) * EB, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[c][e] = (v[c][e] * r) * g[e];
+          amax = fmaxf(amax, fabsf(v[c][e]));
+        }
+      }
+    const float sc = act_scale(wave_max(amax));
+    int rs = 0;
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c)
+      if (c < nch && kof(c) < K) emit(kof(c), v[c], sc, rs);
+    s_out = sc;
+    rowsum_out = wave_sum(rs);
+  } else {
+    // raw chunks (kRowRaw) or batches of 4 re-read chunks (kRowReload)
+    constexpr int NC = MODE == kRowRaw ? kRowRawCache : 4;
+    Chunk8<DT> raw[NC];
+    // for_each(fn): fn(k, x[8]) for every chunk of the lane, in order
+    auto for_each = [&](auto &&fn) {
+      if constexpr (MODE == kRowRaw) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (c < nch && kof(c) < K) {
+            float f[8];
+            widen<DT>(raw[c], f);
+            fn(kof(c), f);
+          }
+      } else {
+        for (int c0 = 0; c0 < nch; c0 += NC) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            if (c0 + c < nch) raw[c] = ld(c0 + c);
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            if (c0 + c < nch && kof(c0 + c) < K) {
+              float f[8];
+              widen<DT>(raw[c], f);
+              fn(kof(c0 + c), f);
+            }
+        }
+      }
+    };
+    if constexpr (MODE == kRowRaw) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c < nch) raw[c] = ld(c);
+    }
+    double ss = 0.0;
+    for_each([&](int, const float *f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)f[e], (double)f[e], ss);
+    });
+    const float r = rms_inv(wave_sum(ss), K, eps);
+    float amax = 0.0f;
+    for_each([&](int k, const float *f) {
+      float g[8];
+      load8<DT>(gr + (int64_t)k * EB, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((f[e] * r) * g[e]));
+    });
+    const float sc = act_scale(wave_max(amax));
+    int rs = 0;
+    for_each([&](int k, const float *f) {
+      float g[8], xn[8];
+      load8<DT>(gr + (int64_t)k * EB, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xn[e] = (f[e] * r) * g[e];
+      emit(k, xn, sc, rs);
+    });
+    s_out = sc;
+    rowsum_out = wave_sum(rs);
+  }
+}
+
+}  // namespace bl

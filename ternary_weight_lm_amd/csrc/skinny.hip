@@ -5,51 +5,67 @@
 // the design goal is bytes in flight, not arithmetic.  One workgroup owns one
 // packed 32-row tile column (32 output features x all of K); its 4 waves
 // split the K-blocks round-robin.
-//   1. Every wave first issues the 16-byte loads of all its weight tiles
-//      (one contiguous 1 KiB per wave per tile), so HBM latency overlaps the
+//   1. Every wave first issues the 16-byte loads of its weight tiles (one
+//      contiguous 1 KiB per wave per tile), so HBM latency overlaps the
 //      prologue.
 //   2. Fused variant: the workgroup normalizes and quantizes the M token
-//      rows itself (RMSNorm before quantization, as in the hysenlabs de
-//      review "MatMul-Free LM: Ternary-Gewichte statt Matrixmultiplikation im
+//      rows itself, a wave per row, with the shared row quantizer
+//      (rowquant.h) into LDS --
+//      RMSNorm right before quantization, as in the hysenlabs de review
+//      "MatMul-Free LM: Ternary-Gewichte statt Matrixmultiplikation im
 //      Transformer", section "HGRNBit: was in einem Block tatsächlich
-//      passiert") into LDS, with fp64 sum of squares and fp32 absmax per row,
-//      exactly the arithmetic of actquant.hip.  Pre-quantized variant: xq,
-//      s, rowsum come from the act-quant kernel and A operands are read
-//      straight from global memory.
+//      passiert".  Pre-quantized variant: xq, s, rowsum come from the
+//      act-quant kernel and A operands are read straight from memory.
 //   3. Each tile feeds four v_mfma_i32_16x16x64_i8 (2 output halves x 2
 //      k-steps); token rows >= M are zero operands.
 //   4. The 4 waves' partial sums are added in LDS; the epilogue subtracts
 //      rowsum and rescales by beta / s_m (datacamp "MatMul-freie LLMs:
 //      Zentrale Konzepte erklärt", figure panel 4).
-#include "bl_common.h"
+// A launch can carry up to kGroupMax independent calls (grouped entry
+// point): workgroups are numbered call after call and each finds its call
+// from the prefix table in the kernel arguments.
 #include "bl_launch.h"
+#include "rowquant.h"
 
 namespace bl {
 
 constexpr int kSkinnyBatch = 16;  // weight tiles held in registers per wave
 
-struct SkinnyParams {
+struct SkinnyCall {
   const void *x;
   const void *gain;
-  float eps;
   const int8_t *xq;
   const float *s;
   const int32_t *rowsum;
   const uint4 *packed;
   const float *beta;
-  int M, N, K;
   void *out;
+  int M, N, K;
 };
 
-template <bool FUSED, int DT, int OUT>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
+template <int MAXC>
+struct SkinnyLaunch {
+  SkinnyCall call[MAXC];
+  int first_block[MAXC + 1];
+  int ncalls;
+  float eps;
+};
+
+template <bool FUSED, int DT, int OUT, int MAXC, int RMODE>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   extern __shared__ __align__(16) int8_t xs[];  // fused: [M][K + 16] int8
   __shared__ int red[4][8][64];
   __shared__ float s_row[16];
   __shared__ int rs_row[16];
 
+  int c = 0;
+  if constexpr (MAXC > 1) {
+    while (c + 1 < L.ncalls && (int)blockIdx.x >= L.first_block[c + 1]) ++c;
+  }
+  const SkinnyCall &p = L.call[c];
+  const int nt = (int)blockIdx.x - L.first_block[c];
+
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nt = blockIdx.x;
   const int M = p.M, K = p.K, KB = K >> 7;
   const int lds_stride = K + 16;
   const int nmine = w < KB ? (KB - w + 3) / 4 : 0;
@@ -64,42 +80,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   // ---- 2. activations
   if constexpr (FUSED) {
     constexpr int EB = dtype_bytes(DT);
-    const char *gr = reinterpret_cast<const char *>(p.gain);
-    for (int m = w; m < M; m += 4) {
+    for (int m = w; m < M; m += 4) {  // a wave per token row
       const char *xr = reinterpret_cast<const char *>(p.x) + (int64_t)m * K * EB;
-      double ss = 0.0;
-      for (int k = lane * 8; k < K; k += 512) {
-        float f[8];
-        load8<DT>(xr + (int64_t)k * EB, f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];
-      }
-      const float r = rms_inv(wave_sum(ss), K, p.eps);
-      float amax = 0.0f;
-      for (int k = lane * 8; k < K; k += 512) {
-        float f[8], g[8];
-        load8<DT>(xr + (int64_t)k * EB, f);
-        load8<DT>(gr + (int64_t)k * EB, g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((f[e] * r) * g[e]));
-      }
-      const float sc = act_scale(wave_max(amax));
-      int rs = 0;
-      for (int k = lane * 8; k < K; k += 512) {
-        float f[8], g[8];
-        load8<DT>(xr + (int64_t)k * EB, f);
-        load8<DT>(gr + (int64_t)k * EB, g);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = quant8((f[e] * r) * g[e], sc);
-          rs += q;
-          if (e < 4) lo |= (uint32_t)(q & 0xFF) << (8 * e);
-          else hi |= (uint32_t)(q & 0xFF) << (8 * (e - 4));
-        }
-        *reinterpret_cast<uint2 *>(xs + m * lds_stride + k) = make_uint2(lo, hi);
-      }
-      rs = wave_sum(rs);
+      int8_t *dst = xs + m * lds_stride;
+      float sc;
+      int rs;
+      auto sink = [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; };
+      // fused calls have K <= 8192: the row stays in registers (RMODE is
+      // chosen on the host from the largest K of the launch)
+      quantize_row<DT, RMODE>(xr, reinterpret_cast<const char *>(p.gain), K, L.eps, sink, sc, rs);
       if (lane == 0) {
         s_row[m] = sc;
         rs_row[m] = rs;
@@ -157,12 +146,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int idx = tid + 256 * q;
-    const int j = idx >> 6, L = idx & 63;
+    const int j = idx >> 6, Lq = idx & 63;
     const int h = j >> 2, i = j & 3;
-    const int m = 4 * (L >> 4) + i;
+    const int m = 4 * (Lq >> 4) + i;
     if (m >= M) continue;
-    const int n = nt * 32 + 16 * h + (L & 15);
-    const int v = red[0][j][L] + red[1][j][L] + red[2][j][L] + red[3][j][L] - rs_row[m];
+    const int n = nt * 32 + 16 * h + (Lq & 15);
+    const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
     const int64_t o = (int64_t)m * p.N + n;
     if constexpr (OUT == kOutI32) {
       reinterpret_cast<int32_t *>(p.out)[o] = v;
@@ -172,41 +161,93 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   }
 }
 
-template <bool FUSED, int DT>
-static void launch_out(const SkinnyParams &p, int out_kind, size_t lds,
+static SkinnyCall to_call(const SkinnyArgs &a) {
+  SkinnyCall c;
+  c.x = a.x;
+  c.gain = a.gain;
+  c.xq = a.xq;
+  c.s = a.s;
+  c.rowsum = a.rowsum;
+  c.packed = reinterpret_cast<const uint4 *>(a.packed);
+  c.beta = a.beta;
+  c.out = a.out;
+  c.M = (int)a.M;
+  c.N = (int)a.N;
+  c.K = (int)a.K;
+  return c;
+}
+
+template <bool FUSED, int DT, int MAXC, int RMODE>
+static void launch_out(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                        hipStream_t stream) {
-  const unsigned grid = (unsigned)(p.N / 32);
   switch (out_kind) {
-    case BL_F32: skinny_kernel<FUSED, DT, BL_F32><<<grid, 256, lds, stream>>>(p); break;
-    case BL_F16: skinny_kernel<FUSED, DT, BL_F16><<<grid, 256, lds, stream>>>(p); break;
-    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16><<<grid, 256, lds, stream>>>(p); break;
-    default: skinny_kernel<FUSED, DT, kOutI32><<<grid, 256, lds, stream>>>(p); break;
+    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
+    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
+    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
+  }
+}
+
+template <bool FUSED, int DT, int MAXC>
+static void launch_mode(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
+                        int64_t kmax, hipStream_t stream) {
+  if constexpr (!FUSED) {
+    launch_out<FUSED, DT, MAXC, kRowFloat>(L, out_kind, grid, lds, stream);
+  } else {
+    if (row_mode((int)kmax) == kRowFloat)
+      launch_out<FUSED, DT, MAXC, kRowFloat>(L, out_kind, grid, lds, stream);
+    else
+      launch_out<FUSED, DT, MAXC, kRowRaw>(L, out_kind, grid, lds, stream);
+  }
+}
+
+template <int MAXC>
+static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
+                       unsigned grid, size_t lds, int64_t kmax, hipStream_t stream) {
+  if (fused) {
+    switch (x_dtype) {
+      case BL_F32: launch_mode<true, BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+      case BL_F16: launch_mode<true, BL_F16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+      default: launch_mode<true, BL_BF16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+    }
+  } else {
+    launch_mode<false, BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream);
   }
 }
 
 hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
-  SkinnyParams p;
-  p.x = a.x;
-  p.gain = a.gain;
-  p.eps = a.eps;
-  p.xq = a.xq;
-  p.s = a.s;
-  p.rowsum = a.rowsum;
-  p.packed = reinterpret_cast<const uint4 *>(a.packed);
-  p.beta = a.beta;
-  p.M = (int)a.M;
-  p.N = (int)a.N;
-  p.K = (int)a.K;
-  p.out = a.out;
-  if (a.fused) {
-    const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
-    switch (a.x_dtype) {
-      case BL_F32: launch_out<true, BL_F32>(p, a.out_kind, lds, stream); break;
-      case BL_F16: launch_out<true, BL_F16>(p, a.out_kind, lds, stream); break;
-      default: launch_out<true, BL_BF16>(p, a.out_kind, lds, stream); break;
+  SkinnyLaunch<1> L;
+  L.call[0] = to_call(a);
+  L.first_block[0] = 0;
+  L.first_block[1] = (int)(a.N / 32);
+  L.ncalls = 1;
+  L.eps = a.eps;
+  const size_t lds = a.fused ? (size_t)a.M * (size_t)(a.K + 16) : 0;
+  launch_any<1>(L, a.fused, a.x_dtype, a.out_kind, (unsigned)(a.N / 32), lds, a.K, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream) {
+  for (int base = 0; base < ncalls; base += kGroupMax) {
+    const int n = ncalls - base < kGroupMax ? ncalls - base : kGroupMax;
+    SkinnyLaunch<kGroupMax> L;
+    int blocks = 0;
+    size_t lds = 0;
+    int64_t kmax = 0;
+    for (int i = 0; i < n; ++i) {
+      const SkinnyArgs &a = calls[base + i];
+      L.call[i] = to_call(a);
+      L.first_block[i] = blocks;
+      blocks += (int)(a.N / 32);
+      const size_t l = (size_t)a.M * (size_t)(a.K + 16);
+      if (l > lds) lds = l;
+      if (a.K > kmax) kmax = a.K;
     }
-  } else {
-    launch_out<false, BL_F32>(p, a.out_kind, 0, stream);
+    for (int i = n; i <= kGroupMax; ++i) L.first_block[i] = blocks;
+    L.ncalls = n;
+    L.eps = calls[base].eps;
+    launch_any<kGroupMax>(L, true, calls[base].x_dtype, calls[base].out_kind, (unsigned)blocks,
+                          lds, kmax, stream);
   }
   return hipGetLastError();
 }

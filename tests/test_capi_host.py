@@ -58,6 +58,19 @@ def test_size_queries_closed_forms():
     assert L.bitlinear_workspace_bytes(0, 128, 32) == 2 * 0 + 0
 
 
+def test_select_path_rule():
+    L = tw.lib()
+    assert L.bitlinear_select_path(1, 1024) == 1
+    assert L.bitlinear_select_path(4, 7040) == 1
+    assert L.bitlinear_select_path(4, 16384) == 2     # fused needs K <= 8192
+    assert L.bitlinear_select_path(5, 1024) == 2
+    assert L.bitlinear_select_path(16, 1024) == 2
+    assert L.bitlinear_select_path(17, 1024) == 3
+    assert L.bitlinear_select_path(4096, 2048) == 3
+    assert L.bitlinear_select_path(0, 1024) == SHAPE
+    assert L.bitlinear_select_path(1, 1000) == SHAPE
+
+
 def test_status_strings():
     L = tw.lib()
     for code in (OK, NULL, DTYPE, SHAPE, ALIGN, WS, EPS, HIP, UNSUP, PATH, 12345):
@@ -141,9 +154,41 @@ def test_stage_entry_points_validation():
     assert L.bitlinear_gemm_i32(A, B, 17, 1024, C, 1024, D, 2, None) == SHAPE
     assert L.bitlinear_gemm_i32(None, B, 4, 1024, C, 1024, D, 0, None) == NULL
     assert L.bitlinear_gemm_i32(A, B + 2, 4, 1024, C, 1024, D, 0, None) == ALIGN
+    assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y, 7, 0, None) == DTYPE
+    assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1000, Y, 1, 0, None) == SHAPE
+    assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y, 1, 1, None) == PATH
+    assert L.bitlinear_contract(A, B, E, 17, 1024, C, D, 1024, Y, 1, 2, None) == SHAPE
+    assert L.bitlinear_contract(A, None, E, 4, 1024, C, D, 1024, Y, 1, 0, None) == NULL
+    assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y + 4, 1, 0, None) == ALIGN
+    assert L.bitlinear_contract(A, B, E, 0, 1024, C, D, 1024, None, 1, 0, None) == OK
     assert L.bitlinear_unpack_weights(C, 32, 100, D, None) == SHAPE
     assert L.bitlinear_unpack_weights(None, 32, 128, D, None) == NULL
     assert L.bitlinear_unpack_weights(C, 32, 128, D + 8, None) == ALIGN
+
+
+def test_grouped_validation():
+    from ternary_weight_lm_amd._lib import BlCall
+    L = tw.lib()
+
+    def grp(calls, xdt=1, ydt=1, eps=1e-8, n=None):
+        arr = (BlCall * max(1, len(calls)))(*calls)
+        return L.bitlinear_forward_grouped(ctypes.cast(arr, ctypes.c_void_p),
+                                           len(calls) if n is None else n, xdt, ydt, eps, None)
+    good = BlCall(A, B, C, D, Y, 1, 1024, 1024)
+    assert grp([good], xdt=9) == DTYPE
+    assert grp([good], eps=0.0) == EPS
+    assert grp([good], n=-1) == SHAPE
+    assert grp([good], n=5000) == SHAPE
+    assert L.bitlinear_forward_grouped(None, 2, 1, 1, 1e-8, None) == NULL
+    assert L.bitlinear_forward_grouped(None, 0, 1, 1, 1e-8, None) == OK
+    assert grp([good, BlCall(A, B, C, D, Y, 1, 1000, 1024)]) == SHAPE
+    assert grp([good, BlCall(A, B, C, D, Y, 17, 1024, 1024)]) == SHAPE   # not fused-eligible
+    assert grp([good, BlCall(A, B, C, D, Y, 16, 8192, 1024)]) == SHAPE   # LDS budget
+    assert grp([good, BlCall(A, None, C, D, Y, 1, 1024, 1024)]) == NULL
+    assert grp([good, BlCall(A, B, C + 8, D, Y, 1, 1024, 1024)]) == ALIGN
+    assert grp([good, BlCall(A, B, C, D + 2, Y, 1, 1024, 1024)]) == ALIGN
+    # empty calls are skipped: nothing to launch
+    assert grp([BlCall(None, None, None, None, None, 0, 1024, 1024)] * 3) == OK
 
 
 def test_binding_refuses_host_tensors():

@@ -160,6 +160,31 @@ def test_paths_agree_and_repeat_bitwise():
         assert torch.equal(o, outs[0])
 
 
+def test_grouped_matches_single_calls():
+    say("grouped")
+    shapes = [(1, 1024, 1024), (1, 2048, 1024), (3, 96, 384), (2, 64, 7040), (4, 160, 1280),
+              (0, 64, 256)]
+    items, singles = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        x = synth.make_x(900 + i, 0, 0, M, K, "bf16").to(DEV)
+        g = synth.make_gain(900 + i, 0, 0, K, "bf16").to(DEV)
+        packed, beta = tw.pack(synth.make_w(900 + i, 0, 0, N, K).to(DEV))
+        y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+        items.append((x, g, packed, beta, y))
+        singles.append(tw.forward(x, g, packed, beta, N, path=tw.BL_PATH_FUSED))
+    tw.bitlinear_forward_grouped(items, torch.bfloat16, torch.bfloat16)
+    torch.cuda.synchronize()
+    for (x, g, packed, beta, y), ref in zip(items, singles):
+        assert torch.equal(y, ref)
+    # more calls than one launch carries (16): split into several launches
+    many = [(items[0][0], items[0][1], items[0][2], items[0][3],
+             torch.empty(1, 1024, dtype=torch.bfloat16, device=DEV)) for _ in range(37)]
+    tw.bitlinear_forward_grouped(many, torch.bfloat16, torch.bfloat16)
+    torch.cuda.synchronize()
+    for it in many:
+        assert torch.equal(it[4], singles[0])
+
+
 def test_empty_batch_is_noop():
     say("empty batch")
     N, K = 64, 256
