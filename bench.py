@@ -245,7 +245,7 @@ def roofline_from_steps(wl, inp, steps, ms):
     grouped = any(len(g) > 1 for g in inp["groups"])
     return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 5), "traffic": None,
-            "kernel": "bl::skinny_kernel<fused=true> (norm+quant+contract+rescale)"
+            "kernel": "bl::decode_kernel (norm+quant+contract+rescale in one launch)"
                       + (", i/f/g grouped per launch" if grouped else ""),
             "launches": launches, "avg_kernel_us": round(sec * 1e6 / launches, 3),
             "algorithmic_bytes_per_launch": round(byt / launches, 1),
@@ -315,7 +315,7 @@ def roofline(wl, inp, reps):
         cb, co = algorithmic(wl, call)
         byt += cb * reps
         ops += co * reps
-    kernel = {tw.BL_PATH_FUSED: "bl::skinny_kernel<fused=true> (norm+quant+contract+rescale)",
+    kernel = {tw.BL_PATH_FUSED: "bl::decode_kernel (norm+quant+contract+rescale)",
               tw.BL_PATH_SKINNY: "bl::skinny_kernel<fused=false> (contract+rescale)",
               tw.BL_PATH_MFMA: "bl::gemm_mfma_kernel (contract+rescale)"}[path]
     if bound == "hbm":

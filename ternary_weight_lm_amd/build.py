@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pack.hip", "actquant.hip", "gemm.hip", "skinny.hip", "capi.cpp"]
+SOURCES = ["pack.hip", "actquant.hip", "gemm.hip", "skinny.hip", "decode.hip", "capi.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -29,6 +29,9 @@ COMMON = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     # never emit packed fp32 ALU ops on this hardware
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # scalar kernel arguments arrive preloaded in SGPRs (gfx950 kernel-
+    # argument preloading; the code object keeps a fallback that loads them)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

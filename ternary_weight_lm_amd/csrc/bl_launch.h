@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bitlinear.h"
+
 namespace bl {
 
 // Output kinds of the contraction kernels: a BL_* dtype code, or kOutI32 for
@@ -57,6 +59,31 @@ hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream);
 // launches).  Every call must be fused-eligible and share x / out dtypes.
 constexpr int kGroupMax = 16;
 hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream);
+
+// Fused decode kernel (M <= kDecodeMaxM, K <= kFusedMaxK): up to
+// kDecodeCalls projections of one shape (same M, K, N) per launch.
+// launch_skinny and launch_skinny_grouped route fused calls here when they
+// fit.
+constexpr int kDecodeCalls = 3;
+constexpr int64_t kDecodeMaxM = 4;
+struct DecodeArgs {
+  const void *x[kDecodeCalls];
+  int x_dtype;
+  int64_t M, N, K;
+  float eps;
+  int ncalls;
+  const void *gain[kDecodeCalls];
+  const void *packed[kDecodeCalls];
+  const float *beta[kDecodeCalls];
+  void *out[kDecodeCalls];
+  int out_kind;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Whether the decode kernel takes a fused call of this shape and dtype (fp32
+// activations: one row only).
+inline bool decode_fits(int64_t M, int64_t K, int x_dtype) {
+  return M >= 1 && K <= 8192 && (M == 1 || (M <= kDecodeMaxM && x_dtype != BL_F32));
+}
 
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;

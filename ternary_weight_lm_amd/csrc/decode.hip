@@ -1,0 +1,303 @@
+// decode.hip -- the whole FusedBitLinear in one launch for M <= 4 tokens.
+//
+// RMSNorm right before the quantizers (hysenlabs de review "MatMul-Free LM:
+// Ternary-Gewichte statt Matrixmultiplikation im Transformer", section
+// "HGRNBit: was in einem Block tatsächlich passiert"), per-token absmax int8
+// codes, the ternary contraction and the rescale of datacamp "MatMul-freie
+// LLMs: Zentrale Konzepte erklärt", figure panels 4 and 5.
+//
+// At decode the layer moves N*K/4 bytes of packed weights and almost nothing
+// else, and at the sizes of a single layer it is latency-bound: the design
+// removes every serial step it can from the path launch -> last store.
+//   * Arguments are plain scalars, so gfx950 preloads them into SGPRs
+//     (kernel-argument preloading) instead of the waves fetching them.
+//   * All loads of a wave are issued at once, first the activation row and
+//     the gain, then the wave's weight tiles.  They are buffer loads whose
+//     out-of-range lanes / tiles read as zero, so none is conditional and the
+//     compiler's wait for the activations does not also wait for the weights.
+//   * The normalization of a row is split over the 4 waves (wave w owns the
+//     8-element chunks 64w + lane + 256c).  The three row reductions are
+//     DPP trees inside each wave plus a 4-entry LDS exchange, combined in a
+//     fixed order: the same association the act-quant kernel uses, so codes
+//     and scales are bit-identical across paths.
+//   * One workgroup owns one packed 32-row tile column; the 4 waves take
+//     its K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
+//     registers (weights) and LDS (codes), and the partial sums meet in LDS.
+// Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
+// one launch: workgroup b works on call b / tiles.
+#include "bl_launch.h"
+#include "rowquant.h"
+
+namespace bl {
+
+constexpr int kDecTiles = 16;   // weight tiles per wave: K <= 4 * 16 * 128
+constexpr int kDecChunks = 4;   // chunks per lane and row: K <= 4 * 256 * 8
+constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  // raw (untyped) buffer, stride 0: offsets >= bytes read as zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ v4i bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <int DT>
+__device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
+  Chunk8<DT> c;
+  c.u[0] = bload(r, off);
+  if constexpr (DT == BL_F32) c.u[1] = bload(r, off + 16);
+  return c;
+}
+
+template <int DT, int OUT, int MR>
+__global__ __launch_bounds__(256, 2) void decode_kernel(
+    const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
+    const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
+    const void *g2, const float *b0, const float *b1, const float *b2, void *o0, void *o1,
+    void *o2) {
+  // Argument order: what the wave needs first comes first (the first 14
+  // SGPRs of arguments are preloaded).  shape = K/128 | M << 7 | tiles << 10.
+  extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
+  __shared__ double part_ss[MR][4];
+  __shared__ float part_max[MR][4];
+  __shared__ int part_rs[MR][4];
+  __shared__ int red[4][MR][2][16];
+
+  constexpr int EB = dtype_bytes(DT);
+  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7, tiles = (int)(shape >> 10);
+  const int bid = (int)blockIdx.x;
+  const int call = (bid >= tiles) + (bid >= 2 * tiles);
+  const int nt = bid - call * tiles;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int KB = K >> 7, nq = K >> 3;
+  const int lds_stride = K + 16;
+
+  // ---- 1. every load of the wave, activations first
+  const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
+  const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
+  // byte offset of this lane's chunk c in a row (out of range past K)
+  const auto choff = [&](int c) {
+    const int q = 64 * w + lane + 256 * c;
+    return q < nq ? (uint32_t)(8 * q * EB) : kOob;
+  };
+  // Order matters: x needs only preloaded arguments and goes out first; the
+  // gain pointer of calls past the second may still be on its way from the
+  // argument buffer, and the weights are not needed until the contraction,
+  // thousands of cycles later.  (Waits are in issue order, so whatever is
+  // issued later never holds up the wait for x.)
+  Chunk8<DT> xc[MR][kDecChunks];
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      xc[m][c] = bload_chunk<DT>(xr, m < M ? choff(c) + (uint32_t)(m * K * EB) : kOob);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint4 *pk = call == 0 ? p0 : (call == 1 ? p1 : p2);
+  const void *gain = call == 0 ? g0 : (call == 1 ? g1 : g2);
+  const float *bp = call == 0 ? b0 : (call == 1 ? b1 : b2);
+  void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
+  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
+  const rsrc_t wr = make_rsrc(pk + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
+  Chunk8<DT> gc[kDecChunks];
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c) gc[c] = bload_chunk<DT>(gr, choff(c));
+  const float beta = *bp;
+  __builtin_amdgcn_sched_barrier(0);
+  v4i wt[kDecTiles];
+#pragma unroll
+  for (int t = 0; t < kDecTiles; ++t) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // chunk c of this wave holds at least one element of the row
+  const auto live = [&](int c) { return 256 * c + 64 * w < nq; };
+
+  // Rows past M read as zeros and are carried through every step (their
+  // results are never stored): the MR row chains stay free of branches and
+  // interleave.
+  // ---- 2. sum of squares: this wave's slot group, then a 4-entry exchange
+  double ss[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) ss[m] = 0.0;
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c)
+    if (live(c)) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float f[8];
+        widen<DT>(xc[m][c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[m] = __builtin_fma((double)f[e], (double)f[e], ss[m]);
+      }
+    }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const double t = wave_sum(ss[m]);
+    if (lane == 0) part_ss[m][w] = t;
+  }
+  __syncthreads();
+
+  // ---- 3. absmax of the normalized row
+  float r[MR], amax[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    r[m] = rms_inv((part_ss[m][0] + part_ss[m][1]) + (part_ss[m][2] + part_ss[m][3]), K, eps);
+    amax[m] = 0.0f;
+  }
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c)
+    if (live(c)) {
+      float g[8];
+      widen<DT>(gc[c], g);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float f[8];
+        widen<DT>(xc[m][c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax[m] = fmaxf(amax[m], fabsf((f[e] * r[m]) * g[e]));
+      }
+    }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const float t = wave_max(amax[m]);
+    if (lane == 0) part_max[m][w] = t;
+  }
+  __syncthreads();
+
+  // ---- 4. int8 codes into LDS, row sums of the codes
+  float sc[MR], fscale[MR];
+  int rs[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    sc[m] = act_scale(fmaxf(fmaxf(part_max[m][0], part_max[m][1]),
+                            fmaxf(part_max[m][2], part_max[m][3])));
+    fscale[m] = div_rn(beta, sc[m]);
+    rs[m] = 0;
+  }
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c)
+    if (live(c)) {
+      const int q = 64 * w + lane + 256 * c;
+      float g[8];
+      widen<DT>(gc[c], g);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float f[8];
+        widen<DT>(xc[m][c], f);
+        int qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = quant8((f[e] * r[m]) * g[e], sc[m]);
+        const uint2 codes = make_uint2(pack4(qv[0], qv[1], qv[2], qv[3]),
+                                       pack4(qv[4], qv[5], qv[6], qv[7]));
+        rs[m] = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs[m], false);
+        rs[m] = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs[m], false);
+        if (q < nq && m < M) *reinterpret_cast<uint2 *>(xs + m * lds_stride + 8 * q) = codes;
+      }
+    }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int t = wave_sum(rs[m]);
+    if (lane == 0) part_rs[m][w] = t;
+  }
+  __syncthreads();
+
+  // ---- 5. contraction: the wave's tiles kb = w + 4t
+  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
+  const int arow = lane & 15;
+  const bool arow_ok = arow < M;
+  const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
+  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  constexpr int kBatch = 4;  // A operands read from LDS together
+#pragma unroll
+  for (int t0 = 0; t0 < kDecTiles; t0 += kBatch) {
+    if (t0 >= nmine) break;
+    v4i a[kBatch][2];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        a[j][s2] = v4i{0, 0, 0, 0};
+        if (arow_ok && t0 + j < nmine)
+          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
+      }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (t0 + j >= nmine) break;
+      const v4i u = wt[t0 + j];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        // word (h, s2) of a lane slot sits at dword 2h + s2
+        acc0 = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0);
+        acc1 = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1);
+      }
+    }
+  }
+
+  // ---- 6. partial sums meet in LDS; rescale and store
+  // lanes 0..15 hold rows 0..3 (acc[i] = row i) of columns lane / 16 + lane
+  if (lane < 16) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      red[w][m][0][lane] = acc0[m];
+      red[w][m][1][lane] = acc1[m];
+    }
+  }
+  __syncthreads();
+  if (tid < 32 * M) {
+    const int m = tid >> 5, n = tid & 31;
+    const int h = n >> 4, l = n & 15;
+    const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
+    const int v = red[0][m][h][l] + red[1][m][h][l] + red[2][m][h][l] + red[3][m][h][l] - rsum;
+    float fs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+      if (i == m) fs = fscale[i];
+    store1<OUT>(out, (int64_t)m * tiles * 32 + nt * 32 + n, (float)v * fs);
+  }
+}
+
+template <int DT, int OUT>
+static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
+  const unsigned tiles = (unsigned)(a.N / 32);
+  const unsigned grid = tiles * (unsigned)a.ncalls;
+  const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
+  const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 10);
+  const uint4 *p[3];
+  for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
+  // fp32 rows take twice the registers: the 4-row variant would spill, so
+  // fp32 decodes one row per launch (decode_fits)
+  if (DT == BL_F32 || a.M == 1)
+    decode_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(
+        a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
+        a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
+  else
+    decode_kernel<DT, OUT, DT == BL_F32 ? 1 : (int)kDecodeMaxM><<<grid, 256, lds, stream>>>(
+        a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
+        a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
+}
+
+template <int DT>
+static void launch_out(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.out_kind) {
+    case BL_F32: launch_mr<DT, BL_F32>(a, stream); break;
+    case BL_F16: launch_mr<DT, BL_F16>(a, stream); break;
+    default: launch_mr<DT, BL_BF16>(a, stream); break;
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.x_dtype) {
+    case BL_F32: launch_out<BL_F32>(a, stream); break;
+    case BL_F16: launch_out<BL_F16>(a, stream); break;
+    default: launch_out<BL_BF16>(a, stream); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -6,11 +6,15 @@
 // Lane L owns the 8-element chunks k = 8L + 512c (c = 0, 1, ...), read with
 // 16-byte loads.  Up to K = 8192 the chunks are loaded once, all in flight
 // together, and kept in registers (widened when K <= 4096, raw above);
-// longer rows are re-read for each pass, four chunks in flight.  Either way
-// a lane adds its x^2 terms in the same order (chunk-major; fma with an exact
-// fp64 square is the plain product-then-add) and the cross-lane reductions
-// are the same fixed xor-shuffle trees, so the result does not depend on
-// which variant ran.  No LDS, no barriers.
+// longer rows are re-read for each pass, four chunks in flight.
+// Sum of squares, association fixed for every kernel of the library: the
+// chunks form 256 slots (chunk index mod 256); each slot adds its x^2 terms
+// in chunk order (fma with an exact fp64 square is the plain product-then-
+// add), the slots 64v .. 64v + 63 are reduced by the DPP tree of wave_sum,
+// and the four group sums are combined as (g0 + g1) + (g2 + g3).  Here one
+// wave holds all four groups (group = c mod 4); the decode kernel gives each
+// group its own wave.  Either way the result is the same bits.  No LDS, no
+// barriers.
 //   pass 1: sum of x^2 (fp64)            -> r = 1/sqrt(fp32(sum/K) + eps)
 //   pass 2: max |(x * r) * g|            -> s = 127 / max(., 1e-5)
 //   pass 3: xq = clamp(rne(xn * s)), handed to the sink 8 at a time; the
@@ -29,6 +33,12 @@ __device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
   const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u);
   const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x0c0c0400u);
   return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
+// The row's sum of squares from the four per-lane group partials: each
+// group reduced across the wave, then (g0 + g1) + (g2 + g3).
+__device__ __forceinline__ double group_sum(const double (&ss)[4]) {
+  return (wave_sum(ss[0]) + wave_sum(ss[1])) + (wave_sum(ss[2]) + wave_sum(ss[3]));
 }
 
 // How a lane holds its chunks of the row between the three passes.
@@ -75,14 +85,15 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c)
       if (c < nch) widen<DT>(ld(c), v[c]);
-    double ss = 0.0;
+    double ss[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c)
       if (c < nch && kof(c) < K) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)v[c][e], (double)v[c][e], ss);
+        for (int e = 0; e < 8; ++e)
+          ss[c & 3] = __builtin_fma((double)v[c][e], (double)v[c][e], ss[c & 3]);
       }
-    const float r = rms_inv(wave_sum(ss), K, eps);
+    const float r = rms_inv(group_sum(ss), K, eps);
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c)
@@ -106,7 +117,10 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
     // raw chunks (kRowRaw) or batches of 4 re-read chunks (kRowReload)
     constexpr int NC = MODE == kRowRaw ? kRowRawCache : 4;
     Chunk8<DT> raw[NC];
-    // for_each(fn): fn(k, x[8]) for every chunk of the lane, in order
+    // for_each(fn): fn(k, group, x[8]) for every chunk of the lane, in
+    // order; group = chunk index mod 4 (a constant once unrolled: NC and the
+    // reload step are multiples of 4)
+    static_assert(NC % 4 == 0, "chunk groups");
     auto for_each = [&](auto &&fn) {
       if constexpr (MODE == kRowRaw) {
 #pragma unroll
@@ -114,7 +128,7 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
           if (c < nch && kof(c) < K) {
             float f[8];
             widen<DT>(raw[c], f);
-            fn(kof(c), f);
+            fn(kof(c), c & 3, f);
           }
       } else {
         for (int c0 = 0; c0 < nch; c0 += NC) {
@@ -126,7 +140,7 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
             if (c0 + c < nch && kof(c0 + c) < K) {
               float f[8];
               widen<DT>(raw[c], f);
-              fn(kof(c0 + c), f);
+              fn(kof(c0 + c), c & 3, f);
             }
         }
       }
@@ -136,14 +150,14 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
       for (int c = 0; c < NC; ++c)
         if (c < nch) raw[c] = ld(c);
     }
-    double ss = 0.0;
-    for_each([&](int, const float *f) {
+    double ss[4] = {0.0, 0.0, 0.0, 0.0};
+    for_each([&](int, int g, const float *f) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)f[e], (double)f[e], ss);
+      for (int e = 0; e < 8; ++e) ss[g] = __builtin_fma((double)f[e], (double)f[e], ss[g]);
     });
-    const float r = rms_inv(wave_sum(ss), K, eps);
+    const float r = rms_inv(group_sum(ss), K, eps);
     float amax = 0.0f;
-    for_each([&](int k, const float *f) {
+    for_each([&](int k, int, const float *f) {
       float g[8];
       load8<DT>(gr + (int64_t)k * EB, g);
 #pragma unroll
@@ -151,7 +165,7 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
     });
     const float sc = act_scale(wave_max(amax));
     int rs = 0;
-    for_each([&](int k, const float *f) {
+    for_each([&](int k, int, const float *f) {
       float g[8], xn[8];
       load8<DT>(gr + (int64_t)k * EB, g);
 #pragma unroll

@@ -24,6 +24,8 @@
 // A launch can carry up to kGroupMax independent calls (grouped entry
 // point): workgroups are numbered call after call and each finds its call
 // from the prefix table in the kernel arguments.
+#include <vector>
+
 #include "bl_launch.h"
 #include "rowquant.h"
 
@@ -215,7 +217,37 @@ static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int
   }
 }
 
+static bool decode_ok(const SkinnyArgs &a) {
+  return a.fused && decode_fits(a.M, a.K, a.x_dtype);
+}
+
+static DecodeArgs decode_args(const SkinnyArgs &a) {
+  DecodeArgs d{};
+  d.x_dtype = a.x_dtype;
+  d.M = a.M;
+  d.N = a.N;
+  d.K = a.K;
+  d.eps = a.eps;
+  d.out_kind = a.out_kind;
+  d.ncalls = 0;
+  return d;
+}
+
+static void decode_add(DecodeArgs &d, const SkinnyArgs &a) {
+  d.x[d.ncalls] = a.x;
+  d.gain[d.ncalls] = a.gain;
+  d.packed[d.ncalls] = a.packed;
+  d.beta[d.ncalls] = a.beta;
+  d.out[d.ncalls] = a.out;
+  ++d.ncalls;
+}
+
 hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
+  if (decode_ok(a)) {
+    DecodeArgs d = decode_args(a);
+    decode_add(d, a);
+    return launch_decode(d, stream);
+  }
   SkinnyLaunch<1> L;
   L.call[0] = to_call(a);
   L.first_block[0] = 0;
@@ -227,15 +259,34 @@ hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Consecutive calls of one shape that the decode kernel takes go out in
+// launches of up to kDecodeCalls; the others are gathered into launches of
+// the skinny kernel of up to kGroupMax calls.
 hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream) {
-  for (int base = 0; base < ncalls; base += kGroupMax) {
-    const int n = ncalls - base < kGroupMax ? ncalls - base : kGroupMax;
+  std::vector<SkinnyArgs> rest;
+  for (int i = 0; i < ncalls;) {
+    const SkinnyArgs &a = calls[i];
+    if (!decode_ok(a)) {
+      rest.push_back(a);
+      ++i;
+      continue;
+    }
+    DecodeArgs d = decode_args(a);
+    while (i < ncalls && d.ncalls < kDecodeCalls && decode_ok(calls[i]) && calls[i].M == a.M &&
+           calls[i].K == a.K && calls[i].N == a.N)
+      decode_add(d, calls[i++]);
+    const hipError_t e = launch_decode(d, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int nrest = (int)rest.size();
+  for (int base = 0; base < nrest; base += kGroupMax) {
+    const int n = nrest - base < kGroupMax ? nrest - base : kGroupMax;
     SkinnyLaunch<kGroupMax> L;
     int blocks = 0;
     size_t lds = 0;
     int64_t kmax = 0;
     for (int i = 0; i < n; ++i) {
-      const SkinnyArgs &a = calls[base + i];
+      const SkinnyArgs &a = rest[base + i];
       L.call[i] = to_call(a);
       L.first_block[i] = blocks;
       blocks += (int)(a.N / 32);
@@ -245,8 +296,8 @@ hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_
     }
     for (int i = n; i <= kGroupMax; ++i) L.first_block[i] = blocks;
     L.ncalls = n;
-    L.eps = calls[base].eps;
-    launch_any<kGroupMax>(L, true, calls[base].x_dtype, calls[base].out_kind, (unsigned)blocks,
+    L.eps = rest[base].eps;
+    launch_any<kGroupMax>(L, true, rest[base].x_dtype, rest[base].out_kind, (unsigned)blocks,
                           lds, kmax, stream);
   }
   return hipGetLastError();
