@@ -54,14 +54,15 @@ __device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
   return c;
 }
 
-template <int DT, int OUT, int MR>
-__global__ __launch_bounds__(256, 2) void decode_kernel(
-    const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
-    const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
-    const void *g2, const float *b0, const float *b1, const float *b2, void *o0, void *o1,
-    void *o2) {
-  // Argument order: what the wave needs first comes first (the first 14
-  // SGPRs of arguments are preloaded).  shape = K/128 | M << 7 | tiles << 10.
+// The body of both kernels below.  The call's packed / gain / beta / out
+// pointers are selected only after the activation loads are issued: in the
+// three-call kernel some of them are not preloaded and must first be fetched
+// from the argument buffer, and that wait must not hold up the first loads.
+template <int DT, int OUT, int MR, bool GAIN_LATE>
+__device__ __forceinline__ void decode_body(
+    const void *x, int K, int M, int tiles, int nt, float eps, int call, const uint4 *p0,
+    const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
+    const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
   __shared__ double part_ss[MR][4];
   __shared__ float part_max[MR][4];
@@ -69,18 +70,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   __shared__ int red[4][MR][2][16];
 
   constexpr int EB = dtype_bytes(DT);
-  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7, tiles = (int)(shape >> 10);
-  const int bid = (int)blockIdx.x;
-  const int call = (bid >= tiles) + (bid >= 2 * tiles);
-  const int nt = bid - call * tiles;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int KB = K >> 7, nq = K >> 3;
   const int lds_stride = K + 16;
 
   // ---- 1. every load of the wave, activations first
-  const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
   const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
   // byte offset of this lane's chunk c in a row (out of range past K)
   const auto choff = [&](int c) {
@@ -88,10 +83,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
     return q < nq ? (uint32_t)(8 * q * EB) : kOob;
   };
   // Order matters: x needs only preloaded arguments and goes out first; the
-  // gain pointer of calls past the second may still be on its way from the
-  // argument buffer, and the weights are not needed until the contraction,
-  // thousands of cycles later.  (Waits are in issue order, so whatever is
-  // issued later never holds up the wait for x.)
+  // gain comes next (it is needed right after the first row reduction), the
+  // weights last: they are not needed until the contraction, thousands of
+  // cycles later.  Waits are in issue order, so whatever is issued later
+  // never holds up the wait for what was issued earlier.
   Chunk8<DT> xc[MR][kDecChunks];
 #pragma unroll
   for (int c = 0; c < kDecChunks; ++c)
@@ -100,20 +95,29 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
       xc[m][c] = bload_chunk<DT>(xr, m < M ? choff(c) + (uint32_t)(m * K * EB) : kOob);
   __builtin_amdgcn_sched_barrier(0);
   const uint4 *pk = call == 0 ? p0 : (call == 1 ? p1 : p2);
+  const rsrc_t wr = make_rsrc(pk + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
   const void *gain = call == 0 ? g0 : (call == 1 ? g1 : g2);
+  Chunk8<DT> gc[kDecChunks];
+  v4i wt[kDecTiles];
+  // GAIN_LATE: the gain pointer has to come from the argument buffer, so
+  // the weights are issued before waiting for it
+#pragma unroll
+  for (int t = 0; t < kDecTiles; ++t)
+    if constexpr (GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
+#pragma unroll
+    for (int c = 0; c < kDecChunks; ++c) gc[c] = bload_chunk<DT>(gr, choff(c));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < kDecTiles; ++t)
+    if constexpr (!GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
   const float *bp = call == 0 ? b0 : (call == 1 ? b1 : b2);
   void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
-  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
-  const rsrc_t wr = make_rsrc(pk + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
-  Chunk8<DT> gc[kDecChunks];
-#pragma unroll
-  for (int c = 0; c < kDecChunks; ++c) gc[c] = bload_chunk<DT>(gr, choff(c));
   const float beta = *bp;
-  __builtin_amdgcn_sched_barrier(0);
-  v4i wt[kDecTiles];
-#pragma unroll
-  for (int t = 0; t < kDecTiles; ++t) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
-  __builtin_amdgcn_sched_barrier(0);
 
   // chunk c of this wave holds at least one element of the row
   const auto live = [&](int c) { return 256 * c + 64 * w < nq; };
@@ -262,6 +266,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   }
 }
 
+// One call.  Every argument fits the 14 preloaded SGPRs.
+// shape = K/128 | M << 7 | tiles << 10.
+template <int DT, int OUT, int MR>
+__global__ __launch_bounds__(256, 2) void decode_kernel(const void *x, uint32_t shape, float eps,
+                                                        const uint4 *packed, const void *gain,
+                                                        const float *beta, void *out) {
+  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
+  decode_body<DT, OUT, MR, false>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0, packed, packed,
+                           packed, gain, gain, gain, beta, beta, beta, out, out, out);
+}
+
+// Up to three calls of one shape; workgroup b works on call b / tiles.  The
+// activation and weight pointers are preloaded, the rest is fetched.
+template <int DT, int OUT, int MR>
+__global__ __launch_bounds__(256, 2) void decode3_kernel(
+    const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
+    const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
+    const void *g2, const float *b0, const float *b1, const float *b2, void *o0, void *o1,
+    void *o2) {
+  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
+  const int tiles = (int)(shape >> 10);
+  const int bid = (int)blockIdx.x;
+  const int call = (bid >= tiles) + (bid >= 2 * tiles);
+  const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
+  decode_body<DT, OUT, MR, true>(x, K, M, tiles, bid - call * tiles, eps, call, p0, p1, p2, g0, g1, g2,
+                           b0, b1, b2, o0, o1, o2);
+}
+
 template <int DT, int OUT>
 static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
@@ -270,14 +302,23 @@ static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
   const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 10);
   const uint4 *p[3];
   for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
-  // fp32 rows take twice the registers: the 4-row variant would spill, so
-  // fp32 decodes one row per launch (decode_fits)
-  if (DT == BL_F32 || a.M == 1)
-    decode_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(
+  // fp32 activations decode one row per launch (decode_fits)
+  constexpr int MR4 = DT == BL_F32 ? 1 : (int)kDecodeMaxM;
+  if (a.ncalls == 1) {
+    if (a.M == 1)
+      decode_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],
+                                                            a.gain[0], a.beta[0], a.out[0]);
+    else
+      decode_kernel<DT, OUT, MR4><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],
+                                                              a.gain[0], a.beta[0], a.out[0]);
+    return;
+  }
+  if (a.M == 1)
+    decode3_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(
         a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
         a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
   else
-    decode_kernel<DT, OUT, DT == BL_F32 ? 1 : (int)kDecodeMaxM><<<grid, 256, lds, stream>>>(
+    decode3_kernel<DT, OUT, MR4><<<grid, 256, lds, stream>>>(
         a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
         a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
 }
