@@ -47,6 +47,38 @@ I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA
 GRAPH_CHUNK = 512             # at most this many steps per captured graph
 GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
 
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (one run each) and scaled by what the same
+# counters read for a plain 256 MiB device copy (2047.8 and 1024.0 bytes per
+# unit); the commands and tables are under profiles/.  A figure holds only
+# for the kernel sources it was taken on: they are hashed, and a changed
+# kernel reports traffic null until it is measured again.
+KERNEL_SOURCES = {"decode": ["decode.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
+                  "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
+TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
+    "c2": ("decode", "498f2845ae0dedbd", 722592),
+    "c4": ("gemm", "d0dd2c91e68c7fd4", 80305882),
+    "c5-M1": ("decode", "498f2845ae0dedbd", 5353258),
+}
+
+
+def sources_sha(family):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "ternary_weight_lm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(key):
+    """Counter-measured HBM bytes per launch, or None if not measured for
+    this workload or the kernel changed since."""
+    if key not in TRAFFIC:
+        return None
+    family, sha, byt = TRAFFIC[key]
+    return byt if sources_sha(family) == sha else None
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -430,6 +462,8 @@ def main():
         roof = roofline(wl, inp, reps)
         roof["timed_region"] = "a graph of the dominant kernel's launches only"
 
+    roof["traffic"] = traffic(wl.key)
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
