@@ -57,7 +57,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "rowquant.h", "bl_common.h", "bl_laun
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "498f2845ae0dedbd", 722592),
-    "c4": ("gemm", "d0dd2c91e68c7fd4", 80305882),
+    "c4": ("gemm", "41635cfea896e503", 57933216),
     "c5-M1": ("decode", "498f2845ae0dedbd", 5353258),
 }
 

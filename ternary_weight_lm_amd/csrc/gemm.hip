@@ -23,8 +23,9 @@
 // Epilogue: subtract rowsum, multiply by beta / s_m, round to the output
 // dtype (or store the exact int32 accumulator).
 // Workgroup ids are remapped so each of the 8 XCDs (which receive ids
-// round-robin) works on a contiguous range of tiles, keeping A rows and B
-// columns of neighbouring tiles in that XCD's L2.
+// round-robin) works on a contiguous range of a banded column-major tile
+// order, keeping the A rows and B columns of the tiles it runs together in
+// that XCD's L2.
 #include <algorithm>
 
 #include "bl_common.h"
@@ -86,6 +87,8 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
   __syncthreads();
 }
 
+constexpr int kBandRows = 4;  // tile rows per band of the tile order
+
 template <int MI, int OUT>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
@@ -106,7 +109,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
   const int xcd = bid % 8, local = bid / 8;
   const int t = xcd < rem ? xcd * (per + 1) + local
                           : rem * (per + 1) + (xcd - rem) * per + local;
-  const int tm = t / tiles_n, tn = t % tiles_n;
+  // Inside the sequence, tiles go column by column through bands of
+  // kBandRows tile rows, so the ~64 workgroups an XCD runs at once share a
+  // few A row tiles and a few B column tiles (about 1 MiB each) in its L2
+  // instead of sweeping every B column tile once per tile row.
+  const int band = t / (kBandRows * tiles_n), r = t - band * kBandRows * tiles_n;
+  const int rows_here = min(kBandRows, tiles_m - band * kBandRows);
+  const int tm = band * kBandRows + r % rows_here, tn = r / rows_here;
   const int m0 = tm * BM, n0 = tn * BN;
   const int KB = K >> 7;
   const int NT = N >> 5;
