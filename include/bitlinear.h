@@ -106,7 +106,7 @@ enum {
 enum {
     BL_PATH_AUTO = 0,    /* choose by M (what bitlinear_forward does)        */
     BL_PATH_FUSED = 1,   /* one kernel: norm + quant + skinny contraction    */
-    BL_PATH_SKINNY = 2,  /* act-quant kernel, then skinny contraction (M<=16)*/
+    BL_PATH_SKINNY = 2,  /* act-quant kernel, then skinny contraction (M<=64)*/
     BL_PATH_MFMA = 3     /* act-quant kernel, then tiled MFMA contraction    */
 };
 
@@ -149,11 +149,10 @@ int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
 
 /* Same as bitlinear_forward with an explicit execution path (BL_PATH_*).
  * BL_PATH_FUSED requires M <= 16, K <= 8192 and M * (K + 16) <= 56320 (its
- * int8 activations live in LDS); BL_PATH_SKINNY requires M <= 16 (else
- * BL_ERR_SHAPE).  Every path computes the same function: the integer codes
- * and accumulators are identical, y may differ only where a pre-rounding
- * activation value lies within a few fp32 ulps of a .5 boundary (the fp64
- * sum of squares is added in a different order). */
+ * int8 activations live in LDS); BL_PATH_SKINNY requires M <= 64 (else
+ * BL_ERR_SHAPE).  Every path computes the same function with the same
+ * arithmetic in the same order (the fp64 sum of squares included), so the
+ * codes, scales, accumulators and y are bit-identical across paths. */
 int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
                            const void *gain, const void *packed,
                            const float *beta, int64_t N, void *y, int y_dtype,
@@ -175,10 +174,12 @@ typedef struct bl_call {
     int64_t M, K, N;
 } bl_call;
 
-/* Several independent FusedBitLinear forwards in as few launches as
- * possible (one launch per 16 calls), for decode steps where each call is
- * too small to fill the GPU on its own -- e.g. the i/f/g/o projections of an
- * HGRNBit block (hysenlabs ja review, section "HGRNBit という層構成を読む").
+/* Several independent FusedBitLinear forwards in few launches, for decode
+ * steps where each call is too small to fill the GPU on its own -- e.g. the
+ * i/f/g/o projections of an HGRNBit block (hysenlabs ja review, section
+ * "HGRNBit という層構成を読む").  Consecutive calls of one shape with
+ * M <= 4 (fp32 x: M == 1) go out up to three per launch of the decode
+ * kernel; the remaining calls up to 16 per launch of the skinny kernel.
  *   calls   HOST array of ncalls descriptors (read during the call only)
  *   Every call must satisfy the BL_PATH_FUSED limits (M <= 16, K <= 8192,
  *   M * (K + 16) <= 56320) and the usual shape / alignment rules, and all
@@ -212,7 +213,7 @@ int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
  *           the stored codes (Wq + 1) back into the signed sum, so a wrong
  *           rowsum gives a wrong acc.
  *   acc     device int32 [M, N] (written)
- *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 16) or BL_PATH_MFMA;
+ *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 64) or BL_PATH_MFMA;
  *           BL_PATH_FUSED is BL_ERR_PATH here. */
 int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
                        int64_t K, const void *packed, int64_t N, int32_t *acc,
@@ -224,7 +225,7 @@ int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
  * ersetzen" and figure panel 4).  xq, s and rowsum are what
  * bitlinear_act_quant writes; with them this is the second half of
  * bitlinear_forward, so one quantized input can feed several projections.
- *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 16) or BL_PATH_MFMA. */
+ *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 64) or BL_PATH_MFMA. */
 int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
                        int64_t M, int64_t K, const void *packed,
                        const float *beta, int64_t N, void *y, int y_dtype,

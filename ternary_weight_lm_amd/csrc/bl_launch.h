@@ -35,7 +35,8 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             int64_t K, void *out, int out_kind,
                             hipStream_t stream);
 
-// Skinny contraction for M <= 16: one workgroup per 32 output rows.
+// Skinny contraction for M <= kSkinnyMaxM (fused: M <= kFusedMaxM): one
+// workgroup per 32 output rows.
 // fused = true: x / gain / eps are read and normalized + quantized inside;
 // fused = false: xq / s / rowsum come from a previous act-quant launch.
 struct SkinnyArgs {
@@ -88,6 +89,6 @@ inline bool decode_fits(int64_t M, int64_t K, int x_dtype) {
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;
 constexpr int64_t kFusedMaxK = 8192;
-constexpr int64_t kSkinnyMaxM = 16;
+constexpr int64_t kSkinnyMaxM = 64;  // pre-quantized skinny calls
 
 }  // namespace bl

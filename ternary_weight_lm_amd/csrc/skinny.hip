@@ -53,12 +53,15 @@ struct SkinnyLaunch {
   float eps;
 };
 
-template <bool FUSED, int DT, int OUT, int MAXC, int RMODE>
+// MB: 16-row MFMA blocks (pre-quantized calls take up to 4, i.e. M <= 64;
+// fused calls 1).
+template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
+  static_assert(!FUSED || MB == 1, "fused calls have at most 16 rows");
   extern __shared__ __align__(16) int8_t xs[];  // fused: [M][K + 16] int8
-  __shared__ int red[4][8][64];
-  __shared__ float s_row[16];
-  __shared__ int rs_row[16];
+  __shared__ int red[4][MB * 8][64];
+  __shared__ float s_row[16 * MB];
+  __shared__ int rs_row[16 * MB];
 
   int c = 0;
   if constexpr (MAXC > 1) {
@@ -67,17 +70,38 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   const SkinnyCall &p = L.call[c];
   const int nt = (int)blockIdx.x - L.first_block[c];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int M = p.M, K = p.K, KB = K >> 7;
   const int lds_stride = K + 16;
   const int nmine = w < KB ? (KB - w + 3) / 4 : 0;
-  const uint4 *wp = p.packed + (int64_t)nt * KB * 64 + lane;
 
-  // ---- 1. weight loads of the first batch
-  uint4 wr[kSkinnyBatch];
+  // ---- 1. loads.  Buffer loads whose out-of-range offsets read as zero:
+  // none is conditional, so each wait below is for exactly the loads it
+  // needs (waits are in issue order).  Pre-quantized calls fetch the row
+  // scale and row sum first (tiny, used only by the epilogue), then the
+  // weight tiles of the first batch.
+  float s_reg = 0.0f;
+  int rs_reg = 0;
+  if constexpr (!FUSED) {
+    const uint32_t ro = tid < M ? (uint32_t)(4 * tid) : 0x40000000u;
+    rs_reg = __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.rowsum), (short)0, 4 * M, 0x00020000),
+        (int)ro, 0, 0);
+    if constexpr (OUT != kOutI32)
+      s_reg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.s), (short)0, 4 * M, 0x00020000),
+          (int)ro, 0, 0));
+  }
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4 *>(p.packed + (int64_t)nt * KB * 64), (short)0, KB * 1024, 0x00020000);
+  const auto w_load = [&](int tile) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                       wrs, (w + 4 * tile) * 1024 + lane * 16, 0, 0));
+  };
+  v4i wr[kSkinnyBatch];
 #pragma unroll
-  for (int t = 0; t < kSkinnyBatch; ++t)
-    if (t < nmine) wr[t] = wp[(int64_t)(w + 4 * t) * 64];
+  for (int t = 0; t < kSkinnyBatch; ++t) wr[t] = w_load(t);
 
   // ---- 2. activations
   if constexpr (FUSED) {
@@ -96,61 +120,101 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
         rs_row[m] = rs;
       }
     }
-  } else {
-    if constexpr (OUT != kOutI32) {
-      if (tid < M) s_row[tid] = p.s[tid];
-    }
-    if (tid < M) rs_row[tid] = p.rowsum[tid];
+    __syncthreads();
+    // rescale factor beta / s_m once per row
+    if (OUT != kOutI32 && tid < M) s_row[tid] = div_rn(*p.beta, s_row[tid]);
   }
-  __syncthreads();
 
   // ---- 3. contraction
-  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  v4i acc0[MB], acc1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = v4i{0, 0, 0, 0};
   const int arow = lane & 15;
-  const bool arow_ok = arow < M;
+  // pre-quantized A: buffer loads over xq (rows >= M read as zero), one tile
+  // ahead of the MFMAs; unconditional (the index is clamped), so the wait
+  // for a tile's operands never waits for the loads issued after them
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t *>(p.xq), (short)0, FUSED ? 0 : M * K, 0x00020000);
+  const auto a_off = [&](int tile, int mb, int s2) {
+    const int kb = w + 4 * tile;
+    return (uint32_t)((16 * mb + arow) * K + kb * 128 + 32 * (lane >> 4) + 16 * s2);
+  };
+  const auto a_load = [&](int tile, int mb, int s2) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)a_off(tile, mb, s2), 0, 0));
+  };
+  v4i an[MB][2];
+  if constexpr (!FUSED) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) an[mb][s2] = a_load(0, mb, s2);
+  }
   for (int base = 0; base < nmine; base += kSkinnyBatch) {
     if (base > 0) {
 #pragma unroll
-      for (int t = 0; t < kSkinnyBatch; ++t)
-        if (base + t < nmine) wr[t] = wp[(int64_t)(w + 4 * (base + t)) * 64];
+      for (int t = 0; t < kSkinnyBatch; ++t) wr[t] = w_load(base + t);
     }
 #pragma unroll
     for (int t = 0; t < kSkinnyBatch; ++t) {
       if (base + t >= nmine) break;
       const int kb = w + 4 * (base + t);
-      const uint4 u = wr[t];
+      const v4i u = wr[t];
+      v4i a[MB][2];
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          a[0][s2] = v4i{0, 0, 0, 0};
+          if (arow < M)
+            a[0][s2] = *reinterpret_cast<const v4i *>(xs + arow * lds_stride + kb * 128 +
+                                                      32 * (lane >> 4) + 16 * s2);
+        }
+      } else {
+        const int nxt = min(base + t + 1, nmine - 1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            a[mb][s2] = an[mb][s2];
+            an[mb][s2] = a_load(nxt, mb, s2);
+          }
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int koff = kb * 128 + 32 * (lane >> 4) + 16 * s2;
-        v4i a = {0, 0, 0, 0};
-        if (arow_ok) {
-          if constexpr (FUSED)
-            a = *reinterpret_cast<const v4i *>(xs + arow * lds_stride + koff);
-          else
-            a = *reinterpret_cast<const v4i *>(p.xq + (int64_t)arow * K + koff);
+        // word (h, s2) of a lane slot sits at dword 2h + s2
+        const v4i b0 = unpack_codes((uint32_t)u[s2]);
+        const v4i b1 = unpack_codes((uint32_t)u[2 + s2]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          acc0[mb] = mfma16x16x64(a[mb][s2], b0, acc0[mb]);
+          acc1[mb] = mfma16x16x64(a[mb][s2], b1, acc1[mb]);
         }
-        const v4i b0 = unpack_codes(s2 ? u.y : u.x);
-        const v4i b1 = unpack_codes(s2 ? u.w : u.z);
-        acc0 = mfma16x16x64(a, b0, acc0);
-        acc1 = mfma16x16x64(a, b1, acc1);
       }
     }
   }
 
   // ---- 4. cross-wave sum and epilogue
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[w][i][lane] = acc0[i];
-    red[w][4 + i][lane] = acc1[i];
+  if constexpr (!FUSED) {
+    if (tid < M) {
+      if constexpr (OUT != kOutI32) s_row[tid] = div_rn(*p.beta, s_reg);
+      rs_row[tid] = rs_reg;
+    }
   }
-  __syncthreads();
-  const float bt = OUT == kOutI32 ? 0.0f : *p.beta;
+  // red[w][8 mb + 4 h + i][lane]: row 16 mb + 4 (lane / 16) + i, column
+  // 16 h + lane % 16 of the tile
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[w][8 * mb + i][lane] = acc0[mb][i];
+      red[w][8 * mb + 4 + i][lane] = acc1[mb][i];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2 * MB; ++q) {
     const int idx = tid + 256 * q;
     const int j = idx >> 6, Lq = idx & 63;
-    const int h = j >> 2, i = j & 3;
-    const int m = 4 * (Lq >> 4) + i;
+    const int mb = j >> 3, h = (j >> 2) & 1, i = j & 3;
+    const int m = 16 * mb + 4 * (Lq >> 4) + i;
     if (m >= M) continue;
     const int n = nt * 32 + 16 * h + (Lq & 15);
     const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
@@ -158,7 +222,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
     if constexpr (OUT == kOutI32) {
       reinterpret_cast<int32_t *>(p.out)[o] = v;
     } else {
-      store1<OUT>(p.out, o, (float)v * div_rn(bt, s_row[m]));
+      store1<OUT>(p.out, o, (float)v * s_row[m]);
     }
   }
 }
@@ -179,41 +243,43 @@ static SkinnyCall to_call(const SkinnyArgs &a) {
   return c;
 }
 
-template <bool FUSED, int DT, int MAXC, int RMODE>
+template <bool FUSED, int DT, int MAXC, int RMODE, int MB>
 static void launch_out(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                        hipStream_t stream) {
   switch (out_kind) {
-    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
-    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
-    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
-    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
+    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
   }
 }
 
-template <bool FUSED, int DT, int MAXC>
-static void launch_mode(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
-                        int64_t kmax, hipStream_t stream) {
-  if constexpr (!FUSED) {
-    launch_out<FUSED, DT, MAXC, kRowFloat>(L, out_kind, grid, lds, stream);
-  } else {
-    if (row_mode((int)kmax) == kRowFloat)
-      launch_out<FUSED, DT, MAXC, kRowFloat>(L, out_kind, grid, lds, stream);
-    else
-      launch_out<FUSED, DT, MAXC, kRowRaw>(L, out_kind, grid, lds, stream);
-  }
+// Fused calls: row-quantizer mode from the largest K of the launch.
+template <int DT, int MAXC>
+static void launch_fused(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
+                         int64_t kmax, hipStream_t stream) {
+  if (row_mode((int)kmax) == kRowFloat)
+    launch_out<true, DT, MAXC, kRowFloat, 1>(L, out_kind, grid, lds, stream);
+  else
+    launch_out<true, DT, MAXC, kRowRaw, 1>(L, out_kind, grid, lds, stream);
 }
 
 template <int MAXC>
 static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
-                       unsigned grid, size_t lds, int64_t kmax, hipStream_t stream) {
+                       unsigned grid, size_t lds, int64_t kmax, int64_t M, hipStream_t stream) {
   if (fused) {
     switch (x_dtype) {
-      case BL_F32: launch_mode<true, BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
-      case BL_F16: launch_mode<true, BL_F16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
-      default: launch_mode<true, BL_BF16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+      case BL_F32: launch_fused<BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+      case BL_F16: launch_fused<BL_F16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
+      default: launch_fused<BL_BF16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
     }
-  } else {
-    launch_mode<false, BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream);
+  } else if constexpr (MAXC == 1) {  // pre-quantized calls are never grouped
+    if (M <= 16)
+      launch_out<false, BL_F32, 1, kRowFloat, 1>(L, out_kind, grid, lds, stream);
+    else if (M <= 32)
+      launch_out<false, BL_F32, 1, kRowFloat, 2>(L, out_kind, grid, lds, stream);
+    else
+      launch_out<false, BL_F32, 1, kRowFloat, 4>(L, out_kind, grid, lds, stream);
   }
 }
 
@@ -255,7 +321,7 @@ hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
   L.ncalls = 1;
   L.eps = a.eps;
   const size_t lds = a.fused ? (size_t)a.M * (size_t)(a.K + 16) : 0;
-  launch_any<1>(L, a.fused, a.x_dtype, a.out_kind, (unsigned)(a.N / 32), lds, a.K, stream);
+  launch_any<1>(L, a.fused, a.x_dtype, a.out_kind, (unsigned)(a.N / 32), lds, a.K, a.M, stream);
   return hipGetLastError();
 }
 
@@ -298,7 +364,7 @@ hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_
     L.ncalls = n;
     L.eps = rest[base].eps;
     launch_any<kGroupMax>(L, true, rest[base].x_dtype, rest[base].out_kind, (unsigned)blocks,
-                          lds, kmax, stream);
+                          lds, kmax, 16, stream);
   }
   return hipGetLastError();
 }

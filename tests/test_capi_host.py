@@ -65,7 +65,9 @@ def test_select_path_rule():
     assert L.bitlinear_select_path(4, 16384) == 2     # fused needs K <= 8192
     assert L.bitlinear_select_path(5, 1024) == 2
     assert L.bitlinear_select_path(16, 1024) == 2
-    assert L.bitlinear_select_path(17, 1024) == 3
+    assert L.bitlinear_select_path(17, 1024) == 2
+    assert L.bitlinear_select_path(64, 7040) == 2
+    assert L.bitlinear_select_path(65, 1024) == 3
     assert L.bitlinear_select_path(4096, 2048) == 3
     assert L.bitlinear_select_path(0, 1024) == SHAPE
     assert L.bitlinear_select_path(1, 1000) == SHAPE
@@ -112,7 +114,7 @@ def test_forward_validation_order_and_codes():
     assert fwd(beta=D + 2) == ALIGN
     # path limits
     assert fwd(M=17, path=1) == SHAPE
-    assert fwd(M=17, path=2) == SHAPE
+    assert fwd(M=65, path=2) == SHAPE
     assert fwd(M=16, K=8192, path=1) == SHAPE   # fused LDS budget exceeded
     assert fwd(M=1, K=8320, path=1) == SHAPE    # fused K limit
 
@@ -151,13 +153,13 @@ def test_stage_entry_points_validation():
     assert L.bitlinear_act_quant(A, 1, B, 0, 1024, 1e-8, None, None, None, None) == OK
     assert L.bitlinear_gemm_i32(A, B, 4, 1024, C, 1000, D, 0, None) == SHAPE
     assert L.bitlinear_gemm_i32(A, B, 4, 1024, C, 1024, D, 1, None) == PATH
-    assert L.bitlinear_gemm_i32(A, B, 17, 1024, C, 1024, D, 2, None) == SHAPE
+    assert L.bitlinear_gemm_i32(A, B, 65, 1024, C, 1024, D, 2, None) == SHAPE
     assert L.bitlinear_gemm_i32(None, B, 4, 1024, C, 1024, D, 0, None) == NULL
     assert L.bitlinear_gemm_i32(A, B + 2, 4, 1024, C, 1024, D, 0, None) == ALIGN
     assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y, 7, 0, None) == DTYPE
     assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1000, Y, 1, 0, None) == SHAPE
     assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y, 1, 1, None) == PATH
-    assert L.bitlinear_contract(A, B, E, 17, 1024, C, D, 1024, Y, 1, 2, None) == SHAPE
+    assert L.bitlinear_contract(A, B, E, 65, 1024, C, D, 1024, Y, 1, 2, None) == SHAPE
     assert L.bitlinear_contract(A, None, E, 4, 1024, C, D, 1024, Y, 1, 0, None) == NULL
     assert L.bitlinear_contract(A, B, E, 4, 1024, C, D, 1024, Y + 4, 1, 0, None) == ALIGN
     assert L.bitlinear_contract(A, B, E, 0, 1024, C, D, 1024, None, 1, 0, None) == OK

@@ -84,10 +84,11 @@ def _random_codes(M, K, seed):
 @pytest.mark.parametrize("path", [tw.BL_PATH_SKINNY, tw.BL_PATH_MFMA])
 @pytest.mark.parametrize("M,N,K", [(1, 32, 128), (3, 96, 384), (16, 160, 1280),
                                    (17, 160, 1280), (33, 1024, 1024), (130, 96, 640),
-                                   (16, 64, 7040), (200, 256, 2048)])
+                                   (16, 64, 7040), (200, 256, 2048), (32, 96, 2560),
+                                   (48, 64, 7040), (64, 160, 1280), (40, 64, 9216)])
 def test_gemm_i32_bit_exact(path, M, N, K):
-    if path == tw.BL_PATH_SKINNY and M > 16:
-        pytest.skip("skinny path is for M <= 16")
+    if path == tw.BL_PATH_SKINNY and M > 64:
+        pytest.skip("skinny path is for M <= 64")
     say(f"gemm_i32 path={path} M={M} N={N} K={K}")
     xq = _random_codes(M, K, M * 7 + K)
     r = np.random.default_rng(N + K)
@@ -112,6 +113,9 @@ FWD_CASES = [
     (tw.BL_PATH_SKINNY, 1, 160, 1280, "fp16", "fp16"),
     (tw.BL_PATH_SKINNY, 11, 1024, 1024, "bf16", "bf16"),
     (tw.BL_PATH_SKINNY, 16, 64, 2048, "fp32", "fp16"),
+    (tw.BL_PATH_SKINNY, 32, 160, 2048, "fp16", "fp16"),
+    (tw.BL_PATH_SKINNY, 45, 96, 5632, "bf16", "bf16"),
+    (tw.BL_PATH_SKINNY, 64, 64, 1024, "fp32", "fp32"),
     (tw.BL_PATH_MFMA, 1, 96, 384, "fp16", "fp16"),
     (tw.BL_PATH_MFMA, 17, 160, 1280, "bf16", "bf16"),
     (tw.BL_PATH_MFMA, 33, 1024, 1024, "fp32", "fp32"),
@@ -120,6 +124,8 @@ FWD_CASES = [
     (tw.BL_PATH_AUTO, 1, 1024, 1024, "fp16", "fp16"),
     (tw.BL_PATH_AUTO, 8, 256, 2560, "bf16", "bf16"),
     (tw.BL_PATH_AUTO, 64, 256, 2560, "bf16", "bf16"),
+    (tw.BL_PATH_AUTO, 3, 96, 7040, "fp16", "fp32"),
+    (tw.BL_PATH_AUTO, 2, 64, 1024, "fp32", "fp32"),
 ]
 
 
@@ -183,6 +189,42 @@ def test_grouped_matches_single_calls():
     torch.cuda.synchronize()
     for it in many:
         assert torch.equal(it[4], singles[0])
+
+
+def test_paths_agree_bitwise_mid_m():
+    say("paths agree mid M")
+    for M in (24, 40, 64):
+        N, K = 160, 2560
+        x = synth.make_x(78 + M, 0, 0, M, K, "bf16", outlier_p=0.01)
+        g = synth.make_gain(78 + M, 0, 0, K, "bf16")
+        packed, beta = tw.pack(synth.make_w(78 + M, 0, 0, N, K).to(DEV))
+        xd, gd = x.to(DEV), g.to(DEV)
+        a = tw.forward(xd, gd, packed, beta, N, path=tw.BL_PATH_SKINNY)
+        b = tw.forward(xd, gd, packed, beta, N, path=tw.BL_PATH_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_grouped_mixed_kernels():
+    """Calls the decode kernel does not take (M of 5..16, fp32 rows with
+    M > 1) share launches of the skinny kernel; results equal single calls."""
+    say("grouped mixed")
+    for dt, shapes in (("bf16", [(8, 96, 1024), (1, 96, 1024), (16, 64, 2560), (1, 96, 1024),
+                                 (1, 96, 1024), (1, 96, 1024), (12, 32, 384)]),
+                       ("fp32", [(2, 64, 1024), (1, 64, 1024), (3, 32, 512)])):
+        tdt = synth.DTYPES[dt]
+        items, singles = [], []
+        for i, (M, N, K) in enumerate(shapes):
+            x = synth.make_x(950 + i, 0, 0, M, K, dt).to(DEV)
+            g = synth.make_gain(950 + i, 0, 0, K, dt).to(DEV)
+            packed, beta = tw.pack(synth.make_w(950 + i, 0, 0, N, K).to(DEV))
+            y = torch.full((M, N), 7.0, dtype=tdt, device=DEV)
+            items.append((x, g, packed, beta, y))
+            singles.append(tw.forward(x, g, packed, beta, N, path=tw.BL_PATH_FUSED))
+        tw.bitlinear_forward_grouped(items, tdt, tdt)
+        torch.cuda.synchronize()
+        for (x, g, packed, beta, y), ref in zip(items, singles):
+            assert torch.equal(y, ref)
 
 
 def test_empty_batch_is_noop():
