@@ -16,10 +16,11 @@
 //     out-of-range lanes / tiles read as zero, so none is conditional and the
 //     compiler's wait for the activations does not also wait for the weights.
 //   * The normalization of a row is split over the 4 waves (wave w owns the
-//     8-element chunks 64w + lane + 256c).  The three row reductions are
-//     DPP trees inside each wave plus a 4-entry LDS exchange, combined in a
-//     fixed order: the same association the act-quant kernel uses, so codes
-//     and scales are bit-identical across paths.
+//     8-element chunks 64w + lane + 256c).  The sum of squares meets per lane
+//     in LDS ((p0 + p1) + (p2 + p3) over the waves) before one DPP tree: the
+//     association the act-quant kernel uses, so codes and scales are
+//     bit-identical across paths.  The absmax and the code row sum (exact
+//     in any order) are DPP trees per wave plus a 4-entry LDS exchange.
 //   * One workgroup owns one packed 32-row tile column; the 4 waves take
 //     its K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
 //     registers (weights) and LDS (codes), and the partial sums meet in LDS.
@@ -34,25 +35,7 @@ constexpr int kDecTiles = 16;   // weight tiles per wave: K <= 4 * 16 * 128
 constexpr int kDecChunks = 4;   // chunks per lane and row: K <= 4 * 256 * 8
 constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  // raw (untyped) buffer, stride 0: offsets >= bytes read as zero
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ v4i bload(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-template <int DT>
-__device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
-  Chunk8<DT> c;
-  c.u[0] = bload(r, off);
-  if constexpr (DT == BL_F32) c.u[1] = bload(r, off + 16);
-  return c;
-}
+// (make_rsrc / bload / bload_chunk: buffer loads from rowquant.h)
 
 // The body of both kernels below.  The call's packed / gain / beta / out
 // pointers are selected only after the activation loads are issued: in the
@@ -64,7 +47,7 @@ __device__ __forceinline__ void decode_body(
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
     const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
-  __shared__ double part_ss[MR][4];
+  __shared__ double part_ss[MR][4][64];
   __shared__ float part_max[MR][4];
   __shared__ int part_rs[MR][4];
   __shared__ int red[4][MR][2][16];
@@ -125,7 +108,7 @@ __device__ __forceinline__ void decode_body(
   // Rows past M read as zeros and are carried through every step (their
   // results are never stored): the MR row chains stay free of branches and
   // interleave.
-  // ---- 2. sum of squares: this wave's slot group, then a 4-entry exchange
+  // ---- 2. sum of squares: this wave's slot group, exchanged per lane
   double ss[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) ss[m] = 0.0;
@@ -141,17 +124,16 @@ __device__ __forceinline__ void decode_body(
       }
     }
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const double t = wave_sum(ss[m]);
-    if (lane == 0) part_ss[m][w] = t;
-  }
+  for (int m = 0; m < MR; ++m) part_ss[m][w][lane] = ss[m];
   __syncthreads();
 
   // ---- 3. absmax of the normalized row
   float r[MR], amax[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    r[m] = rms_inv((part_ss[m][0] + part_ss[m][1]) + (part_ss[m][2] + part_ss[m][3]), K, eps);
+    const double lsum = (part_ss[m][0][lane] + part_ss[m][1][lane]) +
+                        (part_ss[m][2][lane] + part_ss[m][3][lane]);
+    r[m] = rms_inv(wave_sum(lsum), K, eps);
     amax[m] = 0.0f;
   }
 #pragma unroll

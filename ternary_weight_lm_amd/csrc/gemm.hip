@@ -33,9 +33,9 @@
 
 namespace bl {
 
-// One k-block of 128: multiply the A tile in `cur` (LDS) by the B codes in
-// b0/b1, request k-block kb+2 (A into a_load, B into b0/b1 once they are
-// consumed) and stage k-block kb+1 (a_store) into `next`.  Called twice per
+// One k-block of 128: request k-block kb+2 (A into a_load, B into b0/b1
+// once they are consumed), stage k-block kb+1 (a_store) into `next`, and
+// multiply the A tile in `cur` (LDS) by the B codes in b0/b1.  Called twice per
 // loop trip with the register sets swapped, so no register is ever copied
 // (a copy would have to wait for its load and serialize the pipeline).
 template <int MI>
@@ -64,6 +64,15 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
       a[mi][s2] = *reinterpret_cast<const v4i *>(cur + row * 128 + (swz(row, ch) << 4));
     }
   }
+  // Stage k-block kb+1 into `next` now: every wave finished reading that
+  // buffer before the barrier that ended the previous k-block, and writing
+  // it here takes the LDS write latency off the barrier below.
+#pragma unroll
+  for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(next + a_dst[j]) = a_store[j];
+  // all 2*MI LDS reads go out before the first MFMA: left to itself the
+  // scheduler reads two operands at a time and waits for each pair, which
+  // exposes the LDS latency 2*MI/2 times per k-block
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     // word (h, s2) of a lane slot sits at dword 2h + s2
@@ -82,8 +91,6 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
   __builtin_amdgcn_sched_barrier(0);
   b0 = b_src0[k2 * 64];
   b1 = b_src1[k2 * 64];
-#pragma unroll
-  for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(next + a_dst[j]) = a_store[j];
   __syncthreads();
 }
 
@@ -180,35 +187,61 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
     gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, a_src, a_dst, b_src0, b_src1,
                     arow0, lane);
 
-  // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  Lane
-  // l < 16*MI first fetches row sum and rescale factor of the wave's row l
-  // (one division per lane); the others get them by cross-lane shuffles.
-  const int mrow = min(m0 + wm * 16 * MI + lane, M - 1);
-  const int my_rs = lane < 16 * MI ? rowsum[mrow] : 0;
-  float my_scale = 0.0f;
-  if constexpr (OUT != kOutI32) my_scale = lane < 16 * MI ? div_rn(*beta, s[mrow]) : 0.0f;
+  // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
+  // row sums and rescale factors of the wave's 16*MI rows go through a small
+  // LDS table (lane l fetches row l; one division per lane), from which each
+  // lane reads its four consecutive rows with one 16-byte read.  (A wave's
+  // LDS operations complete in order, so no barrier is needed.)
+  __shared__ __align__(16) int e_rs[4][64];
+  __shared__ __align__(16) float e_sc[4][64];
+  const int wrow0 = m0 + wm * 16 * MI;
+  if (lane < 16 * MI) {
+    const int mrow = min(wrow0 + lane, M - 1);
+    e_rs[wave][lane] = rowsum[mrow];
+    if constexpr (OUT != kOutI32) e_sc[wave][lane] = div_rn(*beta, s[mrow]);
+  }
+  const int q4 = 4 * (lane >> 4);
+  const int ncol0 = n0 + 64 * wn + (lane & 15);
+  v4i rs4[MI];
+  float sc4[MI][4];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi) {
+    rs4[mi] = *reinterpret_cast<const v4i *>(&e_rs[wave][16 * mi + q4]);
+    const v4i t = *reinterpret_cast<const v4i *>(&e_sc[wave][16 * mi + q4]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mi + 4 * (lane >> 4) + i;
-      const int m = m0 + wm * 16 * MI + r;
-      const int rs = __shfl(my_rs, r, kWave);
-      const float scale = __shfl(my_scale, r, kWave);
-      if (m >= M) continue;
+    for (int i = 0; i < 4; ++i) sc4[mi][i] = __int_as_float(t[i]);
+  }
+  const auto put = [&](int mi, int i, int nb, int64_t idx) {
+    const int v = acc[mi][nb][i] - rs4[mi][i];
+    if constexpr (OUT == kOutI32)
+      reinterpret_cast<int32_t *>(out)[idx] = v;
+    else
+      store1<OUT>(out, idx, (float)v * sc4[mi][i]);
+  };
+  if (m0 + BM <= M && n0 + BN <= N) {
+    // whole tile (all but the ragged edges): no per-element checks, one row
+    // offset per (mi, i) and constant column offsets
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + 64 * wn + 16 * nb + (lane & 15);
-        if (n >= N) continue;
-        const int v = acc[mi][nb][i] - rs;
-        const int64_t idx = (int64_t)m * N + n;
-        if constexpr (OUT == kOutI32) {
-          reinterpret_cast<int32_t *>(out)[idx] = v;
-        } else {
-          store1<OUT>(out, idx, (float)v * scale);
-        }
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rowbase = (int64_t)(wrow0 + 16 * mi + q4 + i) * N + ncol0;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) put(mi, i, nb, rowbase + 16 * nb);
       }
-    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wrow0 + 16 * mi + q4 + i;
+        if (m >= M) continue;
+        const int64_t rowbase = (int64_t)m * N + ncol0;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          if (ncol0 + 16 * nb < N) put(mi, i, nb, rowbase + 16 * nb);
+      }
+  }
 }
 
 template <int MI>

@@ -10,11 +10,14 @@
 // Sum of squares, association fixed for every kernel of the library: the
 // chunks form 256 slots (chunk index mod 256); each slot adds its x^2 terms
 // in chunk order (fma with an exact fp64 square is the plain product-then-
-// add), the slots 64v .. 64v + 63 are reduced by the DPP tree of wave_sum,
-// and the four group sums are combined as (g0 + g1) + (g2 + g3).  Here one
-// wave holds all four groups (group = c mod 4); the decode kernel gives each
-// group its own wave.  Either way the result is the same bits.  No LDS, no
-// barriers.
+// add); slots l, l+64, l+128, l+192 are combined as (p0 + p1) + (p2 + p3)
+// into lane l's value, and the 64 lane values are reduced by the DPP tree of
+// wave_sum.  Here one wave holds all four slots of a lane (slot group =
+// chunk index mod 4); the decode kernel gives each group its own wave and
+// exchanges the per-lane partials through LDS.  Either way the result is the
+// same bits.  The row and the gain are read with buffer loads (chunks past K
+// read as zero), issued together and unconditionally, so the wait for x
+// never waits for the gain.  No LDS, no barriers.
 //   pass 1: sum of x^2 (fp64)            -> r = 1/sqrt(fp32(sum/K) + eps)
 //   pass 2: max |(x * r) * g|            -> s = 127 / max(., 1e-5)
 //   pass 3: xq = clamp(rne(xn * s)), handed to the sink 8 at a time; the
@@ -35,10 +38,31 @@ __device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
   return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
 }
 
-// The row's sum of squares from the four per-lane group partials: each
-// group reduced across the wave, then (g0 + g1) + (g2 + g3).
+// The row's sum of squares from the four per-lane slot partials:
+// (p0 + p1) + (p2 + p3) in each lane, then the wave's DPP tree.
 __device__ __forceinline__ double group_sum(const double (&ss)[4]) {
-  return (wave_sum(ss[0]) + wave_sum(ss[1])) + (wave_sum(ss[2]) + wave_sum(ss[3]));
+  return wave_sum((ss[0] + ss[1]) + (ss[2] + ss[3]));
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over `bytes` bytes at base: offsets at or past `bytes` read as
+// zero (and touch no memory).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ v4i bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <int DT>
+__device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
+  Chunk8<DT> c;
+  c.u[0] = bload(r, off);
+  if constexpr (DT == BL_F32) c.u[1] = bload(r, off + 16);
+  return c;
 }
 
 // How a lane holds its chunks of the row between the three passes.
@@ -65,9 +89,11 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
   const int lane = threadIdx.x & 63;
   const int nch = (K + 511) >> 9;  // chunk rounds (some lanes idle in the last)
   const auto kof = [&](int c) { return 8 * lane + 512 * c; };
-  // c < nch is uniform across the wave; lanes past K in the last round load
-  // a valid chunk and never use it
-  const auto ld = [&](int c) { return load_chunk<DT>(xr + (int64_t)min(kof(c), K - 8) * EB); };
+  const rsrc_t xrs = make_rsrc(xr, (uint32_t)(K * EB));
+  const rsrc_t grs = make_rsrc(gr, (uint32_t)(K * EB));
+  // chunk c of the lane; zeros past K
+  const auto ld = [&](int c) { return bload_chunk<DT>(xrs, (uint32_t)(kof(c) * EB)); };
+  const auto ldg = [&](int c) { return bload_chunk<DT>(grs, (uint32_t)(kof(c) * EB)); };
 
   auto emit = [&](int k, const float *xn, float sc, int &rs) {
     int q[8];
@@ -81,10 +107,15 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
 
   if constexpr (MODE == kRowFloat) {
     // x widened once; after pass 2 the same registers hold xn
+    Chunk8<DT> xraw[kRowCache], graw[kRowCache];
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c) xraw[c] = ld(c);
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c) graw[c] = ldg(c);
     float v[kRowCache][8];
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c)
-      if (c < nch) widen<DT>(ld(c), v[c]);
+      if (c < nch) widen<DT>(xraw[c], v[c]);
     double ss[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c)
@@ -99,7 +130,7 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
     for (int c = 0; c < kRowCache; ++c)
       if (c < nch && kof(c) < K) {
         float g[8];
-        load8<DT>(gr + (int64_t)kof(c) * EB, g);
+        widen<DT>(graw[c], g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           v[c][e] = (v[c][e] * r) * g[e];
@@ -116,10 +147,14 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
   } else {
     // raw chunks (kRowRaw) or batches of 4 re-read chunks (kRowReload)
     constexpr int NC = MODE == kRowRaw ? kRowRawCache : 4;
+    // the gain is re-read (from cache) in each pass: keeping it in registers
+    // too would cost the raw mode half of its occupancy
+    constexpr bool GCACHE = false;
     Chunk8<DT> raw[NC];
-    // for_each(fn): fn(k, group, x[8]) for every chunk of the lane, in
-    // order; group = chunk index mod 4 (a constant once unrolled: NC and the
-    // reload step are multiples of 4)
+    Chunk8<DT> graw[GCACHE ? NC : 1];
+    // for_each(fn): fn(k, c, x[8]) for every chunk of the lane, in order; c
+    // is the chunk's slot in raw[] (a constant once unrolled), and c mod 4 its
+    // slot group (NC and the reload step are multiples of 4)
     static_assert(NC % 4 == 0, "chunk groups");
     auto for_each = [&](auto &&fn) {
       if constexpr (MODE == kRowRaw) {
@@ -128,46 +163,54 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
           if (c < nch && kof(c) < K) {
             float f[8];
             widen<DT>(raw[c], f);
-            fn(kof(c), c & 3, f);
+            fn(kof(c), c, f);
           }
       } else {
         for (int c0 = 0; c0 < nch; c0 += NC) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c)
-            if (c0 + c < nch) raw[c] = ld(c0 + c);
+          for (int c = 0; c < NC; ++c) raw[c] = ld(c0 + c);
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             if (c0 + c < nch && kof(c0 + c) < K) {
               float f[8];
               widen<DT>(raw[c], f);
-              fn(kof(c0 + c), c & 3, f);
+              fn(kof(c0 + c), c, f);
             }
         }
       }
     };
+    const auto gain8 = [&](int k, int c, float *g) {
+      if constexpr (GCACHE)
+        widen<DT>(graw[c], g);
+      else
+        load8<DT>(gr + (int64_t)k * EB, g);
+    };
     if constexpr (MODE == kRowRaw) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (c < nch) raw[c] = ld(c);
+      for (int c = 0; c < NC; ++c) raw[c] = ld(c);
+    }
+    if constexpr (GCACHE) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) graw[c] = ldg(c);
     }
     double ss[4] = {0.0, 0.0, 0.0, 0.0};
-    for_each([&](int, int g, const float *f) {
+    for_each([&](int, int c, const float *f) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss[g] = __builtin_fma((double)f[e], (double)f[e], ss[g]);
+      for (int e = 0; e < 8; ++e) ss[c & 3] = __builtin_fma((double)f[e], (double)f[e], ss[c & 3]);
     });
     const float r = rms_inv(group_sum(ss), K, eps);
     float amax = 0.0f;
-    for_each([&](int k, int, const float *f) {
+    for_each([&](int k, int c, const float *f) {
       float g[8];
-      load8<DT>(gr + (int64_t)k * EB, g);
+      gain8(k, c, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((f[e] * r) * g[e]));
     });
     const float sc = act_scale(wave_max(amax));
     int rs = 0;
-    for_each([&](int k, int, const float *f) {
+    for_each([&](int k, int c, const float *f) {
       float g[8], xn[8];
-      load8<DT>(gr + (int64_t)k * EB, g);
+      gain8(k, c, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) xn[e] = (f[e] * r) * g[e];
       emit(k, xn, sc, rs);
