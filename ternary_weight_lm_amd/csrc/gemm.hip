@@ -97,7 +97,7 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
 
 template <int MI, int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(
+__global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
@@ -272,9 +272,16 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *beta, int64_t M, int64_t N,
                             int64_t K, void *out, int out_kind,
                             hipStream_t stream) {
-  if (M <= 32) return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
-  if (M <= 64) return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
-  return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
+  // The tallest tile that still gives every CU a workgroup: 128-row tiles
+  // reuse each unpacked weight operand four times, but below one tile per
+  // CU the idle CUs cost more than the extra unpacking of 64-row tiles.
+  const int64_t tn = (N + 127) / 128;
+  const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
+  if (M > 64 && tiles(128) >= 256)
+    return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
+  if (M > 32 && tiles(64) >= 128)
+    return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
+  return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
 }
 
 }  // namespace bl
