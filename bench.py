@@ -56,9 +56,9 @@ GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
 KERNEL_SOURCES = {"decode": ["decode.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "498f2845ae0dedbd", 722592),
-    "c4": ("gemm", "41635cfea896e503", 57933216),
-    "c5-M1": ("decode", "498f2845ae0dedbd", 5353258),
+    "c2": ("decode", "06c57940edd5da96", 722569),
+    "c4": ("gemm", "83021cf205f6218c", 57864315),
+    "c5-M1": ("decode", "06c57940edd5da96", 5353770),
 }
 
 
