@@ -76,6 +76,12 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_epilogue.argtypes = [P, P, F, I64, I64, P]
     L.oracle_epilogue.restype = None
     L.oracle_forward.argtypes = [P, P, I64, I64, P, F, I64, F, P, P, P, P, P]
+    L.oracle_silu.restype = ctypes.c_double
+    L.oracle_silu.argtypes = [ctypes.c_double]
+    L.oracle_glu.restype = None
+    L.oracle_glu.argtypes = [P, I64, I64, P]
+    L.oracle_glu_rows.restype = ctypes.c_int
+    L.oracle_glu_rows.argtypes = [I64, P]
     L.oracle_forward.restype = ctypes.c_int
     return L
 
@@ -215,3 +221,47 @@ def forward(x, g, Wq, beta, eps=1e-8):
     if rc != 0:
         raise RuntimeError("oracle_forward failed")
     return {"y": y, "xq": xq, "s": s, "v": v, "acc": acc}
+
+
+# ------------------------------------------------------------------ GLU MLP
+
+def silu(a: float) -> float:
+    return float(lib().oracle_silu(float(a)))
+
+
+def glu(y) -> np.ndarray:
+    """h [M,F] = silu(y[:, :F]) * y[:, F:] for the gate_proj output y [M,2F]."""
+    y = _c(np.atleast_2d(y), np.float64)
+    M, F2 = y.shape
+    assert F2 % 2 == 0
+    F = F2 // 2
+    h = np.empty((M, F), np.float64)
+    lib().oracle_glu(_p(y), M, F, _p(h))
+    return h
+
+
+def glu_rows(F: int) -> np.ndarray:
+    """Source row of every packed row of a [2F, K] gate_proj in GLU order."""
+    src = np.empty(2 * F, np.int64)
+    if lib().oracle_glu_rows(F, _p(src)) != 0:
+        raise ValueError("F must be a positive multiple of 16")
+    return src
+
+
+def pack_glu_weights(W):
+    """gate_proj W [2F,K] -> (packed in GLU row order, beta, Wq [2F,K] in
+    the original row order).  beta is the per-tensor scale of all 2F rows."""
+    W = _c(W, np.float32)
+    src = glu_rows(W.shape[0] // 2)
+    packed, beta, Wq_perm = pack_weights(W[src])
+    Wq = np.empty_like(Wq_perm)
+    Wq[src] = Wq_perm
+    return packed, beta, Wq
+
+
+def forward_glu(x, g, Wq, beta, eps=1e-8):
+    """gate_proj FusedBitLinear (Wq [2F,K], original row order) followed by
+    the GLU gate.  Returns the forward() dict plus h (fp64 [M,F])."""
+    out = forward(x, g, Wq, beta, eps)
+    out["h"] = glu(out["y"])
+    return out

@@ -240,3 +240,27 @@ done:
     if (!acc_out) free(acc);
     return rc;
 }
+
+/* --------------------------------------------------------------- GLU MLP */
+
+double oracle_silu(double a)
+{
+    return a / (1.0 + exp(-a));
+}
+
+void oracle_glu(const double *y, int64_t M, int64_t F, double *h)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < F; ++j)
+            h[m * F + j] = oracle_silu(y[m * 2 * F + j]) * y[m * 2 * F + F + j];
+}
+
+int oracle_glu_rows(int64_t F, int64_t *src)
+{
+    if (F <= 0 || F % 16 != 0) return -1;
+    for (int64_t r = 0; r < 2 * F; ++r) {
+        const int64_t t = r / 32, half = (r % 32) / 16, c = r % 16;
+        src[r] = (half == 0 ? 0 : F) + 16 * t + c;
+    }
+    return 0;
+}

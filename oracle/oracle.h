@@ -42,7 +42,8 @@
  * done in fp64.  Build with -O2 -ffp-contract=off, no fast-math.
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py
- * (printed worked example, brute force, closed forms, invariants).  Two
+ * and tests/test_oracle_glu.py (printed worked example, brute force, closed
+ * forms, invariants).  Two
  * conventions have no pin on the pages: the 1e-5 floors of the two scales
  * (they never bind on the benchmark data) -- parity unpinned for those
  * floors only.
@@ -118,6 +119,31 @@ void oracle_epilogue(const int32_t *acc, const float *s, float beta,
 int oracle_forward(const float *x, const float *g, int64_t M, int64_t K,
                    const int8_t *Wq, float beta, int64_t N, float eps,
                    double *y, int8_t *xq, float *s, float *v, int32_t *acc);
+
+/* ------------------------------------------------------------ GLU MLP
+ * The MLP of an HGRNBit block is gate_proj -> SiLU gate -> down_proj ([p1]
+ * "HGRNBit という層構成を読む", [p2], [p3]: gate_proj 2048 -> 11264, down_proj
+ * 5632 -> 2048, SiLU activation).  [p4] "Kernkomponenten: MLGRU und GLU":
+ * the input goes through two BitLinear layers, one output passes SiLU and
+ * multiplies the other elementwise, and the gated signal goes through a
+ * third BitLinear.  Reading (the pages do not say which half is which):
+ * gate_proj is those two layers stacked, 2F outputs with F = 5632 = 11264/2;
+ * its first F outputs are the SiLU-gated half, the last F the multiplied
+ * half; one per-tensor weight scale covers all 2F rows (gate_proj is one
+ * FusedBitLinear). */
+
+/* SiLU: a * sigmoid(a) = a / (1 + exp(-a)), fp64. */
+double oracle_silu(double a);
+
+/* h[m,j] = silu(y[m,j]) * y[m,F+j] for y [M, 2F] (fp64). */
+void oracle_glu(const double *y, int64_t M, int64_t F, double *h);
+
+/* Source row of each packed row of a gate_proj weight [2F, K] in the GLU
+ * packed order: packed row 32t + 16h + c holds row 16t + c of the gated half
+ * (h = 0) or row F + 16t + c of the multiplied half (h = 1), so each 32-row
+ * tile carries 16 gated rows and the 16 rows they multiply.  src [2F].
+ * Returns 0, or -1 unless F > 0 and F % 16 == 0. */
+int oracle_glu_rows(int64_t F, int64_t *src);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_glu as glu_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -38,11 +39,18 @@ MUTANTS = {
                          "acc -= A[i * k + p] * B[p * n + j];"),
     "tile_words_h_s_swapped": ("4 * (2 * h + j % 2)", "4 * (2 * (j % 2) + h)"),
     "tile_bits_e_order_swapped": ("8 * (e % 4) + 2 * (e / 4)", "8 * (e / 4) + 2 * (e % 4)"),
+    "silu_sign_slip": ("return a / (1.0 + exp(-a));", "return a / (1.0 + exp(a));"),
+    "silu_missing_factor": ("return a / (1.0 + exp(-a));", "return 1.0 / (1.0 + exp(-a));"),
+    "glu_gates_the_wrong_half": ("oracle_silu(y[m * 2 * F + j]) * y[m * 2 * F + F + j]",
+                                 "y[m * 2 * F + j] * oracle_silu(y[m * 2 * F + F + j])"),
+    "glu_rows_halves_swapped": ("(half == 0 ? 0 : F) + 16 * t + c", "(half == 0 ? F : 0) + 16 * t + c"),
+    "glu_rows_tile_of_32": ("(half == 0 ? 0 : F) + 16 * t + c", "(half == 0 ? 0 : F) + 32 * t + c"),
 }
 
 
 def _pin_tests():
-    return [f for name, f in inspect.getmembers(pins, inspect.isfunction)
+    return [f for mod in (pins, glu_pins)
+            for name, f in inspect.getmembers(mod, inspect.isfunction)
             if name.startswith("test_")]
 
 
@@ -51,7 +59,7 @@ def _run_pins(mod):
     for f in _pin_tests():
         try:
             f(mod)
-        except (AssertionError, ValueError, OverflowError, RuntimeError) as e:
+        except (AssertionError, ValueError, OverflowError, RuntimeError, IndexError) as e:
             failures.append((f.__name__, type(e).__name__))
     return failures
 
