@@ -190,6 +190,39 @@ typedef struct bl_call {
 int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
                               int y_dtype, float eps, hipStream_t stream);
 
+/* ------------------------------------------------------------ GLU MLP
+ * The HGRNBit MLP is gate_proj -> SiLU gate -> down_proj (hysenlabs ja
+ * review, section "HGRNBit という層構成を読む": gate_proj 2048 -> 11264,
+ * down_proj 5632 -> 2048, SiLU).  Its GLU (datacamp page, section
+ * "Kernkomponenten: MLGRU und GLU") passes one BitLinear output through SiLU
+ * and multiplies the other by it.  Here gate_proj is one FusedBitLinear with
+ * 2F outputs (one per-tensor scale): rows 0..F-1 the SiLU-gated half, rows
+ * F..2F-1 the multiplied half, and the gate is fused into its epilogue, so
+ * the [M, 2F] projection output never reaches memory. */
+
+/* Pack a gate_proj weight W fp32 [2F, K] (device, row-major) in the GLU
+ * row order: packed row 32t + 16h + c holds W row h * F + 16t + c, so each
+ * 32-row tile carries 16 gated rows and the 16 rows they multiply.  Same
+ * tile format, sizes (bitlinear_packed_bytes(2F, K)) and beta as
+ * bitlinear_pack_weights of the same W.  F > 0, F % 16 == 0, K % 128 == 0.
+ * Returns BL_OK or a negative BL_ERR_* code. */
+int bitlinear_pack_glu_weights(const float *W, int64_t F, int64_t K, void *packed, float *beta,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* gate_proj + GLU gate: h[m, j] = silu(y[m, j]) * y[m, F + j] with y the
+ * FusedBitLinear output of x through the GLU-packed gate_proj, computed in
+ * fp32 from the exact int32 accumulators and rounded once to h_dtype.
+ *   h       device [M, F], dtype h_dtype (written)
+ *   ws      device scratch of >= bitlinear_workspace_bytes(M, K, 2F) bytes
+ *   path    BL_PATH_* as for bitlinear_forward_path; BL_PATH_FUSED takes
+ *           the one-launch decode kernel where it applies (M <= 4, fp32 x:
+ *           M == 1) and otherwise falls back to the two-kernel paths.
+ * Everything else as bitlinear_forward.  silu(a) = a / (1 + exp(-a)). */
+int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, const void *gain,
+                          const void *packed, const float *beta, int64_t F, void *h,
+                          int h_dtype, float eps, void *ws, size_t ws_bytes, int path,
+                          hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(int status);
 

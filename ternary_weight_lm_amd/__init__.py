@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     BL_BF16, BL_F16, BL_F32, BL_PATH_AUTO, BL_PATH_FUSED, BL_PATH_MFMA,
     BL_PATH_SKINNY, CODE_DTYPE, DTYPE_CODE, BitLinearError, lib,
     bitlinear_act_quant, bitlinear_contract, bitlinear_forward, bitlinear_forward_grouped,
-    bitlinear_forward_path, make_calls,
+    bitlinear_forward_glu, bitlinear_forward_path, bitlinear_pack_glu_weights, make_calls,
     bitlinear_gemm_i32, bitlinear_pack_weights, bitlinear_pack_workspace_bytes,
     bitlinear_packed_bytes, bitlinear_select_path, bitlinear_status_string, bitlinear_unpack_weights,
     bitlinear_workspace_bytes,
@@ -46,6 +46,29 @@ def forward(x: torch.Tensor, gain: torch.Tensor, packed: torch.Tensor,
         ws = _bytes(bitlinear_workspace_bytes(M, K, N), x.device)
     bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=eps)
     return y
+
+
+def pack_glu(W: torch.Tensor):
+    """Pack a gate_proj [2F, K] (fp32, on the GPU; rows 0..F-1 SiLU-gated,
+    F..2F-1 multiplied) in the GLU row order.  Returns (packed, beta)."""
+    N2, K = W.shape
+    packed = torch.empty(bitlinear_packed_bytes(N2, K), dtype=torch.uint8, device=W.device)
+    beta = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = _bytes(bitlinear_pack_workspace_bytes(N2, K), W.device)
+    bitlinear_pack_glu_weights(W, packed, beta, ws)
+    return packed, beta
+
+
+def forward_glu(x: torch.Tensor, gain: torch.Tensor, packed: torch.Tensor,
+                beta: torch.Tensor, F: int, eps: float = 1e-8, out_dtype=None,
+                path: int = BL_PATH_AUTO, ws: torch.Tensor | None = None):
+    """h [M, F] = silu(y[:, :F]) * y[:, F:] for y = gate_proj(x) (GLU-packed)."""
+    M, K = x.shape
+    h = torch.empty(M, F, dtype=out_dtype or x.dtype, device=x.device)
+    if ws is None:
+        ws = _bytes(bitlinear_workspace_bytes(M, K, 2 * F), x.device)
+    bitlinear_forward_glu(x, gain, packed, beta, F, h, ws, path=path, eps=eps)
+    return h
 
 
 def workspace(M: int, K: int, N: int, device="cuda") -> torch.Tensor:

@@ -65,6 +65,8 @@ SIGNATURES = {
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
     "bitlinear_contract": ([P, P, P, I64, I64, P, P, I64, P, I, I, P], I),
+    "bitlinear_pack_glu_weights": ([P, I64, I64, P, P, P, SZ, P], I),
+    "bitlinear_forward_glu": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
 }
 
@@ -152,6 +154,23 @@ def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stre
     _check("bitlinear_forward_path", lib().bitlinear_forward_path(
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
         _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
+        path, _stream(stream)))
+
+
+def bitlinear_pack_glu_weights(W, packed, beta, ws, stream=None):
+    """W: gate_proj [2F, K] fp32 (rows 0..F-1 SiLU-gated, F..2F-1 multiplied)."""
+    N2, K = W.shape
+    _check("bitlinear_pack_glu_weights", lib().bitlinear_pack_glu_weights(
+        _ptr(W), N2 // 2, K, _ptr(packed), _ptr(beta), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def bitlinear_forward_glu(x, gain, packed, beta, F, h, ws, path=BL_PATH_AUTO, eps=1e-8,
+                          stream=None):
+    M, K = x.shape
+    _check("bitlinear_forward_glu", lib().bitlinear_forward_glu(
+        _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), F,
+        _ptr(h), DTYPE_CODE[h.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
         path, _stream(stream)))
 
 

@@ -194,6 +194,11 @@ __device__ __forceinline__ int quant8(float xn, float s) {
   return (int)q;
 }
 
+// SiLU in fp32, a / (1 + e^-a) (the activation of the HGRNBit MLP gate).
+// For a very negative a the exponential overflows to +inf and the quotient
+// is -0, the exact limit.
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+
 // ---------------------------------------------------------- weight codes
 
 // The 16 two-bit codes of one packed word as the 16 int8 bytes of an MFMA

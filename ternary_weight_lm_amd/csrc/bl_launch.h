@@ -17,8 +17,10 @@ constexpr int kOutI32 = 3;
 // Workspace bytes of the weight packer (partial sums of |W|).
 size_t pack_workspace_bytes();
 
+// glu_F > 0: W is a gate_proj [2F, K] (F = glu_F) packed in the GLU row
+// order (see pack.hip); 0: plain row order.
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, void *packed,
-                       float *beta, void *ws, hipStream_t stream);
+                       float *beta, void *ws, int64_t glu_F, hipStream_t stream);
 
 hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *Wq,
                          hipStream_t stream);
@@ -29,10 +31,12 @@ hipError_t launch_act_quant(const void *x, int x_dtype, const void *gain,
 
 // Tiled MFMA contraction of pre-quantized activations (any M).
 // out_kind = BL_* writes y = (acc) * beta / s; kOutI32 writes acc.
+// glu: the N = 2F packed rows are a gate_proj in GLU order and out is
+// h [M, F] = silu(y_gate) * y_up (out_kind a float dtype).
 hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N,
-                            int64_t K, void *out, int out_kind,
+                            int64_t K, void *out, int out_kind, bool glu,
                             hipStream_t stream);
 
 // Skinny contraction for M <= kSkinnyMaxM (fused: M <= kFusedMaxM): one
@@ -53,6 +57,7 @@ struct SkinnyArgs {
   int64_t M, N, K;
   void *out;
   int out_kind;
+  bool glu;  // GLU epilogue (pre-quantized calls, or fused calls the decode kernel takes)
 };
 hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream);
 
@@ -78,6 +83,7 @@ struct DecodeArgs {
   const float *beta[kDecodeCalls];
   void *out[kDecodeCalls];
   int out_kind;
+  bool glu;  // one call only: out = h [M, N/2] = silu(y_gate) * y_up
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Whether the decode kernel takes a fused call of this shape and dtype (fp32

@@ -111,7 +111,18 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, void *packed,
   if (!aligned16(W) || !aligned16(packed) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
-  return hip_status(bl::launch_pack(W, N, K, packed, beta, ws, stream));
+  return hip_status(bl::launch_pack(W, N, K, packed, beta, ws, 0, stream));
+}
+
+int bitlinear_pack_glu_weights(const float *W, int64_t F, int64_t K, void *packed, float *beta,
+                               void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (F <= 0 || F % 16 != 0 || !nk_ok(2 * F, K)) return BL_ERR_SHAPE;
+  if (!W || !packed || !beta) return BL_ERR_NULL;
+  if (!ws || ws_bytes < bl::pack_workspace_bytes()) return BL_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  return hip_status(bl::launch_pack(W, 2 * F, K, packed, beta, ws, F, stream));
 }
 
 size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -119,11 +130,17 @@ size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   return fwd_ws_bytes(M, K);
 }
 
-int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
-                           const void *gain, const void *packed,
-                           const float *beta, int64_t N, void *y, int y_dtype,
-                           float eps, void *ws, size_t ws_bytes, int path,
-                           hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of bitlinear_forward_path (glu = false: y [M, N]) and of
+// bitlinear_forward_glu (glu = true: N = 2F packed rows in GLU order, y is
+// h [M, F]).  The fused path takes a GLU call only where the decode kernel
+// does (decode_fits).
+int forward_impl(const void *x, int x_dtype, int64_t M, int64_t K, const void *gain,
+                 const void *packed, const float *beta, int64_t N, void *y, int y_dtype,
+                 float eps, void *ws, size_t ws_bytes, int path, bool glu, hipStream_t stream) {
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
   if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
   if (!eps_ok(eps)) return BL_ERR_EPS;
@@ -135,6 +152,8 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
       !aligned16(ws) || (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
   if (path == BL_PATH_AUTO) path = auto_path(M, K);
+  if (glu && path == BL_PATH_FUSED && !bl::decode_fits(M, K, x_dtype))
+    path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
   if (path == BL_PATH_FUSED && !fused_fits(M, K)) return BL_ERR_SHAPE;
   if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
 
@@ -152,6 +171,7 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
     a.K = K;
     a.out = y;
     a.out_kind = y_dtype;
+    a.glu = glu;
     return hip_status(bl::launch_skinny(a, stream));
   }
   const FwdWs w = carve(ws, M, K);
@@ -170,10 +190,33 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
     a.K = K;
     a.out = y;
     a.out_kind = y_dtype;
+    a.glu = glu;
     return hip_status(bl::launch_skinny(a, stream));
   }
   return hip_status(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
-                                         y_dtype, stream));
+                                         y_dtype, glu, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
+                           const void *gain, const void *packed,
+                           const float *beta, int64_t N, void *y, int y_dtype,
+                           float eps, void *ws, size_t ws_bytes, int path,
+                           hipStream_t stream) {
+  return forward_impl(x, x_dtype, M, K, gain, packed, beta, N, y, y_dtype, eps, ws, ws_bytes,
+                      path, false, stream);
+}
+
+int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, const void *gain,
+                          const void *packed, const float *beta, int64_t F, void *h,
+                          int h_dtype, float eps, void *ws, size_t ws_bytes, int path,
+                          hipStream_t stream) {
+  if (F <= 0 || F % 16 != 0) return BL_ERR_SHAPE;
+  return forward_impl(x, x_dtype, M, K, gain, packed, beta, 2 * F, h, h_dtype, eps, ws,
+                      ws_bytes, path, true, stream);
 }
 
 int bitlinear_forward(const void *x, int x_dtype, int64_t M, int64_t K,
@@ -261,7 +304,7 @@ int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
     return hip_status(bl::launch_skinny(a, stream));
   }
   return hip_status(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
-                                         bl::kOutI32, stream));
+                                         bl::kOutI32, false, stream));
 }
 
 int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
@@ -294,7 +337,8 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
     a.out_kind = y_dtype;
     return hip_status(bl::launch_skinny(a, stream));
   }
-  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, stream));
+  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, false,
+                                         stream));
 }
 
 int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,

@@ -41,7 +41,7 @@ constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
 // pointers are selected only after the activation loads are issued: in the
 // three-call kernel some of them are not preloaded and must first be fetched
 // from the argument buffer, and that wait must not hold up the first loads.
-template <int DT, int OUT, int MR, bool GAIN_LATE>
+template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU = false>
 __device__ __forceinline__ void decode_body(
     const void *x, int K, int M, int tiles, int nt, float eps, int call, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
@@ -235,6 +235,22 @@ __device__ __forceinline__ void decode_body(
     }
   }
   __syncthreads();
+  if constexpr (GLU) {
+    // GLU order: tile rows 0..15 are gated, 16..31 the rows they multiply;
+    // output h[m, 16 nt + l] = silu(y[m, l]) * y[m, 16 + l]
+    if (tid < 16 * M) {
+      const int m = tid >> 4, l = tid & 15;
+      const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
+      const int vg = red[0][m][0][l] + red[1][m][0][l] + red[2][m][0][l] + red[3][m][0][l] - rsum;
+      const int vu = red[0][m][1][l] + red[1][m][1][l] + red[2][m][1][l] + red[3][m][1][l] - rsum;
+      float fs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+        if (i == m) fs = fscale[i];
+      store1<OUT>(out, (int64_t)m * tiles * 16 + nt * 16 + l, silu((float)vg * fs) * ((float)vu * fs));
+    }
+    return;
+  }
   if (tid < 32 * M) {
     const int m = tid >> 5, n = tid & 31;
     const int h = n >> 4, l = n & 15;
@@ -249,13 +265,14 @@ __device__ __forceinline__ void decode_body(
 }
 
 // One call.  Every argument fits the 14 preloaded SGPRs.
-// shape = K/128 | M << 7 | tiles << 10.
-template <int DT, int OUT, int MR>
+// shape = K/128 | M << 7 | tiles << 10.  GLU: the packed rows are a
+// gate_proj in GLU order and out is h [M, tiles * 16].
+template <int DT, int OUT, int MR, bool GLU>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const void *x, uint32_t shape, float eps,
                                                         const uint4 *packed, const void *gain,
                                                         const float *beta, void *out) {
   const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
-  decode_body<DT, OUT, MR, false>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0, packed, packed,
+  decode_body<DT, OUT, MR, false, GLU>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0, packed, packed,
                            packed, gain, gain, gain, beta, beta, beta, out, out, out);
 }
 
@@ -287,12 +304,15 @@ static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
   // fp32 activations decode one row per launch (decode_fits)
   constexpr int MR4 = DT == BL_F32 ? 1 : (int)kDecodeMaxM;
   if (a.ncalls == 1) {
-    if (a.M == 1)
-      decode_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],
-                                                            a.gain[0], a.beta[0], a.out[0]);
-    else
-      decode_kernel<DT, OUT, MR4><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],
-                                                              a.gain[0], a.beta[0], a.out[0]);
+#define BL_DECODE1(MR_, G)                                                                 \
+  decode_kernel<DT, OUT, MR_, G><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],    \
+                                                             a.gain[0], a.beta[0], a.out[0])
+    if (a.M == 1) {
+      if (a.glu) BL_DECODE1(1, true); else BL_DECODE1(1, false);
+    } else {
+      if (a.glu) BL_DECODE1(MR4, true); else BL_DECODE1(MR4, false);
+    }
+#undef BL_DECODE1
     return;
   }
   if (a.M == 1)

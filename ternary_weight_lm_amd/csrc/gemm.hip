@@ -96,7 +96,9 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
 
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
 
-template <int MI, int OUT>
+// GLU: the packed rows are a gate_proj in GLU order (each 32-row tile = 16
+// gated rows + the 16 rows they multiply) and out is h [M, N/2].
+template <int MI, int OUT, bool GLU>
 __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
@@ -218,6 +220,28 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
     else
       store1<OUT>(out, idx, (float)v * sc4[mi][i]);
   };
+  if constexpr (GLU) {
+    // tiles t0 and t0 + 1 of the wave: nb = 2p holds the gated rows of tile
+    // t0 + p, nb = 2p + 1 the rows they multiply; output column 16 (t0 + p) + c
+    const int t0 = (n0 >> 5) + 2 * wn;
+    const int64_t F = N >> 1;
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wrow0 + 16 * mi + q4 + i;
+        if (!full && m >= M) continue;
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          if (!full && 32 * (t0 + pr) >= N) continue;
+          const float yg = (float)(acc[mi][2 * pr][i] - rs4[mi][i]) * sc4[mi][i];
+          const float yu = (float)(acc[mi][2 * pr + 1][i] - rs4[mi][i]) * sc4[mi][i];
+          store1<OUT>(out, (int64_t)m * F + 16 * (t0 + pr) + (lane & 15), silu(yg) * yu);
+        }
+      }
+    return;
+  }
   if (m0 + BM <= M && n0 + BN <= N) {
     // whole tile (all but the ragged edges): no per-element checks, one row
     // offset per (mi, i) and constant column offsets
@@ -248,20 +272,28 @@ template <int MI>
 static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N, int64_t K,
-                            void *out, int out_kind, hipStream_t stream) {
+                            void *out, int out_kind, bool glu, hipStream_t stream) {
   const int BM = 32 * MI;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + 127) / 128);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
   const uint4 *pk = reinterpret_cast<const uint4 *>(packed);
-#define BL_GEMM_CASE(KIND)                                                   \
-  gemm_mfma_kernel<MI, KIND><<<grid, 256, 0, stream>>>(                      \
+#define BL_GEMM_CASE(KIND, G)                                                \
+  gemm_mfma_kernel<MI, KIND, G><<<grid, 256, 0, stream>>>(                   \
       xq, rowsum, s, pk, beta, (int)M, (int)N, (int)K, out, tiles_m, tiles_n)
-  switch (out_kind) {
-    case BL_F32: BL_GEMM_CASE(BL_F32); break;
-    case BL_F16: BL_GEMM_CASE(BL_F16); break;
-    case BL_BF16: BL_GEMM_CASE(BL_BF16); break;
-    default: BL_GEMM_CASE(kOutI32); break;
+  if (glu) {
+    switch (out_kind) {
+      case BL_F32: BL_GEMM_CASE(BL_F32, true); break;
+      case BL_F16: BL_GEMM_CASE(BL_F16, true); break;
+      default: BL_GEMM_CASE(BL_BF16, true); break;
+    }
+  } else {
+    switch (out_kind) {
+      case BL_F32: BL_GEMM_CASE(BL_F32, false); break;
+      case BL_F16: BL_GEMM_CASE(BL_F16, false); break;
+      case BL_BF16: BL_GEMM_CASE(BL_BF16, false); break;
+      default: BL_GEMM_CASE(kOutI32, false); break;
+    }
   }
 #undef BL_GEMM_CASE
   return hipGetLastError();
@@ -270,7 +302,7 @@ static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
 hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N,
-                            int64_t K, void *out, int out_kind,
+                            int64_t K, void *out, int out_kind, bool glu,
                             hipStream_t stream) {
   // The tallest tile that still gives every CU a workgroup: 128-row tiles
   // reuse each unpacked weight operand four times, but below one tile per
@@ -278,10 +310,10 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
   if (M > 64 && tiles(128) >= 256)
-    return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
+    return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 32 && tiles(64) >= 128)
-    return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
-  return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, stream);
+    return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+  return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
 }
 
 }  // namespace bl

@@ -57,10 +57,14 @@ __global__ __launch_bounds__(256) void beta_kernel(const double *__restrict__ pa
   }
 }
 
+// glu_F > 0: W is a gate_proj [2F, K] packed in the GLU row order (packed
+// row 32t + 16h + c holds source row h * F + 16t + c), so that each 32-row
+// tile carries 16 SiLU-gated rows and the 16 rows they multiply.
 __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W,
                                                    int64_t N, int64_t K,
                                                    const float *__restrict__ beta,
-                                                   uint4 *__restrict__ packed) {
+                                                   uint4 *__restrict__ packed,
+                                                   int64_t glu_F) {
   const int64_t KB = K / 128;
   const int64_t nslots = (N / 32) * KB * 64;
   const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = i >> 1, s = i & 1;
-    const int64_t n = nt * 32 + h * 16 + (L & 15);
+    const int64_t n = glu_F > 0 ? h * glu_F + nt * 16 + (L & 15) : nt * 32 + h * 16 + (L & 15);
     const int64_t k0 = kb * 128 + 16 * (2 * (L >> 4) + s);
     const float4 *src = reinterpret_cast<const float4 *>(W + n * K + k0);
     float w[16];
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ p
 }
 
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, void *packed,
-                       float *beta, void *ws, hipStream_t stream) {
+                       float *beta, void *ws, int64_t glu_F, hipStream_t stream) {
   const int64_t n4 = N * K / 4;
   const int nparts = (int)std::min<int64_t>(kAbsBlocks, (n4 + 255) / 256);
   double *partial = reinterpret_cast<double *>(ws);
@@ -132,7 +136,7 @@ hipError_t launch_pack(const float *W, int64_t N, int64_t K, void *packed,
   beta_kernel<<<1, 256, 0, stream>>>(partial, nparts, N * K, beta);
   const int64_t nslots = N * K / 64;
   pack_kernel<<<(unsigned)((nslots + 255) / 256), 256, 0, stream>>>(
-      W, N, K, beta, reinterpret_cast<uint4 *>(packed));
+      W, N, K, beta, reinterpret_cast<uint4 *>(packed), glu_F);
   return hipGetLastError();
 }
 

@@ -55,9 +55,13 @@ struct SkinnyLaunch {
 
 // MB: 16-row MFMA blocks (pre-quantized calls take up to 4, i.e. M <= 64;
 // fused calls 1).
-template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB>
+// GLU (pre-quantized calls): the packed rows are a gate_proj in GLU order
+// and the output is h [M, N/2] = silu(y_gate) * y_up (tile rows 0..15 are
+// gated, 16..31 the rows they multiply).
+template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB, bool GLU = false>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   static_assert(!FUSED || MB == 1, "fused calls have at most 16 rows");
+  static_assert(!GLU || (!FUSED && OUT != kOutI32), "GLU: pre-quantized, float output");
   extern __shared__ __align__(16) int8_t xs[];  // fused: [M][K + 16] int8
   __shared__ int red[4][MB * 8][64];
   __shared__ float s_row[16 * MB];
@@ -209,6 +213,24 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
       red[w][8 * mb + 4 + i][lane] = acc1[mb][i];
     }
   __syncthreads();
+  if constexpr (GLU) {
+    // output (m, c), c < 16: row m's gated value sits at red[.][8 mb + i][L]
+    // and the value it multiplies at red[.][8 mb + 4 + i][L], with
+    // L = 16 (r / 4) + c, i = r % 4 for r = m % 16
+#pragma unroll
+    for (int q = 0; q < MB; ++q) {
+      const int idx = tid + 256 * q;
+      const int m = idx >> 4, c = idx & 15;
+      if (m >= M) continue;
+      const int mb = m >> 4, r = m & 15;
+      const int Lq = 16 * (r >> 2) + c, jg = 8 * mb + (r & 3), ju = jg + 4;
+      const int vg = red[0][jg][Lq] + red[1][jg][Lq] + red[2][jg][Lq] + red[3][jg][Lq] - rs_row[m];
+      const int vu = red[0][ju][Lq] + red[1][ju][Lq] + red[2][ju][Lq] + red[3][ju][Lq] - rs_row[m];
+      const float yg = (float)vg * s_row[m], yu = (float)vu * s_row[m];
+      store1<OUT>(p.out, (int64_t)m * (p.N >> 1) + nt * 16 + c, silu(yg) * yu);
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 2 * MB; ++q) {
     const int idx = tid + 256 * q;
@@ -245,7 +267,17 @@ static SkinnyCall to_call(const SkinnyArgs &a) {
 
 template <bool FUSED, int DT, int MAXC, int RMODE, int MB>
 static void launch_out(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
-                       hipStream_t stream) {
+                       bool glu, hipStream_t stream) {
+  if constexpr (!FUSED && MAXC == 1) {
+    if (glu) {
+      switch (out_kind) {
+        case BL_F32: skinny_kernel<false, DT, BL_F32, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
+        case BL_F16: skinny_kernel<false, DT, BL_F16, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
+        default: skinny_kernel<false, DT, BL_BF16, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
+      }
+      return;
+    }
+  }
   switch (out_kind) {
     case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
     case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
@@ -259,14 +291,15 @@ template <int DT, int MAXC>
 static void launch_fused(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                          int64_t kmax, hipStream_t stream) {
   if (row_mode((int)kmax) == kRowFloat)
-    launch_out<true, DT, MAXC, kRowFloat, 1>(L, out_kind, grid, lds, stream);
+    launch_out<true, DT, MAXC, kRowFloat, 1>(L, out_kind, grid, lds, false, stream);
   else
-    launch_out<true, DT, MAXC, kRowRaw, 1>(L, out_kind, grid, lds, stream);
+    launch_out<true, DT, MAXC, kRowRaw, 1>(L, out_kind, grid, lds, false, stream);
 }
 
 template <int MAXC>
 static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
-                       unsigned grid, size_t lds, int64_t kmax, int64_t M, hipStream_t stream) {
+                       unsigned grid, size_t lds, int64_t kmax, int64_t M, bool glu,
+                       hipStream_t stream) {
   if (fused) {
     switch (x_dtype) {
       case BL_F32: launch_fused<BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
@@ -275,11 +308,11 @@ static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int
     }
   } else if constexpr (MAXC == 1) {  // pre-quantized calls are never grouped
     if (M <= 16)
-      launch_out<false, BL_F32, 1, kRowFloat, 1>(L, out_kind, grid, lds, stream);
+      launch_out<false, BL_F32, 1, kRowFloat, 1>(L, out_kind, grid, lds, glu, stream);
     else if (M <= 32)
-      launch_out<false, BL_F32, 1, kRowFloat, 2>(L, out_kind, grid, lds, stream);
+      launch_out<false, BL_F32, 1, kRowFloat, 2>(L, out_kind, grid, lds, glu, stream);
     else
-      launch_out<false, BL_F32, 1, kRowFloat, 4>(L, out_kind, grid, lds, stream);
+      launch_out<false, BL_F32, 1, kRowFloat, 4>(L, out_kind, grid, lds, glu, stream);
   }
 }
 
@@ -295,6 +328,7 @@ static DecodeArgs decode_args(const SkinnyArgs &a) {
   d.K = a.K;
   d.eps = a.eps;
   d.out_kind = a.out_kind;
+  d.glu = a.glu;
   d.ncalls = 0;
   return d;
 }
@@ -321,7 +355,8 @@ hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
   L.ncalls = 1;
   L.eps = a.eps;
   const size_t lds = a.fused ? (size_t)a.M * (size_t)(a.K + 16) : 0;
-  launch_any<1>(L, a.fused, a.x_dtype, a.out_kind, (unsigned)(a.N / 32), lds, a.K, a.M, stream);
+  launch_any<1>(L, a.fused, a.x_dtype, a.out_kind, (unsigned)(a.N / 32), lds, a.K, a.M, a.glu,
+                stream);
   return hipGetLastError();
 }
 
@@ -364,7 +399,7 @@ hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_
     L.ncalls = n;
     L.eps = rest[base].eps;
     launch_any<kGroupMax>(L, true, rest[base].x_dtype, rest[base].out_kind, (unsigned)blocks,
-                          lds, kmax, 16, stream);
+                          lds, kmax, 16, false, stream);
   }
   return hipGetLastError();
 }

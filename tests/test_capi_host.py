@@ -205,3 +205,27 @@ def test_missing_library_is_an_error(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError):
         _lib.lib()
+
+
+def test_glu_entry_points_validation():
+    L = tw.lib()
+    ws = L.bitlinear_pack_workspace_bytes(64, 256)
+    assert L.bitlinear_pack_glu_weights(A, 24, 256, C, D, WSP, ws, None) == SHAPE   # F % 16
+    assert L.bitlinear_pack_glu_weights(A, 0, 256, C, D, WSP, ws, None) == SHAPE
+    assert L.bitlinear_pack_glu_weights(A, 32, 200, C, D, WSP, ws, None) == SHAPE   # K % 128
+    assert L.bitlinear_pack_glu_weights(None, 32, 256, C, D, WSP, ws, None) == NULL
+    assert L.bitlinear_pack_glu_weights(A, 32, 256, C, D, WSP, 8, None) == WS
+    assert L.bitlinear_pack_glu_weights(A + 4, 32, 256, C, D, WSP, ws, None) == ALIGN
+    wsf = L.bitlinear_workspace_bytes(4, 1024, 2 * 48)
+    glu = L.bitlinear_forward_glu
+    assert glu(A, 1, 4, 1024, B, C, D, 40, Y, 1, 1e-8, WSP, wsf, 0, None) == SHAPE  # F % 16
+    assert glu(A, 1, 4, 1000, B, C, D, 48, Y, 1, 1e-8, WSP, wsf, 0, None) == SHAPE
+    assert glu(A, 9, 4, 1024, B, C, D, 48, Y, 1, 1e-8, WSP, wsf, 0, None) == DTYPE
+    assert glu(A, 1, 4, 1024, B, C, D, 48, Y, 1, 0.0, WSP, wsf, 0, None) == EPS
+    assert glu(A, 1, 4, 1024, B, None, D, 48, Y, 1, 1e-8, WSP, wsf, 0, None) == NULL
+    assert glu(A, 1, 4, 1024, B, C, D, 48, Y, 1, 1e-8, WSP, 16, 0, None) == WS
+    assert glu(A, 1, 4, 1024, B, C, D, 48, Y + 2, 1, 1e-8, WSP, wsf, 0, None) == ALIGN
+    assert glu(A, 1, 4, 1024, B, C, D, 48, Y, 1, 1e-8, WSP, wsf, 7, None) == PATH
+    assert glu(A, 1, 65, 1024, B, C, D, 48, Y, 1, 1e-8, WSP,
+               L.bitlinear_workspace_bytes(65, 1024, 96), 2, None) == SHAPE
+    assert glu(A, 1, 0, 1024, B, C, D, 48, None, 1, 1e-8, None, 0, 0, None) == OK
