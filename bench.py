@@ -9,7 +9,9 @@ rescale -- over every projection of the workload, on seeded synthetic inputs
 already resident in HBM.  Default workload: the 370M-shaped attention
 projections at decode (M = 1 token, four 1024 -> 1024 FusedBitLinear layers,
 fp16 activations).  Other workloads (--workload c1 | c3 | c4 | c5-M<M>) are
-the parity configurations, measurable the same way.
+the parity configurations, measurable the same way; <config>-mlp runs the
+block's MLP instead (gate_proj with the SiLU gate fused into its epilogue,
+then down_proj on the gated output).
 
 Method
   * Weights come from a rotating pool of distinct packed copies of at least
@@ -86,7 +88,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c2",
-                    help="c1 | c2 | c3 | c4 | c5-M1 | c5-M8 | c5-M64 | c5-M512 | c5-M8192")
+                    help="c1 | c2 | c3 | c4 | c5-M1 | c5-M8 | c5-M64 | c5-M512 | c5-M8192, "
+                         "or an MLP workload c3-mlp | c4-mlp | c5-M<M>-mlp (gate_proj with the fused "
+                         "GLU gate, then down_proj)")
     ap.add_argument("--pool-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -367,6 +371,150 @@ def roofline(wl, inp, reps):
     return out
 
 
+# ------------------------------------------------------------- MLP (GLU)
+
+def run_mlp(args):
+    """The HGRNBit MLP: gate_proj with the SiLU gate fused into its
+    epilogue (bitlinear_forward_glu, GLU-packed weights), then down_proj on
+    the gated output -- the real dependency chain.  Workloads <config>-mlp:
+    c3-mlp (M = 32), c4-mlp (M = 4096), c5-M<M>-mlp (2.7B, 32 layers)."""
+    import numpy as np
+    import torch
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+    import oracle
+
+    base = args.workload[:-len("-mlp")]
+    cfg = synth.CONFIGS["c5" if base.startswith("c5") else base]
+    M = int(base.split("-M")[1]) if "-M" in base else cfg.M_list[0]
+    layers = cfg.layers
+    names = [p.name for p in cfg.projs]
+    gi, di = names.index("gate_proj"), names.index("down_proj")
+    K, F2 = cfg.projs[gi].K, cfg.projs[gi].N
+    F, N = F2 // 2, cfg.projs[di].N
+    assert cfg.projs[di].K == F
+    dev = torch.device("cuda:0")
+    xdt, ydt = synth.DTYPES[cfg.dtype], synth.DTYPES[cfg.y_dtype]
+    x, g_gate, W_gate = synth.config_inputs(cfg, M, 0, gi)
+    _, g_down, W_down = synth.config_inputs(cfg, M, 0, di)
+    pk_g, b_g = tw.pack_glu(W_gate.to(dev))
+    pk_d, b_d = tw.pack(W_down.to(dev))
+    set_bytes = pk_g.numel() + pk_d.numel()
+    copies = max(layers, math.ceil((args.pool_mib << 20) / set_bytes))
+    pool = [(pk_g, pk_d)] + [(pk_g.clone(), pk_d.clone()) for _ in range(copies - 1)]
+    xd, ggd, gdd = x.to(dev), g_gate.to(dev), g_down.to(dev)
+    h = torch.empty(M, F, dtype=xdt, device=dev)
+    y = torch.empty(M, N, dtype=ydt, device=dev)
+    ws_g = tw.workspace(M, K, F2)
+    ws_d = tw.workspace(M, F, N)
+    torch.cuda.synchronize()
+
+    def step(s):
+        for l in range(layers):
+            pg, pd = pool[(s * layers + l) % copies]
+            tw.bitlinear_forward_glu(xd, ggd, pg, b_g, F, h, ws_g)
+            tw.bitlinear_forward(h, gdd, pd, b_d, N, y, ws_d)
+
+    big = M >= 512
+    steps = args.steps if args.steps is not None else (20 if big else (100 if layers > 1 else 2000))
+    warmup = args.warmup if args.warmup is not None else (3 if big else 10)
+    per_graph = max(1, min(GRAPH_CHUNK, GRAPH_MAX_LAUNCHES // (4 * layers)))
+
+    def capture(first, count, fn, per):
+        graphs, s0 = [], first
+        while count > 0:
+            n = min(count, per)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for k in range(n):
+                    fn(s0 + k)
+            graphs.append(g)
+            s0 += n
+            count -= n
+        return graphs
+
+    def timed(graphs):
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for g in graphs:
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    for g in capture(0, warmup, step, per_graph):
+        g.replay()
+    ms = timed(capture(warmup, steps, step, per_graph))
+
+    # roofline of the fused gate_proj + GLU launches alone
+    reps = 2 if big else (10 if layers > 1 else 200)
+
+    def glu_only(r):
+        pg, _ = pool[(r + 3) % copies]
+        tw.bitlinear_forward_glu(xd, ggd, pg, b_g, F, h, ws_g)
+
+    gms = timed(capture(0, reps * layers, glu_only, GRAPH_MAX_LAUNCHES // 2))
+    launches = reps * layers
+    sec = gms / 1e3
+    ops = 2 * M * F2 * K
+    xb = x.element_size()
+    byt = F2 * K // 4 + M * K * xb + K * xb + M * F * xb + 4
+    path = tw.bitlinear_select_path(M, K)
+    kern = {tw.BL_PATH_FUSED: "bl::decode_kernel<GLU> (norm+quant+contract+SiLU gate)",
+            tw.BL_PATH_SKINNY: "act_quant + bl::skinny_kernel<GLU> (contract+SiLU gate)",
+            tw.BL_PATH_MFMA: "act_quant + bl::gemm_mfma_kernel<GLU> (contract+SiLU gate)"}[path]
+    if path == tw.BL_PATH_MFMA:
+        ach = ops * launches / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(ach / I8_PEAK_TOPS, 5)}
+    else:
+        ach = byt * launches / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 5)}
+    roof.update({"traffic": None, "kernel": kern, "launches": launches,
+                 "avg_kernel_us": round(sec * 1e6 / launches, 3),
+                 "algorithmic_bytes_per_launch": byt, "ops_per_launch": ops,
+                 "timed_region": "a graph of the gate_proj + GLU calls only"
+                                 + (" (act-quant and contraction launches)" if path != tw.BL_PATH_FUSED else "")})
+    out = {
+        "metric": METRIC, "value": round(M * steps / (ms / 1e3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}{'_M%d' % M if base.startswith('c5') else ''}_mlp_glu",
+                   "tokens_per_step": M, "layers": layers,
+                   "projections": [f"gate_proj {K}->2x{F} + SiLU gate (fused)", f"down_proj {F}->{N}"],
+                   "x_dtype": cfg.dtype, "y_dtype": cfg.y_dtype,
+                   "weight_pool_MiB": round(set_bytes * copies / 2**20, 1),
+                   "launch": "hipGraph; per layer bitlinear_forward_glu then bitlinear_forward",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rows = M if M <= 32 else 8
+        sel = np.linspace(0, M - 1, rows).round().astype(int)
+        xw = synth.widen(x)[sel]
+        _, beta_g, Wq_g = oracle.pack_glu_weights(W_gate.numpy())
+        _, beta_d, Wq_d = oracle.pack_weights(W_down.numpy())
+        gw, dw = synth.widen(g_gate), synth.widen(g_down)
+        t0, n = time.perf_counter(), 0
+        while True:
+            hh = oracle.forward_glu(xw, gw, Wq_g, beta_g)["h"].astype(np.float32)
+            oracle.forward(hh, dw, Wq_d, beta_d)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {
+            "value": round(rows * n / el / layers, 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} passes of {rows} of {M} token rows through one layer's MLP "
+                      f"({el:.1f} s single-threaded; scaled to {layers} layer(s))"}
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(wl, inp, seconds):
@@ -426,6 +574,9 @@ def main():
         calibrate_copy()
         return
     dev = torch.device("cuda:0")
+    if args.workload.endswith("-mlp"):
+        run_mlp(args)
+        return
 
     wl = Workload(args.workload)
     big = wl.M >= 512 or wl.key == "c5-M64"
