@@ -38,13 +38,16 @@ namespace bl {
 // multiply the A tile in `cur` (LDS) by the B codes in b0/b1.  Called twice per
 // loop trip with the register sets swapped, so no register is ever copied
 // (a copy would have to wait for its load and serialize the pipeline).
+// Loads are buffer loads: a per-lane offset fixed for the whole loop plus a
+// k-block offset in a scalar register, so no vector address arithmetic runs
+// per k-block; rows and tiles past the matrix read as zero.
 template <int MI>
 __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, uint8_t *next,
                                             v4i (&acc)[MI][4], v4i (&a_store)[MI],
                                             v4i (&a_load)[MI], v4i &b0, v4i &b1,
-                                            const int8_t *const (&a_src)[MI],
-                                            const int (&a_dst)[MI], const v4i *b_src0,
-                                            const v4i *b_src1, int arow0, int lane) {
+                                            rsrc_t ars, const int (&a_voff)[MI],
+                                            const int (&a_dst)[MI], rsrc_t brs, int b_voff,
+                                            int b_tile_bytes, int arow0, int lane) {
   const int k2 = min(kb + 2, KB - 1);  // the tail re-reads the last block (unused)
   // scheduling fences keep each k-block's work in its own slot: without
   // them the scheduler pulls the next block's unpack (and so its wait for
@@ -52,7 +55,8 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < MI; ++j)
-    a_load[j] = *reinterpret_cast<const v4i *>(a_src[j] + (int64_t)k2 * 128);
+    a_load[j] = __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k2 * 128, 0));
   __builtin_amdgcn_sched_barrier(0);
   v4i a[MI][2];
 #pragma unroll
@@ -89,8 +93,9 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  b0 = b_src0[k2 * 64];
-  b1 = b_src1[k2 * 64];
+  b0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, k2 * 1024, 0));
+  b1 = __builtin_bit_cast(
+      v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + b_tile_bytes, k2 * 1024, 0));
   __syncthreads();
 }
 
@@ -108,7 +113,8 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   constexpr int BN = 128;
   __shared__ __align__(16) uint8_t lds[2][BM * 128];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
   // XCD-aware tile order.
@@ -130,21 +136,28 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   const int NT = N >> 5;
 
   // ---- A tile: BM rows x 8 chunks of 16 B, MI chunks per thread; thread
-  // chunk j covers row (tid + 256 j) / 8, chunk (tid + 256 j) % 8.
-  const int8_t *a_src[MI];
-  int a_dst[MI];
+  // chunk j covers row (tid + 256 j) / 8, chunk (tid + 256 j) % 8.  The
+  // buffer covers the tile's rows that exist (rows past M read as zero and
+  // their outputs are never stored).
+  const rsrc_t ars = make_rsrc(xq + (int64_t)m0 * K, (uint32_t)(min(BM, M - m0) * K));
+  int a_voff[MI], a_dst[MI];
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
     const int c = tid + 256 * j;
     const int row = c >> 3, ch = c & 7;
-    a_src[j] = xq + (int64_t)min(m0 + row, M - 1) * K + ch * 16;
+    a_voff[j] = row * K + ch * 16;
     a_dst[j] = row * 128 + (swz(row, ch) << 4);
   }
-  // ---- B: the wave's two packed 32-row tiles.  Tiles past N (partial last
-  // output tile) re-read the last real tile: their columns are never stored.
+  // ---- B: the wave's two packed 32-row tiles (tiles past N read as zero:
+  // their columns are never stored).
   const int nt0 = (n0 >> 5) + 2 * wn;
-  const v4i *b_src0 = reinterpret_cast<const v4i *>(packed) + (int64_t)min(nt0, NT - 1) * KB * 64 + lane;
-  const v4i *b_src1 = reinterpret_cast<const v4i *>(packed) + (int64_t)min(nt0 + 1, NT - 1) * KB * 64 + lane;
+  const int tile_bytes = KB * 1024;
+  // (readfirstlane: tell the compiler these are wave-uniform, so the buffer
+  // descriptor lives in scalar registers)
+  const int b_first = __builtin_amdgcn_readfirstlane(min(nt0, NT));
+  const int b_bytes = __builtin_amdgcn_readfirstlane(max(0, min(2, NT - nt0)) * tile_bytes);
+  const rsrc_t brs = make_rsrc(packed + (int64_t)b_first * KB * 64, (uint32_t)b_bytes);
+  const int b_voff = lane * 16;
 
   v4i acc[MI][4];
 #pragma unroll
@@ -162,14 +175,15 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   {
     const int k1 = min(1, KB - 1);
 #pragma unroll
-    for (int j = 0; j < MI; ++j) Q[j] = *reinterpret_cast<const v4i *>(a_src[j]);
+    for (int j = 0; j < MI; ++j)
+      Q[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], 0, 0));
 #pragma unroll
     for (int j = 0; j < MI; ++j)
-      P[j] = *reinterpret_cast<const v4i *>(a_src[j] + (int64_t)k1 * 128);
-    X0 = b_src0[0];
-    X1 = b_src1[0];
-    Y0 = b_src0[k1 * 64];
-    Y1 = b_src1[k1 * 64];
+      P[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k1 * 128, 0));
+    X0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, 0, 0));
+    X1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + tile_bytes, 0, 0));
+    Y0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, k1 * 1024, 0));
+    Y1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + tile_bytes, k1 * 1024, 0));
 #pragma unroll
     for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(&lds[0][a_dst[j]]) = Q[j];
   }
@@ -180,14 +194,14 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   // let the compiler sink the first half's prefetch loads into it.
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
-    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, a_src, a_dst, b_src0, b_src1,
-                    arow0, lane);
-    gemm_kblock<MI>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y0, Y1, a_src, a_dst, b_src0,
-                    b_src1, arow0, lane);
+    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, ars, a_voff, a_dst, brs, b_voff,
+                    tile_bytes, arow0, lane);
+    gemm_kblock<MI>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y0, Y1, ars, a_voff, a_dst, brs,
+                    b_voff, tile_bytes, arow0, lane);
   }
   if (kb < KB)
-    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, a_src, a_dst, b_src0, b_src1,
-                    arow0, lane);
+    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, ars, a_voff, a_dst, brs, b_voff,
+                    tile_bytes, arow0, lane);
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
   // row sums and rescale factors of the wave's 16*MI rows go through a small

@@ -44,27 +44,6 @@ __device__ __forceinline__ double group_sum(const double (&ss)[4]) {
   return wave_sum((ss[0] + ss[1]) + (ss[2] + ss[3]));
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer over `bytes` bytes at base: offsets at or past `bytes` read as
-// zero (and touch no memory).
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ v4i bload(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-template <int DT>
-__device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
-  Chunk8<DT> c;
-  c.u[0] = bload(r, off);
-  if constexpr (DT == BL_F32) c.u[1] = bload(r, off + 16);
-  return c;
-}
-
 // How a lane holds its chunks of the row between the three passes.
 enum RowMode {
   kRowFloat = 0,  // widened once, xn kept in registers: K <= 512 * kRowCache
