@@ -213,11 +213,17 @@ __device__ __forceinline__ float act_scale(float absmax) {
   return div_rn(127.0f, fmaxf(absmax, 1e-5f));
 }
 
-// int8 code of one normalized activation: clamp(rne(xn * s), -128, 127).
+// int8 code of one normalized activation, clamp(rne(v), -128, 127) with
+// v = fp32(xn * s), returned in the LOW BYTE of the result (the other bytes
+// are not a sign extension; pack4 and the row sum read the low byte only).
+// The clamp never binds: s = fp32(127 / max|xn|) makes |v| <= 127 (1 + 3 *
+// 2^-24) < 127.5.  Adding 1.5 * 2^23 puts v where the float spacing is 1,
+// so the sum is 1.5 * 2^23 + rne(v) (ties to even, as the mantissa parity
+// follows rne(v)), and its low mantissa byte is rne(v) mod 256: two adds'
+// worth of work instead of rint, clamp and convert.
 __device__ __forceinline__ int quant8(float xn, float s) {
-  float q = __builtin_rintf(xn * s);
-  q = fminf(fmaxf(q, -128.0f), 127.0f);
-  return (int)q;
+  const float v = xn * s;
+  return __float_as_int(v + 12582912.0f);
 }
 
 // SiLU in fp32, a / (1 + e^-a) (the activation of the HGRNBit MLP gate).

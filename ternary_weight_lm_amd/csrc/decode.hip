@@ -198,7 +198,9 @@ __device__ __forceinline__ void decode_body(
   const int arow = lane & 15;
   const bool arow_ok = arow < M;
   const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
-  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  // two accumulators per output half (s2 = 0 / 1): each MFMA depends on the
+  // one two steps back, not on the previous one
+  v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   constexpr int kBatch = 4;  // A operands read from LDS together
 #pragma unroll
   for (int t0 = 0; t0 < kDecTiles; t0 += kBatch) {
@@ -219,8 +221,8 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         // word (h, s2) of a lane slot sits at dword 2h + s2
-        acc0 = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0);
-        acc1 = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1);
+        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
+        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
       }
     }
   }
@@ -230,8 +232,8 @@ __device__ __forceinline__ void decode_body(
   if (lane < 16) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      red[w][m][0][lane] = acc0[m];
-      red[w][m][1][lane] = acc1[m];
+      red[w][m][0][lane] = acc0[0][m] + acc0[1][m];
+      red[w][m][1][lane] = acc1[0][m] + acc1[1][m];
     }
   }
   __syncthreads();

@@ -30,8 +30,8 @@ namespace bl {
 
 constexpr int kRowCache = 8;  // cached chunks per lane: K <= 4096
 
-// Four int32 codes in [-128, 127] -> one dword of int8 (byte i = code i),
-// three byte permutes.
+// The low bytes of four words (int8 codes from quant8) -> one dword of
+// int8 (byte i = code i), three byte permutes.
 __device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
   const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u);
   const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x0c0c0400u);
