@@ -236,3 +236,44 @@ def test_empty_batch_is_noop():
     y = tw.forward(x, g, packed, beta, N)
     torch.cuda.synchronize()
     assert y.shape == (0, N)
+
+
+@pytest.mark.parametrize("path,M,N,K,xdt", [
+    (tw.BL_PATH_FUSED, 1, 64, 8192, "bf16"),      # largest K of the one-launch kernel
+    (tw.BL_PATH_FUSED, 4, 96, 8192, "fp16"),
+    (tw.BL_PATH_AUTO, 1, 64, 8320, "bf16"),       # just past it: two kernels
+    (tw.BL_PATH_AUTO, 2, 32, 65536, "bf16"),      # largest K: act-quant re-reads the row
+    (tw.BL_PATH_MFMA, 3, 160, 65536, "fp16"),
+])
+def test_forward_size_limits(path, M, N, K, xdt):
+    say(f"size limits path={path} M={M} N={N} K={K}")
+    seed = 4000 + M + K
+    x = synth.make_x(seed, 0, 0, M, K, xdt)
+    g = synth.make_gain(seed, 0, 0, K, xdt)
+    W = synth.make_w(seed, 0, 0, N, K)
+    (o_packed, o_beta, o_Wq), (d_packed, d_beta) = check_pack(W)
+    y, x_dev, g_dev = run_forward(x, g, d_packed, d_beta, N, xdt, path=path)
+    ref = oracle.forward(synth.widen(x), synth.widen(g), o_Wq, o_beta)
+    xq_gpu, s_gpu, _ = gpu_act_quant(x_dev, g_dev)
+    check_xq(xq_gpu, s_gpu, ref)
+    check_y(y, ref, xdt, Wq=o_Wq, beta=o_beta, xq_gpu=xq_gpu, s_gpu=s_gpu)
+
+
+@pytest.mark.parametrize("path", [tw.BL_PATH_SKINNY, tw.BL_PATH_MFMA])
+def test_gemm_i32_largest_k(path):
+    """K = 65536: |acc| up to 128 * 65536, and the skinny kernel's weight
+    registers are refilled 8 times per wave."""
+    say(f"gemm_i32 K=65536 path={path}")
+    M, N, K = 5, 64, 65536
+    xq = _random_codes(M, K, 99)
+    r = np.random.default_rng(100)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wq[0] = 1
+    Wq[1] = -1
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc, path=path)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
