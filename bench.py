@@ -297,12 +297,16 @@ def roofline(wl, inp, reps):
     nothing but contraction launches."""
     import torch
     import ternary_weight_lm_amd as tw
-    path = tw.bitlinear_select_path(wl.M, wl.shape(wl.calls[0])[0])
+    # the dominant kernel: the path most of the step's calls take
+    paths = [tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) for c in wl.calls]
+    path = max(set(paths), key=paths.count)
+    sel = [j for j, p in enumerate(paths) if p == path]
     bound = "hbm" if path in (tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY) else "mfma"
-    ncalls = len(wl.calls)
+    ncalls = len(sel)
     stage = {}
     if path != tw.BL_PATH_FUSED:
-        for j, call in enumerate(wl.calls):
+        for j in sel:
+            call = wl.calls[j]
             K, N = wl.shape(call)
             xkey = (0 if wl.layers > 1 else call[0], call[1])
             if xkey not in stage:
@@ -313,7 +317,8 @@ def roofline(wl, inp, reps):
                 stage[xkey] = (xq, sc, rs)
 
     def launch(r):
-        s, j = divmod(r, ncalls)
+        s, jj = divmod(r, ncalls)
+        j = sel[jj]
         call = wl.calls[j]
         K, N = wl.shape(call)
         pk = inp["pool"][(s + 7) % inp["copies"]][j]
@@ -347,8 +352,8 @@ def roofline(wl, inp, reps):
     torch.cuda.synchronize()
     sec = a.elapsed_time(b) / 1e3
     byt = ops = 0
-    for call in wl.calls:
-        cb, co = algorithmic(wl, call)
+    for j in sel:
+        cb, co = algorithmic(wl, wl.calls[j])
         byt += cb * reps
         ops += co * reps
     kernel = {tw.BL_PATH_FUSED: "bl::decode_kernel (norm+quant+contract+rescale)",
@@ -364,6 +369,7 @@ def roofline(wl, inp, reps):
                "frac": round(ach / I8_PEAK_TOPS, 5)}
     out["traffic"] = None
     out["kernel"] = kernel
+    out["calls_timed"] = f"{len(sel)} of {len(wl.calls)} calls per step (those on this path)"
     out["launches"] = total
     out["avg_kernel_us"] = round(sec * 1e6 / total, 3)
     out["algorithmic_bytes_per_launch"] = round(byt / total, 1)
@@ -606,8 +612,8 @@ def main():
     tokens_per_s = wl.M * steps / (ms / 1e3)
 
     import ternary_weight_lm_amd as tw
-    path = tw.bitlinear_select_path(wl.M, wl.shape(wl.calls[0])[0])
-    if path == tw.BL_PATH_FUSED:
+    paths = {tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) for c in wl.calls}
+    if paths == {tw.BL_PATH_FUSED}:
         roof = roofline_from_steps(wl, inp, steps, ms)
     else:
         roof = roofline(wl, inp, reps)

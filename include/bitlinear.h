@@ -160,7 +160,11 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
                            hipStream_t stream);
 
 /* The BL_PATH_FUSED / _SKINNY / _MFMA path bitlinear_forward takes for a
- * token count M and in_features K (BL_ERR_SHAPE for an invalid M or K). */
+ * token count M and in_features K with 16-bit activations (BL_ERR_SHAPE for
+ * an invalid M or K): FUSED for M <= 4 and K <= 8192 and for M <= 8 and
+ * K <= 4096, SKINNY up to M = 64, MFMA above.  fp32 activations take FUSED
+ * only for M == 1 (K <= 8192) and M <= 4 (K <= 4096), SKINNY otherwise up to
+ * M = 64. */
 int bitlinear_select_path(int64_t M, int64_t K);
 
 /* One projection of a grouped forward (all pointers device, as in
@@ -178,8 +182,10 @@ typedef struct bl_call {
  * steps where each call is too small to fill the GPU on its own -- e.g. the
  * i/f/g/o projections of an HGRNBit block (hysenlabs ja review, section
  * "HGRNBit という層構成を読む").  Consecutive calls of one shape with
- * M <= 4 (fp32 x: M == 1) go out up to three per launch of the decode
- * kernel; the remaining calls up to 16 per launch of the skinny kernel.
+ * M <= 4 and K <= 8192 (fp32 x: M == 1) go out up to three per launch of
+ * the decode kernel, calls with M <= 8 and K <= 4096 one per launch of its
+ * row mode, and the remaining calls up to 16 per launch of the skinny
+ * kernel.
  *   calls   HOST array of ncalls descriptors (read during the call only)
  *   Every call must satisfy the BL_PATH_FUSED limits (M <= 16, K <= 8192,
  *   M * (K + 16) <= 56320) and the usual shape / alignment rules, and all

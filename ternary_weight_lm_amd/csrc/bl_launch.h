@@ -86,10 +86,20 @@ struct DecodeArgs {
   bool glu;  // one call only: out = h [M, N/2] = silu(y_gate) * y_up
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-// Whether the decode kernel takes a fused call of this shape and dtype (fp32
-// activations: one row only).
-inline bool decode_fits(int64_t M, int64_t K, int x_dtype) {
+// Row mode of the decode kernel (one wave per token row): single calls with
+// 2 <= M <= 8 (fp32 x: M <= 4) and K <= 4096.
+constexpr int64_t kDecodeRowsMaxM = 8;
+inline bool decode_rows_fits(int64_t M, int64_t K, int x_dtype) {
+  return M >= 2 && K <= 4096 && M <= (x_dtype == BL_F32 ? 4 : kDecodeRowsMaxM);
+}
+// Split mode (every wave takes a share of each row; up to three calls per
+// launch): M <= 4 (fp32 x: M == 1), K <= 8192.
+inline bool decode_split_fits(int64_t M, int64_t K, int x_dtype) {
   return M >= 1 && K <= 8192 && (M == 1 || (M <= kDecodeMaxM && x_dtype != BL_F32));
+}
+// Whether the decode kernel takes a single fused call of this shape/dtype.
+inline bool decode_fits(int64_t M, int64_t K, int x_dtype) {
+  return decode_split_fits(M, K, x_dtype) || decode_rows_fits(M, K, x_dtype);
 }
 
 // Largest M and K the fused skinny kernel accepts.

@@ -62,9 +62,14 @@ bool fused_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= bl::kFusedMaxM && K <= bl::kFusedMaxK && M * (K + 16) <= kFusedLdsBytes;
 }
 
-// Default path by token count.
-int auto_path(int64_t M, int64_t K) {
-  if (M <= 4 && fused_fits(M, K)) return BL_PATH_FUSED;
+// Default path by token count: the one-launch decode kernel wherever it
+// applies (split mode M <= 4 up to K = 8192, row mode M <= 8 up to K = 4096;
+// fp32 activations: M == 1, resp. M <= 4), then the act-quant + skinny
+// pair up to 64 tokens, then the MFMA GEMM.
+int auto_path(int64_t M, int64_t K, int x_dtype) {
+  if (M <= 4 && fused_fits(M, K) && (x_dtype != BL_F32 || bl::decode_fits(M, K, x_dtype)))
+    return BL_PATH_FUSED;
+  if (bl::decode_rows_fits(M, K, x_dtype)) return BL_PATH_FUSED;
   if (M <= bl::kSkinnyMaxM) return BL_PATH_SKINNY;
   return BL_PATH_MFMA;
 }
@@ -91,7 +96,7 @@ const char *bitlinear_status_string(int status) {
 
 int bitlinear_select_path(int64_t M, int64_t K) {
   if (!m_ok(M) || M == 0 || K < 128 || K > kMaxK || K % 128 != 0) return BL_ERR_SHAPE;
-  return auto_path(M, K);
+  return auto_path(M, K, BL_BF16);
 }
 
 size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
@@ -151,7 +156,7 @@ int forward_impl(const void *x, int x_dtype, int64_t M, int64_t K, const void *g
   if (!aligned16(x) || !aligned16(gain) || !aligned16(packed) || !aligned16(y) ||
       !aligned16(ws) || (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
-  if (path == BL_PATH_AUTO) path = auto_path(M, K);
+  if (path == BL_PATH_AUTO) path = auto_path(M, K, x_dtype);
   if (glu && path == BL_PATH_FUSED && !bl::decode_fits(M, K, x_dtype))
     path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
   if (path == BL_PATH_FUSED && !fused_fits(M, K)) return BL_ERR_SHAPE;

@@ -295,6 +295,151 @@ __global__ __launch_bounds__(256, 2) void decode3_kernel(
                            b0, b1, b2, o0, o1, o2);
 }
 
+// ---------------------------------------------------------------- row mode
+// 2 <= M <= 4 * RPW tokens, K <= 4096: wave w normalizes and quantizes rows
+// w, w + 4, ... by itself (the shared float-mode row passes of rowquant.h,
+// bit-identical to the act-quant kernel), so no row reduction crosses a
+// wave and one barrier (the codes in LDS) suffices.  Loads go out x rows ->
+// gain (once per wave) -> weights; every argument is preloaded.
+constexpr int kRowTiles = 8;  // K <= 4 * 8 * 128
+
+template <int DT, int OUT, int RPW, bool GLU>
+__global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint32_t shape,
+                                                             float eps, const uint4 *packed,
+                                                             const void *gain, const float *bp,
+                                                             void *out) {
+  extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
+  __shared__ int red[4][8][64];
+  __shared__ float f_row[16];
+  __shared__ int rs_row[16];
+
+  constexpr int EB = dtype_bytes(DT);
+  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 31;
+  const int tiles = (int)(shape >> 12);
+  const int nt = (int)blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = K >> 7;
+  const int lds_stride = K + 16;
+
+  // ---- 1. loads: this wave's rows, the gain, then the weight tiles
+  const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
+  Chunk8<DT> xraw[RPW][kRowCache];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int m = w + 4 * j;
+#pragma unroll
+    for (int c = 0; c < kRowCache; ++c) {
+      const int k = 8 * lane + 512 * c;
+      xraw[j][c] = bload_chunk<DT>(xr, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
+  Chunk8<DT> graw[kRowCache];
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c) graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
+  __builtin_amdgcn_sched_barrier(0);
+  const rsrc_t wr = make_rsrc(packed + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
+  v4i wt[kRowTiles];
+#pragma unroll
+  for (int t = 0; t < kRowTiles; ++t) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  const float beta = *bp;
+
+  // ---- 2. the wave's rows: codes into LDS, scale factor and row sum
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int m = w + 4 * j;
+    if (m >= M) break;
+    int8_t *dst = xs + m * lds_stride;
+    float sc;
+    int rs;
+    quantize_loaded<DT>(xraw[j], graw, K, eps,
+                        [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
+                        sc, rs);
+    if (lane == 0) {
+      f_row[m] = div_rn(beta, sc);
+      rs_row[m] = rs;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. contraction: tiles kb = w + 4t, rows 0..15 as one MFMA block
+  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
+  const int arow = lane & 15;
+  const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
+  v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  constexpr int kBatch = 4;
+#pragma unroll
+  for (int t0 = 0; t0 < kRowTiles; t0 += kBatch) {
+    if (t0 >= nmine) break;
+    v4i a[kBatch][2];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        a[j][s2] = v4i{0, 0, 0, 0};
+        if (arow < M && t0 + j < nmine)
+          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
+      }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (t0 + j >= nmine) break;
+      const v4i u = wt[t0 + j];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
+        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
+      }
+    }
+  }
+
+  // ---- 4. partial sums meet in LDS; rescale and store.  red[w][4 h + i][L]
+  // holds row 4 (L / 16) + i, column 16 h + L % 16 of the tile.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[w][i][lane] = acc0[0][i] + acc0[1][i];
+    red[w][4 + i][lane] = acc1[0][i] + acc1[1][i];
+  }
+  __syncthreads();
+  if constexpr (GLU) {
+    const int m = tid >> 4, c = tid & 15;  // 16 rows x 16 outputs
+    if (m < M) {
+      const int Lq = 16 * (m >> 2) + c, jg = m & 3, ju = jg + 4;
+      const int vg = red[0][jg][Lq] + red[1][jg][Lq] + red[2][jg][Lq] + red[3][jg][Lq] - rs_row[m];
+      const int vu = red[0][ju][Lq] + red[1][ju][Lq] + red[2][ju][Lq] + red[3][ju][Lq] - rs_row[m];
+      store1<OUT>(out, (int64_t)m * tiles * 16 + nt * 16 + c,
+                  silu((float)vg * f_row[m]) * ((float)vu * f_row[m]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q;
+      const int j = idx >> 6, Lq = idx & 63;
+      const int h = j >> 2, i = j & 3;
+      const int m = 4 * (Lq >> 4) + i;
+      if (m >= M) continue;
+      const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
+      store1<OUT>(out, (int64_t)m * tiles * 32 + nt * 32 + 16 * h + (Lq & 15), (float)v * f_row[m]);
+    }
+  }
+}
+
+template <int DT, int OUT, bool GLU>
+static void launch_rows(const DecodeArgs &a, hipStream_t stream) {
+  const unsigned tiles = (unsigned)(a.N / 32);
+  const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
+  const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
+  const uint4 *pk = reinterpret_cast<const uint4 *>(a.packed[0]);
+  if (a.M <= 4)
+    decode_rows_kernel<DT, OUT, 1, GLU><<<tiles, 256, lds, stream>>>(a.x[0], shape, a.eps, pk,
+                                                                      a.gain[0], a.beta[0], a.out[0]);
+  else
+    decode_rows_kernel<DT, OUT, DT == BL_F32 ? 1 : 2, GLU><<<tiles, 256, lds, stream>>>(
+        a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
+}
+
 template <int DT, int OUT>
 static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
@@ -329,6 +474,17 @@ static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
 
 template <int DT>
 static void launch_out(const DecodeArgs &a, hipStream_t stream) {
+  if (a.ncalls == 1 && decode_rows_fits(a.M, a.K, a.x_dtype)) {
+#define BL_ROWS(O)                                                   \
+  (a.glu ? launch_rows<DT, O, true>(a, stream) : launch_rows<DT, O, false>(a, stream))
+    switch (a.out_kind) {
+      case BL_F32: BL_ROWS(BL_F32); break;
+      case BL_F16: BL_ROWS(BL_F16); break;
+      default: BL_ROWS(BL_BF16); break;
+    }
+#undef BL_ROWS
+    return;
+  }
   switch (a.out_kind) {
     case BL_F32: launch_mr<DT, BL_F32>(a, stream); break;
     case BL_F16: launch_mr<DT, BL_F16>(a, stream); break;

@@ -56,6 +56,63 @@ __host__ __device__ constexpr int row_mode(int K) {
   return K <= 512 * kRowCache ? kRowFloat : (K <= 512 * kRowRawCache ? kRowRaw : kRowReload);
 }
 
+// The three passes of the float mode on a row already in registers: chunk
+// c of the lane (elements 8 lane + 512 c .. +7, c < kRowCache) in xraw[c],
+// the gain's matching chunk in graw[c] (chunks past K read as zero).
+// `sink(k, codes)` receives the 8 codes of elements k..k+7 as two dwords; on
+// return every lane holds s and the row sum.  Shared by quantize_row and by
+// kernels that issue the row's loads themselves, so both give the same bits.
+template <int DT, class Sink>
+__device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[kRowCache],
+                                                const Chunk8<DT> (&graw)[kRowCache], int K,
+                                                float eps, Sink sink, float &s_out,
+                                                int &rowsum_out) {
+  const int lane = threadIdx.x & 63;
+  const int nch = (K + 511) >> 9;  // chunk rounds (some lanes idle in the last)
+  const auto kof = [&](int c) { return 8 * lane + 512 * c; };
+  // x widened once; after pass 2 the same registers hold xn
+  float v[kRowCache][8];
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c)
+    if (c < nch) widen<DT>(xraw[c], v[c]);
+  double ss[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c)
+    if (c < nch && kof(c) < K) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        ss[c & 3] = __builtin_fma((double)v[c][e], (double)v[c][e], ss[c & 3]);
+    }
+  const float r = rms_inv(group_sum(ss), K, eps);
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c)
+    if (c < nch && kof(c) < K) {
+      float g[8];
+      widen<DT>(graw[c], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[c][e] = (v[c][e] * r) * g[e];
+        amax = fmaxf(amax, fabsf(v[c][e]));
+      }
+    }
+  const float sc = act_scale(wave_max(amax));
+  int rs = 0;
+#pragma unroll
+  for (int c = 0; c < kRowCache; ++c)
+    if (c < nch && kof(c) < K) {
+      int q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = quant8(v[c][e], sc);
+      const uint2 codes = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      rs = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs, false);
+      rs = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs, false);
+      sink(kof(c), codes);
+    }
+  s_out = sc;
+  rowsum_out = wave_sum(rs);
+}
+
 // Quantizes one row with the calling wave.  `sink(k, codes)` receives the 8
 // codes of elements k..k+7 as two dwords.  On return every lane holds s and
 // the row sum.  The three modes run the same operations in the same order.
@@ -85,44 +142,12 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
   };
 
   if constexpr (MODE == kRowFloat) {
-    // x widened once; after pass 2 the same registers hold xn
     Chunk8<DT> xraw[kRowCache], graw[kRowCache];
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c) xraw[c] = ld(c);
 #pragma unroll
     for (int c = 0; c < kRowCache; ++c) graw[c] = ldg(c);
-    float v[kRowCache][8];
-#pragma unroll
-    for (int c = 0; c < kRowCache; ++c)
-      if (c < nch) widen<DT>(xraw[c], v[c]);
-    double ss[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int c = 0; c < kRowCache; ++c)
-      if (c < nch && kof(c) < K) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          ss[c & 3] = __builtin_fma((double)v[c][e], (double)v[c][e], ss[c & 3]);
-      }
-    const float r = rms_inv(group_sum(ss), K, eps);
-    float amax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kRowCache; ++c)
-      if (c < nch && kof(c) < K) {
-        float g[8];
-        widen<DT>(graw[c], g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[c][e] = (v[c][e] * r) * g[e];
-          amax = fmaxf(amax, fabsf(v[c][e]));
-        }
-      }
-    const float sc = act_scale(wave_max(amax));
-    int rs = 0;
-#pragma unroll
-    for (int c = 0; c < kRowCache; ++c)
-      if (c < nch && kof(c) < K) emit(kof(c), v[c], sc, rs);
-    s_out = sc;
-    rowsum_out = wave_sum(rs);
+    quantize_loaded<DT>(xraw, graw, K, eps, sink, s_out, rowsum_out);
   } else {
     // raw chunks (kRowRaw) or batches of 4 re-read chunks (kRowReload)
     constexpr int NC = MODE == kRowRaw ? kRowRawCache : 4;

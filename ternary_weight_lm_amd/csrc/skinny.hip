@@ -373,9 +373,15 @@ hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_
       continue;
     }
     DecodeArgs d = decode_args(a);
-    while (i < ncalls && d.ncalls < kDecodeCalls && decode_ok(calls[i]) && calls[i].M == a.M &&
-           calls[i].K == a.K && calls[i].N == a.N)
-      decode_add(d, calls[i++]);
+    if (!decode_split_fits(a.M, a.K, a.x_dtype)) {
+      decode_add(d, calls[i++]);  // row mode: one call per launch
+    } else {
+      const auto same = [&](const SkinnyArgs &c) {
+        return c.fused && decode_split_fits(c.M, c.K, c.x_dtype) && c.M == a.M && c.K == a.K &&
+               c.N == a.N;
+      };
+      while (i < ncalls && d.ncalls < kDecodeCalls && same(calls[i])) decode_add(d, calls[i++]);
+    }
     const hipError_t e = launch_decode(d, stream);
     if (e != hipSuccess) return e;
   }

@@ -63,7 +63,10 @@ def test_select_path_rule():
     assert L.bitlinear_select_path(1, 1024) == 1
     assert L.bitlinear_select_path(4, 7040) == 1
     assert L.bitlinear_select_path(4, 16384) == 2     # fused needs K <= 8192
-    assert L.bitlinear_select_path(5, 1024) == 2
+    assert L.bitlinear_select_path(5, 1024) == 1     # row mode of the decode kernel
+    assert L.bitlinear_select_path(8, 4096) == 1
+    assert L.bitlinear_select_path(8, 4224) == 2     # row mode needs K <= 4096
+    assert L.bitlinear_select_path(9, 1024) == 2
     assert L.bitlinear_select_path(16, 1024) == 2
     assert L.bitlinear_select_path(17, 1024) == 2
     assert L.bitlinear_select_path(64, 7040) == 2
