@@ -55,7 +55,8 @@ GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
 # unit); the commands and tables are under profiles/.  A figure holds only
 # for the kernel sources it was taken on: they are hashed, and a changed
 # kernel reports traffic null until it is measured again.
-KERNEL_SOURCES = {"decode": ["decode.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
+KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip", "decode_f16.hip",
+                             "decode_bf16.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "06c57940edd5da96", 722569),

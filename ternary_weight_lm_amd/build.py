@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pack.hip", "actquant.hip", "gemm.hip", "skinny.hip", "decode.hip", "capi.cpp"]
+SOURCES = ["pack.hip", "actquant.hip", "gemm.hip", "skinny.hip", "decode.hip", "decode_f32.hip",
+           "decode_f16.hip", "decode_bf16.hip", "capi.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

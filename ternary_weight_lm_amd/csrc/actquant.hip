@@ -15,7 +15,7 @@
 
 namespace bl {
 
-template <int DT, int MODE>
+template <int DT, int MODE, int NC>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const void *__restrict__ x, const void *__restrict__ gain, int64_t M, int K, float eps,
     int8_t *__restrict__ xq, float *__restrict__ s_out, int32_t *__restrict__ rowsum_out) {
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
   int8_t *qr = xq + row * K;
   float sc;
   int rs;
-  quantize_row<DT, MODE>(
+  quantize_row<DT, MODE, NC>(
       xr, reinterpret_cast<const char *>(gain), K, eps,
       [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(qr + k) = codes; }, sc, rs);
   if ((threadIdx.x & 63) == 0) {
@@ -39,17 +39,22 @@ template <int DT>
 static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, float eps,
                       int8_t *xq, float *s, int32_t *rowsum, hipStream_t stream) {
   const unsigned blocks = (unsigned)((M + 3) / 4);
+#define BL_AQ(MODE, NC) \
+  act_quant_kernel<DT, MODE, NC><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum)
   switch (row_mode((int)K)) {
     case kRowFloat:
-      act_quant_kernel<DT, kRowFloat><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum);
+      // the float mode issues only the chunk loads a row of K needs
+      switch (row_cache((int)K)) {
+        case 2: BL_AQ(kRowFloat, 2); break;
+        case 4: BL_AQ(kRowFloat, 4); break;
+        case 6: BL_AQ(kRowFloat, 6); break;
+        default: BL_AQ(kRowFloat, 8); break;
+      }
       break;
-    case kRowRaw:
-      act_quant_kernel<DT, kRowRaw><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum);
-      break;
-    default:
-      act_quant_kernel<DT, kRowReload><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum);
-      break;
+    case kRowRaw: BL_AQ(kRowRaw, kRowCache); break;
+    default: BL_AQ(kRowReload, kRowCache); break;
   }
+#undef BL_AQ
 }
 
 hipError_t launch_act_quant(const void *x, int x_dtype, const void *gain,

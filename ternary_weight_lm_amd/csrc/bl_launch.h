@@ -86,6 +86,11 @@ struct DecodeArgs {
   bool glu;  // one call only: out = h [M, N/2] = silu(y_gate) * y_up
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// the kernels for one activation dtype (decode_f32.hip, decode_f16.hip,
+// decode_bf16.hip); launch_decode picks one
+void launch_decode_f32(const DecodeArgs &a, hipStream_t stream);
+void launch_decode_f16(const DecodeArgs &a, hipStream_t stream);
+void launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 // Row mode of the decode kernel (one wave per token row): single calls with
 // 2 <= M <= 8 (fp32 x: M <= 4) and K <= 4096.
 constexpr int64_t kDecodeRowsMaxM = 8;

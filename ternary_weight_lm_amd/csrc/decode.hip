@@ -1,502 +1,14 @@
-// decode.hip -- the whole FusedBitLinear in one launch for M <= 4 tokens.
-//
-// RMSNorm right before the quantizers (hysenlabs de review "MatMul-Free LM:
-// Ternary-Gewichte statt Matrixmultiplikation im Transformer", section
-// "HGRNBit: was in einem Block tatsächlich passiert"), per-token absmax int8
-// codes, the ternary contraction and the rescale of datacamp "MatMul-freie
-// LLMs: Zentrale Konzepte erklärt", figure panels 4 and 5.
-//
-// At decode the layer moves N*K/4 bytes of packed weights and almost nothing
-// else, and at the sizes of a single layer it is latency-bound: the design
-// removes every serial step it can from the path launch -> last store.
-//   * Arguments are plain scalars, so gfx950 preloads them into SGPRs
-//     (kernel-argument preloading) instead of the waves fetching them.
-//   * All loads of a wave are issued at once, first the activation row and
-//     the gain, then the wave's weight tiles.  They are buffer loads whose
-//     out-of-range lanes / tiles read as zero, so none is conditional and the
-//     compiler's wait for the activations does not also wait for the weights.
-//   * The normalization of a row is split over the 4 waves (wave w owns the
-//     8-element chunks 64w + lane + 256c).  The sum of squares meets per lane
-//     in LDS ((p0 + p1) + (p2 + p3) over the waves) before one DPP tree: the
-//     association the act-quant kernel uses, so codes and scales are
-//     bit-identical across paths.  The absmax and the code row sum (exact
-//     in any order) are DPP trees per wave plus a 4-entry LDS exchange.
-//   * One workgroup owns one packed 32-row tile column; the 4 waves take
-//     its K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
-//     registers (weights) and LDS (codes), and the partial sums meet in LDS.
-// Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
-// one launch: workgroup b works on call b / tiles.
+// decode.hip -- dispatch of the decode kernels (decode_kernels.h) on the
+// activation dtype; each dtype's kernels live in a source file of their own.
 #include "bl_launch.h"
-#include "rowquant.h"
 
 namespace bl {
 
-constexpr int kDecTiles = 16;   // weight tiles per wave: K <= 4 * 16 * 128
-constexpr int kDecChunks = 4;   // chunks per lane and row: K <= 4 * 256 * 8
-constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
-
-// (make_rsrc / bload / bload_chunk: buffer loads from rowquant.h)
-
-// The body of both kernels below.  The call's packed / gain / beta / out
-// pointers are selected only after the activation loads are issued: in the
-// three-call kernel some of them are not preloaded and must first be fetched
-// from the argument buffer, and that wait must not hold up the first loads.
-template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU = false>
-__device__ __forceinline__ void decode_body(
-    const void *x, int K, int M, int tiles, int nt, float eps, int call, const uint4 *p0,
-    const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
-    const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
-  extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
-  __shared__ double part_ss[MR][4][64];
-  __shared__ float part_max[MR][4];
-  __shared__ int part_rs[MR][4];
-  __shared__ int red[4][MR][2][16];
-
-  constexpr int EB = dtype_bytes(DT);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-  const int KB = K >> 7, nq = K >> 3;
-  const int lds_stride = K + 16;
-
-  // ---- 1. every load of the wave, activations first
-  const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
-  // byte offset of this lane's chunk c in a row (out of range past K)
-  const auto choff = [&](int c) {
-    const int q = 64 * w + lane + 256 * c;
-    return q < nq ? (uint32_t)(8 * q * EB) : kOob;
-  };
-  // Order matters: x needs only preloaded arguments and goes out first; the
-  // gain comes next (it is needed right after the first row reduction), the
-  // weights last: they are not needed until the contraction, thousands of
-  // cycles later.  Waits are in issue order, so whatever is issued later
-  // never holds up the wait for what was issued earlier.
-  Chunk8<DT> xc[MR][kDecChunks];
-#pragma unroll
-  for (int c = 0; c < kDecChunks; ++c)
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-      xc[m][c] = bload_chunk<DT>(xr, m < M ? choff(c) + (uint32_t)(m * K * EB) : kOob);
-  __builtin_amdgcn_sched_barrier(0);
-  const uint4 *pk = call == 0 ? p0 : (call == 1 ? p1 : p2);
-  const rsrc_t wr = make_rsrc(pk + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
-  const void *gain = call == 0 ? g0 : (call == 1 ? g1 : g2);
-  Chunk8<DT> gc[kDecChunks];
-  v4i wt[kDecTiles];
-  // GAIN_LATE: the gain pointer has to come from the argument buffer, so
-  // the weights are issued before waiting for it
-#pragma unroll
-  for (int t = 0; t < kDecTiles; ++t)
-    if constexpr (GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
-#pragma unroll
-    for (int c = 0; c < kDecChunks; ++c) gc[c] = bload_chunk<DT>(gr, choff(c));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t = 0; t < kDecTiles; ++t)
-    if constexpr (!GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
-  __builtin_amdgcn_sched_barrier(0);
-  const float *bp = call == 0 ? b0 : (call == 1 ? b1 : b2);
-  void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
-  const float beta = *bp;
-
-  // chunk c of this wave holds at least one element of the row
-  const auto live = [&](int c) { return 256 * c + 64 * w < nq; };
-
-  // Rows past M read as zeros and are carried through every step (their
-  // results are never stored): the MR row chains stay free of branches and
-  // interleave.
-  // ---- 2. sum of squares: this wave's slot group, exchanged per lane
-  double ss[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) ss[m] = 0.0;
-#pragma unroll
-  for (int c = 0; c < kDecChunks; ++c)
-    if (live(c)) {
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float f[8];
-        widen<DT>(xc[m][c], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss[m] = __builtin_fma((double)f[e], (double)f[e], ss[m]);
-      }
-    }
-#pragma unroll
-  for (int m = 0; m < MR; ++m) part_ss[m][w][lane] = ss[m];
-  __syncthreads();
-
-  // ---- 3. absmax of the normalized row
-  float r[MR], amax[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const double lsum = (part_ss[m][0][lane] + part_ss[m][1][lane]) +
-                        (part_ss[m][2][lane] + part_ss[m][3][lane]);
-    r[m] = rms_inv(wave_sum(lsum), K, eps);
-    amax[m] = 0.0f;
-  }
-#pragma unroll
-  for (int c = 0; c < kDecChunks; ++c)
-    if (live(c)) {
-      float g[8];
-      widen<DT>(gc[c], g);
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float f[8];
-        widen<DT>(xc[m][c], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax[m] = fmaxf(amax[m], fabsf((f[e] * r[m]) * g[e]));
-      }
-    }
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const float t = wave_max(amax[m]);
-    if (lane == 0) part_max[m][w] = t;
-  }
-  __syncthreads();
-
-  // ---- 4. int8 codes into LDS, row sums of the codes
-  float sc[MR], fscale[MR];
-  int rs[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    sc[m] = act_scale(fmaxf(fmaxf(part_max[m][0], part_max[m][1]),
-                            fmaxf(part_max[m][2], part_max[m][3])));
-    fscale[m] = div_rn(beta, sc[m]);
-    rs[m] = 0;
-  }
-#pragma unroll
-  for (int c = 0; c < kDecChunks; ++c)
-    if (live(c)) {
-      const int q = 64 * w + lane + 256 * c;
-      float g[8];
-      widen<DT>(gc[c], g);
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float f[8];
-        widen<DT>(xc[m][c], f);
-        int qv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = quant8((f[e] * r[m]) * g[e], sc[m]);
-        const uint2 codes = make_uint2(pack4(qv[0], qv[1], qv[2], qv[3]),
-                                       pack4(qv[4], qv[5], qv[6], qv[7]));
-        rs[m] = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs[m], false);
-        rs[m] = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs[m], false);
-        if (q < nq && m < M) *reinterpret_cast<uint2 *>(xs + m * lds_stride + 8 * q) = codes;
-      }
-    }
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const int t = wave_sum(rs[m]);
-    if (lane == 0) part_rs[m][w] = t;
-  }
-  __syncthreads();
-
-  // ---- 5. contraction: the wave's tiles kb = w + 4t
-  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
-  const int arow = lane & 15;
-  const bool arow_ok = arow < M;
-  const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
-  // two accumulators per output half (s2 = 0 / 1): each MFMA depends on the
-  // one two steps back, not on the previous one
-  v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  constexpr int kBatch = 4;  // A operands read from LDS together
-#pragma unroll
-  for (int t0 = 0; t0 < kDecTiles; t0 += kBatch) {
-    if (t0 >= nmine) break;
-    v4i a[kBatch][2];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        a[j][s2] = v4i{0, 0, 0, 0};
-        if (arow_ok && t0 + j < nmine)
-          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
-      }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (t0 + j >= nmine) break;
-      const v4i u = wt[t0 + j];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        // word (h, s2) of a lane slot sits at dword 2h + s2
-        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
-        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
-      }
-    }
-  }
-
-  // ---- 6. partial sums meet in LDS; rescale and store
-  // lanes 0..15 hold rows 0..3 (acc[i] = row i) of columns lane / 16 + lane
-  if (lane < 16) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      red[w][m][0][lane] = acc0[0][m] + acc0[1][m];
-      red[w][m][1][lane] = acc1[0][m] + acc1[1][m];
-    }
-  }
-  __syncthreads();
-  if constexpr (GLU) {
-    // GLU order: tile rows 0..15 are gated, 16..31 the rows they multiply;
-    // output h[m, 16 nt + l] = silu(y[m, l]) * y[m, 16 + l]
-    if (tid < 16 * M) {
-      const int m = tid >> 4, l = tid & 15;
-      const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
-      const int vg = red[0][m][0][l] + red[1][m][0][l] + red[2][m][0][l] + red[3][m][0][l] - rsum;
-      const int vu = red[0][m][1][l] + red[1][m][1][l] + red[2][m][1][l] + red[3][m][1][l] - rsum;
-      float fs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < MR; ++i)
-        if (i == m) fs = fscale[i];
-      store1<OUT>(out, (int64_t)m * tiles * 16 + nt * 16 + l, silu((float)vg * fs) * ((float)vu * fs));
-    }
-    return;
-  }
-  if (tid < 32 * M) {
-    const int m = tid >> 5, n = tid & 31;
-    const int h = n >> 4, l = n & 15;
-    const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
-    const int v = red[0][m][h][l] + red[1][m][h][l] + red[2][m][h][l] + red[3][m][h][l] - rsum;
-    float fs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-      if (i == m) fs = fscale[i];
-    store1<OUT>(out, (int64_t)m * tiles * 32 + nt * 32 + n, (float)v * fs);
-  }
-}
-
-// One call.  Every argument fits the 14 preloaded SGPRs.
-// shape = K/128 | M << 7 | tiles << 10.  GLU: the packed rows are a
-// gate_proj in GLU order and out is h [M, tiles * 16].
-template <int DT, int OUT, int MR, bool GLU>
-__global__ __launch_bounds__(256, 2) void decode_kernel(const void *x, uint32_t shape, float eps,
-                                                        const uint4 *packed, const void *gain,
-                                                        const float *beta, void *out) {
-  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
-  decode_body<DT, OUT, MR, false, GLU>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0, packed, packed,
-                           packed, gain, gain, gain, beta, beta, beta, out, out, out);
-}
-
-// Up to three calls of one shape; workgroup b works on call b / tiles.  The
-// activation and weight pointers are preloaded, the rest is fetched.
-template <int DT, int OUT, int MR>
-__global__ __launch_bounds__(256, 2) void decode3_kernel(
-    const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
-    const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
-    const void *g2, const float *b0, const float *b1, const float *b2, void *o0, void *o1,
-    void *o2) {
-  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
-  const int tiles = (int)(shape >> 10);
-  const int bid = (int)blockIdx.x;
-  const int call = (bid >= tiles) + (bid >= 2 * tiles);
-  const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
-  decode_body<DT, OUT, MR, true>(x, K, M, tiles, bid - call * tiles, eps, call, p0, p1, p2, g0, g1, g2,
-                           b0, b1, b2, o0, o1, o2);
-}
-
-// ---------------------------------------------------------------- row mode
-// 2 <= M <= 4 * RPW tokens, K <= 4096: wave w normalizes and quantizes rows
-// w, w + 4, ... by itself (the shared float-mode row passes of rowquant.h,
-// bit-identical to the act-quant kernel), so no row reduction crosses a
-// wave and one barrier (the codes in LDS) suffices.  Loads go out x rows ->
-// gain (once per wave) -> weights; every argument is preloaded.
-constexpr int kRowTiles = 8;  // K <= 4 * 8 * 128
-
-template <int DT, int OUT, int RPW, bool GLU>
-__global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint32_t shape,
-                                                             float eps, const uint4 *packed,
-                                                             const void *gain, const float *bp,
-                                                             void *out) {
-  extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
-  __shared__ int red[4][8][64];
-  __shared__ float f_row[16];
-  __shared__ int rs_row[16];
-
-  constexpr int EB = dtype_bytes(DT);
-  const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 31;
-  const int tiles = (int)(shape >> 12);
-  const int nt = (int)blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int KB = K >> 7;
-  const int lds_stride = K + 16;
-
-  // ---- 1. loads: this wave's rows, the gain, then the weight tiles
-  const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
-  Chunk8<DT> xraw[RPW][kRowCache];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int m = w + 4 * j;
-#pragma unroll
-    for (int c = 0; c < kRowCache; ++c) {
-      const int k = 8 * lane + 512 * c;
-      xraw[j][c] = bload_chunk<DT>(xr, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
-  Chunk8<DT> graw[kRowCache];
-#pragma unroll
-  for (int c = 0; c < kRowCache; ++c) graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
-  __builtin_amdgcn_sched_barrier(0);
-  const rsrc_t wr = make_rsrc(packed + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
-  v4i wt[kRowTiles];
-#pragma unroll
-  for (int t = 0; t < kRowTiles; ++t) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
-  __builtin_amdgcn_sched_barrier(0);
-  const float beta = *bp;
-
-  // ---- 2. the wave's rows: codes into LDS, scale factor and row sum
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int m = w + 4 * j;
-    if (m >= M) break;
-    int8_t *dst = xs + m * lds_stride;
-    float sc;
-    int rs;
-    quantize_loaded<DT>(xraw[j], graw, K, eps,
-                        [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
-                        sc, rs);
-    if (lane == 0) {
-      f_row[m] = div_rn(beta, sc);
-      rs_row[m] = rs;
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. contraction: tiles kb = w + 4t, rows 0..15 as one MFMA block
-  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
-  const int arow = lane & 15;
-  const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
-  v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  constexpr int kBatch = 4;
-#pragma unroll
-  for (int t0 = 0; t0 < kRowTiles; t0 += kBatch) {
-    if (t0 >= nmine) break;
-    v4i a[kBatch][2];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        a[j][s2] = v4i{0, 0, 0, 0};
-        if (arow < M && t0 + j < nmine)
-          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
-      }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (t0 + j >= nmine) break;
-      const v4i u = wt[t0 + j];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
-        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
-      }
-    }
-  }
-
-  // ---- 4. partial sums meet in LDS; rescale and store.  red[w][4 h + i][L]
-  // holds row 4 (L / 16) + i, column 16 h + L % 16 of the tile.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[w][i][lane] = acc0[0][i] + acc0[1][i];
-    red[w][4 + i][lane] = acc1[0][i] + acc1[1][i];
-  }
-  __syncthreads();
-  if constexpr (GLU) {
-    const int m = tid >> 4, c = tid & 15;  // 16 rows x 16 outputs
-    if (m < M) {
-      const int Lq = 16 * (m >> 2) + c, jg = m & 3, ju = jg + 4;
-      const int vg = red[0][jg][Lq] + red[1][jg][Lq] + red[2][jg][Lq] + red[3][jg][Lq] - rs_row[m];
-      const int vu = red[0][ju][Lq] + red[1][ju][Lq] + red[2][ju][Lq] + red[3][ju][Lq] - rs_row[m];
-      store1<OUT>(out, (int64_t)m * tiles * 16 + nt * 16 + c,
-                  silu((float)vg * f_row[m]) * ((float)vu * f_row[m]));
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q;
-      const int j = idx >> 6, Lq = idx & 63;
-      const int h = j >> 2, i = j & 3;
-      const int m = 4 * (Lq >> 4) + i;
-      if (m >= M) continue;
-      const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
-      store1<OUT>(out, (int64_t)m * tiles * 32 + nt * 32 + 16 * h + (Lq & 15), (float)v * f_row[m]);
-    }
-  }
-}
-
-template <int DT, int OUT, bool GLU>
-static void launch_rows(const DecodeArgs &a, hipStream_t stream) {
-  const unsigned tiles = (unsigned)(a.N / 32);
-  const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
-  const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
-  const uint4 *pk = reinterpret_cast<const uint4 *>(a.packed[0]);
-  if (a.M <= 4)
-    decode_rows_kernel<DT, OUT, 1, GLU><<<tiles, 256, lds, stream>>>(a.x[0], shape, a.eps, pk,
-                                                                      a.gain[0], a.beta[0], a.out[0]);
-  else
-    decode_rows_kernel<DT, OUT, DT == BL_F32 ? 1 : 2, GLU><<<tiles, 256, lds, stream>>>(
-        a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
-}
-
-template <int DT, int OUT>
-static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
-  const unsigned tiles = (unsigned)(a.N / 32);
-  const unsigned grid = tiles * (unsigned)a.ncalls;
-  const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
-  const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 10);
-  const uint4 *p[3];
-  for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
-  // fp32 activations decode one row per launch (decode_fits)
-  constexpr int MR4 = DT == BL_F32 ? 1 : (int)kDecodeMaxM;
-  if (a.ncalls == 1) {
-#define BL_DECODE1(MR_, G)                                                                 \
-  decode_kernel<DT, OUT, MR_, G><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],    \
-                                                             a.gain[0], a.beta[0], a.out[0])
-    if (a.M == 1) {
-      if (a.glu) BL_DECODE1(1, true); else BL_DECODE1(1, false);
-    } else {
-      if (a.glu) BL_DECODE1(MR4, true); else BL_DECODE1(MR4, false);
-    }
-#undef BL_DECODE1
-    return;
-  }
-  if (a.M == 1)
-    decode3_kernel<DT, OUT, 1><<<grid, 256, lds, stream>>>(
-        a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
-        a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
-  else
-    decode3_kernel<DT, OUT, MR4><<<grid, 256, lds, stream>>>(
-        a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],
-        a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
-}
-
-template <int DT>
-static void launch_out(const DecodeArgs &a, hipStream_t stream) {
-  if (a.ncalls == 1 && decode_rows_fits(a.M, a.K, a.x_dtype)) {
-#define BL_ROWS(O)                                                   \
-  (a.glu ? launch_rows<DT, O, true>(a, stream) : launch_rows<DT, O, false>(a, stream))
-    switch (a.out_kind) {
-      case BL_F32: BL_ROWS(BL_F32); break;
-      case BL_F16: BL_ROWS(BL_F16); break;
-      default: BL_ROWS(BL_BF16); break;
-    }
-#undef BL_ROWS
-    return;
-  }
-  switch (a.out_kind) {
-    case BL_F32: launch_mr<DT, BL_F32>(a, stream); break;
-    case BL_F16: launch_mr<DT, BL_F16>(a, stream); break;
-    default: launch_mr<DT, BL_BF16>(a, stream); break;
-  }
-}
-
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   switch (a.x_dtype) {
-    case BL_F32: launch_out<BL_F32>(a, stream); break;
-    case BL_F16: launch_out<BL_F16>(a, stream); break;
-    default: launch_out<BL_BF16>(a, stream); break;
+    case BL_F32: launch_decode_f32(a, stream); break;
+    case BL_F16: launch_decode_f16(a, stream); break;
+    default: launch_decode_bf16(a, stream); break;
   }
   return hipGetLastError();
 }

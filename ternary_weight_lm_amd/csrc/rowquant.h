@@ -30,6 +30,14 @@ namespace bl {
 
 constexpr int kRowCache = 8;  // cached chunks per lane: K <= 4096
 
+// Chunks a lane caches for a row of K elements in the float mode: the
+// smallest of 2, 4, 6, 8 rounds of 512 elements that covers K.  Every load
+// instruction costs the CU's address unit a slot even where all its lanes
+// are out of range, so a short row issues only the loads it needs.
+__host__ __device__ constexpr int row_cache(int K) {
+  return K <= 1024 ? 2 : (K <= 2048 ? 4 : (K <= 3072 ? 6 : 8));
+}
+
 // The low bytes of four words (int8 codes from quant8) -> one dword of
 // int8 (byte i = code i), three byte permutes.
 __device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
@@ -57,27 +65,27 @@ __host__ __device__ constexpr int row_mode(int K) {
 }
 
 // The three passes of the float mode on a row already in registers: chunk
-// c of the lane (elements 8 lane + 512 c .. +7, c < kRowCache) in xraw[c],
+// c of the lane (elements 8 lane + 512 c .. +7, c < NC) in xraw[c],
 // the gain's matching chunk in graw[c] (chunks past K read as zero).
 // `sink(k, codes)` receives the 8 codes of elements k..k+7 as two dwords; on
 // return every lane holds s and the row sum.  Shared by quantize_row and by
 // kernels that issue the row's loads themselves, so both give the same bits.
-template <int DT, class Sink>
-__device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[kRowCache],
-                                                const Chunk8<DT> (&graw)[kRowCache], int K,
+template <int DT, int NC, class Sink>
+__device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[NC],
+                                                const Chunk8<DT> (&graw)[NC], int K,
                                                 float eps, Sink sink, float &s_out,
                                                 int &rowsum_out) {
   const int lane = threadIdx.x & 63;
   const int nch = (K + 511) >> 9;  // chunk rounds (some lanes idle in the last)
   const auto kof = [&](int c) { return 8 * lane + 512 * c; };
   // x widened once; after pass 2 the same registers hold xn
-  float v[kRowCache][8];
+  float v[NC][8];
 #pragma unroll
-  for (int c = 0; c < kRowCache; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nch) widen<DT>(xraw[c], v[c]);
   double ss[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int c = 0; c < kRowCache; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nch && kof(c) < K) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -86,7 +94,7 @@ __device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[kRowCac
   const float r = rms_inv(group_sum(ss), K, eps);
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kRowCache; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nch && kof(c) < K) {
       float g[8];
       widen<DT>(graw[c], g);
@@ -99,7 +107,7 @@ __device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[kRowCac
   const float sc = act_scale(wave_max(amax));
   int rs = 0;
 #pragma unroll
-  for (int c = 0; c < kRowCache; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nch && kof(c) < K) {
       int q[8];
 #pragma unroll
@@ -116,7 +124,8 @@ __device__ __forceinline__ void quantize_loaded(const Chunk8<DT> (&xraw)[kRowCac
 // Quantizes one row with the calling wave.  `sink(k, codes)` receives the 8
 // codes of elements k..k+7 as two dwords.  On return every lane holds s and
 // the row sum.  The three modes run the same operations in the same order.
-template <int DT, int MODE, class Sink>
+// NC: chunks cached per lane in the float mode (K <= 512 * NC).
+template <int DT, int MODE, int NC_FLOAT = kRowCache, class Sink>
 __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
                                              const char *__restrict__ gr, int K,
                                              float eps, Sink sink, float &s_out,
@@ -142,12 +151,12 @@ __device__ __forceinline__ void quantize_row(const char *__restrict__ xr,
   };
 
   if constexpr (MODE == kRowFloat) {
-    Chunk8<DT> xraw[kRowCache], graw[kRowCache];
+    Chunk8<DT> xraw[NC_FLOAT], graw[NC_FLOAT];
 #pragma unroll
-    for (int c = 0; c < kRowCache; ++c) xraw[c] = ld(c);
+    for (int c = 0; c < NC_FLOAT; ++c) xraw[c] = ld(c);
 #pragma unroll
-    for (int c = 0; c < kRowCache; ++c) graw[c] = ldg(c);
-    quantize_loaded<DT>(xraw, graw, K, eps, sink, s_out, rowsum_out);
+    for (int c = 0; c < NC_FLOAT; ++c) graw[c] = ldg(c);
+    quantize_loaded<DT, NC_FLOAT>(xraw, graw, K, eps, sink, s_out, rowsum_out);
   } else {
     // raw chunks (kRowRaw) or batches of 4 re-read chunks (kRowReload)
     constexpr int NC = MODE == kRowRaw ? kRowRawCache : 4;
