@@ -25,10 +25,12 @@
 //     its K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
 //     registers (weights) and LDS (codes), and the partial sums meet in LDS.
 //   * The kernels are compiled for a few sizes of a wave's share of the row
-//     (TPW weight tiles, 2 .. 16) and the launch takes the smallest that
+//     (K capacity 1024 KC, KC = 1 .. 8) and the launch takes the smallest that
 //     covers K: each load instruction costs the CU's address unit a slot even
 //     where every lane is out of range, and with loads sized for the largest
 //     K a short row spent most of its time issuing them.
+//   * Rows longer than 1024 are shared by 8 waves (NW): the contraction and
+//     the per-element passes are split 8 ways, the sum of squares 4 ways.
 // Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
 // one launch: workgroup b works on call b / tiles.
 //
@@ -42,104 +44,132 @@ namespace bl {
 
 constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
 
-// Weight tiles per wave for a row of K: the smallest of 2, 4, 6, 8, 12, 16
-// with 4 * 128 * TPW >= K.  The split mode's chunks per lane follow as
-// ceil(TPW / 4) (256 lanes x 8 elements per round), the row mode's as TPW.
-constexpr int dec_tpw(int64_t K) {
-  return K <= 1024 ? 2 : K <= 2048 ? 4 : K <= 3072 ? 6 : K <= 4096 ? 8 : K <= 6144 ? 12 : 16;
+// K capacity of a kernel instance in units of 1024: the smallest of 1, 2, 3,
+// 4, 6, 8 with 1024 * KC >= K.  A wave's share of a row follows from it.
+constexpr int dec_kc(int64_t K) {
+  return K <= 1024 ? 1 : K <= 2048 ? 2 : K <= 3072 ? 3 : K <= 4096 ? 4 : K <= 6144 ? 6 : 8;
 }
 
-// (make_rsrc / bload / bload_chunk: buffer loads from rowquant.h)
+// Waves per workgroup in the split mode.  More waves share the tile
+// column's contraction and the per-element passes; the sum of squares stays
+// on waves 0..3 (its fp64 association, below, is fixed).
+constexpr int dec_nw(int64_t K) { return K <= 1024 ? 4 : 8; }
 
-// The body of both kernels below.  The call's packed / gain / beta / out
-// pointers are selected only after the activation loads are issued: in the
-// three-call kernel some of them are not preloaded and must first be fetched
-// from the argument buffer, and that wait must not hold up the first loads.
-template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU, int TPW>
+// The body of both kernels below: NW waves own one 32-row tile column.
+//   * Sum of squares (waves 0..3): lane `l` of wave w owns the 8-element
+//     chunks q = 64 w + l + 256 r, r = 0, 1, ... (slot q mod 256, summed in r
+//     order); the slots meet per lane in LDS ((p0 + p1) + (p2 + p3) over
+//     the 4 waves) before one DPP tree -- the association of the act-quant
+//     kernel, so codes and scales are bit-identical across paths.
+//   * Absmax and codes (all waves, order-free): wave w takes the rounds
+//     r = (NW / 4) c + w / 4 of wave w mod 4's chunks.
+//   * Contraction: wave w takes the K-blocks w, w + NW, ...
+// The call's packed / gain / beta / out pointers are selected only after
+// the activation loads are issued: in the three-call kernel some of them are
+// not preloaded and must first be fetched from the argument buffer, and that
+// wait must not hold up the first loads.
+template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU, int KC, int NW>
 __device__ __forceinline__ void decode_body(
     const void *x, int K, int M, int tiles, int nt, float eps, int call, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
     const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
   __shared__ double part_ss[MR][4][64];
-  __shared__ float part_max[MR][4];
-  __shared__ int part_rs[MR][4];
-  __shared__ int red[4][MR][2][16];
+  __shared__ float part_max[MR][NW];
+  __shared__ int part_rs[MR][NW];
+  __shared__ int red[NW][MR][2][16];
 
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int EB = dtype_bytes(DT);
-  constexpr int CPL = (TPW + 3) / 4;  // chunks per lane and row
+  constexpr int R = NW / 4;                      // rounds stride of the per-element passes
+  constexpr int TPW = (8 * KC + NW - 1) / NW;     // weight tiles per wave
+  constexpr int C4 = (KC + 1) / 2;                // sum-of-squares rounds (waves 0..3)
+  constexpr int CA = (2 * KC + NW - 1) / NW;      // absmax / code rounds per wave
+  constexpr int CO = R == 2 ? C4 / 2 : 0;         // odd rounds loaded only for the sum
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int w4 = w & 3, wh = w >> 2;
   const int KB = K >> 7, nq = K >> 3;
   const int lds_stride = K + 16;
 
   // ---- 1. every load of the wave, activations first
   const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
-  // byte offset of this lane's chunk c in a row (out of range past K)
-  const auto choff = [&](int c) {
-    const int q = 64 * w + lane + 256 * c;
-    return q < nq ? (uint32_t)(8 * q * EB) : kOob;
-  };
+  // chunk index of round r of wave w mod 4 (past nq: out of range)
+  const auto qof = [&](int r) { return 64 * w4 + lane + 256 * r; };
+  const auto off = [&](int r) { return qof(r) < nq ? (uint32_t)(8 * qof(r) * EB) : kOob; };
   // Order matters: x needs only preloaded arguments and goes out first; the
   // gain comes next (it is needed right after the first row reduction), the
   // weights last: they are not needed until the contraction, thousands of
   // cycles later.  Waits are in issue order, so whatever is issued later
   // never holds up the wait for what was issued earlier.
-  Chunk8<DT> xc[MR][CPL];
+  Chunk8<DT> xa[MR][CA], xo[MR][CO > 0 ? CO : 1];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
+  for (int c = 0; c < CA; ++c)
 #pragma unroll
     for (int m = 0; m < MR; ++m)
-      xc[m][c] = bload_chunk<DT>(xr, m < M ? choff(c) + (uint32_t)(m * K * EB) : kOob);
+      xa[m][c] = bload_chunk<DT>(xr, m < M ? off(R * c + wh) + (uint32_t)(m * K * EB) : kOob);
+  if constexpr (CO > 0) {
+    if (w < 4) {
+#pragma unroll
+      for (int c = 0; c < CO; ++c)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+          xo[m][c] = bload_chunk<DT>(xr, m < M ? off(2 * c + 1) + (uint32_t)(m * K * EB) : kOob);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   const uint4 *pk = call == 0 ? p0 : (call == 1 ? p1 : p2);
   const rsrc_t wr = make_rsrc(pk + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
   const void *gain = call == 0 ? g0 : (call == 1 ? g1 : g2);
-  Chunk8<DT> gc[CPL];
+  Chunk8<DT> gc[CA];
   v4i wt[TPW];
   // GAIN_LATE: the gain pointer has to come from the argument buffer, so
   // the weights are issued before waiting for it
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
-    if constexpr (GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+    if constexpr (GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
   __builtin_amdgcn_sched_barrier(0);
   {
     const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) gc[c] = bload_chunk<DT>(gr, choff(c));
+    for (int c = 0; c < CA; ++c) gc[c] = bload_chunk<DT>(gr, off(R * c + wh));
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
-    if constexpr (!GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+    if constexpr (!GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
   __builtin_amdgcn_sched_barrier(0);
   const float *bp = call == 0 ? b0 : (call == 1 ? b1 : b2);
   void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
   const float beta = *bp;
 
-  // chunk c of this wave holds at least one element of the row
-  const auto live = [&](int c) { return 256 * c + 64 * w < nq; };
+  // round r of wave w mod 4 holds at least one element of the row
+  const auto live = [&](int r) { return 256 * r + 64 * w4 < nq; };
 
   // Rows past M read as zeros and are carried through every step (their
   // results are never stored): the MR row chains stay free of branches and
   // interleave.
-  // ---- 2. sum of squares: this wave's slot group, exchanged per lane
-  double ss[MR];
+  // ---- 2. sum of squares (waves 0..3): rounds in order, exchanged per lane
+  if (w < 4) {
+    double ss[MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) ss[m] = 0.0;
+    for (int m = 0; m < MR; ++m) ss[m] = 0.0;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    if (live(c)) {
+    for (int r = 0; r < C4; ++r)
+      if (live(r)) {
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float f[8];
-        widen<DT>(xc[m][c], f);
+        for (int m = 0; m < MR; ++m) {
+          float f[8];
+          // round r: xa[r / R] if this wave's per-element passes own it, else
+          // the odd round loaded for the sum alone
+          widen<DT>(R == 1 || (r & 1) == 0 ? xa[m][r / R] : xo[m][CO > 0 ? r >> 1 : 0], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss[m] = __builtin_fma((double)f[e], (double)f[e], ss[m]);
+          for (int e = 0; e < 8; ++e) ss[m] = __builtin_fma((double)f[e], (double)f[e], ss[m]);
+        }
       }
-    }
 #pragma unroll
-  for (int m = 0; m < MR; ++m) part_ss[m][w][lane] = ss[m];
+    for (int m = 0; m < MR; ++m) part_ss[m][w][lane] = ss[m];
+  }
   __syncthreads();
 
   // ---- 3. absmax of the normalized row
@@ -152,14 +182,14 @@ __device__ __forceinline__ void decode_body(
     amax[m] = 0.0f;
   }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    if (live(c)) {
+  for (int c = 0; c < CA; ++c)
+    if (live(R * c + wh)) {
       float g[8];
       widen<DT>(gc[c], g);
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         float f[8];
-        widen<DT>(xc[m][c], f);
+        widen<DT>(xa[m][c], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax[m] = fmaxf(amax[m], fabsf((f[e] * r[m]) * g[e]));
       }
@@ -176,21 +206,23 @@ __device__ __forceinline__ void decode_body(
   int rs[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    sc[m] = act_scale(fmaxf(fmaxf(part_max[m][0], part_max[m][1]),
-                            fmaxf(part_max[m][2], part_max[m][3])));
+    float mx = part_max[m][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) mx = fmaxf(mx, part_max[m][i]);
+    sc[m] = act_scale(mx);
     fscale[m] = div_rn(beta, sc[m]);
     rs[m] = 0;
   }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    if (live(c)) {
-      const int q = 64 * w + lane + 256 * c;
+  for (int c = 0; c < CA; ++c)
+    if (live(R * c + wh)) {
+      const int q = qof(R * c + wh);
       float g[8];
       widen<DT>(gc[c], g);
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         float f[8];
-        widen<DT>(xc[m][c], f);
+        widen<DT>(xa[m][c], f);
         int qv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = quant8((f[e] * r[m]) * g[e], sc[m]);
@@ -208,8 +240,8 @@ __device__ __forceinline__ void decode_body(
   }
   __syncthreads();
 
-  // ---- 5. contraction: the wave's tiles kb = w + 4t
-  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
+  // ---- 5. contraction: the wave's tiles kb = w + NW t
+  const int nmine = w < KB ? (KB - w + NW - 1) / NW : 0;
   const int arow = lane & 15;
   const bool arow_ok = arow < M;
   const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
@@ -227,7 +259,7 @@ __device__ __forceinline__ void decode_body(
       for (int s2 = 0; s2 < 2; ++s2) {
         a[j][s2] = v4i{0, 0, 0, 0};
         if (t0 + j < TPW && arow_ok && t0 + j < nmine)
-          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
+          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + NW * (t0 + j)) * 128 + 16 * s2);
       }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -252,14 +284,26 @@ __device__ __forceinline__ void decode_body(
     }
   }
   __syncthreads();
+  const auto tile_sum = [&](int m, int h, int l) {
+    int v = red[0][m][h][l];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v += red[i][m][h][l];
+    return v;
+  };
+  const auto row_sum = [&](int m) {
+    int v = part_rs[m][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v += part_rs[m][i];
+    return v;
+  };
   if constexpr (GLU) {
     // GLU order: tile rows 0..15 are gated, 16..31 the rows they multiply;
     // output h[m, 16 nt + l] = silu(y[m, l]) * y[m, 16 + l]
     if (tid < 16 * M) {
       const int m = tid >> 4, l = tid & 15;
-      const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
-      const int vg = red[0][m][0][l] + red[1][m][0][l] + red[2][m][0][l] + red[3][m][0][l] - rsum;
-      const int vu = red[0][m][1][l] + red[1][m][1][l] + red[2][m][1][l] + red[3][m][1][l] - rsum;
+      const int rsum = row_sum(m);
+      const int vg = tile_sum(m, 0, l) - rsum;
+      const int vu = tile_sum(m, 1, l) - rsum;
       float fs = 0.0f;
 #pragma unroll
       for (int i = 0; i < MR; ++i)
@@ -271,8 +315,7 @@ __device__ __forceinline__ void decode_body(
   if (tid < 32 * M) {
     const int m = tid >> 5, n = tid & 31;
     const int h = n >> 4, l = n & 15;
-    const int rsum = (part_rs[m][0] + part_rs[m][1]) + (part_rs[m][2] + part_rs[m][3]);
-    const int v = red[0][m][h][l] + red[1][m][h][l] + red[2][m][h][l] + red[3][m][h][l] - rsum;
+    const int v = tile_sum(m, h, l) - row_sum(m);
     float fs = 0.0f;
 #pragma unroll
     for (int i = 0; i < MR; ++i)
@@ -284,19 +327,21 @@ __device__ __forceinline__ void decode_body(
 // One call.  Every argument fits the 14 preloaded SGPRs.
 // shape = K/128 | M << 7 | tiles << 10.  GLU: the packed rows are a
 // gate_proj in GLU order and out is h [M, tiles * 16].
-template <int DT, int OUT, int MR, bool GLU, int TPW>
-__global__ __launch_bounds__(256, 2) void decode_kernel(const void *x, uint32_t shape, float eps,
-                                                        const uint4 *packed, const void *gain,
-                                                        const float *beta, void *out) {
+template <int DT, int OUT, int MR, bool GLU, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(const void *x, uint32_t shape,
+                                                                 float eps, const uint4 *packed,
+                                                                 const void *gain,
+                                                                 const float *beta, void *out) {
   const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
-  decode_body<DT, OUT, MR, false, GLU, TPW>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0, packed, packed,
-                           packed, gain, gain, gain, beta, beta, beta, out, out, out);
+  decode_body<DT, OUT, MR, false, GLU, KC, NW>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0,
+                                               packed, packed, packed, gain, gain, gain, beta, beta,
+                                               beta, out, out, out);
 }
 
 // Up to three calls of one shape; workgroup b works on call b / tiles.  The
 // activation and weight pointers are preloaded, the rest is fetched.
-template <int DT, int OUT, int MR, int TPW>
-__global__ __launch_bounds__(256, 2) void decode3_kernel(
+template <int DT, int OUT, int MR, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
     const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
     const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
     const void *g2, const float *b0, const float *b1, const float *b2, void *o0, void *o1,
@@ -306,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void decode3_kernel(
   const int bid = (int)blockIdx.x;
   const int call = (bid >= tiles) + (bid >= 2 * tiles);
   const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
-  decode_body<DT, OUT, MR, true, false, TPW>(x, K, M, tiles, bid - call * tiles, eps, call, p0, p1, p2, g0, g1, g2,
-                           b0, b1, b2, o0, o1, o2);
+  decode_body<DT, OUT, MR, true, false, KC, NW>(x, K, M, tiles, bid - call * tiles, eps, call, p0,
+                                                p1, p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
 }
 
 // ---------------------------------------------------------------- row mode
@@ -455,19 +500,20 @@ static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
         a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
 }
 
-// row mode: K <= 4096 (decode_rows_fits), so TPW <= 8
+// row mode: K <= 4096 (decode_rows_fits); tiles per wave = 2 KC <= 8
 template <int DT, int OUT, bool GLU>
 static void launch_rows(const DecodeArgs &a, hipStream_t stream) {
-  switch (dec_tpw(a.K)) {
-    case 2: launch_rows_t<DT, OUT, GLU, 2>(a, stream); break;
-    case 4: launch_rows_t<DT, OUT, GLU, 4>(a, stream); break;
-    case 6: launch_rows_t<DT, OUT, GLU, 6>(a, stream); break;
+  switch (dec_kc(a.K)) {
+    case 1: launch_rows_t<DT, OUT, GLU, 2>(a, stream); break;
+    case 2: launch_rows_t<DT, OUT, GLU, 4>(a, stream); break;
+    case 3: launch_rows_t<DT, OUT, GLU, 6>(a, stream); break;
     default: launch_rows_t<DT, OUT, GLU, 8>(a, stream); break;
   }
 }
 
-template <int DT, int OUT, int TPW>
+template <int DT, int OUT, int KC>
 static void launch_mr_t(const DecodeArgs &a, hipStream_t stream) {
+  constexpr int NW = dec_nw(1024 * KC);
   const unsigned tiles = (unsigned)(a.N / 32);
   const unsigned grid = tiles * (unsigned)a.ncalls;
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
@@ -477,9 +523,9 @@ static void launch_mr_t(const DecodeArgs &a, hipStream_t stream) {
   // fp32 activations decode one row per launch (decode_fits)
   constexpr int MR4 = DT == BL_F32 ? 1 : (int)kDecodeMaxM;
   if (a.ncalls == 1) {
-#define BL_DECODE1(MR_, G)                                                                    \
-  decode_kernel<DT, OUT, MR_, G, TPW><<<grid, 256, lds, stream>>>(a.x[0], shape, a.eps, p[0],  \
-                                                                  a.gain[0], a.beta[0], a.out[0])
+#define BL_DECODE1(MR_, G)                                                                  \
+  decode_kernel<DT, OUT, MR_, G, KC, NW><<<grid, 64 * NW, lds, stream>>>(                    \
+      a.x[0], shape, a.eps, p[0], a.gain[0], a.beta[0], a.out[0])
     if (a.M == 1) {
       if (a.glu) BL_DECODE1(1, true); else BL_DECODE1(1, false);
     } else {
@@ -489,7 +535,7 @@ static void launch_mr_t(const DecodeArgs &a, hipStream_t stream) {
     return;
   }
 #define BL_DECODE3(MR_)                                                                     \
-  decode3_kernel<DT, OUT, MR_, TPW><<<grid, 256, lds, stream>>>(                             \
+  decode3_kernel<DT, OUT, MR_, KC, NW><<<grid, 64 * NW, lds, stream>>>(                      \
       a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],          \
       a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2])
   if (a.M == 1) BL_DECODE3(1); else BL_DECODE3(MR4);
@@ -499,13 +545,13 @@ static void launch_mr_t(const DecodeArgs &a, hipStream_t stream) {
 // split mode: K <= 8192 (decode_split_fits)
 template <int DT, int OUT>
 static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
-  switch (dec_tpw(a.K)) {
+  switch (dec_kc(a.K)) {
+    case 1: launch_mr_t<DT, OUT, 1>(a, stream); break;
     case 2: launch_mr_t<DT, OUT, 2>(a, stream); break;
+    case 3: launch_mr_t<DT, OUT, 3>(a, stream); break;
     case 4: launch_mr_t<DT, OUT, 4>(a, stream); break;
     case 6: launch_mr_t<DT, OUT, 6>(a, stream); break;
-    case 8: launch_mr_t<DT, OUT, 8>(a, stream); break;
-    case 12: launch_mr_t<DT, OUT, 12>(a, stream); break;
-    default: launch_mr_t<DT, OUT, 16>(a, stream); break;
+    default: launch_mr_t<DT, OUT, 8>(a, stream); break;
   }
 }
 
