@@ -11,6 +11,7 @@
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -92,8 +93,22 @@ __device__ __forceinline__ Chunk8<DT> bload_chunk(rsrc_t r, uint32_t off) {
 // Bytes per element of a dtype code.
 __host__ __device__ constexpr int dtype_bytes(int dt) { return dt == BL_F32 ? 4 : 2; }
 
+// fp32 -> fp16, round to nearest even, from the fp32 value as it stands.
+// The empty asm pins f as a materialized fp32 value: otherwise the compiler
+// folds a preceding fp32 multiply into the conversion (v_fma_mixlo_f16, one
+// rounding of the exact product straight to fp16), which differs from
+// rounding the fp32 product at every fp16 tie it creates.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  __asm__("" : "+v"(f));
   return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// The 16-bit pattern of v rounded to a 2-byte output dtype (fp16 / bf16),
+// as store1 rounds it.
+template <int DT>
+__device__ __forceinline__ uint16_t out_bits(float v) {
+  if constexpr (DT == BL_F16) return f32_to_f16_bits(v);
+  else return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 template <int DT>

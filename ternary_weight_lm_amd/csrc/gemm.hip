@@ -256,6 +256,46 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
       }
     return;
   }
+  if constexpr (OUT == BL_F16 || OUT == BL_BF16) {
+    // Whole tile of 2-byte outputs in a long launch: the wave's 16 MI x 64
+    // block goes through the A buffers (idle since the barrier that ended
+    // the last k-block), row-major with each row's 16-byte chunks XOR-
+    // swizzled by (row / 4) mod 4 so the 2-byte writes are conflict-free,
+    // and leaves as 16-byte stores covering whole 128-byte row segments:
+    // 2 MI store instructions per wave instead of 16 MI.  In a launch whose
+    // tiles all run at once the LDS round trip lengthens the tail that no
+    // other tile overlaps, so short launches store directly (measured
+    // threshold: tiles x k-blocks > 16384).
+    if (m0 + BM <= M && n0 + BN <= N && ntiles * KB > 16384) {
+      uint8_t *st = &lds[0][0] + wave * (16 * MI * 128);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * mi + q4 + i;
+          const int sw = ((row >> 2) & 3) << 1;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int col = 16 * nb + (lane & 15);
+            const float y = (float)(acc[mi][nb][i] - rs4[mi][i]) * sc4[mi][i];
+            *reinterpret_cast<uint16_t *>(st + row * 128 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2) =
+                out_bits<OUT>(y);
+          }
+        }
+      const rsrc_t ors =
+          make_rsrc(reinterpret_cast<uint16_t *>(out) + (int64_t)wrow0 * N + n0 + 64 * wn,
+                    (uint32_t)((16 * MI - 1) * N + 64) * 2u);
+#pragma unroll
+      for (int r8 = 0; r8 < 2 * MI; ++r8) {
+        const int row = 8 * r8 + (lane >> 3), chunk = lane & 7;
+        const int sw = ((row >> 2) & 3) << 1;
+        const v4i v = *reinterpret_cast<const v4i *>(st + row * 128 + ((chunk ^ sw) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ors,
+                                               (row * N + chunk * 8) * 2, 0, 0);
+      }
+      return;
+    }
+  }
   if (m0 + BM <= M && n0 + BN <= N) {
     // whole tile (all but the ragged edges): no per-element checks, one row
     // offset per (mi, i) and constant column offsets

@@ -277,3 +277,33 @@ def test_gemm_i32_largest_k(path):
     tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc, path=path)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
+
+
+@pytest.mark.parametrize("ydt", ["bf16", "fp16"])
+def test_long_launch_epilogue_bitwise(ydt):
+    """A launch long enough for the MFMA kernel to stage its output tiles
+    through LDS (2000 x 11264 x 2048: 1408 tiles of 16 k-blocks), with a
+    ragged last tile row that stores directly.  Every output element must
+    equal the exact int32 contraction rescaled by fl32(beta / s) in fp32 and
+    rounded to the output dtype -- the epilogue's arithmetic, done on the
+    host from the int32 result -- and sampled rows must match the oracle."""
+    M, N, K = 2000, 11264, 2048
+    say(f"long-launch epilogue M={M} N={N} K={K} y={ydt}")
+    xq = _random_codes(M, K, 11)
+    r = np.random.default_rng(12)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    beta = torch.tensor([0.0173], dtype=torch.float32, device=DEV)
+    s = torch.from_numpy(r.uniform(0.5, 40.0, size=M).astype(np.float32)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc, path=tw.BL_PATH_MFMA)
+    y = torch.empty((M, N), dtype=synth.DTYPES[ydt], device=DEV)
+    tw.bitlinear_contract(d_xq, s, d_rs, packed, beta, N, y, path=tw.BL_PATH_MFMA)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, M - 1, 9).round().astype(int))
+    np.testing.assert_array_equal(acc.cpu().numpy()[rows], oracle.contract(xq[rows], Wq))
+    scale = (beta.cpu() / s.cpu()).to(torch.float32)          # fp32, correctly rounded
+    want = (acc.cpu().to(torch.float32) * scale[:, None]).to(y.dtype)
+    assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16))
