@@ -196,6 +196,30 @@ typedef struct bl_call {
 int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
                               int y_dtype, float eps, hipStream_t stream);
 
+/* Grouped forward of calls of any size, with a workspace.  Each call is
+ * independent and gives bitlinear_forward's result bit for bit.  Calls the
+ * default path sends to the one-launch kernels (bitlinear_select_path ==
+ * BL_PATH_FUSED for that call's M, K and x_dtype) go out as in
+ * bitlinear_forward_grouped.  Every other call runs its two-kernel path, and
+ * up to three consecutive calls of one shape (M, K, N) on the MFMA path --
+ * HGRNBit's i/f/g projections at prefill, which read the same block input
+ * (hysenlabs ja review, section "HGRNBit という層構成を読む") -- share one
+ * act-quant launch and one MFMA launch: three 2048-wide projections of 4096
+ * tokens fill the GPU for several rounds instead of one each.
+ *   calls    HOST array of ncalls descriptors (read during the call only);
+ *            shapes, pointers and alignment as for bitlinear_forward, all
+ *            sharing x_dtype, y_dtype and eps; calls with M == 0 skipped.
+ *   ws       device workspace of at least
+ *            bitlinear_grouped_workspace_bytes(calls, ncalls, x_dtype)
+ *            bytes, 16-byte aligned (may be NULL when that is 0); reused by
+ *            the launches one after another, so two grouped calls may share
+ *            it only on one stream.
+ * 0 <= ncalls <= 4096; any invalid call rejects the group (BL_ERR_*) before
+ * anything is launched. */
+size_t bitlinear_grouped_workspace_bytes(const bl_call *calls, int ncalls, int x_dtype);
+int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, int y_dtype,
+                                 float eps, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ GLU MLP
  * The HGRNBit MLP is gate_proj -> SiLU gate -> down_proj (hysenlabs ja
  * review, section "HGRNBit という層構成を読む": gate_proj 2048 -> 11264,

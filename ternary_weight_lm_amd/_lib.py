@@ -62,6 +62,8 @@ SIGNATURES = {
     "bitlinear_forward_grouped": ([P, I, I, I, F, P], I),
     "bitlinear_status_string": ([I], ctypes.c_char_p),
     "bitlinear_select_path": ([I64, I64], I),
+    "bitlinear_grouped_workspace_bytes": ([P, I, I], SZ),
+    "bitlinear_forward_grouped_ws": ([P, I, I, I, F, P, SZ, P], I),
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
     "bitlinear_contract": ([P, P, P, I64, I64, P, P, I64, P, I, I, P], I),
@@ -192,6 +194,26 @@ def bitlinear_forward_grouped(calls, x_dtype, y_dtype, eps=1e-8, stream=None):
     _check("bitlinear_forward_grouped", lib().bitlinear_forward_grouped(
         ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[x_dtype],
         DTYPE_CODE[y_dtype], eps, _stream(stream)))
+
+
+def bitlinear_grouped_workspace_bytes(calls, x_dtype) -> int:
+    """calls: a make_calls() array or a list of (x, gain, packed, beta, y)."""
+    if not isinstance(calls, ctypes.Array):
+        calls = make_calls(calls)
+    return int(lib().bitlinear_grouped_workspace_bytes(
+        ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[x_dtype]))
+
+
+def bitlinear_forward_grouped_ws(calls, x_dtype, y_dtype, ws, eps=1e-8, stream=None):
+    """calls: a make_calls() array (kept by the caller, e.g. for graph capture)
+    or a list of (x, gain, packed, beta, y) tuples; ws: a device tensor of at
+    least bitlinear_grouped_workspace_bytes(calls, x_dtype) bytes, or None."""
+    if not isinstance(calls, ctypes.Array):
+        calls = make_calls(calls)
+    _check("bitlinear_forward_grouped_ws", lib().bitlinear_forward_grouped_ws(
+        ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[x_dtype],
+        DTYPE_CODE[y_dtype], eps, _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bitlinear_act_quant(x, gain, xq, s, rowsum, eps=1e-8, stream=None):

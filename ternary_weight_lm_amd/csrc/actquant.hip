@@ -16,11 +16,9 @@
 namespace bl {
 
 template <int DT, int MODE, int NC>
-__global__ __launch_bounds__(256) void act_quant_kernel(
-    const void *__restrict__ x, const void *__restrict__ gain, int64_t M, int K, float eps,
+__device__ __forceinline__ void act_quant_row(
+    const void *__restrict__ x, const void *__restrict__ gain, int64_t row, int K, float eps,
     int8_t *__restrict__ xq, float *__restrict__ s_out, int32_t *__restrict__ rowsum_out) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;  // a whole wave leaves; nothing below synchronizes
   constexpr int EB = dtype_bytes(DT);
   const char *xr = reinterpret_cast<const char *>(x) + row * K * EB;
   int8_t *qr = xq + row * K;
@@ -33,6 +31,25 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     s_out[row] = sc;
     rowsum_out[row] = rs;
   }
+}
+
+template <int DT, int MODE, int NC>
+__global__ __launch_bounds__(256) void act_quant_kernel(
+    const void *__restrict__ x, const void *__restrict__ gain, int64_t M, int K, float eps,
+    int8_t *__restrict__ xq, float *__restrict__ s_out, int32_t *__restrict__ rowsum_out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // a whole wave leaves; nothing below synchronizes
+  act_quant_row<DT, MODE, NC>(x, gain, row, K, eps, xq, s_out, rowsum_out);
+}
+
+// Several projections' rows in one launch: blockIdx.y selects the call.
+template <int DT, int MODE, int NC>
+__global__ __launch_bounds__(256) void act_quant_group_kernel(int64_t M, int K, float eps,
+                                                              AqCalls calls) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const AqCall &c = calls.c[blockIdx.y];
+  act_quant_row<DT, MODE, NC>(c.x, c.gain, row, K, eps, c.xq, c.s, c.rowsum);
 }
 
 template <int DT>
@@ -55,6 +72,37 @@ static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, flo
     default: BL_AQ(kRowReload, kRowCache); break;
   }
 #undef BL_AQ
+}
+
+template <int DT>
+static void launch_group_dt(const AqCalls &calls, int ncalls, int64_t M, int64_t K, float eps,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((M + 3) / 4), (unsigned)ncalls);
+#define BL_AQG(MODE, NC) \
+  act_quant_group_kernel<DT, MODE, NC><<<grid, 256, 0, stream>>>(M, (int)K, eps, calls)
+  switch (row_mode((int)K)) {
+    case kRowFloat:
+      switch (row_cache((int)K)) {
+        case 2: BL_AQG(kRowFloat, 2); break;
+        case 4: BL_AQG(kRowFloat, 4); break;
+        case 6: BL_AQG(kRowFloat, 6); break;
+        default: BL_AQG(kRowFloat, 8); break;
+      }
+      break;
+    case kRowRaw: BL_AQG(kRowRaw, kRowCache); break;
+    default: BL_AQG(kRowReload, kRowCache); break;
+  }
+#undef BL_AQG
+}
+
+hipError_t launch_act_quant_group(const AqCalls &calls, int ncalls, int x_dtype, int64_t M,
+                                  int64_t K, float eps, hipStream_t stream) {
+  switch (x_dtype) {
+    case BL_F32: launch_group_dt<BL_F32>(calls, ncalls, M, K, eps, stream); break;
+    case BL_F16: launch_group_dt<BL_F16>(calls, ncalls, M, K, eps, stream); break;
+    default: launch_group_dt<BL_BF16>(calls, ncalls, M, K, eps, stream); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_act_quant(const void *x, int x_dtype, const void *gain,

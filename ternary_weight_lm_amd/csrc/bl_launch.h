@@ -29,6 +29,23 @@ hipError_t launch_act_quant(const void *x, int x_dtype, const void *gain,
                             int64_t M, int64_t K, float eps, int8_t *xq,
                             float *s, int32_t *rowsum, hipStream_t stream);
 
+// Up to kGroupCalls same-shape projections per launch on the two-kernel
+// path (HGRN's i/f/g at prefill): one act-quant launch and one MFMA launch
+// for all of them.  Pointers travel in the argument buffer.
+constexpr int kGroupCalls = 3;
+struct AqCall {
+  const void *x;
+  const void *gain;
+  int8_t *xq;
+  float *s;
+  int32_t *rowsum;
+};
+struct AqCalls {
+  AqCall c[kGroupCalls];
+};
+hipError_t launch_act_quant_group(const AqCalls &calls, int ncalls, int x_dtype, int64_t M,
+                                  int64_t K, float eps, hipStream_t stream);
+
 // Tiled MFMA contraction of pre-quantized activations (any M).
 // out_kind = BL_* writes y = (acc) * beta / s; kOutI32 writes acc.
 // glu: the N = 2F packed rows are a gate_proj in GLU order and out is
@@ -38,6 +55,21 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *beta, int64_t M, int64_t N,
                             int64_t K, void *out, int out_kind, bool glu,
                             hipStream_t stream);
+
+struct GemmCall {
+  const int8_t *xq;
+  const int32_t *rowsum;
+  const float *s;
+  const void *packed;
+  const float *beta;
+  void *out;
+};
+struct GemmCalls {
+  GemmCall c[kGroupCalls];
+};
+// ncalls <= kGroupCalls contractions of one shape, out_kind a float dtype.
+hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
+                                  int64_t K, int out_kind, hipStream_t stream);
 
 // Skinny contraction for M <= kSkinnyMaxM (fused: M <= kFusedMaxM): one
 // workgroup per 32 output rows.

@@ -4,6 +4,7 @@
 // launches anything (so a rejected call touches no memory and needs no GPU),
 // then dispatches to the kernel launchers in bl_launch.h.  No exception
 // crosses the boundary; every failure is a negative status code.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -267,6 +268,129 @@ int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
   }
   if (args.empty()) return BL_OK;
   return hip_status(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The plan of bitlinear_forward_grouped_ws: calls the fused kernels take
+// (default path FUSED) go out together as in bitlinear_forward_grouped;
+// every other call runs its two-kernel path, and up to kGroupCalls
+// consecutive MFMA-path calls of one shape (M, K, N) form one run that
+// shares an act-quant launch and a GEMM launch.  Runs execute one after
+// another on the stream, so they share the workspace.
+struct GroupRun {
+  int first, n, path;
+};
+
+int plan_grouped(const bl_call *calls, int ncalls, int x_dtype, std::vector<GroupRun> &runs,
+                 std::vector<int> &fused, size_t &ws_need) {
+  if (!dtype_ok(x_dtype)) return BL_ERR_DTYPE;
+  if (ncalls < 0 || ncalls > 4096) return BL_ERR_SHAPE;
+  if (ncalls > 0 && !calls) return BL_ERR_NULL;
+  ws_need = 0;
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_call &c = calls[i];
+    if (!nk_ok(c.N, c.K) || !m_ok(c.M)) return BL_ERR_SHAPE;
+    if (c.M == 0) continue;
+    const int path = auto_path(c.M, c.K, x_dtype);
+    if (path == BL_PATH_FUSED) {
+      fused.push_back(i);
+      continue;
+    }
+    if (path == BL_PATH_MFMA && !runs.empty()) {
+      GroupRun &r = runs.back();
+      const bl_call &p = calls[r.first];
+      if (r.path == BL_PATH_MFMA && r.first + r.n == i && r.n < bl::kGroupCalls && p.M == c.M &&
+          p.K == c.K && p.N == c.N) {
+        ++r.n;
+        ws_need = std::max(ws_need, (size_t)r.n * fwd_ws_bytes(c.M, c.K));
+        continue;
+      }
+    }
+    runs.push_back(GroupRun{i, 1, path});
+    ws_need = std::max(ws_need, fwd_ws_bytes(c.M, c.K));
+  }
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_grouped_workspace_bytes(const bl_call *calls, int ncalls, int x_dtype) {
+  std::vector<GroupRun> runs;
+  std::vector<int> fused;
+  size_t need = 0;
+  return plan_grouped(calls, ncalls, x_dtype, runs, fused, need) == BL_OK ? need : 0;
+}
+
+int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, int y_dtype,
+                                 float eps, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  std::vector<GroupRun> runs;
+  std::vector<int> fused;
+  size_t need = 0;
+  const int st = plan_grouped(calls, ncalls, x_dtype, runs, fused, need);
+  if (st != BL_OK) return st;
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_call &c = calls[i];
+    if (c.M == 0) continue;
+    if (!c.x || !c.gain || !c.packed || !c.beta || !c.y) return BL_ERR_NULL;
+    if (!aligned16(c.x) || !aligned16(c.gain) || !aligned16(c.packed) || !aligned16(c.y) ||
+        (reinterpret_cast<uintptr_t>(c.beta) & 3u))
+      return BL_ERR_ALIGN;
+  }
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return BL_ERR_WORKSPACE;
+    if (!aligned16(ws)) return BL_ERR_ALIGN;
+  }
+  for (const GroupRun &r : runs) {
+    const bl_call &c0 = calls[r.first];
+    if (r.n == 1) {
+      const int e = forward_impl(c0.x, x_dtype, c0.M, c0.K, c0.gain, c0.packed, c0.beta, c0.N,
+                                 c0.y, y_dtype, eps, ws, ws_bytes, r.path, false, stream);
+      if (e != BL_OK) return e;
+      continue;
+    }
+    const size_t stride = fwd_ws_bytes(c0.M, c0.K);
+    bl::AqCalls aq{};
+    bl::GemmCalls gm{};
+    for (int j = 0; j < r.n; ++j) {
+      const bl_call &c = calls[r.first + j];
+      const FwdWs w = carve(static_cast<char *>(ws) + j * stride, c.M, c.K);
+      aq.c[j] = bl::AqCall{c.x, c.gain, w.xq, w.s, w.rowsum};
+      gm.c[j] = bl::GemmCall{w.xq, w.rowsum, w.s, c.packed, c.beta, c.y};
+    }
+    if (bl::launch_act_quant_group(aq, r.n, x_dtype, c0.M, c0.K, eps, stream) != hipSuccess)
+      return BL_ERR_HIP;
+    if (bl::launch_gemm_mfma_group(gm, r.n, c0.M, c0.N, c0.K, y_dtype, stream) != hipSuccess)
+      return BL_ERR_HIP;
+  }
+  if (!fused.empty()) {
+    std::vector<bl::SkinnyArgs> args;
+    for (const int i : fused) {
+      const bl_call &c = calls[i];
+      bl::SkinnyArgs a{};
+      a.fused = true;
+      a.x = c.x;
+      a.x_dtype = x_dtype;
+      a.gain = c.gain;
+      a.eps = eps;
+      a.packed = c.packed;
+      a.beta = c.beta;
+      a.M = c.M;
+      a.N = c.N;
+      a.K = c.K;
+      a.out = c.y;
+      a.out_kind = y_dtype;
+      args.push_back(a);
+    }
+    return hip_status(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream));
+  }
+  return BL_OK;
 }
 
 int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,

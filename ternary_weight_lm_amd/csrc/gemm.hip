@@ -101,14 +101,25 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
 
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
 
-// GLU: the packed rows are a gate_proj in GLU order (each 32-row tile = 16
-// gated rows + the 16 rows they multiply) and out is h [M, N/2].
+// Tile t of the XCD-aware order for workgroup `bid` of a launch of `ntiles`
+// tiles: workgroup ids reach the 8 XCDs round-robin, so XCD x gets the
+// contiguous range of the sequence that starts at x * ntiles / 8.
+__device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
+  const int per = ntiles / 8, rem = ntiles % 8;
+  const int xcd = bid % 8, local = bid / 8;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// One tile of one contraction.  t: the tile's place in the sequence of this
+// contraction's tiles; work: tiles x k-blocks of the whole launch (picks the
+// epilogue).  GLU: the packed rows are a gate_proj in GLU order (each 32-row
+// tile = 16 gated rows + the 16 rows they multiply) and out is h [M, N/2].
 template <int MI, int OUT, bool GLU>
-__global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
+__device__ __forceinline__ void gemm_body(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
-    void *__restrict__ out, int tiles_m, int tiles_n) {
+    void *__restrict__ out, int tiles_m, int tiles_n, int t, int work) {
   constexpr int BM = 32 * MI;
   constexpr int BN = 128;
   __shared__ __align__(16) uint8_t lds[2][BM * 128];
@@ -117,13 +128,6 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware tile order.
-  const int ntiles = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int per = ntiles / 8, rem = ntiles % 8;
-  const int xcd = bid % 8, local = bid / 8;
-  const int t = xcd < rem ? xcd * (per + 1) + local
-                          : rem * (per + 1) + (xcd - rem) * per + local;
   // Inside the sequence, tiles go column by column through bands of
   // kBandRows tile rows, so the ~64 workgroups an XCD runs at once share a
   // few A row tiles and a few B column tiles (about 1 MiB each) in its L2
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
     // tiles all run at once the LDS round trip lengthens the tail that no
     // other tile overlaps, so short launches store directly (measured
     // threshold: tiles x k-blocks > 16384).
-    if (m0 + BM <= M && n0 + BN <= N && ntiles * KB > 16384) {
+    if (m0 + BM <= M && n0 + BN <= N && work > 16384) {
       uint8_t *st = &lds[0][0] + wave * (16 * MI * 128);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
@@ -322,6 +326,35 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
   }
 }
 
+template <int MI, int OUT, bool GLU>
+__global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
+    const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
+    const float *__restrict__ s, const uint4 *__restrict__ packed,
+    const float *__restrict__ beta, int M, int N, int K,
+    void *__restrict__ out, int tiles_m, int tiles_n) {
+  const int ntiles = tiles_m * tiles_n;
+  gemm_body<MI, OUT, GLU>(xq, rowsum, s, packed, beta, M, N, K, out, tiles_m, tiles_n,
+                          xcd_tile((int)blockIdx.x, ntiles), ntiles * (K >> 7));
+}
+
+// Up to kGemmCalls contractions of one shape in one launch (HGRN's i/f/g at
+// prefill): the tile sequence is call 0's tiles, then call 1's, ..., so a
+// launch of three one-round contractions runs as several rounds whose
+// epilogues overlap other tiles' main loops.  The pointers come from the
+// argument buffer.
+template <int MI, int OUT>
+__global__ __launch_bounds__(256, 3) void gemm_mfma_group_kernel(int ncalls, int M, int N, int K,
+                                                                 int tiles_m, int tiles_n,
+                                                                 GemmCalls calls) {
+  const int ntiles = tiles_m * tiles_n;
+  const int tg = xcd_tile((int)blockIdx.x, ncalls * ntiles);
+  const int call = __builtin_amdgcn_readfirstlane(tg / ntiles);
+  const GemmCall &c = calls.c[call];
+  gemm_body<MI, OUT, false>(c.xq, c.rowsum, c.s, reinterpret_cast<const uint4 *>(c.packed), c.beta,
+                            M, N, K, c.out, tiles_m, tiles_n, tg - call * ntiles,
+                            ncalls * ntiles * (K >> 7));
+}
+
 template <int MI>
 static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
@@ -368,6 +401,35 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   if (M > 32 && tiles(64) >= 128)
     return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+}
+
+template <int MI>
+static hipError_t launch_group_mi(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
+                                  int64_t K, int out_kind, hipStream_t stream) {
+  const int BM = 32 * MI;
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + 127) / 128);
+  const unsigned grid = (unsigned)(tiles_m * tiles_n * ncalls);
+#define BL_GEMMG_CASE(KIND)                                                     \
+  gemm_mfma_group_kernel<MI, KIND><<<grid, 256, 0, stream>>>(ncalls, (int)M, (int)N, (int)K, \
+                                                             tiles_m, tiles_n, calls)
+  switch (out_kind) {
+    case BL_F32: BL_GEMMG_CASE(BL_F32); break;
+    case BL_F16: BL_GEMMG_CASE(BL_F16); break;
+    default: BL_GEMMG_CASE(BL_BF16); break;
+  }
+#undef BL_GEMMG_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
+                                  int64_t K, int out_kind, hipStream_t stream) {
+  // tile height as for one call, over the tiles of all the calls
+  const int64_t tn = (N + 127) / 128;
+  const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn * ncalls; };
+  if (M > 64 && tiles(128) >= 256) return launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
+  if (M > 32 && tiles(64) >= 128) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
+  return launch_group_mi<1>(calls, ncalls, M, N, K, out_kind, stream);
 }
 
 }  // namespace bl

@@ -196,6 +196,55 @@ def test_grouped_validation():
     assert grp([BlCall(None, None, None, None, None, 0, 1024, 1024)] * 3) == OK
 
 
+def test_grouped_ws_plan_and_validation():
+    """The workspace query follows the run rule (up to three consecutive
+    MFMA-path calls of one shape share a launch pair and need one workspace
+    each; runs reuse it), and every malformed group is rejected first."""
+    from ternary_weight_lm_amd._lib import BlCall
+    L = tw.lib()
+
+    def arr(calls):
+        return (BlCall * max(1, len(calls)))(*calls)
+
+    def need(calls, xdt=2):
+        return L.bitlinear_grouped_workspace_bytes(ctypes.cast(arr(calls), ctypes.c_void_p),
+                                                   len(calls), xdt)
+
+    def grp(calls, ws=WSP, ws_bytes=1 << 40, xdt=2, ydt=2, eps=1e-8, n=None):
+        return L.bitlinear_forward_grouped_ws(ctypes.cast(arr(calls), ctypes.c_void_p),
+                                              len(calls) if n is None else n, xdt, ydt, eps,
+                                              ws, ws_bytes, None)
+
+    def wsb(M, K, N):
+        return L.bitlinear_workspace_bytes(M, K, N)
+    big = BlCall(A, B, C, D, Y, 4096, 2048, 2048)
+    other = BlCall(A, B, C, D, Y, 4096, 2048, 11264)
+    dec = BlCall(A, B, C, D, Y, 1, 1024, 1024)
+    sk = BlCall(A, B, C, D, Y, 20, 512, 160)
+    assert need([dec, dec, dec]) == 0                        # fused calls need none
+    assert need([big]) == wsb(4096, 2048, 2048)
+    assert need([big, big, big]) == 3 * wsb(4096, 2048, 2048)
+    assert need([big, big, big, big]) == 3 * wsb(4096, 2048, 2048)   # runs of at most 3
+    assert need([big, other, big]) == max(wsb(4096, 2048, 2048), wsb(4096, 2048, 11264))
+    assert need([sk, dec]) == wsb(20, 512, 160)              # skinny path: its own workspace
+    assert need([big, BlCall(A, B, C, D, Y, 4096, 1000, 2048)]) == 0   # invalid group
+    assert need([big], xdt=7) == 0
+    assert grp([big], xdt=9) == DTYPE
+    assert grp([big], ydt=9) == DTYPE
+    assert grp([big], eps=float("nan")) == EPS
+    assert grp([big], n=-1) == SHAPE
+    assert grp([big], n=5000) == SHAPE
+    assert L.bitlinear_forward_grouped_ws(None, 2, 2, 2, 1e-8, WSP, 1 << 40, None) == NULL
+    assert L.bitlinear_forward_grouped_ws(None, 0, 2, 2, 1e-8, None, 0, None) == OK
+    assert grp([big, BlCall(A, B, C, D, Y, 4096, 2048, 100)]) == SHAPE
+    assert grp([big, BlCall(A, None, C, D, Y, 4096, 2048, 2048)]) == NULL
+    assert grp([big, BlCall(A, B, C, D, Y + 4, 4096, 2048, 2048)]) == ALIGN
+    assert grp([big, big], ws=None) == WS
+    assert grp([big, big], ws_bytes=2 * wsb(4096, 2048, 2048) - 1) == WS
+    assert grp([big], ws=WSP + 8) == ALIGN
+    assert grp([BlCall(None, None, None, None, None, 0, 1024, 1024)] * 3, ws=None, ws_bytes=0) == OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.float16)

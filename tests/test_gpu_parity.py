@@ -191,6 +191,38 @@ def test_grouped_matches_single_calls():
         assert torch.equal(it[4], singles[0])
 
 
+@pytest.mark.parametrize("case", ["mixed", "prefill_1p3b"])
+def test_grouped_ws_matches_single_calls(case):
+    """bitlinear_forward_grouped_ws gives bitlinear_forward's result on every
+    call, bit for bit: runs of three same-shape MFMA-path calls sharing an
+    act-quant and a GEMM launch (ragged M, partial output tiles, a run of
+    four split 3 + 1), an MFMA call of another shape, a skinny-path call and
+    calls the fused kernels take -- and, full size, the 1.3B i/f/g triple at
+    prefill."""
+    if case == "mixed":
+        shapes = [(300, 384, 640)] * 4 + [(100, 96, 256), (20, 160, 512), (1, 64, 1024),
+                                          (3, 96, 384), (0, 64, 256), (65, 160, 1280),
+                                          (65, 160, 1280)]
+    else:
+        shapes = [(4096, 2048, 2048)] * 3
+    say(f"grouped_ws {case}")
+    items, singles = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        x = synth.make_x(950 + i, 0, 0, M, K, "bf16").to(DEV)
+        g = synth.make_gain(950 + i, 0, 0, K, "bf16").to(DEV)
+        packed, beta = tw.pack(synth.make_w(950 + i, 0, 0, N, K).to(DEV))
+        y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+        items.append((x, g, packed, beta, y))
+        singles.append(tw.forward(x, g, packed, beta, N))
+    calls = tw.make_calls(items)
+    nbytes = tw.bitlinear_grouped_workspace_bytes(calls, torch.bfloat16)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    tw.bitlinear_forward_grouped_ws(calls, torch.bfloat16, torch.bfloat16, ws)
+    torch.cuda.synchronize()
+    for (x, g, packed, beta, y), ref in zip(items, singles):
+        assert torch.equal(y, ref)
+
+
 def test_paths_agree_bitwise_mid_m():
     say("paths agree mid M")
     for M in (24, 40, 64):
