@@ -136,24 +136,27 @@ class Workload:
         self.calls = [(l, i) for l in range(layers) for i in range(len(cfg.projs))]
 
     def groups(self):
-        """Launch groups of a step: the i/f/g projections of one layer read
-        the same block input in HGRNBit, so when they all take the fused
-        decode path they go out as one grouped launch; every other projection
-        (o_proj after the recurrence, the MLP pair) is launched on its own."""
+        """Launch groups of a step.  HGRNBit's i/f/g projections of one layer
+        read the same block input, so when they take the fused decode path
+        they go out as one grouped decode launch, and on the MFMA path as one
+        grouped act-quant launch plus one grouped GEMM launch
+        (bitlinear_forward_grouped_ws); every other projection (o_proj after
+        the recurrence, the MLP pair, the skinny path) is launched on its own."""
         import ternary_weight_lm_amd as tw
-        out, cur = [], []
+        out, cur, cur_path = [], [], None
         for j, (layer, pi) in enumerate(self.calls):
             name = self.cfg.projs[pi].name
-            fused = tw.bitlinear_select_path(self.M, self.cfg.projs[pi].K) == tw.BL_PATH_FUSED
-            if fused and name in ("i_proj", "f_proj", "g_proj") and (
-                    not cur or self.calls[cur[0]][0] == layer):
+            path = tw.bitlinear_select_path(self.M, self.cfg.projs[pi].K)
+            groupable = path in (tw.BL_PATH_FUSED, tw.BL_PATH_MFMA) and name in (
+                "i_proj", "f_proj", "g_proj")
+            if groupable and cur and self.calls[cur[0]][0] == layer and path == cur_path:
                 cur.append(j)
                 continue
             if cur:
                 out.append(cur)
                 cur = []
-            if fused and name in ("i_proj", "f_proj", "g_proj"):
-                cur = [j]
+            if groupable:
+                cur, cur_path = [j], path
             else:
                 out.append([j])
         if cur:
@@ -206,9 +209,20 @@ def build_inputs(wl: Workload, pool_bytes: int, dev):
     per_type_ws = {pi: tw.workspace(M, p.K, p.N, device=dev) for pi, p in enumerate(cfg.projs)}
     ys = [per_type_y[c[1]] for c in wl.calls]
     wss = [per_type_ws[c[1]] for c in wl.calls]
+    groups = wl.groups()
+    # one workspace for the grouped two-kernel launches (they run one after
+    # another on the stream)
+    gws_bytes = 0
+    for grp in groups:
+        if len(grp) > 1:
+            items = [(xs[(0 if wl.layers > 1 else wl.calls[j][0], wl.calls[j][1])],
+                      gs[wl.calls[j]], pool[0][j], betas[j], ys[j]) for j in grp]
+            gws_bytes = max(gws_bytes, tw.bitlinear_grouped_workspace_bytes(
+                items, synth.DTYPES[cfg.dtype]))
+    gws = torch.empty(max(gws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    return {"xs": xs, "gs": gs, "pool": pool, "betas": betas, "ys": ys, "wss": wss,
-            "set_bytes": set_bytes, "copies": copies, "host": host, "groups": wl.groups()}
+    return {"xs": xs, "gs": gs, "pool": pool, "betas": betas, "ys": ys, "wss": wss, "gws": gws,
+            "set_bytes": set_bytes, "copies": copies, "host": host, "groups": groups}
 
 
 def step_fn(wl, inp, s, keep):
@@ -226,8 +240,13 @@ def step_fn(wl, inp, s, keep):
                 items.append((x, inp["gs"][call], pool[j], inp["betas"][j], inp["ys"][j]))
             arr = tw.make_calls(items)
             keep.append(arr)
-            tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
-                                         synth.DTYPES[wl.cfg.y_dtype])
+            call = wl.calls[grp[0]]
+            if tw.bitlinear_select_path(wl.M, wl.shape(call)[0]) == tw.BL_PATH_FUSED:
+                tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
+                                             synth.DTYPES[wl.cfg.y_dtype])
+            else:
+                tw.bitlinear_forward_grouped_ws(arr, synth.DTYPES[wl.cfg.dtype],
+                                                synth.DTYPES[wl.cfg.y_dtype], inp["gws"])
             continue
         j = grp[0]
         call = wl.calls[j]
@@ -298,6 +317,7 @@ def roofline(wl, inp, reps):
     nothing but contraction launches."""
     import torch
     import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
     # the dominant kernel: the path most of the step's calls take
     paths = [tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) for c in wl.calls]
     path = max(set(paths), key=paths.count)
@@ -317,21 +337,44 @@ def roofline(wl, inp, reps):
                 tw.bitlinear_act_quant(inp["xs"][xkey], inp["gs"][call], xq, sc, rs)
                 stage[xkey] = (xq, sc, rs)
 
-    def launch(r):
-        s, jj = divmod(r, ncalls)
-        j = sel[jj]
-        call = wl.calls[j]
-        K, N = wl.shape(call)
-        pk = inp["pool"][(s + 7) % inp["copies"]][j]
-        xkey = (0 if wl.layers > 1 else call[0], call[1])
-        if path == tw.BL_PATH_FUSED:
-            tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j], N,
-                                      inp["ys"][j], inp["wss"][j], path)
+    # the step's launch groups restricted to the dominant path: on the MFMA
+    # path grouped i/f/g calls are one grouped contraction launch, as in a step
+    units = []
+    for grp in inp["groups"]:
+        mine = [j for j in grp if j in sel]
+        if not mine:
+            continue
+        if len(mine) > 1 and path == tw.BL_PATH_MFMA:
+            units.append(mine)
         else:
-            xq, sc, rs = stage[xkey]
-            tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
+            units.extend([j] for j in mine)
+    nunits = len(units)
+    keep = []
 
-    total = reps * ncalls
+    def launch(r):
+        s, uu = divmod(r, nunits)
+        unit = units[uu]
+        items = []
+        for j in unit:
+            call = wl.calls[j]
+            K, N = wl.shape(call)
+            pk = inp["pool"][(s + 7) % inp["copies"]][j]
+            xkey = (0 if wl.layers > 1 else call[0], call[1])
+            if path == tw.BL_PATH_FUSED:
+                tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j],
+                                          N, inp["ys"][j], inp["wss"][j], path)
+            elif len(unit) == 1:
+                xq, sc, rs = stage[xkey]
+                tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
+            else:
+                xq, sc, rs = stage[xkey]
+                items.append((xq, sc, rs, pk, inp["betas"][j], inp["ys"][j]))
+        if items:
+            arr = tw.make_contract_calls(items)
+            keep.append(arr)
+            tw.bitlinear_contract_grouped(arr, synth.DTYPES[wl.cfg.y_dtype])
+
+    total = reps * nunits
     graphs = []
     r = 0
     while r < total:
@@ -370,7 +413,8 @@ def roofline(wl, inp, reps):
                "frac": round(ach / I8_PEAK_TOPS, 5)}
     out["traffic"] = None
     out["kernel"] = kernel
-    out["calls_timed"] = f"{len(sel)} of {len(wl.calls)} calls per step (those on this path)"
+    out["calls_timed"] = (f"{len(sel)} of {len(wl.calls)} calls per step (those on this path) in "
+                          f"{nunits} launches")
     out["launches"] = total
     out["avg_kernel_us"] = round(sec * 1e6 / total, 3)
     out["algorithmic_bytes_per_launch"] = round(byt / total, 1)
@@ -629,8 +673,9 @@ def main():
         "dtype": "i8", "data": "synthetic",
         "config": dict(wl.describe(), weight_pool_MiB=round(inp["set_bytes"] * inp["copies"] / 2**20, 1),
                        weight_copies=inp["copies"],
-                       launch=f"hipGraph; {len(inp['groups'])} launches per step "
-                              f"({'i/f/g grouped' if any(len(g) > 1 for g in inp['groups']) else 'one per projection'})",
+                       launch=f"hipGraph; {len(inp['groups'])} launch groups per step "
+                              f"({'i/f/g grouped' if any(len(g) > 1 for g in inp['groups']) else 'one per projection'}; "
+                              "two-kernel paths: act-quant + contraction per group)",
                        parallelism="single GPU"),
         "roofline": roof,
     }

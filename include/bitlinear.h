@@ -294,6 +294,29 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
                        const float *beta, int64_t N, void *y, int y_dtype,
                        int path, hipStream_t stream);
 
+/* One contraction of bitlinear_contract_grouped (device pointers as in
+ * bitlinear_contract). */
+typedef struct bl_contract_call {
+    const int8_t *xq;        /* [M, K]                                     */
+    const float *s;          /* [M]                                        */
+    const int32_t *rowsum;   /* [M]                                        */
+    const void *packed;      /* packed weights of an [N, K] matrix         */
+    const float *beta;       /* per-tensor weight scale                    */
+    void *y;                 /* [M, N], dtype y_dtype (written)            */
+    int64_t M, K, N;
+} bl_contract_call;
+
+/* bitlinear_contract on the MFMA kernel for several independent calls, with
+ * up to three consecutive calls of one shape (M, K, N) in one launch (the
+ * stage-level counterpart of bitlinear_forward_grouped_ws's runs).  Each
+ * call's y equals bitlinear_contract(..., BL_PATH_MFMA) bit for bit.
+ *   calls   HOST array of ncalls descriptors; shapes, pointers and alignment
+ *           as for bitlinear_contract; calls with M == 0 are skipped.
+ * 0 <= ncalls <= 4096; any invalid call rejects the group before anything
+ * is launched. */
+int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
+                               hipStream_t stream);
+
 /* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device). */
 int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
                              int8_t *Wq, hipStream_t stream);

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     BL_PATH_SKINNY, CODE_DTYPE, DTYPE_CODE, BitLinearError, lib,
     bitlinear_act_quant, bitlinear_contract, bitlinear_forward, bitlinear_forward_grouped,
     bitlinear_forward_grouped_ws, bitlinear_grouped_workspace_bytes,
+    bitlinear_contract_grouped, make_contract_calls,
     bitlinear_forward_glu, bitlinear_forward_path, bitlinear_pack_glu_weights, make_calls,
     bitlinear_gemm_i32, bitlinear_pack_weights, bitlinear_pack_workspace_bytes,
     bitlinear_packed_bytes, bitlinear_select_path, bitlinear_status_string, bitlinear_unpack_weights,

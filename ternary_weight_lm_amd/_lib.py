@@ -39,6 +39,13 @@ _lib = None
 P = ctypes.c_void_p
 
 
+class BlContractCall(ctypes.Structure):
+    """struct bl_contract_call of bitlinear.h"""
+    _fields_ = [("xq", ctypes.c_void_p), ("s", ctypes.c_void_p), ("rowsum", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
+
+
 class BlCall(ctypes.Structure):
     """struct bl_call of bitlinear.h"""
     _fields_ = [("x", ctypes.c_void_p), ("gain", ctypes.c_void_p),
@@ -63,6 +70,7 @@ SIGNATURES = {
     "bitlinear_status_string": ([I], ctypes.c_char_p),
     "bitlinear_select_path": ([I64, I64], I),
     "bitlinear_grouped_workspace_bytes": ([P, I, I], SZ),
+    "bitlinear_contract_grouped": ([P, I, I, P], I),
     "bitlinear_forward_grouped_ws": ([P, I, I, I, F, P, SZ, P], I),
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
@@ -234,6 +242,25 @@ def bitlinear_contract(xq, s, rowsum, packed, beta, N, y, path=BL_PATH_AUTO, str
     _check("bitlinear_contract", lib().bitlinear_contract(
         _ptr(xq), _ptr(s), _ptr(rowsum), M, K, _ptr(packed), _ptr(beta), N, _ptr(y),
         DTYPE_CODE[y.dtype], path, _stream(stream)))
+
+
+def make_contract_calls(items):
+    """ctypes array of bl_contract_call from (xq, s, rowsum, packed, beta, y)
+    tensor tuples."""
+    arr = (BlContractCall * len(items))()
+    for i, (xq, s, rowsum, packed, beta, y) in enumerate(items):
+        M, K = xq.shape
+        arr[i] = BlContractCall(_ptr(xq), _ptr(s), _ptr(rowsum), _ptr(packed), _ptr(beta),
+                                _ptr(y), M, K, y.shape[1])
+    return arr
+
+
+def bitlinear_contract_grouped(calls, y_dtype, stream=None):
+    """calls: a make_contract_calls() array or a list of tuples for it."""
+    if not isinstance(calls, ctypes.Array):
+        calls = make_contract_calls(calls)
+    _check("bitlinear_contract_grouped", lib().bitlinear_contract_grouped(
+        ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[y_dtype], _stream(stream)))
 
 
 def bitlinear_unpack_weights(packed, N, K, Wq, stream=None):

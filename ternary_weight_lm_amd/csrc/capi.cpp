@@ -470,6 +470,47 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
                                          stream));
 }
 
+int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
+                               hipStream_t stream) {
+  if (!dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (ncalls < 0 || ncalls > 4096) return BL_ERR_SHAPE;
+  if (ncalls == 0) return BL_OK;
+  if (!calls) return BL_ERR_NULL;
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_contract_call &c = calls[i];
+    if (!nk_ok(c.N, c.K) || !m_ok(c.M)) return BL_ERR_SHAPE;
+    if (c.M == 0) continue;
+    if (!c.xq || !c.s || !c.rowsum || !c.packed || !c.beta || !c.y) return BL_ERR_NULL;
+    if (!aligned16(c.xq) || !aligned16(c.packed) || !aligned16(c.y) ||
+        (reinterpret_cast<uintptr_t>(c.s) & 3u) || (reinterpret_cast<uintptr_t>(c.rowsum) & 3u) ||
+        (reinterpret_cast<uintptr_t>(c.beta) & 3u))
+      return BL_ERR_ALIGN;
+  }
+  for (int i = 0; i < ncalls;) {
+    const bl_contract_call &c0 = calls[i];
+    if (c0.M == 0) {
+      ++i;
+      continue;
+    }
+    int n = 1;
+    while (n < bl::kGroupCalls && i + n < ncalls && calls[i + n].M == c0.M &&
+           calls[i + n].K == c0.K && calls[i + n].N == c0.N)
+      ++n;
+    bl::GemmCalls gm{};
+    for (int j = 0; j < n; ++j) {
+      const bl_contract_call &c = calls[i + j];
+      gm.c[j] = bl::GemmCall{c.xq, c.rowsum, c.s, c.packed, c.beta, c.y};
+    }
+    const hipError_t e =
+        n == 1 ? bl::launch_gemm_mfma(c0.xq, c0.rowsum, c0.s, c0.packed, c0.beta, c0.M, c0.N,
+                                      c0.K, c0.y, y_dtype, false, stream)
+               : bl::launch_gemm_mfma_group(gm, n, c0.M, c0.N, c0.K, y_dtype, stream);
+    if (e != hipSuccess) return BL_ERR_HIP;
+    i += n;
+  }
+  return BL_OK;
+}
+
 int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
                              int8_t *Wq, hipStream_t stream) {
   if (!nk_ok(N, K)) return BL_ERR_SHAPE;

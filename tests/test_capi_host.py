@@ -245,6 +245,27 @@ def test_grouped_ws_plan_and_validation():
     assert grp([BlCall(None, None, None, None, None, 0, 1024, 1024)] * 3, ws=None, ws_bytes=0) == OK
 
 
+def test_contract_grouped_validation():
+    from ternary_weight_lm_amd._lib import BlContractCall
+    L = tw.lib()
+
+    def grp(calls, ydt=2, n=None):
+        arr = (BlContractCall * max(1, len(calls)))(*calls)
+        return L.bitlinear_contract_grouped(ctypes.cast(arr, ctypes.c_void_p),
+                                            len(calls) if n is None else n, ydt, None)
+    good = BlContractCall(A, B, C, D, E, Y, 4096, 2048, 2048)
+    assert grp([good], ydt=9) == DTYPE
+    assert grp([good], n=-1) == SHAPE
+    assert grp([good], n=5000) == SHAPE
+    assert L.bitlinear_contract_grouped(None, 2, 2, None) == NULL
+    assert L.bitlinear_contract_grouped(None, 0, 2, None) == OK
+    assert grp([good, BlContractCall(A, B, C, D, E, Y, 4096, 2000, 2048)]) == SHAPE
+    assert grp([good, BlContractCall(A, None, C, D, E, Y, 4096, 2048, 2048)]) == NULL
+    assert grp([good, BlContractCall(A + 4, B, C, D, E, Y, 4096, 2048, 2048)]) == ALIGN
+    assert grp([good, BlContractCall(A, B + 2, C, D, E, Y, 4096, 2048, 2048)]) == ALIGN
+    assert grp([BlContractCall(None, None, None, None, None, None, 0, 2048, 2048)] * 3) == OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.float16)

@@ -223,6 +223,29 @@ def test_grouped_ws_matches_single_calls(case):
         assert torch.equal(y, ref)
 
 
+def test_contract_grouped_matches_single_calls():
+    """bitlinear_contract_grouped (runs of up to three same-shape calls per
+    MFMA launch) gives bitlinear_contract(..., BL_PATH_MFMA) bit for bit."""
+    say("contract_grouped")
+    shapes = [(300, 384, 640)] * 4 + [(40, 96, 256), (300, 384, 640), (0, 64, 256)]
+    items, singles = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        xq = (torch.from_numpy(_random_codes(M, K, 70 + i)) if M else
+              torch.empty((0, K), dtype=torch.int8)).to(DEV)
+        rs = xq.to(torch.int32).sum(1, dtype=torch.int32)
+        sc = (torch.rand(M, device=DEV) * 30 + 0.5).to(torch.float32)
+        packed, beta = tw.pack(synth.make_w(970 + i, 0, 0, N, K).to(DEV))
+        y = torch.full((M, N), 7.0, dtype=torch.float16, device=DEV)
+        ref = torch.empty_like(y)
+        tw.bitlinear_contract(xq, sc, rs, packed, beta, N, ref, path=tw.BL_PATH_MFMA)
+        items.append((xq, sc, rs, packed, beta, y))
+        singles.append(ref)
+    tw.bitlinear_contract_grouped(items, torch.float16)
+    torch.cuda.synchronize()
+    for it, ref in zip(items, singles):
+        assert torch.equal(it[5], ref)
+
+
 def test_paths_agree_bitwise_mid_m():
     say("paths agree mid M")
     for M in (24, 40, 64):
