@@ -356,24 +356,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
 }
 
 // ---------------------------------------------------------------- row mode
-// 2 <= M <= 4 * RPW tokens, K <= 4096: wave w normalizes and quantizes rows
-// w, w + 4, ... by itself (the shared float-mode row passes of rowquant.h,
-// bit-identical to the act-quant kernel), so no row reduction crosses a
-// wave and one barrier (the codes in LDS) suffices.  Loads go out x rows ->
-// gain (once per wave) -> weights; every argument is preloaded.
-// TPW: weight tiles per wave, equal to the chunks per lane of a row (both
-// cover 512 elements of K each); K <= 512 * TPW.
-template <int DT, int OUT, int RPW, bool GLU, int TPW>
-__global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint32_t shape,
-                                                             float eps, const uint4 *packed,
-                                                             const void *gain, const float *bp,
-                                                             void *out) {
+// 2 <= M <= NW tokens, K <= 4096: wave w normalizes and quantizes row w by
+// itself (the shared float-mode row passes of rowquant.h, bit-identical to
+// the act-quant kernel), so no row reduction crosses a wave and one barrier
+// (the codes in LDS) suffices; then the NW waves (4 or 8) share the tile
+// column's contraction.  Loads go out x row -> gain -> weights; every
+// argument is preloaded.  KC: K capacity 1024 KC; a lane caches 2 KC chunks
+// of its row.
+template <int DT, int OUT, bool GLU, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void *x, uint32_t shape,
+                                                                      float eps,
+                                                                      const uint4 *packed,
+                                                                      const void *gain,
+                                                                      const float *bp, void *out) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
-  __shared__ int red[4][8][64];
+  __shared__ int red[NW][8][64];
   __shared__ float f_row[16];
   __shared__ int rs_row[16];
 
   constexpr int EB = dtype_bytes(DT);
+  constexpr int RC = 2 * KC;                    // chunks of 512 elements per row
+  constexpr int TPW = (8 * KC + NW - 1) / NW;   // weight tiles per wave
   const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 31;
   const int tiles = (int)(shape >> 12);
   const int nt = (int)blockIdx.x;
@@ -382,51 +385,44 @@ __global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint
   const int KB = K >> 7;
   const int lds_stride = K + 16;
 
-  // ---- 1. loads: this wave's rows, the gain, then the weight tiles
+  // ---- 1. loads: this wave's row, the gain, then the weight tiles
   const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
-  Chunk8<DT> xraw[RPW][TPW];
+  Chunk8<DT> xraw[RC];
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int m = w + 4 * j;
-#pragma unroll
-    for (int c = 0; c < TPW; ++c) {
-      const int k = 8 * lane + 512 * c;
-      xraw[j][c] = bload_chunk<DT>(xr, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
-    }
+  for (int c = 0; c < RC; ++c) {
+    const int k = 8 * lane + 512 * c;
+    xraw[c] = bload_chunk<DT>(xr, w < M && k < K ? (uint32_t)((w * K + k) * EB) : kOob);
   }
   __builtin_amdgcn_sched_barrier(0);
   const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
-  Chunk8<DT> graw[TPW];
+  Chunk8<DT> graw[RC];
 #pragma unroll
-  for (int c = 0; c < TPW; ++c) graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
+  for (int c = 0; c < RC; ++c) graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
   __builtin_amdgcn_sched_barrier(0);
   const rsrc_t wr = make_rsrc(packed + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
   v4i wt[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) wt[t] = bload(wr, (uint32_t)((w + 4 * t) * 1024 + lane * 16));
+  for (int t = 0; t < TPW; ++t) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
   __builtin_amdgcn_sched_barrier(0);
   const float beta = *bp;
 
-  // ---- 2. the wave's rows: codes into LDS, scale factor and row sum
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int m = w + 4 * j;
-    if (m >= M) break;
-    int8_t *dst = xs + m * lds_stride;
+  // ---- 2. the wave's row: codes into LDS, scale factor and row sum
+  if (w < M) {
+    int8_t *dst = xs + w * lds_stride;
     float sc;
     int rs;
-    quantize_loaded<DT, TPW>(xraw[j], graw, K, eps,
-                        [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
-                        sc, rs);
+    quantize_loaded<DT, RC>(xraw, graw, K, eps,
+                            [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
+                            sc, rs);
     if (lane == 0) {
-      f_row[m] = div_rn(beta, sc);
-      rs_row[m] = rs;
+      f_row[w] = div_rn(beta, sc);
+      rs_row[w] = rs;
     }
   }
   __syncthreads();
 
-  // ---- 3. contraction: tiles kb = w + 4t, rows 0..15 as one MFMA block
-  const int nmine = w < KB ? (KB - w + 3) >> 2 : 0;
+  // ---- 3. contraction: tiles kb = w + NW t, rows 0..15 as one MFMA block
+  const int nmine = w < KB ? (KB - w + NW - 1) / NW : 0;
   const int arow = lane & 15;
   const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
   v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -441,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint
       for (int s2 = 0; s2 < 2; ++s2) {
         a[j][s2] = v4i{0, 0, 0, 0};
         if (t0 + j < TPW && arow < M && t0 + j < nmine)
-          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + 4 * (t0 + j)) * 128 + 16 * s2);
+          a[j][s2] = *reinterpret_cast<const v4i *>(abase + (w + NW * (t0 + j)) * 128 + 16 * s2);
       }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -463,51 +459,62 @@ __global__ __launch_bounds__(256, 2) void decode_rows_kernel(const void *x, uint
     red[w][4 + i][lane] = acc1[0][i] + acc1[1][i];
   }
   __syncthreads();
+  const auto wsum = [&](int j, int L) {
+    int v = red[0][j][L];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v += red[i][j][L];
+    return v;
+  };
   if constexpr (GLU) {
     const int m = tid >> 4, c = tid & 15;  // 16 rows x 16 outputs
     if (m < M) {
       const int Lq = 16 * (m >> 2) + c, jg = m & 3, ju = jg + 4;
-      const int vg = red[0][jg][Lq] + red[1][jg][Lq] + red[2][jg][Lq] + red[3][jg][Lq] - rs_row[m];
-      const int vu = red[0][ju][Lq] + red[1][ju][Lq] + red[2][ju][Lq] + red[3][ju][Lq] - rs_row[m];
+      const int vg = wsum(jg, Lq) - rs_row[m];
+      const int vu = wsum(ju, Lq) - rs_row[m];
       store1<OUT>(out, (int64_t)m * tiles * 16 + nt * 16 + c,
                   silu((float)vg * f_row[m]) * ((float)vu * f_row[m]));
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q;
+    for (int q = 0; q < 512 / (64 * NW); ++q) {
+      const int idx = tid + 64 * NW * q;
       const int j = idx >> 6, Lq = idx & 63;
       const int h = j >> 2, i = j & 3;
       const int m = 4 * (Lq >> 4) + i;
       if (m >= M) continue;
-      const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
+      const int v = wsum(j, Lq) - rs_row[m];
       store1<OUT>(out, (int64_t)m * tiles * 32 + nt * 32 + 16 * h + (Lq & 15), (float)v * f_row[m]);
     }
   }
 }
 
-template <int DT, int OUT, bool GLU, int TPW>
+// Waves per workgroup in the row mode: one per row up to 4 rows and K up to
+// 1024, else 8 (5..8 rows need 8; longer rows gain from splitting the
+// contraction 8 ways, as in the split mode).
+constexpr int dec_rows_nw(int64_t M, int64_t K) { return M <= 4 && K <= 1024 ? 4 : 8; }
+
+template <int DT, int OUT, bool GLU, int KC>
 static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
   const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
   const uint4 *pk = reinterpret_cast<const uint4 *>(a.packed[0]);
-  if (a.M <= 4)
-    decode_rows_kernel<DT, OUT, 1, GLU, TPW><<<tiles, 256, lds, stream>>>(
+  if (dec_rows_nw(a.M, a.K) == 4)
+    decode_rows_kernel<DT, OUT, GLU, KC, 4><<<tiles, 256, lds, stream>>>(
         a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
   else
-    decode_rows_kernel<DT, OUT, DT == BL_F32 ? 1 : 2, GLU, TPW><<<tiles, 256, lds, stream>>>(
+    decode_rows_kernel<DT, OUT, GLU, KC, 8><<<tiles, 512, lds, stream>>>(
         a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
 }
 
-// row mode: K <= 4096 (decode_rows_fits); tiles per wave = 2 KC <= 8
+// row mode: K <= 4096 (decode_rows_fits)
 template <int DT, int OUT, bool GLU>
 static void launch_rows(const DecodeArgs &a, hipStream_t stream) {
   switch (dec_kc(a.K)) {
-    case 1: launch_rows_t<DT, OUT, GLU, 2>(a, stream); break;
-    case 2: launch_rows_t<DT, OUT, GLU, 4>(a, stream); break;
-    case 3: launch_rows_t<DT, OUT, GLU, 6>(a, stream); break;
-    default: launch_rows_t<DT, OUT, GLU, 8>(a, stream); break;
+    case 1: launch_rows_t<DT, OUT, GLU, 1>(a, stream); break;
+    case 2: launch_rows_t<DT, OUT, GLU, 2>(a, stream); break;
+    case 3: launch_rows_t<DT, OUT, GLU, 3>(a, stream); break;
+    default: launch_rows_t<DT, OUT, GLU, 4>(a, stream); break;
   }
 }
 
