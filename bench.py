@@ -337,14 +337,15 @@ def roofline(wl, inp, reps):
                 tw.bitlinear_act_quant(inp["xs"][xkey], inp["gs"][call], xq, sc, rs)
                 stage[xkey] = (xq, sc, rs)
 
-    # the step's launch groups restricted to the dominant path: on the MFMA
-    # path grouped i/f/g calls are one grouped contraction launch, as in a step
+    # the step's launch groups restricted to the dominant path: grouped i/f/g
+    # calls are one grouped launch (decode kernel, resp. contraction), as in
+    # a step
     units = []
     for grp in inp["groups"]:
         mine = [j for j in grp if j in sel]
         if not mine:
             continue
-        if len(mine) > 1 and path == tw.BL_PATH_MFMA:
+        if len(mine) > 1 and path in (tw.BL_PATH_MFMA, tw.BL_PATH_FUSED):
             units.append(mine)
         else:
             units.extend([j] for j in mine)
@@ -360,16 +361,23 @@ def roofline(wl, inp, reps):
             K, N = wl.shape(call)
             pk = inp["pool"][(s + 7) % inp["copies"]][j]
             xkey = (0 if wl.layers > 1 else call[0], call[1])
-            if path == tw.BL_PATH_FUSED:
+            if path == tw.BL_PATH_FUSED and len(unit) == 1:
                 tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j],
                                           N, inp["ys"][j], inp["wss"][j], path)
+            elif path == tw.BL_PATH_FUSED:
+                items.append((inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j], inp["ys"][j]))
             elif len(unit) == 1:
                 xq, sc, rs = stage[xkey]
                 tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
             else:
                 xq, sc, rs = stage[xkey]
                 items.append((xq, sc, rs, pk, inp["betas"][j], inp["ys"][j]))
-        if items:
+        if items and path == tw.BL_PATH_FUSED:
+            arr = tw.make_calls(items)
+            keep.append(arr)
+            tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
+                                         synth.DTYPES[wl.cfg.y_dtype])
+        elif items:
             arr = tw.make_contract_calls(items)
             keep.append(arr)
             tw.bitlinear_contract_grouped(arr, synth.DTYPES[wl.cfg.y_dtype])

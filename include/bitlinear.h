@@ -181,11 +181,11 @@ typedef struct bl_call {
 /* Several independent FusedBitLinear forwards in few launches, for decode
  * steps where each call is too small to fill the GPU on its own -- e.g. the
  * i/f/g/o projections of an HGRNBit block (hysenlabs ja review, section
- * "HGRNBit という層構成を読む").  Consecutive calls of one shape with
- * M <= 4 and K <= 8192 (fp32 x: M == 1) go out up to three per launch of
- * the decode kernel, calls with M <= 8 and K <= 4096 one per launch of its
- * row mode, and the remaining calls up to 16 per launch of the skinny
- * kernel.
+ * "HGRNBit という層構成を読む").  Consecutive calls of one shape that the
+ * decode kernel takes (2 <= M <= 8 and K <= 4096 in its row mode, else
+ * M <= 4 and K <= 8192 in its split mode; fp32 x: M <= 4, resp. M == 1) go
+ * out up to three per launch, the remaining calls up to 16 per launch of
+ * the skinny kernel.
  *   calls   HOST array of ncalls descriptors (read during the call only)
  *   Every call must satisfy the BL_PATH_FUSED limits (M <= 16, K <= 8192,
  *   M * (K + 16) <= 56320) and the usual shape / alignment rules, and all

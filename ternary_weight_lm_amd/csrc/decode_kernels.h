@@ -363,12 +363,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
 // column's contraction.  Loads go out x row -> gain -> weights; every
 // argument is preloaded.  KC: K capacity 1024 KC; a lane caches 2 KC chunks
 // of its row.
-template <int DT, int OUT, bool GLU, int KC, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void *x, uint32_t shape,
-                                                                      float eps,
-                                                                      const uint4 *packed,
-                                                                      const void *gain,
-                                                                      const float *bp, void *out) {
+// GAIN_LATE (three-call kernel): the gain pointer comes from the argument
+// buffer, so the weights are issued before waiting for it.
+template <int DT, int OUT, bool GLU, int KC, int NW, bool GAIN_LATE>
+__device__ __forceinline__ void decode_rows_body(
+    const void *x, uint32_t shape, float eps, int nt, int call, const uint4 *p0, const uint4 *p1,
+    const uint4 *p2, const void *g0, const void *g1, const void *g2, const float *b0,
+    const float *b1, const float *b2, void *o0, void *o1, void *o2) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
   __shared__ int red[NW][8][64];
   __shared__ float f_row[16];
@@ -379,7 +380,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void
   constexpr int TPW = (8 * KC + NW - 1) / NW;   // weight tiles per wave
   const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 31;
   const int tiles = (int)(shape >> 12);
-  const int nt = (int)blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 7;
@@ -394,16 +394,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void
     xraw[c] = bload_chunk<DT>(xr, w < M && k < K ? (uint32_t)((w * K + k) * EB) : kOob);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
-  Chunk8<DT> graw[RC];
-#pragma unroll
-  for (int c = 0; c < RC; ++c) graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
-  __builtin_amdgcn_sched_barrier(0);
+  const uint4 *packed = call == 0 ? p0 : (call == 1 ? p1 : p2);
   const rsrc_t wr = make_rsrc(packed + (int64_t)nt * KB * 64, (uint32_t)KB * 1024u);
+  const void *gain = call == 0 ? g0 : (call == 1 ? g1 : g2);
+  Chunk8<DT> graw[RC];
   v4i wt[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
+  for (int t = 0; t < TPW; ++t)
+    if constexpr (GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
   __builtin_amdgcn_sched_barrier(0);
+  {
+    const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
+#pragma unroll
+    for (int c = 0; c < RC; ++c)
+      graw[c] = bload_chunk<DT>(gr, (uint32_t)((8 * lane + 512 * c) * EB));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    if constexpr (!GAIN_LATE) wt[t] = bload(wr, (uint32_t)((w + NW * t) * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  const float *bp = call == 0 ? b0 : (call == 1 ? b1 : b2);
+  void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
   const float beta = *bp;
 
   // ---- 2. the wave's row: codes into LDS, scale factor and row sum
@@ -488,6 +500,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void
   }
 }
 
+template <int DT, int OUT, bool GLU, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void *x, uint32_t shape,
+                                                                      float eps,
+                                                                      const uint4 *packed,
+                                                                      const void *gain,
+                                                                      const float *bp, void *out) {
+  decode_rows_body<DT, OUT, GLU, KC, NW, false>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
+                                                packed, gain, gain, gain, bp, bp, bp, out, out,
+                                                out);
+}
+
+// Up to three row-mode calls of one shape; workgroup b works on call
+// b / tiles.  The activation and weight pointers are preloaded, the rest is
+// fetched.
+template <int DT, int OUT, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
+    const void *x0, const void *x1, const void *x2, uint32_t shape, float eps, const uint4 *p0,
+    const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
+    const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
+  const int tiles = (int)(shape >> 12);
+  const int bid = (int)blockIdx.x;
+  const int call = (bid >= tiles) + (bid >= 2 * tiles);
+  const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
+  decode_rows_body<DT, OUT, false, KC, NW, true>(x, shape, eps, bid - call * tiles, call, p0, p1,
+                                                 p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
+}
+
 // Waves per workgroup in the row mode: one per row up to 4 rows and K up to
 // 1024, else 8 (5..8 rows need 8; longer rows gain from splitting the
 // contraction 8 ways, as in the split mode).
@@ -499,6 +538,18 @@ static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
   const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
   const uint4 *pk = reinterpret_cast<const uint4 *>(a.packed[0]);
+  if (a.ncalls > 1) {
+    const uint4 *p[3];
+    for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
+    const unsigned grid = tiles * (unsigned)a.ncalls;
+#define BL_ROWS3(NW_)                                                                          \
+  decode_rows3_kernel<DT, OUT, KC, NW_><<<grid, 64 * NW_, lds, stream>>>(                       \
+      a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2], \
+      a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2])
+    if (dec_rows_nw(a.M, a.K) == 4) BL_ROWS3(4); else BL_ROWS3(8);
+#undef BL_ROWS3
+    return;
+  }
   if (dec_rows_nw(a.M, a.K) == 4)
     decode_rows_kernel<DT, OUT, GLU, KC, 4><<<tiles, 256, lds, stream>>>(
         a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
@@ -562,9 +613,11 @@ static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
   }
 }
 
+// Row mode whenever it fits (one call, or up to three of one shape without
+// the GLU epilogue), else split mode.
 template <int DT>
 static void launch_decode_dt(const DecodeArgs &a, hipStream_t stream) {
-  if (a.ncalls == 1 && decode_rows_fits(a.M, a.K, a.x_dtype)) {
+  if (decode_rows_fits(a.M, a.K, a.x_dtype) && (a.ncalls == 1 || !a.glu)) {
 #define BL_ROWS(O)                                                   \
   (a.glu ? launch_rows<DT, O, true>(a, stream) : launch_rows<DT, O, false>(a, stream))
     switch (a.out_kind) {

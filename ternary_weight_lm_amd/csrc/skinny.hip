@@ -373,15 +373,14 @@ hipError_t launch_skinny_grouped(const SkinnyArgs *calls, int ncalls, hipStream_
       continue;
     }
     DecodeArgs d = decode_args(a);
-    if (!decode_split_fits(a.M, a.K, a.x_dtype)) {
-      decode_add(d, calls[i++]);  // row mode: one call per launch
-    } else {
-      const auto same = [&](const SkinnyArgs &c) {
-        return c.fused && decode_split_fits(c.M, c.K, c.x_dtype) && c.M == a.M && c.K == a.K &&
-               c.N == a.N;
-      };
-      while (i < ncalls && d.ncalls < kDecodeCalls && same(calls[i])) decode_add(d, calls[i++]);
-    }
+    // up to kDecodeCalls consecutive calls of one shape per launch (row mode
+    // or split mode alike: the shape decides the mode)
+    const auto same = [&](const SkinnyArgs &c) {
+      return c.fused && !c.glu && !a.glu && decode_ok(c) && c.M == a.M && c.K == a.K &&
+             c.N == a.N;
+    };
+    decode_add(d, calls[i++]);
+    while (i < ncalls && d.ncalls < kDecodeCalls && same(calls[i])) decode_add(d, calls[i++]);
     const hipError_t e = launch_decode(d, stream);
     if (e != hipSuccess) return e;
   }
