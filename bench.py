@@ -138,17 +138,16 @@ class Workload:
     def groups(self):
         """Launch groups of a step.  HGRNBit's i/f/g projections of one layer
         read the same block input, so when they take the fused decode path
-        they go out as one grouped decode launch, and on the MFMA path as one
-        grouped act-quant launch plus one grouped GEMM launch
-        (bitlinear_forward_grouped_ws); every other projection (o_proj after
-        the recurrence, the MLP pair, the skinny path) is launched on its own."""
+        they go out as one grouped decode launch; on the two-kernel paths they
+        share one act-quant launch (and on the MFMA path one GEMM launch:
+        bitlinear_forward_grouped_ws); every other projection (o_proj after
+        the recurrence, the MLP pair) is launched on its own."""
         import ternary_weight_lm_amd as tw
         out, cur, cur_path = [], [], None
         for j, (layer, pi) in enumerate(self.calls):
             name = self.cfg.projs[pi].name
             path = tw.bitlinear_select_path(self.M, self.cfg.projs[pi].K)
-            groupable = path in (tw.BL_PATH_FUSED, tw.BL_PATH_MFMA) and name in (
-                "i_proj", "f_proj", "g_proj")
+            groupable = name in ("i_proj", "f_proj", "g_proj")
             if groupable and cur and self.calls[cur[0]][0] == layer and path == cur_path:
                 cur.append(j)
                 continue

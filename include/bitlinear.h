@@ -201,11 +201,12 @@ int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
  * default path sends to the one-launch kernels (bitlinear_select_path ==
  * BL_PATH_FUSED for that call's M, K and x_dtype) go out as in
  * bitlinear_forward_grouped.  Every other call runs its two-kernel path, and
- * up to three consecutive calls of one shape (M, K, N) on the MFMA path --
- * HGRNBit's i/f/g projections at prefill, which read the same block input
- * (hysenlabs ja review, section "HGRNBit という層構成を読む") -- share one
- * act-quant launch and one MFMA launch: three 2048-wide projections of 4096
- * tokens fill the GPU for several rounds instead of one each.
+ * up to three consecutive calls of one shape (M, K, N) on the same path --
+ * HGRNBit's i/f/g projections, which read the same block input (hysenlabs
+ * ja review, section "HGRNBit という層構成を読む") -- share one act-quant
+ * launch; on the MFMA path also one GEMM launch (three 2048-wide
+ * projections of 4096 tokens fill the GPU for several rounds instead of one
+ * each), on the skinny path (M <= 64) each keeps its contraction launch.
  *   calls    HOST array of ncalls descriptors (read during the call only);
  *            shapes, pointers and alignment as for bitlinear_forward, all
  *            sharing x_dtype, y_dtype and eps; calls with M == 0 skipped.

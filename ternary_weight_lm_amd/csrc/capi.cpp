@@ -277,9 +277,10 @@ namespace {
 // The plan of bitlinear_forward_grouped_ws: calls the fused kernels take
 // (default path FUSED) go out together as in bitlinear_forward_grouped;
 // every other call runs its two-kernel path, and up to kGroupCalls
-// consecutive MFMA-path calls of one shape (M, K, N) form one run that
-// shares an act-quant launch and a GEMM launch.  Runs execute one after
-// another on the stream, so they share the workspace.
+// consecutive calls of one shape (M, K, N) and path form one run that shares
+// an act-quant launch (and, on the MFMA path, a GEMM launch; skinny-path
+// calls keep one contraction launch each).  Runs execute one after another
+// on the stream, so they share the workspace.
 struct GroupRun {
   int first, n, path;
 };
@@ -299,10 +300,10 @@ int plan_grouped(const bl_call *calls, int ncalls, int x_dtype, std::vector<Grou
       fused.push_back(i);
       continue;
     }
-    if (path == BL_PATH_MFMA && !runs.empty()) {
+    if (!runs.empty()) {
       GroupRun &r = runs.back();
       const bl_call &p = calls[r.first];
-      if (r.path == BL_PATH_MFMA && r.first + r.n == i && r.n < bl::kGroupCalls && p.M == c.M &&
+      if (r.path == path && r.first + r.n == i && r.n < bl::kGroupCalls && p.M == c.M &&
           p.K == c.K && p.N == c.N) {
         ++r.n;
         ws_need = std::max(ws_need, (size_t)r.n * fwd_ws_bytes(c.M, c.K));
@@ -366,8 +367,26 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
     }
     if (bl::launch_act_quant_group(aq, r.n, x_dtype, c0.M, c0.K, eps, stream) != hipSuccess)
       return BL_ERR_HIP;
-    if (bl::launch_gemm_mfma_group(gm, r.n, c0.M, c0.N, c0.K, y_dtype, stream) != hipSuccess)
-      return BL_ERR_HIP;
+    if (r.path == BL_PATH_MFMA) {
+      if (bl::launch_gemm_mfma_group(gm, r.n, c0.M, c0.N, c0.K, y_dtype, stream) != hipSuccess)
+        return BL_ERR_HIP;
+      continue;
+    }
+    for (int j = 0; j < r.n; ++j) {
+      bl::SkinnyArgs a{};
+      a.fused = false;
+      a.xq = gm.c[j].xq;
+      a.s = gm.c[j].s;
+      a.rowsum = gm.c[j].rowsum;
+      a.packed = gm.c[j].packed;
+      a.beta = gm.c[j].beta;
+      a.M = c0.M;
+      a.N = c0.N;
+      a.K = c0.K;
+      a.out = gm.c[j].out;
+      a.out_kind = y_dtype;
+      if (bl::launch_skinny(a, stream) != hipSuccess) return BL_ERR_HIP;
+    }
   }
   if (!fused.empty()) {
     std::vector<bl::SkinnyArgs> args;

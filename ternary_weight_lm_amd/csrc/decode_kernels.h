@@ -527,10 +527,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
                                                  p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
 }
 
-// Waves per workgroup in the row mode: one per row up to 4 rows and K up to
-// 1024, else 8 (5..8 rows need 8; longer rows gain from splitting the
-// contraction 8 ways, as in the split mode).
-constexpr int dec_rows_nw(int64_t M, int64_t K) { return M <= 4 && K <= 1024 ? 4 : 8; }
+// Waves per workgroup in the row mode: 8 (one per row; the contraction is
+// split 8 ways -- measured faster than 4 waves from 2 rows and K = 1024 up).
+constexpr int kRowsNW = 8;
 
 template <int DT, int OUT, bool GLU, int KC>
 static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
@@ -542,20 +541,13 @@ static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
     const uint4 *p[3];
     for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
     const unsigned grid = tiles * (unsigned)a.ncalls;
-#define BL_ROWS3(NW_)                                                                          \
-  decode_rows3_kernel<DT, OUT, KC, NW_><<<grid, 64 * NW_, lds, stream>>>(                       \
-      a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2], \
-      a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2])
-    if (dec_rows_nw(a.M, a.K) == 4) BL_ROWS3(4); else BL_ROWS3(8);
-#undef BL_ROWS3
+    decode_rows3_kernel<DT, OUT, KC, kRowsNW><<<grid, 64 * kRowsNW, lds, stream>>>(
+        a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2],
+        a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
     return;
   }
-  if (dec_rows_nw(a.M, a.K) == 4)
-    decode_rows_kernel<DT, OUT, GLU, KC, 4><<<tiles, 256, lds, stream>>>(
-        a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
-  else
-    decode_rows_kernel<DT, OUT, GLU, KC, 8><<<tiles, 512, lds, stream>>>(
-        a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
+  decode_rows_kernel<DT, OUT, GLU, KC, kRowsNW><<<tiles, 64 * kRowsNW, lds, stream>>>(
+      a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
 }
 
 // row mode: K <= 4096 (decode_rows_fits)

@@ -227,6 +227,8 @@ def test_grouped_ws_plan_and_validation():
     assert need([big, big, big, big]) == 3 * wsb(4096, 2048, 2048)   # runs of at most 3
     assert need([big, other, big]) == max(wsb(4096, 2048, 2048), wsb(4096, 2048, 11264))
     assert need([sk, dec]) == wsb(20, 512, 160)              # skinny path: its own workspace
+    assert need([sk, sk, sk]) == 3 * wsb(20, 512, 160)      # skinny run: one act-quant launch
+    assert need([sk, big]) == wsb(4096, 2048, 2048)
     assert need([big, BlCall(A, B, C, D, Y, 4096, 1000, 2048)]) == 0   # invalid group
     assert need([big], xdt=7) == 0
     assert grp([big], xdt=9) == DTYPE

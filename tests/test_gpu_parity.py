@@ -204,7 +204,7 @@ def test_grouped_ws_matches_single_calls(case):
     if case == "mixed":
         shapes = [(300, 384, 640)] * 4 + [(100, 96, 256), (20, 160, 512), (1, 64, 1024),
                                           (3, 96, 384), (0, 64, 256), (65, 160, 1280),
-                                          (65, 160, 1280)]
+                                          (65, 160, 1280)] + [(40, 96, 512)] * 3
     else:
         shapes = [(4096, 2048, 2048)] * 3
     say(f"grouped_ws {case}")
