@@ -31,7 +31,12 @@
 
 namespace bl {
 
-constexpr int kSkinnyBatch = 16;  // weight tiles held in registers per wave
+// weight tiles a wave holds in registers: TB = 4, 8 or 16, the smallest that
+// covers a wave's share of the largest K of the launch (every issued load
+// instruction costs the CU's address unit a slot, in range or not)
+constexpr int skinny_tb(int64_t kmax) {
+  return kmax <= 2048 ? 4 : (kmax <= 4096 ? 8 : 16);
+}
 
 struct SkinnyCall {
   const void *x;
@@ -58,7 +63,7 @@ struct SkinnyLaunch {
 // GLU (pre-quantized calls): the packed rows are a gate_proj in GLU order
 // and the output is h [M, N/2] = silu(y_gate) * y_up (tile rows 0..15 are
 // gated, 16..31 the rows they multiply).
-template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB, bool GLU = false>
+template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB, int TB, bool GLU = false>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   static_assert(!FUSED || MB == 1, "fused calls have at most 16 rows");
   static_assert(!GLU || (!FUSED && OUT != kOutI32), "GLU: pre-quantized, float output");
@@ -103,9 +108,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                        wrs, (w + 4 * tile) * 1024 + lane * 16, 0, 0));
   };
-  v4i wr[kSkinnyBatch];
+  v4i wr[TB];
 #pragma unroll
-  for (int t = 0; t < kSkinnyBatch; ++t) wr[t] = w_load(t);
+  for (int t = 0; t < TB; ++t) wr[t] = w_load(t);
 
   // ---- 2. activations
   if constexpr (FUSED) {
@@ -153,13 +158,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) an[mb][s2] = a_load(0, mb, s2);
   }
-  for (int base = 0; base < nmine; base += kSkinnyBatch) {
+  for (int base = 0; base < nmine; base += TB) {
     if (base > 0) {
 #pragma unroll
-      for (int t = 0; t < kSkinnyBatch; ++t) wr[t] = w_load(base + t);
+      for (int t = 0; t < TB; ++t) wr[t] = w_load(base + t);
     }
 #pragma unroll
-    for (int t = 0; t < kSkinnyBatch; ++t) {
+    for (int t = 0; t < TB; ++t) {
       if (base + t >= nmine) break;
       const int kb = w + 4 * (base + t);
       const v4i u = wr[t];
@@ -265,54 +270,65 @@ static SkinnyCall to_call(const SkinnyArgs &a) {
   return c;
 }
 
-template <bool FUSED, int DT, int MAXC, int RMODE, int MB>
+template <bool FUSED, int DT, int MAXC, int RMODE, int MB, int TB>
 static void launch_out(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                        bool glu, hipStream_t stream) {
   if constexpr (!FUSED && MAXC == 1) {
     if (glu) {
       switch (out_kind) {
-        case BL_F32: skinny_kernel<false, DT, BL_F32, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
-        case BL_F16: skinny_kernel<false, DT, BL_F16, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
-        default: skinny_kernel<false, DT, BL_BF16, 1, RMODE, MB, true><<<grid, 256, lds, stream>>>(L); break;
+        case BL_F32: skinny_kernel<false, DT, BL_F32, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
+        case BL_F16: skinny_kernel<false, DT, BL_F16, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
+        default: skinny_kernel<false, DT, BL_BF16, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
       }
       return;
     }
   }
   switch (out_kind) {
-    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
-    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
-    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
-    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE, MB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
+    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
   }
 }
 
 // Fused calls: row-quantizer mode from the largest K of the launch.
-template <int DT, int MAXC>
+template <int DT, int MAXC, int TB>
 static void launch_fused(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                          int64_t kmax, hipStream_t stream) {
   if (row_mode((int)kmax) == kRowFloat)
-    launch_out<true, DT, MAXC, kRowFloat, 1>(L, out_kind, grid, lds, false, stream);
+    launch_out<true, DT, MAXC, kRowFloat, 1, TB>(L, out_kind, grid, lds, false, stream);
   else
-    launch_out<true, DT, MAXC, kRowRaw, 1>(L, out_kind, grid, lds, false, stream);
+    launch_out<true, DT, MAXC, kRowRaw, 1, TB>(L, out_kind, grid, lds, false, stream);
+}
+
+template <int MAXC, int TB>
+static void launch_any_tb(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
+                          unsigned grid, size_t lds, int64_t kmax, int64_t M, bool glu,
+                          hipStream_t stream) {
+  if (fused) {
+    switch (x_dtype) {
+      case BL_F32: launch_fused<BL_F32, MAXC, TB>(L, out_kind, grid, lds, kmax, stream); break;
+      case BL_F16: launch_fused<BL_F16, MAXC, TB>(L, out_kind, grid, lds, kmax, stream); break;
+      default: launch_fused<BL_BF16, MAXC, TB>(L, out_kind, grid, lds, kmax, stream); break;
+    }
+  } else if constexpr (MAXC == 1) {  // pre-quantized calls are never grouped
+    if (M <= 16)
+      launch_out<false, BL_F32, 1, kRowFloat, 1, TB>(L, out_kind, grid, lds, glu, stream);
+    else if (M <= 32)
+      launch_out<false, BL_F32, 1, kRowFloat, 2, TB>(L, out_kind, grid, lds, glu, stream);
+    else
+      launch_out<false, BL_F32, 1, kRowFloat, 4, TB>(L, out_kind, grid, lds, glu, stream);
+  }
 }
 
 template <int MAXC>
 static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
                        unsigned grid, size_t lds, int64_t kmax, int64_t M, bool glu,
                        hipStream_t stream) {
-  if (fused) {
-    switch (x_dtype) {
-      case BL_F32: launch_fused<BL_F32, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
-      case BL_F16: launch_fused<BL_F16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
-      default: launch_fused<BL_BF16, MAXC>(L, out_kind, grid, lds, kmax, stream); break;
-    }
-  } else if constexpr (MAXC == 1) {  // pre-quantized calls are never grouped
-    if (M <= 16)
-      launch_out<false, BL_F32, 1, kRowFloat, 1>(L, out_kind, grid, lds, glu, stream);
-    else if (M <= 32)
-      launch_out<false, BL_F32, 1, kRowFloat, 2>(L, out_kind, grid, lds, glu, stream);
-    else
-      launch_out<false, BL_F32, 1, kRowFloat, 4>(L, out_kind, grid, lds, glu, stream);
+  switch (skinny_tb(kmax)) {
+    case 4: launch_any_tb<MAXC, 4>(L, fused, x_dtype, out_kind, grid, lds, kmax, M, glu, stream); break;
+    case 8: launch_any_tb<MAXC, 8>(L, fused, x_dtype, out_kind, grid, lds, kmax, M, glu, stream); break;
+    default: launch_any_tb<MAXC, 16>(L, fused, x_dtype, out_kind, grid, lds, kmax, M, glu, stream); break;
   }
 }
 
