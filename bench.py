@@ -59,9 +59,9 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                              "decode_bf16.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "a1a31844f7dd1ef4", 658500),
-    "c4": ("gemm", "17fd3df3d70b075b", 57891048),
-    "c5-M1": ("decode", "a1a31844f7dd1ef4", 5270549),
+    "c2": ("decode", "c2d1b129f5689ee2", 664084),
+    "c4": ("gemm", "294ec350bc48f3b4", 85967688),
+    "c5-M1": ("decode", "c2d1b129f5689ee2", 5279000),
 }
 
 
