@@ -56,7 +56,10 @@ def test_pack_exact_ties_and_extremes():
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
-@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (33, 1280), (64, 2048), (7, 7040)])
+# K spans every register-cache instance of the kernel: 2, 4, 6, 8, 12 chunks per lane,
+# the raw mode (K <= 8192) and the reload mode (K > 8192)
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (33, 1280), (64, 2048), (6, 3072), (9, 4096),
+                                 (7, 4224), (12, 5632), (5, 6144), (7, 7040), (3, 9216)])
 def test_act_quant(dtype, M, K):
     say(f"act_quant {dtype} M={M} K={K}")
     x = synth.make_x(7, 0, 0, M, K, dtype, outlier_p=0.01)
