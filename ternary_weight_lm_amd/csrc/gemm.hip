@@ -393,12 +393,13 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             hipStream_t stream) {
   // The tallest tile that still gives every CU a workgroup: 128-row tiles
   // reuse each unpacked weight operand four times, but below one tile per
-  // CU the idle CUs cost more than the extra unpacking of 64-row tiles.
+  // CU the idle CUs cost more than the extra unpacking of shorter tiles
+  // (measured at M = 512: 32-row tiles beat 64-row ones up to 256 tiles).
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
   if (M > 64 && tiles(128) >= 256)
     return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
-  if (M > 32 && tiles(64) >= 128)
+  if (M > 32 && tiles(64) >= 256)
     return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
 }
@@ -428,7 +429,7 @@ hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M,
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn * ncalls; };
   if (M > 64 && tiles(128) >= 256) return launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
-  if (M > 32 && tiles(64) >= 128) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
+  if (M > 32 && tiles(64) >= 256) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
   return launch_group_mi<1>(calls, ncalls, M, N, K, out_kind, stream);
 }
 
