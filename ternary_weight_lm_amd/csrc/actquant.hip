@@ -6,10 +6,12 @@
 // "HGRNBit: was in einem Block tatsächlich passiert"; datacamp "MatMul-freie
 // LLMs: Zentrale Konzepte erklärt", figure panel 5).  One 64-lane wave per
 // token row runs the shared row quantizer (rowquant.h): the row is read once
-// with 16-byte loads (kept in registers up to K = 8192), the three
-// reductions are cross-lane shuffles, and the int8 codes leave as coalesced
-// 8-byte stores.  Four rows per 256-thread workgroup, no barriers.  HBM
-// traffic: one read of x, one write of xq, 8 bytes of scale + row sum.
+// with 16-byte loads (widened and kept in registers up to K = 6144, kept raw
+// up to K = 8192, re-read from cache beyond), the three reductions are
+// cross-lane shuffles, and the int8 codes leave as coalesced 8-byte stores.
+// Four rows per 256-thread workgroup, no barriers; the grouped kernel takes
+// up to three projections' rows in one launch.  HBM traffic: one read of x,
+// one write of xq, 8 bytes of scale + row sum.
 #include "bl_launch.h"
 #include "rowquant.h"
 

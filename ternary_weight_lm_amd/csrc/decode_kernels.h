@@ -10,29 +10,33 @@
 // else, and at the sizes of a single layer it is latency-bound: the design
 // removes every serial step it can from the path launch -> last store.
 //   * Arguments are plain scalars, so gfx950 preloads them into SGPRs
-//     (kernel-argument preloading) instead of the waves fetching them.
+//     (kernel-argument preloading) instead of the waves fetching them (the
+//     three-call kernels fetch what does not fit: gain, beta, output).
 //   * All loads of a wave are issued at once, first the activation row and
 //     the gain, then the wave's weight tiles.  They are buffer loads whose
 //     out-of-range lanes / tiles read as zero, so none is conditional and the
 //     compiler's wait for the activations does not also wait for the weights.
-//   * The normalization of a row is split over the 4 waves (wave w owns the
-//     8-element chunks 64w + lane + 256c).  The sum of squares meets per lane
-//     in LDS ((p0 + p1) + (p2 + p3) over the waves) before one DPP tree: the
-//     association the act-quant kernel uses, so codes and scales are
-//     bit-identical across paths.  The absmax and the code row sum (exact
-//     in any order) are DPP trees per wave plus a 4-entry LDS exchange.
-//   * One workgroup owns one packed 32-row tile column; the 4 waves take
-//     its K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
+//   * The kernels are compiled for a few K capacities (1024 KC, KC = 1 .. 8)
+//     and the launch takes the smallest that covers K: each load instruction
+//     costs the CU's address unit a slot even where every lane is out of
+//     range, and loads sized for the largest K made a short row spend most
+//     of its time issuing them.
+//   * One workgroup owns one packed 32-row tile column; its waves take the
+//     K-blocks round-robin, each feeding v_mfma_i32_16x16x64_i8 from
 //     registers (weights) and LDS (codes), and the partial sums meet in LDS.
-//   * The kernels are compiled for a few sizes of a wave's share of the row
-//     (K capacity 1024 KC, KC = 1 .. 8) and the launch takes the smallest that
-//     covers K: each load instruction costs the CU's address unit a slot even
-//     where every lane is out of range, and with loads sized for the largest
-//     K a short row spent most of its time issuing them.
-//   * Rows longer than 1024 are shared by 8 waves (NW): the contraction and
-//     the per-element passes are split 8 ways, the sum of squares 4 ways.
+//   * Split mode (1..4 rows, K <= 8192): the normalization of a row is
+//     split over the waves.  The sum of squares stays on waves 0..3 (wave w
+//     owns the 8-element chunks 64w + lane + 256r) and meets per lane in LDS
+//     ((p0 + p1) + (p2 + p3)) before one DPP tree: the association of the
+//     act-quant kernel, so codes and scales are bit-identical across paths.
+//     Absmax and codes (exact in any order) are split over all waves.  4
+//     waves up to K = 1024, 8 above.
+//   * Row mode (2..8 rows, K <= 4096): 8 waves, wave w normalizes and
+//     quantizes row w alone with the shared row passes of rowquant.h (no
+//     cross-wave reduction, one barrier), then the 8 waves share the
+//     contraction.
 // Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
-// one launch: workgroup b works on call b / tiles.
+// one launch in either mode: workgroup b works on call b / tiles.
 //
 // The templates are instantiated once per activation dtype (decode_f32.hip,
 // decode_f16.hip, decode_bf16.hip), so the three compile in parallel.

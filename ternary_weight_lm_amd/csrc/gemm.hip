@@ -21,11 +21,13 @@
 //           shift + mask; no LDS traffic for weights.
 //   Loads run two k-blocks ahead of the MFMAs.
 // Epilogue: subtract rowsum, multiply by beta / s_m, round to the output
-// dtype (or store the exact int32 accumulator).
+// dtype (or store the exact int32 accumulator); long launches stage 2-byte
+// output tiles through LDS for whole-row-segment stores.
 // Workgroup ids are remapped so each of the 8 XCDs (which receive ids
 // round-robin) works on a contiguous range of a banded column-major tile
 // order, keeping the A rows and B columns of the tiles it runs together in
-// that XCD's L2.
+// that XCD's L2.  A grouped launch (gemm_mfma_group_kernel) runs up to three
+// same-shape contractions as one tile sequence.
 #include <algorithm>
 
 #include "bl_common.h"

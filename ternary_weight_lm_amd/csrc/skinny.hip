@@ -1,4 +1,5 @@
-// skinny.hip -- decode-shaped FusedBitLinear (M <= 16 tokens).
+// skinny.hip -- FusedBitLinear for a few tokens: the contraction of up to 64
+// pre-quantized rows, or up to 16 rows normalized and quantized in place.
 //
 // At a handful of tokens the layer is a stream over the packed weights
 // (N*K/4 bytes): the matrix cores have far more throughput than needed, so
@@ -6,8 +7,8 @@
 // packed 32-row tile column (32 output features x all of K); its 4 waves
 // split the K-blocks round-robin.
 //   1. Every wave first issues the 16-byte loads of its weight tiles (one
-//      contiguous 1 KiB per wave per tile), so HBM latency overlaps the
-//      prologue.
+//      contiguous 1 KiB per wave per tile; 4, 8 or 16 tiles by the largest K
+//      of the launch), so HBM latency overlaps the prologue.
 //   2. Fused variant: the workgroup normalizes and quantizes the M token
 //      rows itself, a wave per row, with the shared row quantizer
 //      (rowquant.h) into LDS --
