@@ -161,9 +161,10 @@ int bitlinear_forward_path(const void *x, int x_dtype, int64_t M, int64_t K,
 
 /* The BL_PATH_FUSED / _SKINNY / _MFMA path bitlinear_forward takes for a
  * token count M and in_features K with 16-bit activations (BL_ERR_SHAPE for
- * an invalid M or K): FUSED for M <= 4 and K <= 8192 and for M <= 8 and
- * K <= 4096, SKINNY up to M = 64, MFMA above.  fp32 activations take FUSED
- * only for M == 1 (K <= 8192) and M <= 4 (K <= 4096), SKINNY otherwise up to
+ * an invalid M or K): FUSED for M <= 4 and K <= 8192 and for M <= 16 and
+ * K <= 4096 with M * (K + 16) <= 45056, SKINNY up to M = 64, MFMA above.
+ * fp32 activations take FUSED for M == 1 (K <= 8192) and M <= 8
+ * (K <= 4096), M <= 16 only up to K = 2048, SKINNY otherwise up to
  * M = 64. */
 int bitlinear_select_path(int64_t M, int64_t K);
 
@@ -182,10 +183,10 @@ typedef struct bl_call {
  * steps where each call is too small to fill the GPU on its own -- e.g. the
  * i/f/g/o projections of an HGRNBit block (hysenlabs ja review, section
  * "HGRNBit という層構成を読む").  Consecutive calls of one shape that the
- * decode kernel takes (2 <= M <= 8 and K <= 4096 in its row mode, else
- * M <= 4 and K <= 8192 in its split mode; fp32 x: M <= 4, resp. M == 1) go
- * out up to three per launch, the remaining calls up to 16 per launch of
- * the skinny kernel.
+ * decode kernel takes (in its row mode 2 <= M <= 16, K <= 4096, M * (K + 16)
+ * <= 45056, fp32 x with M > 8 only K <= 2048; else in its split mode M <= 4
+ * and K <= 8192, fp32 x M == 1) go out up to three per launch, the
+ * remaining calls up to 16 per launch of the skinny kernel.
  *   calls   HOST array of ncalls descriptors (read during the call only)
  *   Every call must satisfy the BL_PATH_FUSED limits (M <= 16, K <= 8192,
  *   M * (K + 16) <= 56320) and the usual shape / alignment rules, and all

@@ -123,11 +123,15 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 void launch_decode_f32(const DecodeArgs &a, hipStream_t stream);
 void launch_decode_f16(const DecodeArgs &a, hipStream_t stream);
 void launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
-// Row mode of the decode kernel (one wave per token row): single calls with
-// 2 <= M <= 8 (fp32 x: M <= 4) and K <= 4096.
-constexpr int64_t kDecodeRowsMaxM = 8;
+// Row mode of the decode kernel (8 waves, one token row per wave up to 8
+// rows, two up to 16): 2 <= M <= 16, K <= 4096, the codes M (K + 16) bytes
+// within the LDS budget; fp32 activations with more than 8 rows K <= 2048.
+constexpr int64_t kDecodeRowsMaxM = 16;
+constexpr int64_t kDecodeRowsLds = 45056;  // M * (K + 16) bytes of int8 codes in LDS
 inline bool decode_rows_fits(int64_t M, int64_t K, int x_dtype) {
-  return M >= 2 && K <= 4096 && M <= (x_dtype == BL_F32 ? 4 : kDecodeRowsMaxM);
+  if (M < 2 || K > 4096 || M > kDecodeRowsMaxM || M * (K + 16) > kDecodeRowsLds) return false;
+  // fp32 rows hold twice the registers: two rows per wave only up to K = 2048
+  return x_dtype != BL_F32 || M <= 8 || K <= 2048;
 }
 // Split mode (every wave takes a share of each row; up to three calls per
 // launch): M <= 4 (fp32 x: M == 1), K <= 8192.

@@ -64,9 +64,9 @@ bool fused_fits(int64_t M, int64_t K) {
 }
 
 // Default path by token count: the one-launch decode kernel wherever it
-// applies (split mode M <= 4 up to K = 8192, row mode M <= 8 up to K = 4096;
-// fp32 activations: M == 1, resp. M <= 4), then the act-quant + skinny
-// pair up to 64 tokens, then the MFMA GEMM.
+// applies (split mode M <= 4 up to K = 8192, fp32 activations M == 1; row
+// mode up to 16 rows as decode_rows_fits allows), then the act-quant +
+// skinny pair up to 64 tokens, then the MFMA GEMM.
 int auto_path(int64_t M, int64_t K, int x_dtype) {
   if (M <= 4 && fused_fits(M, K) && (x_dtype != BL_F32 || bl::decode_fits(M, K, x_dtype)))
     return BL_PATH_FUSED;

@@ -360,16 +360,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
 }
 
 // ---------------------------------------------------------------- row mode
-// 2 <= M <= NW tokens, K <= 4096: wave w normalizes and quantizes row w by
-// itself (the shared float-mode row passes of rowquant.h, bit-identical to
-// the act-quant kernel), so no row reduction crosses a wave and one barrier
-// (the codes in LDS) suffices; then the NW waves (4 or 8) share the tile
-// column's contraction.  Loads go out x row -> gain -> weights; every
+// 2 <= M <= RPW * NW tokens, K <= 4096: wave w normalizes and quantizes
+// rows w, w + NW, ... by itself (the shared float-mode row passes of
+// rowquant.h, bit-identical to the act-quant kernel), so no row reduction
+// crosses a wave and one barrier (the codes in LDS) suffices; then the NW
+// waves share the tile column's contraction (rows 0..15: one MFMA block).  Loads go out x row -> gain -> weights; every
 // argument is preloaded.  KC: K capacity 1024 KC; a lane caches 2 KC chunks
 // of its row.
 // GAIN_LATE (three-call kernel): the gain pointer comes from the argument
 // buffer, so the weights are issued before waiting for it.
-template <int DT, int OUT, bool GLU, int KC, int NW, bool GAIN_LATE>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool GAIN_LATE>
 __device__ __forceinline__ void decode_rows_body(
     const void *x, uint32_t shape, float eps, int nt, int call, const uint4 *p0, const uint4 *p1,
     const uint4 *p2, const void *g0, const void *g1, const void *g2, const float *b0,
@@ -389,13 +389,17 @@ __device__ __forceinline__ void decode_rows_body(
   const int KB = K >> 7;
   const int lds_stride = K + 16;
 
-  // ---- 1. loads: this wave's row, the gain, then the weight tiles
+  // ---- 1. loads: this wave's rows, the gain, then the weight tiles
   const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * EB));
-  Chunk8<DT> xraw[RC];
+  Chunk8<DT> xraw[RPW][RC];
 #pragma unroll
-  for (int c = 0; c < RC; ++c) {
-    const int k = 8 * lane + 512 * c;
-    xraw[c] = bload_chunk<DT>(xr, w < M && k < K ? (uint32_t)((w * K + k) * EB) : kOob);
+  for (int j = 0; j < RPW; ++j) {
+    const int m = w + NW * j;
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+      const int k = 8 * lane + 512 * c;
+      xraw[j][c] = bload_chunk<DT>(xr, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint4 *packed = call == 0 ? p0 : (call == 1 ? p1 : p2);
@@ -422,17 +426,20 @@ __device__ __forceinline__ void decode_rows_body(
   void *out = call == 0 ? o0 : (call == 1 ? o1 : o2);
   const float beta = *bp;
 
-  // ---- 2. the wave's row: codes into LDS, scale factor and row sum
-  if (w < M) {
-    int8_t *dst = xs + w * lds_stride;
+  // ---- 2. the wave's rows: codes into LDS, scale factor and row sum
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int m = w + NW * j;
+    if (m >= M) break;
+    int8_t *dst = xs + m * lds_stride;
     float sc;
     int rs;
-    quantize_loaded<DT, RC>(xraw, graw, K, eps,
+    quantize_loaded<DT, RC>(xraw[j], graw, K, eps,
                             [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
                             sc, rs);
     if (lane == 0) {
-      f_row[w] = div_rn(beta, sc);
-      rs_row[w] = rs;
+      f_row[m] = div_rn(beta, sc);
+      rs_row[m] = rs;
     }
   }
   __syncthreads();
@@ -504,13 +511,13 @@ __device__ __forceinline__ void decode_rows_body(
   }
 }
 
-template <int DT, int OUT, bool GLU, int KC, int NW>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void *x, uint32_t shape,
                                                                       float eps,
                                                                       const uint4 *packed,
                                                                       const void *gain,
                                                                       const float *bp, void *out) {
-  decode_rows_body<DT, OUT, GLU, KC, NW, false>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
+  decode_rows_body<DT, OUT, GLU, KC, NW, RPW, false>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
                                                 packed, gain, gain, gain, bp, bp, bp, out, out,
                                                 out);
 }
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void
 // Up to three row-mode calls of one shape; workgroup b works on call
 // b / tiles.  The activation and weight pointers are preloaded, the rest is
 // fetched.
-template <int DT, int OUT, int KC, int NW>
+template <int DT, int OUT, int KC, int NW, int RPW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
     const void *x0, const void *x1, const void *x2, uint32_t shape, float eps, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
@@ -527,7 +534,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
   const int bid = (int)blockIdx.x;
   const int call = (bid >= tiles) + (bid >= 2 * tiles);
   const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
-  decode_rows_body<DT, OUT, false, KC, NW, true>(x, shape, eps, bid - call * tiles, call, p0, p1,
+  decode_rows_body<DT, OUT, false, KC, NW, RPW, true>(x, shape, eps, bid - call * tiles, call, p0, p1,
                                                  p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
 }
 
@@ -535,8 +542,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
 // split 8 ways -- measured faster than 4 waves from 2 rows and K = 1024 up).
 constexpr int kRowsNW = 8;
 
-template <int DT, int OUT, bool GLU, int KC>
-static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
+template <int DT, int OUT, bool GLU, int KC, int RPW>
+static void launch_rows_rpw(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
   const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
@@ -545,13 +552,20 @@ static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
     const uint4 *p[3];
     for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
     const unsigned grid = tiles * (unsigned)a.ncalls;
-    decode_rows3_kernel<DT, OUT, KC, kRowsNW><<<grid, 64 * kRowsNW, lds, stream>>>(
+    decode_rows3_kernel<DT, OUT, KC, kRowsNW, RPW><<<grid, 64 * kRowsNW, lds, stream>>>(
         a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2],
         a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
     return;
   }
-  decode_rows_kernel<DT, OUT, GLU, KC, kRowsNW><<<tiles, 64 * kRowsNW, lds, stream>>>(
+  decode_rows_kernel<DT, OUT, GLU, KC, kRowsNW, RPW><<<tiles, 64 * kRowsNW, lds, stream>>>(
       a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
+}
+
+// one row per wave up to 8 rows, two up to 16
+template <int DT, int OUT, bool GLU, int KC>
+static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
+  if (a.M <= kRowsNW) launch_rows_rpw<DT, OUT, GLU, KC, 1>(a, stream);
+  else launch_rows_rpw<DT, OUT, GLU, KC, 2>(a, stream);
 }
 
 // row mode: K <= 4096 (decode_rows_fits)

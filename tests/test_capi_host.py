@@ -66,8 +66,12 @@ def test_select_path_rule():
     assert L.bitlinear_select_path(5, 1024) == 1     # row mode of the decode kernel
     assert L.bitlinear_select_path(8, 4096) == 1
     assert L.bitlinear_select_path(8, 4224) == 2     # row mode needs K <= 4096
-    assert L.bitlinear_select_path(9, 1024) == 2
-    assert L.bitlinear_select_path(16, 1024) == 2
+    assert L.bitlinear_select_path(9, 1024) == 1     # two rows per wave
+    assert L.bitlinear_select_path(16, 1024) == 1
+    assert L.bitlinear_select_path(10, 4096) == 1    # 10 * 4112 bytes of codes fit
+    assert L.bitlinear_select_path(12, 4096) == 2    # 12 * 4112 do not
+    assert L.bitlinear_select_path(16, 2688) == 1
+    assert L.bitlinear_select_path(16, 2816) == 2
     assert L.bitlinear_select_path(17, 1024) == 2
     assert L.bitlinear_select_path(64, 7040) == 2
     assert L.bitlinear_select_path(65, 1024) == 3

@@ -77,7 +77,10 @@ CASES = [
     (tw.BL_PATH_MFMA, 17, 80, 1280, "bf16", "bf16"),
     (tw.BL_PATH_MFMA, 130, 176, 1024, "fp16", "fp16"),
     (tw.BL_PATH_MFMA, 257, 48, 2048, "bf16", "fp32"),
-    (tw.BL_PATH_FUSED, 9, 80, 1024, "bf16", "bf16"),   # falls back: M > 4
+    (tw.BL_PATH_FUSED, 9, 80, 1024, "bf16", "bf16"),   # row mode, two rows per wave
+    (tw.BL_PATH_FUSED, 16, 48, 2048, "fp32", "fp32"),
+    (tw.BL_PATH_FUSED, 13, 80, 2560, "bf16", "fp16"),
+    (tw.BL_PATH_FUSED, 6, 16, 7040, "bf16", "bf16"),   # past the decode kernel: skinny fused
 ]
 
 

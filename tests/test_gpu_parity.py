@@ -129,6 +129,11 @@ FWD_CASES = [
     (tw.BL_PATH_AUTO, 64, 256, 2560, "bf16", "bf16"),
     (tw.BL_PATH_AUTO, 3, 96, 7040, "fp16", "fp32"),
     (tw.BL_PATH_AUTO, 2, 64, 1024, "fp32", "fp32"),
+    # decode row mode with two rows per wave (9..16 rows)
+    (tw.BL_PATH_FUSED, 12, 160, 2048, "bf16", "bf16"),
+    (tw.BL_PATH_FUSED, 10, 96, 4096, "fp16", "fp16"),
+    (tw.BL_PATH_AUTO, 16, 256, 1024, "fp32", "fp32"),
+    (tw.BL_PATH_FUSED, 16, 64, 2560, "fp32", "fp32"),   # fp32 past K = 2048: skinny fused
 ]
 
 
@@ -174,7 +179,8 @@ def test_grouped_matches_single_calls():
     # (M, N, K); consecutive same-shape runs share launches: split mode for
     # M = 1, the row mode (4 and 8 waves) for 2 <= M <= 8 up to K = 4096
     shapes = [(1, 1024, 1024), (1, 2048, 1024), (3, 96, 384), (2, 64, 7040), (4, 160, 1280),
-              (0, 64, 256)] + [(6, 256, 2048)] * 3 + [(3, 96, 1024)] * 3 + [(8, 64, 4096)] * 2
+              (0, 64, 256)] + [(6, 256, 2048)] * 3 + [(3, 96, 1024)] * 3 + [(8, 64, 4096)] * 2 \
+        + [(12, 96, 1024)] * 3
     items, singles = [], []
     for i, (M, N, K) in enumerate(shapes):
         x = synth.make_x(900 + i, 0, 0, M, K, "bf16").to(DEV)
