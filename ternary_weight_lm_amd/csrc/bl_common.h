@@ -123,6 +123,16 @@ __device__ __forceinline__ void store1(void *base, int64_t idx, float v) {
   }
 }
 
+// Between LDS writes by some lanes of a wave and reads of that data by other
+// lanes of the same wave.  The hardware already runs one wave's LDS
+// operations in order, so this emits no instruction; it is a wavefront-scope
+// fence for the compiler, which otherwise treats each lane as alone and may
+// move a lane's reads ahead of the writes it does not itself depend on.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row: conflict-free for
 // 16-byte accesses by 8 consecutive rows (32 banks) and by 16 consecutive
 // rows (64 banks), the two ways gfx9 LDS serves ds_read/write_b128.

@@ -212,8 +212,8 @@ __device__ __forceinline__ void gemm_body(
   // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
   // row sums and rescale factors of the wave's 16*MI rows go through a small
   // LDS table (lane l fetches row l; one division per lane), from which each
-  // lane reads its four consecutive rows with one 16-byte read.  (A wave's
-  // LDS operations complete in order, so no barrier is needed.)
+  // lane reads its four consecutive rows with one 16-byte read (the table is
+  // the wave's own: a wavefront fence, no barrier).
   __shared__ __align__(16) int e_rs[4][64];
   __shared__ __align__(16) float e_sc[4][64];
   const int wrow0 = m0 + wm * 16 * MI;
@@ -222,6 +222,7 @@ __device__ __forceinline__ void gemm_body(
     e_rs[wave][lane] = rowsum[mrow];
     if constexpr (OUT != kOutI32) e_sc[wave][lane] = div_rn(*beta, s[mrow]);
   }
+  wave_lds_sync();
   const int q4 = 4 * (lane >> 4);
   const int ncol0 = n0 + 64 * wn + (lane & 15);
   v4i rs4[MI];
@@ -288,6 +289,7 @@ __device__ __forceinline__ void gemm_body(
                 out_bits<OUT>(y);
           }
         }
+      wave_lds_sync();
       const rsrc_t ors =
           make_rsrc(reinterpret_cast<uint16_t *>(out) + (int64_t)wrow0 * N + n0 + 64 * wn,
                     (uint32_t)((16 * MI - 1) * N + 64) * 2u);

@@ -140,24 +140,33 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = v4i{0, 0, 0, 0};
   const int arow = lane & 15;
-  // pre-quantized A: buffer loads over xq (rows >= M read as zero), one tile
-  // ahead of the MFMAs; unconditional (the index is clamped), so the wait
-  // for a tile's operands never waits for the loads issued after them
+  // Pre-quantized A.  The MFMA operand layout (lane l: row l mod 16, 16
+  // bytes of chunk 2 (l / 16) + s2) gathered straight from memory puts every
+  // lane of a load in another row, and such loads cost the address and
+  // cache units several times what row-contiguous ones do (the contraction
+  // of 64 rows at K = 7040 ran 17 us that way, 10.4 us staged).  So a wave
+  // loads its k-block's 16 MB x 128-byte slice with row-contiguous 16-byte
+  // loads (load j: rows 8 j + l / 8, chunk l mod 8; rows >= M read as zero),
+  // one tile ahead of its MFMAs, and turns it into operands through its own
+  // LDS stage (XOR-swizzled rows, conflict-free both ways).  Every load is
+  // issued (past the wave's last tile the offset is out of range: zeros, no
+  // memory traffic), so the wait for a tile's slice never waits for the
+  // loads issued after it.  (A deeper ring of slices in registers was
+  // slower: more loads in flight per wave, more registers.)
+  __shared__ __align__(16) int8_t astage[FUSED ? 1 : 4][FUSED ? 16 : 16 * MB * 128];
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t *>(p.xq), (short)0, FUSED ? 0 : M * K, 0x00020000);
-  const auto a_off = [&](int tile, int mb, int s2) {
+  const int crow = lane >> 3, cch = lane & 7;
+  const auto a_load = [&](int tile, int j) {
     const int kb = w + 4 * tile;
-    return (uint32_t)((16 * mb + arow) * K + kb * 128 + 32 * (lane >> 4) + 16 * s2);
+    const uint32_t off = tile < nmine ? (uint32_t)((8 * j + crow) * K + kb * 128 + 16 * cch)
+                                      : 0x40000000u;
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0));
   };
-  const auto a_load = [&](int tile, int mb, int s2) {
-    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)a_off(tile, mb, s2), 0, 0));
-  };
-  v4i an[MB][2];
+  v4i an[2 * MB];
   if constexpr (!FUSED) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) an[mb][s2] = a_load(0, mb, s2);
+    for (int j = 0; j < 2 * MB; ++j) an[j] = a_load(0, j);
   }
   for (int base = 0; base < nmine; base += TB) {
     if (base > 0) {
@@ -179,14 +188,24 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
                                                       32 * (lane >> 4) + 16 * s2);
         }
       } else {
-        const int nxt = min(base + t + 1, nmine - 1);
+        int8_t *st = astage[w];
+        // the previous tile's operand reads are done before this overwrite
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < 2 * MB; ++j) {
+          const int row = 8 * j + crow;
+          *reinterpret_cast<v4i *>(st + row * 128 + (swz(row, cch) << 4)) = an[j];
+        }
+        wave_lds_sync();
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            a[mb][s2] = an[mb][s2];
-            an[mb][s2] = a_load(nxt, mb, s2);
+            const int row = 16 * mb + arow, ch = 2 * (lane >> 4) + s2;
+            a[mb][s2] = *reinterpret_cast<const v4i *>(st + row * 128 + (swz(row, ch) << 4));
           }
+#pragma unroll
+        for (int j = 0; j < 2 * MB; ++j) an[j] = a_load(base + t + 1, j);
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
