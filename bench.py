@@ -57,11 +57,13 @@ GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
 # kernel reports traffic null until it is measured again.
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip", "decode_f16.hip",
                              "decode_bf16.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
-                  "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"]}
+                  "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
+                  "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "c2d1b129f5689ee2", 664084),
-    "c4": ("gemm", "294ec350bc48f3b4", 85967688),
-    "c5-M1": ("decode", "c2d1b129f5689ee2", 5279000),
+    "c2": ("decode", "f04bea17cb5cf105", 664125),
+    "c3": ("skinny", "66217f1d420fdb57", 3143253),
+    "c4": ("gemm", "8c7ffcb3155eee12", 85890399),
+    "c5-M1": ("decode", "f04bea17cb5cf105", 5279002),
 }
 
 
