@@ -64,12 +64,25 @@ struct SkinnyLaunch {
 // GLU (pre-quantized calls): the packed rows are a gate_proj in GLU order
 // and the output is h [M, N/2] = silu(y_gate) * y_up (tile rows 0..15 are
 // gated, 16..31 the rows they multiply).
-template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB, int TB, bool GLU = false>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
+// NW: waves per workgroup, splitting the K-blocks round-robin (4; the
+// pre-quantized path takes 8 from K = 2048 in launches of fewer workgroups
+// than CUs, halving each wave's chain of tiles).
+template <bool FUSED, int DT, int OUT, int MAXC, int RMODE, int MB, int TB, bool GLU = false,
+          int NW = 4>
+__global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   static_assert(!FUSED || MB == 1, "fused calls have at most 16 rows");
+  static_assert(!FUSED || NW == 4, "fused calls run 4 waves");
   static_assert(!GLU || (!FUSED && OUT != kOutI32), "GLU: pre-quantized, float output");
   extern __shared__ __align__(16) int8_t xs[];  // fused: [M][K + 16] int8
-  __shared__ int red[4][MB * 8][64];
+  // per-wave LDS region: the pre-quantized path's A stage during the
+  // contraction, then the wave's partial sums
+  constexpr int kStage = 16 * MB * 128;
+  constexpr int kRed = MB * 8 * 64 * 4;
+  constexpr int kWave = FUSED ? kRed : (kStage > kRed ? kStage : kRed);
+  __shared__ __align__(16) int8_t wbuf[NW][kWave];
+  const auto red = [&](int ww, int j, int l) -> int & {
+    return reinterpret_cast<int *>(wbuf[ww])[j * 64 + l];
+  };
   __shared__ float s_row[16 * MB];
   __shared__ int rs_row[16 * MB];
 
@@ -84,7 +97,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int M = p.M, K = p.K, KB = K >> 7;
   const int lds_stride = K + 16;
-  const int nmine = w < KB ? (KB - w + 3) / 4 : 0;
+  const int nmine = w < KB ? (KB - w + NW - 1) / NW : 0;
 
   // ---- 1. loads.  Buffer loads whose out-of-range offsets read as zero:
   // none is conditional, so each wait below is for exactly the loads it
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
       const_cast<uint4 *>(p.packed + (int64_t)nt * KB * 64), (short)0, KB * 1024, 0x00020000);
   const auto w_load = [&](int tile) {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                       wrs, (w + 4 * tile) * 1024 + lane * 16, 0, 0));
+                                       wrs, (w + NW * tile) * 1024 + lane * 16, 0, 0));
   };
   v4i wr[TB];
 #pragma unroll
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   // ---- 2. activations
   if constexpr (FUSED) {
     constexpr int EB = dtype_bytes(DT);
-    for (int m = w; m < M; m += 4) {  // a wave per token row
+    for (int m = w; m < M; m += NW) {  // a wave per token row
       const char *xr = reinterpret_cast<const char *>(p.x) + (int64_t)m * K * EB;
       int8_t *dst = xs + m * lds_stride;
       float sc;
@@ -153,12 +166,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
   // memory traffic), so the wait for a tile's slice never waits for the
   // loads issued after it.  (A deeper ring of slices in registers was
   // slower: more loads in flight per wave, more registers.)
-  __shared__ __align__(16) int8_t astage[FUSED ? 1 : 4][FUSED ? 16 : 16 * MB * 128];
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t *>(p.xq), (short)0, FUSED ? 0 : M * K, 0x00020000);
   const int crow = lane >> 3, cch = lane & 7;
   const auto a_load = [&](int tile, int j) {
-    const int kb = w + 4 * tile;
+    const int kb = w + NW * tile;
     const uint32_t off = tile < nmine ? (uint32_t)((8 * j + crow) * K + kb * 128 + 16 * cch)
                                       : 0x40000000u;
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0));
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       if (base + t >= nmine) break;
-      const int kb = w + 4 * (base + t);
+      const int kb = w + NW * (base + t);
       const v4i u = wr[t];
       v4i a[MB][2];
       if constexpr (FUSED) {
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
                                                       32 * (lane >> 4) + 16 * s2);
         }
       } else {
-        int8_t *st = astage[w];
+        int8_t *st = wbuf[w];
         // the previous tile's operand reads are done before this overwrite
         wave_lds_sync();
 #pragma unroll
@@ -228,43 +240,54 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyLaunch<MAXC> L) {
       rs_row[tid] = rs_reg;
     }
   }
-  // red[w][8 mb + 4 h + i][lane]: row 16 mb + 4 (lane / 16) + i, column
-  // 16 h + lane % 16 of the tile
+  // red(w, 8 mb + 4 h + i, lane): row 16 mb + 4 (lane / 16) + i, column
+  // 16 h + lane % 16 of the tile; it overwrites the wave's own A stage,
+  // whose last operand reads come first
+  wave_lds_sync();
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      red[w][8 * mb + i][lane] = acc0[mb][i];
-      red[w][8 * mb + 4 + i][lane] = acc1[mb][i];
+      red(w, 8 * mb + i, lane) = acc0[mb][i];
+      red(w, 8 * mb + 4 + i, lane) = acc1[mb][i];
     }
   __syncthreads();
+  constexpr int T = 64 * NW;
+  // sum of the NW waves' partial sums at one place of the table (int32:
+  // exact in any order)
+  const auto total = [&](int j, int l) {
+    int v = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += red(ww, j, l);
+    return v;
+  };
   if constexpr (GLU) {
-    // output (m, c), c < 16: row m's gated value sits at red[.][8 mb + i][L]
-    // and the value it multiplies at red[.][8 mb + 4 + i][L], with
+    // output (m, c), c < 16: row m's gated value sits at red(., 8 mb + i, L)
+    // and the value it multiplies at red(., 8 mb + 4 + i, L), with
     // L = 16 (r / 4) + c, i = r % 4 for r = m % 16
 #pragma unroll
-    for (int q = 0; q < MB; ++q) {
-      const int idx = tid + 256 * q;
+    for (int q = 0; q < (256 * MB + T - 1) / T; ++q) {
+      const int idx = tid + T * q;
       const int m = idx >> 4, c = idx & 15;
       if (m >= M) continue;
       const int mb = m >> 4, r = m & 15;
       const int Lq = 16 * (r >> 2) + c, jg = 8 * mb + (r & 3), ju = jg + 4;
-      const int vg = red[0][jg][Lq] + red[1][jg][Lq] + red[2][jg][Lq] + red[3][jg][Lq] - rs_row[m];
-      const int vu = red[0][ju][Lq] + red[1][ju][Lq] + red[2][ju][Lq] + red[3][ju][Lq] - rs_row[m];
+      const int vg = total(jg, Lq) - rs_row[m];
+      const int vu = total(ju, Lq) - rs_row[m];
       const float yg = (float)vg * s_row[m], yu = (float)vu * s_row[m];
       store1<OUT>(p.out, (int64_t)m * (p.N >> 1) + nt * 16 + c, silu(yg) * yu);
     }
     return;
   }
 #pragma unroll
-  for (int q = 0; q < 2 * MB; ++q) {
-    const int idx = tid + 256 * q;
+  for (int q = 0; q < 512 * MB / T; ++q) {
+    const int idx = tid + T * q;
     const int j = idx >> 6, Lq = idx & 63;
     const int mb = j >> 3, h = (j >> 2) & 1, i = j & 3;
     const int m = 16 * mb + 4 * (Lq >> 4) + i;
     if (m >= M) continue;
     const int n = nt * 32 + 16 * h + (Lq & 15);
-    const int v = red[0][j][Lq] + red[1][j][Lq] + red[2][j][Lq] + red[3][j][Lq] - rs_row[m];
+    const int v = total(j, Lq) - rs_row[m];
     const int64_t o = (int64_t)m * p.N + n;
     if constexpr (OUT == kOutI32) {
       reinterpret_cast<int32_t *>(p.out)[o] = v;
@@ -290,24 +313,25 @@ static SkinnyCall to_call(const SkinnyArgs &a) {
   return c;
 }
 
-template <bool FUSED, int DT, int MAXC, int RMODE, int MB, int TB>
+template <bool FUSED, int DT, int MAXC, int RMODE, int MB, int TB, int NW = 4>
 static void launch_out(const SkinnyLaunch<MAXC> &L, int out_kind, unsigned grid, size_t lds,
                        bool glu, hipStream_t stream) {
+  constexpr unsigned T = 64 * NW;
   if constexpr (!FUSED && MAXC == 1) {
     if (glu) {
       switch (out_kind) {
-        case BL_F32: skinny_kernel<false, DT, BL_F32, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
-        case BL_F16: skinny_kernel<false, DT, BL_F16, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
-        default: skinny_kernel<false, DT, BL_BF16, 1, RMODE, MB, TB, true><<<grid, 256, lds, stream>>>(L); break;
+        case BL_F32: skinny_kernel<false, DT, BL_F32, 1, RMODE, MB, TB, true, NW><<<grid, T, lds, stream>>>(L); break;
+        case BL_F16: skinny_kernel<false, DT, BL_F16, 1, RMODE, MB, TB, true, NW><<<grid, T, lds, stream>>>(L); break;
+        default: skinny_kernel<false, DT, BL_BF16, 1, RMODE, MB, TB, true, NW><<<grid, T, lds, stream>>>(L); break;
       }
       return;
     }
   }
   switch (out_kind) {
-    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
-    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
-    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
-    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE, MB, TB><<<grid, 256, lds, stream>>>(L); break;
+    case BL_F32: skinny_kernel<FUSED, DT, BL_F32, MAXC, RMODE, MB, TB, false, NW><<<grid, T, lds, stream>>>(L); break;
+    case BL_F16: skinny_kernel<FUSED, DT, BL_F16, MAXC, RMODE, MB, TB, false, NW><<<grid, T, lds, stream>>>(L); break;
+    case BL_BF16: skinny_kernel<FUSED, DT, BL_BF16, MAXC, RMODE, MB, TB, false, NW><<<grid, T, lds, stream>>>(L); break;
+    default: skinny_kernel<FUSED, DT, kOutI32, MAXC, RMODE, MB, TB, false, NW><<<grid, T, lds, stream>>>(L); break;
   }
 }
 
@@ -331,20 +355,44 @@ static void launch_any_tb(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, 
       case BL_F16: launch_fused<BL_F16, MAXC, TB>(L, out_kind, grid, lds, kmax, stream); break;
       default: launch_fused<BL_BF16, MAXC, TB>(L, out_kind, grid, lds, kmax, stream); break;
     }
-  } else if constexpr (MAXC == 1) {  // pre-quantized calls are never grouped
-    if (M <= 16)
-      launch_out<false, BL_F32, 1, kRowFloat, 1, TB>(L, out_kind, grid, lds, glu, stream);
-    else if (M <= 32)
-      launch_out<false, BL_F32, 1, kRowFloat, 2, TB>(L, out_kind, grid, lds, glu, stream);
-    else
-      launch_out<false, BL_F32, 1, kRowFloat, 4, TB>(L, out_kind, grid, lds, glu, stream);
   }
+}
+
+// Pre-quantized calls (never grouped): 16-row blocks by M, NW waves.
+template <int TB, int NW>
+static void launch_pre(const SkinnyLaunch<1> &L, int out_kind, unsigned grid, int64_t M, bool glu,
+                       hipStream_t stream) {
+  if (M <= 16)
+    launch_out<false, BL_F32, 1, kRowFloat, 1, TB, NW>(L, out_kind, grid, 0, glu, stream);
+  else if (M <= 32)
+    launch_out<false, BL_F32, 1, kRowFloat, 2, TB, NW>(L, out_kind, grid, 0, glu, stream);
+  else
+    launch_out<false, BL_F32, 1, kRowFloat, 4, TB, NW>(L, out_kind, grid, 0, glu, stream);
 }
 
 template <int MAXC>
 static void launch_any(const SkinnyLaunch<MAXC> &L, bool fused, int x_dtype, int out_kind,
                        unsigned grid, size_t lds, int64_t kmax, int64_t M, bool glu,
                        hipStream_t stream) {
+  if constexpr (MAXC == 1) {
+    if (!fused) {
+      // Fewer tile columns than CUs and K >= 2048: 8 waves per workgroup (4
+      // or 8 tiles each) halve each wave's chain of tiles (N = 2048 at M =
+      // 32, K = 5632: 6.8 -> 5.5 us).  Wider launches keep 4 waves: more
+      // workgroups fit a CU, and 8 were 1-5 % slower there.
+      if (kmax >= 2048 && grid < 256) {
+        if (kmax <= 4096) launch_pre<4, 8>(L, out_kind, grid, M, glu, stream);
+        else launch_pre<8, 8>(L, out_kind, grid, M, glu, stream);
+      } else {
+        switch (skinny_tb(kmax)) {
+          case 4: launch_pre<4, 4>(L, out_kind, grid, M, glu, stream); break;
+          case 8: launch_pre<8, 4>(L, out_kind, grid, M, glu, stream); break;
+          default: launch_pre<16, 4>(L, out_kind, grid, M, glu, stream); break;
+        }
+      }
+      return;
+    }
+  }
   switch (skinny_tb(kmax)) {
     case 4: launch_any_tb<MAXC, 4>(L, fused, x_dtype, out_kind, grid, lds, kmax, M, glu, stream); break;
     case 8: launch_any_tb<MAXC, 8>(L, fused, x_dtype, out_kind, grid, lds, kmax, M, glu, stream); break;

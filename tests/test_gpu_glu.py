@@ -74,6 +74,7 @@ CASES = [
     (tw.BL_PATH_SKINNY, 8, 48, 2048, "fp16", "fp16"),
     (tw.BL_PATH_SKINNY, 45, 80, 1280, "bf16", "bf16"),
     (tw.BL_PATH_SKINNY, 64, 16, 640, "fp32", "fp32"),
+    (tw.BL_PATH_SKINNY, 40, 48, 5632, "bf16", "bf16"),   # 8 waves, 8 tiles each
     (tw.BL_PATH_MFMA, 17, 80, 1280, "bf16", "bf16"),
     (tw.BL_PATH_MFMA, 130, 176, 1024, "fp16", "fp16"),
     (tw.BL_PATH_MFMA, 257, 48, 2048, "bf16", "fp32"),
