@@ -61,7 +61,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "f04bea17cb5cf105", 664125),
-    "c3": ("skinny", "66217f1d420fdb57", 3143253),
+    "c3": ("skinny", "ff283e13768eea3d", 3129942),
     "c4": ("gemm", "8c7ffcb3155eee12", 85890399),
     "c5-M1": ("decode", "f04bea17cb5cf105", 5279002),
 }
