@@ -1,4 +1,4 @@
-// decode_kernels.h -- the whole FusedBitLinear in one launch for M <= 8 tokens.
+// decode_kernels.h -- the whole FusedBitLinear in one launch for M <= 16 tokens.
 //
 // RMSNorm right before the quantizers (hysenlabs de review "MatMul-Free LM:
 // Ternary-Gewichte statt Matrixmultiplikation im Transformer", section
@@ -31,10 +31,10 @@
 //     act-quant kernel, so codes and scales are bit-identical across paths.
 //     Absmax and codes (exact in any order) are split over all waves.  4
 //     waves up to K = 1024, 8 above.
-//   * Row mode (2..8 rows, K <= 4096): 8 waves, wave w normalizes and
-//     quantizes row w alone with the shared row passes of rowquant.h (no
-//     cross-wave reduction, one barrier), then the 8 waves share the
-//     contraction.
+//   * Row mode (2..16 rows, K <= 4096): 8 waves (16 from 13 rows), wave w
+//     normalizes and quantizes rows w (and w + 8 at 9..12 rows) alone with
+//     the shared row passes of rowquant.h (no cross-wave reduction, one
+//     barrier), then the waves share the contraction.
 // Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
 // one launch in either mode: workgroup b works on call b / tiles.
 //
@@ -499,8 +499,9 @@ __device__ __forceinline__ void decode_rows_body(
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 512 / (64 * NW); ++q) {
+    for (int q = 0; q < (512 + 64 * NW - 1) / (64 * NW); ++q) {
       const int idx = tid + 64 * NW * q;
+      if (NW > 8 && idx >= 512) break;  // 16 waves: half the threads store
       const int j = idx >> 6, Lq = idx & 63;
       const int h = j >> 2, i = j & 3;
       const int m = 4 * (Lq >> 4) + i;
@@ -512,7 +513,7 @@ __device__ __forceinline__ void decode_rows_body(
 }
 
 template <int DT, int OUT, bool GLU, int KC, int NW, int RPW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void *x, uint32_t shape,
+__global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows_kernel(const void *x, uint32_t shape,
                                                                       float eps,
                                                                       const uint4 *packed,
                                                                       const void *gain,
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_kernel(const void
 // b / tiles.  The activation and weight pointers are preloaded, the rest is
 // fetched.
 template <int DT, int OUT, int KC, int NW, int RPW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
+__global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows3_kernel(
     const void *x0, const void *x1, const void *x2, uint32_t shape, float eps, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
     const float *b0, const float *b1, const float *b2, void *o0, void *o1, void *o2) {
@@ -539,10 +540,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows3_kernel(
 }
 
 // Waves per workgroup in the row mode: 8 (one per row; the contraction is
-// split 8 ways -- measured faster than 4 waves from 2 rows and K = 1024 up).
+// split 8 ways -- measured faster than 4 waves from 2 rows and K = 1024 up),
+// 16 from 13 rows.
 constexpr int kRowsNW = 8;
 
-template <int DT, int OUT, bool GLU, int KC, int RPW>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW>
 static void launch_rows_rpw(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
@@ -552,20 +554,27 @@ static void launch_rows_rpw(const DecodeArgs &a, hipStream_t stream) {
     const uint4 *p[3];
     for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
     const unsigned grid = tiles * (unsigned)a.ncalls;
-    decode_rows3_kernel<DT, OUT, KC, kRowsNW, RPW><<<grid, 64 * kRowsNW, lds, stream>>>(
+    decode_rows3_kernel<DT, OUT, KC, NW, RPW><<<grid, 64 * NW, lds, stream>>>(
         a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2],
         a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
     return;
   }
-  decode_rows_kernel<DT, OUT, GLU, KC, kRowsNW, RPW><<<tiles, 64 * kRowsNW, lds, stream>>>(
+  decode_rows_kernel<DT, OUT, GLU, KC, NW, RPW><<<tiles, 64 * NW, lds, stream>>>(
       a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
 }
 
 // one row per wave up to 8 rows, two up to 16
 template <int DT, int OUT, bool GLU, int KC>
 static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
-  if (a.M <= kRowsNW) launch_rows_rpw<DT, OUT, GLU, KC, 1>(a, stream);
-  else launch_rows_rpw<DT, OUT, GLU, KC, 2>(a, stream);
+  // 9..12 rows: 8 waves, two rows on some; 13..16 rows: 16 waves of one row
+  // each, so no wave runs two row chains in a row (16 rows: 6-12 % faster;
+  // at 9 rows the wider workgroup was 5 % slower).  fp32 rows past K = 2048
+  // do not fit 16 waves' registers; decode_rows_fits never sends them more
+  // than 8 rows, and the 8-wave kernel stands in for that instance.
+  if (a.M <= kRowsNW) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 1>(a, stream);
+  else if (a.M <= 12) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 2>(a, stream);
+  else if constexpr (DT == BL_F32 && KC > 2) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 2>(a, stream);
+  else launch_rows_rpw<DT, OUT, GLU, KC, 2 * kRowsNW, 1>(a, stream);
 }
 
 // row mode: K <= 4096 (decode_rows_fits)

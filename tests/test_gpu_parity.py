@@ -181,7 +181,7 @@ def test_grouped_matches_single_calls():
     # M = 1, the row mode (4 and 8 waves) for 2 <= M <= 8 up to K = 4096
     shapes = [(1, 1024, 1024), (1, 2048, 1024), (3, 96, 384), (2, 64, 7040), (4, 160, 1280),
               (0, 64, 256)] + [(6, 256, 2048)] * 3 + [(3, 96, 1024)] * 3 + [(8, 64, 4096)] * 2 \
-        + [(12, 96, 1024)] * 3
+        + [(12, 96, 1024)] * 3 + [(14, 64, 2048)] * 3
     items, singles = [], []
     for i, (M, N, K) in enumerate(shapes):
         x = synth.make_x(900 + i, 0, 0, M, K, "bf16").to(DEV)
