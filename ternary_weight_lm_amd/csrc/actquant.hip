@@ -9,9 +9,11 @@
 // with 16-byte loads (widened and kept in registers up to K = 6144, kept raw
 // up to K = 8192, re-read from cache beyond), the three reductions are
 // cross-lane shuffles, and the int8 codes leave as coalesced 8-byte stores.
-// Four rows per 256-thread workgroup, no barriers; the grouped kernel takes
-// up to three projections' rows in one launch.  HBM traffic: one read of x,
-// one write of xq, 8 bytes of scale + row sum.
+// Four rows per 256-thread workgroup, no barriers.  Few rows, or rows past
+// K = 4096, instead get a workgroup each, split over its four waves with
+// the same association of every sum (act_quant_split_row).  The grouped
+// kernels take up to three projections' rows in one launch.  HBM traffic:
+// one read of x, one write of xq, 8 bytes of scale + row sum.
 #include "bl_launch.h"
 #include "rowquant.h"
 
@@ -60,9 +62,123 @@ __global__ __launch_bounds__(256) void act_quant_group_kernel(int64_t M, int K, 
   act_quant_row<DT, MODE, NC>(c.x, c.gain, row, K, eps, c.xq, c.s, c.rowsum);
 }
 
+// ---- few rows: one row per workgroup, split over its 4 waves.  A wave
+// per row leaves a long row's passes (K = 5632: 11 chunks of 8 per lane)
+// in one wave's instruction stream while most CUs idle; here wave w takes
+// the chunk rounds c = w + 4 r of the row quantizer's layout (lane L: the 8
+// elements 8 L + 512 c), which are exactly its slot group w of the sum of
+// squares.  The four per-lane partials meet in LDS and are combined as
+// (p0 + p1) + (p2 + p3) before the same DPP tree, so the sum -- and every
+// code and scale -- is bit-identical to the one-wave kernel's; the absmax
+// and the row sum are exact in any order.  NR: chunk rounds per wave
+// (K <= 2048 NR).
+template <int DT, int NR>
+__device__ __forceinline__ void act_quant_split_row(
+    const void *__restrict__ x, const void *__restrict__ gain, int64_t row, int K, float eps,
+    int8_t *__restrict__ xq, float *__restrict__ s_out, int32_t *__restrict__ rowsum_out) {
+  __shared__ double part_ss[4][64];
+  __shared__ float part_max[4];
+  __shared__ int part_rs[4];
+  constexpr int EB = dtype_bytes(DT);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = (K + 511) >> 9;
+  const auto kof = [&](int r) { return 8 * lane + 512 * (w + 4 * r); };
+  const auto live = [&](int r) { return w + 4 * r < nch && kof(r) < K; };
+  const rsrc_t xr = make_rsrc(reinterpret_cast<const char *>(x) + row * K * EB, (uint32_t)(K * EB));
+  const rsrc_t gr = make_rsrc(gain, (uint32_t)(K * EB));
+  Chunk8<DT> xraw[NR], graw[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) xraw[r] = bload_chunk<DT>(xr, live(r) ? (uint32_t)(kof(r) * EB) : kOob);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) graw[r] = bload_chunk<DT>(gr, live(r) ? (uint32_t)(kof(r) * EB) : kOob);
+  float v[NR][8];
+  double ss = 0.0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (live(r)) {
+      widen<DT>(xraw[r], v[r]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)v[r][e], (double)v[r][e], ss);
+    }
+  part_ss[w][lane] = ss;
+  __syncthreads();
+  const float rr = rms_inv(wave_sum((part_ss[0][lane] + part_ss[1][lane]) +
+                                    (part_ss[2][lane] + part_ss[3][lane])),
+                           K, eps);
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (live(r)) {
+      float g[8];
+      widen<DT>(graw[r], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[r][e] = (v[r][e] * rr) * g[e];
+        amax = fmaxf(amax, fabsf(v[r][e]));
+      }
+    }
+  amax = wave_max(amax);
+  if (lane == 0) part_max[w] = amax;
+  __syncthreads();
+  const float sc = act_scale(fmaxf(fmaxf(part_max[0], part_max[1]), fmaxf(part_max[2], part_max[3])));
+  int8_t *qr = xq + row * K;
+  int rs = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (live(r)) {
+      int q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = quant8(v[r][e], sc);
+      const uint2 codes = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      rs = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs, false);
+      rs = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs, false);
+      *reinterpret_cast<uint2 *>(qr + kof(r)) = codes;
+    }
+  rs = wave_sum(rs);
+  if (lane == 0) part_rs[w] = rs;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_out[row] = sc;
+    rowsum_out[row] = (part_rs[0] + part_rs[1]) + (part_rs[2] + part_rs[3]);
+  }
+}
+
+template <int DT, int NR>
+__global__ __launch_bounds__(256) void act_quant_split_kernel(
+    const void *__restrict__ x, const void *__restrict__ gain, int K, float eps,
+    int8_t *__restrict__ xq, float *__restrict__ s_out, int32_t *__restrict__ rowsum_out) {
+  act_quant_split_row<DT, NR>(x, gain, blockIdx.x, K, eps, xq, s_out, rowsum_out);
+}
+
+template <int DT, int NR>
+__global__ __launch_bounds__(256) void act_quant_split_group_kernel(int K, float eps, AqCalls calls) {
+  const AqCall &c = calls.c[blockIdx.y];
+  act_quant_split_row<DT, NR>(c.x, c.gain, blockIdx.x, K, eps, c.xq, c.s, c.rowsum);
+}
+
+// Rows the split kernel takes: K <= 8192 (at most 4 chunk rounds per wave)
+// and either few rows (one wave per row leaves CUs idle: M = 64, K = 7040
+// 9.2 -> 3.6 us; M = 512, K = 2560 4.1 -> 3.5 us) or rows past K = 4096,
+// whose one-wave passes keep raw chunks (M = 8192, K = 7040: 45 -> 33 us).
+// Many short rows stay one per wave (M = 4096, K = 2048: 7.4 us, split 10).
+constexpr bool split_fits(int64_t M, int64_t K) { return K <= 8192 && (M <= 1024 || K > 4096); }
+constexpr int split_nr(int64_t K) { return (int)((((K + 511) >> 9) + 3) >> 2); }
+
 template <int DT>
 static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, float eps,
                       int8_t *xq, float *s, int32_t *rowsum, hipStream_t stream) {
+  if (split_fits(M, K)) {
+#define BL_AQS(NR) act_quant_split_kernel<DT, NR><<<(unsigned)M, 256, 0, stream>>>(x, gain, (int)K, eps, xq, s, rowsum)
+    switch (split_nr(K)) {
+      case 1: BL_AQS(1); break;
+      case 2: BL_AQS(2); break;
+      case 3: BL_AQS(3); break;
+      default: BL_AQS(4); break;
+    }
+#undef BL_AQS
+    return;
+  }
   const unsigned blocks = (unsigned)((M + 3) / 4);
 #define BL_AQ(MODE, NC) \
   act_quant_kernel<DT, MODE, NC><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum)
@@ -84,6 +200,18 @@ static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, flo
 template <int DT>
 static void launch_group_dt(const AqCalls &calls, int ncalls, int64_t M, int64_t K, float eps,
                             hipStream_t stream) {
+  if (split_fits(M, K)) {
+    const dim3 g((unsigned)M, (unsigned)ncalls);
+#define BL_AQSG(NR) act_quant_split_group_kernel<DT, NR><<<g, 256, 0, stream>>>((int)K, eps, calls)
+    switch (split_nr(K)) {
+      case 1: BL_AQSG(1); break;
+      case 2: BL_AQSG(2); break;
+      case 3: BL_AQSG(3); break;
+      default: BL_AQSG(4); break;
+    }
+#undef BL_AQSG
+    return;
+  }
   const dim3 grid((unsigned)((M + 3) / 4), (unsigned)ncalls);
 #define BL_AQG(MODE, NC) \
   act_quant_group_kernel<DT, MODE, NC><<<grid, 256, 0, stream>>>(M, (int)K, eps, calls)

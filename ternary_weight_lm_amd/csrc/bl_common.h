@@ -73,6 +73,8 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer over `bytes` bytes at base: offsets at or past `bytes` read as
 // zero (and touch no memory).
+constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);

@@ -46,7 +46,6 @@
 
 namespace bl {
 
-constexpr uint32_t kOob = 0x40000000u;  // a buffer offset past every range
 
 // K capacity of a kernel instance in units of 1024: the smallest of 1, 2, 3,
 // 4, 6, 8 with 1024 * KC >= K.  A wave's share of a row follows from it.
