@@ -6,8 +6,8 @@
 // "HGRNBit: was in einem Block tatsächlich passiert"; datacamp "MatMul-freie
 // LLMs: Zentrale Konzepte erklärt", figure panel 5).  One 64-lane wave per
 // token row runs the shared row quantizer (rowquant.h): the row is read once
-// with 16-byte loads (widened and kept in registers up to K = 6144, kept raw
-// up to K = 8192, re-read from cache beyond), the three reductions are
+// with 16-byte loads (widened and kept in registers up to K = 4096, re-read
+// from cache per pass beyond K = 8192), the three reductions are
 // cross-lane shuffles, and the int8 codes leave as coalesced 8-byte stores.
 // Four rows per 256-thread workgroup, no barriers.  Few rows, or rows past
 // K = 4096, instead get a workgroup each, split over its four waves with
@@ -19,11 +19,6 @@
 
 namespace bl {
 
-// Chunks cached per lane when the row fits the float mode (the widened row
-// in registers): 2, 4, 6, 8 or 12 rounds of 512 elements, so K <= 6144
-// (one wave per row can afford 12: the act-quant kernel holds nothing
-// else); 0 beyond that (raw / reload modes).
-constexpr int aq_float_nc(int64_t K) { return K <= 4096 ? row_cache((int)K) : (K <= 6144 ? 12 : 0); }
 
 template <int DT, int MODE, int NC>
 __device__ __forceinline__ void act_quant_row(
@@ -179,20 +174,20 @@ static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, flo
 #undef BL_AQS
     return;
   }
+  // many rows of K <= 4096, or K > 8192 (re-read per pass)
   const unsigned blocks = (unsigned)((M + 3) / 4);
 #define BL_AQ(MODE, NC) \
   act_quant_kernel<DT, MODE, NC><<<blocks, 256, 0, stream>>>(x, gain, M, (int)K, eps, xq, s, rowsum)
   // the float mode issues only the chunk loads a row of K needs
-  switch (aq_float_nc(K)) {
-    case 2: BL_AQ(kRowFloat, 2); break;
-    case 4: BL_AQ(kRowFloat, 4); break;
-    case 6: BL_AQ(kRowFloat, 6); break;
-    case 8: BL_AQ(kRowFloat, 8); break;
-    case 12: BL_AQ(kRowFloat, 12); break;
-    default:
-      if (row_mode((int)K) == kRowRaw) BL_AQ(kRowRaw, kRowCache);
-      else BL_AQ(kRowReload, kRowCache);
-      break;
+  if (K > 4096) {
+    BL_AQ(kRowReload, kRowCache);
+  } else {
+    switch (row_cache((int)K)) {
+      case 2: BL_AQ(kRowFloat, 2); break;
+      case 4: BL_AQ(kRowFloat, 4); break;
+      case 6: BL_AQ(kRowFloat, 6); break;
+      default: BL_AQ(kRowFloat, 8); break;
+    }
   }
 #undef BL_AQ
 }
@@ -215,16 +210,15 @@ static void launch_group_dt(const AqCalls &calls, int ncalls, int64_t M, int64_t
   const dim3 grid((unsigned)((M + 3) / 4), (unsigned)ncalls);
 #define BL_AQG(MODE, NC) \
   act_quant_group_kernel<DT, MODE, NC><<<grid, 256, 0, stream>>>(M, (int)K, eps, calls)
-  switch (aq_float_nc(K)) {
-    case 2: BL_AQG(kRowFloat, 2); break;
-    case 4: BL_AQG(kRowFloat, 4); break;
-    case 6: BL_AQG(kRowFloat, 6); break;
-    case 8: BL_AQG(kRowFloat, 8); break;
-    case 12: BL_AQG(kRowFloat, 12); break;
-    default:
-      if (row_mode((int)K) == kRowRaw) BL_AQG(kRowRaw, kRowCache);
-      else BL_AQG(kRowReload, kRowCache);
-      break;
+  if (K > 4096) {
+    BL_AQG(kRowReload, kRowCache);
+  } else {
+    switch (row_cache((int)K)) {
+      case 2: BL_AQG(kRowFloat, 2); break;
+      case 4: BL_AQG(kRowFloat, 4); break;
+      case 6: BL_AQG(kRowFloat, 6); break;
+      default: BL_AQG(kRowFloat, 8); break;
+    }
   }
 #undef BL_AQG
 }

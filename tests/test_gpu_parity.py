@@ -56,10 +56,12 @@ def test_pack_exact_ties_and_extremes():
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
-# K spans every register-cache instance of the kernel: 2, 4, 6, 8, 12 chunks per lane,
-# the raw mode (K <= 8192) and the reload mode (K > 8192)
+# M <= 1024 or 4096 < K <= 8192: the split kernel, every chunk-round capacity (1..4 rounds per
+# wave); M > 1024 with K <= 4096: one wave per row, every register-cache instance (2, 4, 6, 8
+# chunks per lane); K > 8192: one wave per row re-reading the row per pass
 @pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (33, 1280), (64, 2048), (6, 3072), (9, 4096),
-                                 (7, 4224), (12, 5632), (5, 6144), (7, 7040), (3, 9216)])
+                                 (7, 4224), (12, 5632), (5, 6144), (7, 7040), (1030, 8192),
+                                 (3, 9216), (1100, 1024), (1027, 2048), (1025, 2944), (1029, 4096)])
 def test_act_quant(dtype, M, K):
     say(f"act_quant {dtype} M={M} K={K}")
     x = synth.make_x(7, 0, 0, M, K, dtype, outlier_p=0.01)
@@ -73,6 +75,22 @@ def test_act_quant(dtype, M, K):
     ref = {"xq": oq, "s": os_, "v": ov}
     check_xq(xq, s, ref)
     np.testing.assert_array_equal(rs, xq.astype(np.int64).sum(1))
+
+
+@pytest.mark.parametrize("K", [1024, 2048, 3072, 4096])
+def test_act_quant_kernels_agree(K):
+    """The same rows through both act-quant kernels -- 1100 rows take one wave
+    per row, their first 1000 one workgroup per row split over four waves --
+    give the same codes, scales and row sums, bit for bit (both keep the
+    fixed association of the sum of squares)."""
+    say(f"act_quant one-wave vs split K={K}")
+    x = synth.make_x(21, 0, 0, 1100, K, "bf16", outlier_p=0.01).to(DEV)
+    g = synth.make_gain(21, 0, 0, K, "bf16").to(DEV)
+    xq1, s1, rs1 = gpu_act_quant(x, g)
+    xq2, s2, rs2 = gpu_act_quant(x[:1000].contiguous(), g)
+    np.testing.assert_array_equal(xq1[:1000], xq2)
+    np.testing.assert_array_equal(s1[:1000].view(np.uint32), s2.view(np.uint32))
+    np.testing.assert_array_equal(rs1[:1000], rs2)
 
 
 def _random_codes(M, K, seed):
