@@ -60,10 +60,10 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "f04bea17cb5cf105", 664125),
-    "c3": ("skinny", "ff283e13768eea3d", 3129942),
-    "c4": ("gemm", "8c7ffcb3155eee12", 85890399),
-    "c5-M1": ("decode", "f04bea17cb5cf105", 5279002),
+    "c2": ("decode", "034b2927e1318052", 656004),
+    "c3": ("skinny", "9499134eac5521a3", 3129943),
+    "c4": ("gemm", "53fde9a7ac417c10", 85885377),
+    "c5-M1": ("decode", "034b2927e1318052", 5279000),
 }
 
 
