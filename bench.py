@@ -168,6 +168,17 @@ class Workload:
         p = self.cfg.projs[call[1]]
         return p.K, p.N
 
+    def xkey(self, call):
+        """The activation tensor a call reads: one per (layer, input), where
+        i/f/g share their block input (synth.SHARED_INPUT) and the 2.7B
+        stack reuses one per projection type across layers."""
+        from ternary_weight_lm_amd import synth
+        layer, pi = call
+        names = [q.name for q in self.cfg.projs]
+        if names[pi] in synth.SHARED_INPUT:
+            pi = names.index(synth.SHARED_INPUT[0])
+        return (0 if self.layers > 1 else layer, pi)
+
     def describe(self):
         projs = [f"{p.name} {p.K}->{p.N}" for p in self.cfg.projs]
         return {"workload": self.cfg.name + ("" if not self.key.startswith("c5") else f"_M{self.M}"),
@@ -188,7 +199,7 @@ def build_inputs(wl: Workload, pool_bytes: int, dev):
     for call in wl.calls:
         layer, pi = call
         x, g, W = synth.config_inputs(cfg, M, layer, pi)
-        key = (0 if wl.layers > 1 else layer, pi)
+        key = wl.xkey(call)
         if key not in xs:
             xs[key] = x.to(dev)
         gs[call] = g.to(dev)
@@ -216,7 +227,7 @@ def build_inputs(wl: Workload, pool_bytes: int, dev):
     gws_bytes = 0
     for grp in groups:
         if len(grp) > 1:
-            items = [(xs[(0 if wl.layers > 1 else wl.calls[j][0], wl.calls[j][1])],
+            items = [(xs[wl.xkey(wl.calls[j])],
                       gs[wl.calls[j]], pool[0][j], betas[j], ys[j]) for j in grp]
             gws_bytes = max(gws_bytes, tw.bitlinear_grouped_workspace_bytes(
                 items, synth.DTYPES[cfg.dtype]))
@@ -237,7 +248,7 @@ def step_fn(wl, inp, s, keep):
             items = []
             for j in grp:
                 call = wl.calls[j]
-                x = inp["xs"][(0 if wl.layers > 1 else call[0], call[1])]
+                x = inp["xs"][wl.xkey(call)]
                 items.append((x, inp["gs"][call], pool[j], inp["betas"][j], inp["ys"][j]))
             arr = tw.make_calls(items)
             keep.append(arr)
@@ -252,7 +263,7 @@ def step_fn(wl, inp, s, keep):
         j = grp[0]
         call = wl.calls[j]
         K, N = wl.shape(call)
-        x = inp["xs"][(0 if wl.layers > 1 else call[0], call[1])]
+        x = inp["xs"][wl.xkey(call)]
         tw.bitlinear_forward(x, inp["gs"][call], pool[j], inp["betas"][j], N, inp["ys"][j],
                              inp["wss"][j])
 
@@ -330,13 +341,13 @@ def roofline(wl, inp, reps):
         for j in sel:
             call = wl.calls[j]
             K, N = wl.shape(call)
-            xkey = (0 if wl.layers > 1 else call[0], call[1])
-            if xkey not in stage:
+            # per call: calls that share x still quantize it with their own gain
+            if j not in stage:
                 xq = torch.empty(wl.M, K, dtype=torch.int8, device="cuda")
                 sc = torch.empty(wl.M, dtype=torch.float32, device="cuda")
                 rs = torch.empty(wl.M, dtype=torch.int32, device="cuda")
-                tw.bitlinear_act_quant(inp["xs"][xkey], inp["gs"][call], xq, sc, rs)
-                stage[xkey] = (xq, sc, rs)
+                tw.bitlinear_act_quant(inp["xs"][wl.xkey(call)], inp["gs"][call], xq, sc, rs)
+                stage[j] = (xq, sc, rs)
 
     # the step's launch groups restricted to the dominant path: grouped i/f/g
     # calls are one grouped launch (decode kernel, resp. contraction), as in
@@ -361,17 +372,17 @@ def roofline(wl, inp, reps):
             call = wl.calls[j]
             K, N = wl.shape(call)
             pk = inp["pool"][(s + 7) % inp["copies"]][j]
-            xkey = (0 if wl.layers > 1 else call[0], call[1])
+            xkey = wl.xkey(call)
             if path == tw.BL_PATH_FUSED and len(unit) == 1:
                 tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j],
                                           N, inp["ys"][j], inp["wss"][j], path)
             elif path == tw.BL_PATH_FUSED:
                 items.append((inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j], inp["ys"][j]))
             elif len(unit) == 1:
-                xq, sc, rs = stage[xkey]
+                xq, sc, rs = stage[j]
                 tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
             else:
-                xq, sc, rs = stage[xkey]
+                xq, sc, rs = stage[j]
                 items.append((xq, sc, rs, pk, inp["betas"][j], inp["ys"][j]))
         if items and path == tw.BL_PATH_FUSED:
             arr = tw.make_calls(items)

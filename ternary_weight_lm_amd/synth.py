@@ -127,14 +127,24 @@ CONFIGS = {
 }
 
 
+# projections that read one block input (the first one names its seed)
+SHARED_INPUT = ("i_proj", "f_proj", "g_proj")
+
+
 def config_inputs(cfg: Config, M: int, layer: int, proj_index: int):
     """x, gain, W (torch CPU tensors) for one projection call of a config.
 
-    In the 2.7B stack one activation tensor per (projection type, M) is
-    reused across layers; weights differ per layer."""
+    i_proj, f_proj and g_proj read the same block input (HGRNBit's token
+    mixer applies the three to one hidden state), so their x is drawn once,
+    under i_proj's index; each keeps its own gain and weights.  In the 2.7B
+    stack one activation tensor per (projection type, M) is reused across
+    layers; weights differ per layer."""
     p = cfg.projs[proj_index]
     x_layer = 0 if cfg.layers > 1 else layer
-    x = make_x(cfg.seed, x_layer, proj_index, M, p.K, cfg.dtype,
+    x_index = proj_index
+    if p.name in SHARED_INPUT:
+        x_index = next(i for i, q in enumerate(cfg.projs) if q.name == SHARED_INPUT[0])
+    x = make_x(cfg.seed, x_layer, x_index, M, p.K, cfg.dtype,
                outlier_p=cfg.outlier_p)
     g = make_gain(cfg.seed, layer, proj_index, p.K, cfg.dtype, kind=cfg.gain)
     W = make_w(cfg.seed, layer, proj_index, p.N, p.K,

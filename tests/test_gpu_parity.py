@@ -221,6 +221,36 @@ def test_grouped_matches_single_calls():
         assert torch.equal(it[4], singles[0])
 
 
+@pytest.mark.parametrize("xdt", ["fp16", "bf16", "fp32"])
+def test_grouped_shared_input(xdt):
+    """Grouped calls that read one activation tensor (HGRN's i/f/g, as the
+    benchmark runs them) and calls whose third x is a copy: every output
+    equals its single call bit for bit, for split-mode triples (M = 1, 4 and
+    8 waves), a split-mode pair, and row-mode triples (8 and 16 waves)."""
+    say(f"grouped shared x {xdt}")
+    runs = [(1, 96, 1024, 3), (1, 64, 2560, 3), (1, 160, 1024, 2), (2, 64, 2048, 3),
+            (3, 96, 1024, 3), (6, 64, 2048, 3), (14, 64, 1024, 3)]
+    if xdt == "fp32":  # fp32 rows: split mode one row at a time, row mode to 8 rows
+        runs = [r for r in runs if r[0] <= 8]
+    ydt = "fp32" if xdt == "fp32" else xdt
+    for r, (M, N, K, n) in enumerate(runs):
+        x = synth.make_x(700 + r, 0, 0, M, K, xdt).to(DEV)
+        for shared in (True, False):
+            items, singles = [], []
+            for i in range(n):
+                xi = x if shared or i < n - 1 else x.clone()
+                g = synth.make_gain(700 + r, 0, i, K, xdt).to(DEV)
+                packed, beta = tw.pack(synth.make_w(700 + r, 0, i, N, K).to(DEV))
+                y = torch.full((M, N), 7.0, dtype=synth.DTYPES[ydt], device=DEV)
+                items.append((xi, g, packed, beta, y))
+                singles.append(tw.forward(xi, g, packed, beta, N, path=tw.BL_PATH_FUSED,
+                                          out_dtype=synth.DTYPES[ydt]))
+            tw.bitlinear_forward_grouped(items, synth.DTYPES[xdt], synth.DTYPES[ydt])
+            torch.cuda.synchronize()
+            for (_, _, _, _, y), ref in zip(items, singles):
+                assert torch.equal(y, ref), (M, N, K, n, shared)
+
+
 @pytest.mark.parametrize("case", ["mixed", "prefill_1p3b"])
 def test_grouped_ws_matches_single_calls(case):
     """bitlinear_forward_grouped_ws gives bitlinear_forward's result on every
