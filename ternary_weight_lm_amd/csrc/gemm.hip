@@ -43,10 +43,10 @@ namespace bl {
 // Loads are buffer loads: a per-lane offset fixed for the whole loop plus a
 // k-block offset in a scalar register, so no vector address arithmetic runs
 // per k-block; rows and tiles past the matrix read as zero.
-template <int MI>
+template <int MI, int TPW>
 __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, uint8_t *next,
-                                            v4i (&acc)[MI][4], v4i (&a_store)[MI],
-                                            v4i (&a_load)[MI], v4i &b0, v4i &b1,
+                                            v4i (&acc)[MI][2 * TPW], v4i (&a_store)[MI],
+                                            v4i (&a_load)[MI], v4i (&b)[TPW],
                                             rsrc_t ars, const int (&a_voff)[MI],
                                             const int (&a_dst)[MI], rsrc_t brs, int b_voff,
                                             int b_tile_bytes, int arow0, int lane) {
@@ -80,28 +80,29 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
   // exposes the LDS latency 2*MI/2 times per k-block
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    // word (h, s2) of a lane slot sits at dword 2h + s2
-    const v4i w00 = unpack_codes(s2 ? b0.y : b0.x);
-    const v4i w01 = unpack_codes(s2 ? b0.w : b0.z);
-    const v4i w10 = unpack_codes(s2 ? b1.y : b1.x);
-    const v4i w11 = unpack_codes(s2 ? b1.w : b1.z);
+  for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      acc[mi][0] = mfma16x16x64(a[mi][s2], w00, acc[mi][0]);
-      acc[mi][1] = mfma16x16x64(a[mi][s2], w01, acc[mi][1]);
-      acc[mi][2] = mfma16x16x64(a[mi][s2], w10, acc[mi][2]);
-      acc[mi][3] = mfma16x16x64(a[mi][s2], w11, acc[mi][3]);
+    for (int t = 0; t < TPW; ++t) {
+      // word (h, s2) of a lane slot sits at dword 2h + s2: h = 0 is the
+      // tile's first 16 rows (block 2t), h = 1 its last 16 (block 2t + 1)
+      const v4i w0 = unpack_codes(s2 ? b[t].y : b[t].x);
+      const v4i w1 = unpack_codes(s2 ? b[t].w : b[t].z);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
+        acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
+      }
     }
-  }
   __builtin_amdgcn_sched_barrier(0);
-  b0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, k2 * 1024, 0));
-  b1 = __builtin_bit_cast(
-      v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + b_tile_bytes, k2 * 1024, 0));
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    b[t] = __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * b_tile_bytes, k2 * 1024, 0));
   __syncthreads();
 }
 
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
+constexpr int64_t kWideTiles = 1024;  // 128 x 256 tiles from which a launch takes them
 
 // Tile t of the XCD-aware order for workgroup `bid` of a launch of `ntiles`
 // tiles: workgroup ids reach the 8 XCDs round-robin, so XCD x gets the
@@ -116,14 +117,14 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 // contraction's tiles; work: tiles x k-blocks of the whole launch (picks the
 // epilogue).  GLU: the packed rows are a gate_proj in GLU order (each 32-row
 // tile = 16 gated rows + the 16 rows they multiply) and out is h [M, N/2].
-template <int MI, int OUT, bool GLU>
+template <int MI, int OUT, bool GLU, int TPW>
 __device__ __forceinline__ void gemm_body(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
     void *__restrict__ out, int tiles_m, int tiles_n, int t, int work) {
   constexpr int BM = 32 * MI;
-  constexpr int BN = 128;
+  constexpr int BN = 64 * TPW;  // a wave: 16 MI rows x 32 TPW outputs (TPW packed tiles)
   __shared__ __align__(16) uint8_t lds[2][BM * 128];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -156,28 +157,28 @@ __device__ __forceinline__ void gemm_body(
   }
   // ---- B: the wave's two packed 32-row tiles (tiles past N read as zero:
   // their columns are never stored).
-  const int nt0 = (n0 >> 5) + 2 * wn;
+  const int nt0 = (n0 >> 5) + TPW * wn;
   const int tile_bytes = KB * 1024;
   // (readfirstlane: tell the compiler these are wave-uniform, so the buffer
   // descriptor lives in scalar registers)
   const int b_first = __builtin_amdgcn_readfirstlane(min(nt0, NT));
-  const int b_bytes = __builtin_amdgcn_readfirstlane(max(0, min(2, NT - nt0)) * tile_bytes);
+  const int b_bytes = __builtin_amdgcn_readfirstlane(max(0, min(TPW, NT - nt0)) * tile_bytes);
   const rsrc_t brs = make_rsrc(packed + (int64_t)b_first * KB * 64, (uint32_t)b_bytes);
   const int b_voff = lane * 16;
 
-  v4i acc[MI][4];
+  v4i acc[MI][2 * TPW];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
 
   // Prefetch distance 2: the A chunks and B tiles of k-block kb+2 are
   // requested while k-block kb is multiplied, so each load has about two
   // iterations of MFMA work to arrive; A goes through a double-buffered LDS
   // stage one iteration before use.  (Native int vectors, not uint4: struct
   // copies are lowered to memcpy through private memory.)
-  v4i P[MI], Q[MI];   // A staging sets
-  v4i X0, X1, Y0, Y1; // B of even / odd k-blocks
+  v4i P[MI], Q[MI];     // A staging sets
+  v4i X[TPW], Y[TPW];   // B of even / odd k-blocks
   {
     const int k1 = min(1, KB - 1);
 #pragma unroll
@@ -186,10 +187,14 @@ __device__ __forceinline__ void gemm_body(
 #pragma unroll
     for (int j = 0; j < MI; ++j)
       P[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k1 * 128, 0));
-    X0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, 0, 0));
-    X1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + tile_bytes, 0, 0));
-    Y0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff, k1 * 1024, 0));
-    Y1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + tile_bytes, k1 * 1024, 0));
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      X[t] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, 0, 0));
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      Y[t] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k1 * 1024, 0));
 #pragma unroll
     for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(&lds[0][a_dst[j]]) = Q[j];
   }
@@ -200,14 +205,14 @@ __device__ __forceinline__ void gemm_body(
   // let the compiler sink the first half's prefetch loads into it.
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
-    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, ars, a_voff, a_dst, brs, b_voff,
-                    tile_bytes, arow0, lane);
-    gemm_kblock<MI>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y0, Y1, ars, a_voff, a_dst, brs,
-                    b_voff, tile_bytes, arow0, lane);
+    gemm_kblock<MI, TPW>(kb, KB, lds[0], lds[1], acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+                         tile_bytes, arow0, lane);
+    gemm_kblock<MI, TPW>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y, ars, a_voff, a_dst, brs,
+                         b_voff, tile_bytes, arow0, lane);
   }
   if (kb < KB)
-    gemm_kblock<MI>(kb, KB, lds[0], lds[1], acc, P, Q, X0, X1, ars, a_voff, a_dst, brs, b_voff,
-                    tile_bytes, arow0, lane);
+    gemm_kblock<MI, TPW>(kb, KB, lds[0], lds[1], acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+                         tile_bytes, arow0, lane);
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
   // row sums and rescale factors of the wave's 16*MI rows go through a small
@@ -224,7 +229,7 @@ __device__ __forceinline__ void gemm_body(
   }
   wave_lds_sync();
   const int q4 = 4 * (lane >> 4);
-  const int ncol0 = n0 + 64 * wn + (lane & 15);
+  const int ncol0 = n0 + 32 * TPW * wn + (lane & 15);
   v4i rs4[MI];
   float sc4[MI][4];
 #pragma unroll
@@ -244,7 +249,7 @@ __device__ __forceinline__ void gemm_body(
   if constexpr (GLU) {
     // tiles t0 and t0 + 1 of the wave: nb = 2p holds the gated rows of tile
     // t0 + p, nb = 2p + 1 the rows they multiply; output column 16 (t0 + p) + c
-    const int t0 = (n0 >> 5) + 2 * wn;
+    const int t0 = (n0 >> 5) + TPW * wn;
     const int64_t F = N >> 1;
     const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
@@ -254,7 +259,7 @@ __device__ __forceinline__ void gemm_body(
         const int m = wrow0 + 16 * mi + q4 + i;
         if (!full && m >= M) continue;
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
+        for (int pr = 0; pr < TPW; ++pr) {
           if (!full && 32 * (t0 + pr) >= N) continue;
           const float yg = (float)(acc[mi][2 * pr][i] - rs4[mi][i]) * sc4[mi][i];
           const float yu = (float)(acc[mi][2 * pr + 1][i] - rs4[mi][i]) * sc4[mi][i];
@@ -263,7 +268,7 @@ __device__ __forceinline__ void gemm_body(
       }
     return;
   }
-  if constexpr (OUT == BL_F16 || OUT == BL_BF16) {
+  if constexpr ((OUT == BL_F16 || OUT == BL_BF16) && TPW == 2) {
     // Whole tile of 2-byte outputs in a long launch: the wave's 16 MI x 64
     // block goes through the A buffers (idle since the barrier that ended
     // the last k-block), row-major with each row's 16-byte chunks XOR-
@@ -313,7 +318,7 @@ __device__ __forceinline__ void gemm_body(
       for (int i = 0; i < 4; ++i) {
         const int64_t rowbase = (int64_t)(wrow0 + 16 * mi + q4 + i) * N + ncol0;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) put(mi, i, nb, rowbase + 16 * nb);
+        for (int nb = 0; nb < 2 * TPW; ++nb) put(mi, i, nb, rowbase + 16 * nb);
       }
   } else {
 #pragma unroll
@@ -324,21 +329,21 @@ __device__ __forceinline__ void gemm_body(
         if (m >= M) continue;
         const int64_t rowbase = (int64_t)m * N + ncol0;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 2 * TPW; ++nb)
           if (ncol0 + 16 * nb < N) put(mi, i, nb, rowbase + 16 * nb);
       }
   }
 }
 
-template <int MI, int OUT, bool GLU>
-__global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
+template <int MI, int OUT, bool GLU, int TPW = 2>
+__global__ __launch_bounds__(256, TPW == 2 ? 3 : 2) void gemm_mfma_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
     void *__restrict__ out, int tiles_m, int tiles_n) {
   const int ntiles = tiles_m * tiles_n;
-  gemm_body<MI, OUT, GLU>(xq, rowsum, s, packed, beta, M, N, K, out, tiles_m, tiles_n,
-                          xcd_tile((int)blockIdx.x, ntiles), ntiles * (K >> 7));
+  gemm_body<MI, OUT, GLU, TPW>(xq, rowsum, s, packed, beta, M, N, K, out, tiles_m, tiles_n,
+                               xcd_tile((int)blockIdx.x, ntiles), ntiles * (K >> 7));
 }
 
 // Up to kGemmCalls contractions of one shape in one launch (HGRN's i/f/g at
@@ -346,31 +351,31 @@ __global__ __launch_bounds__(256, 3) void gemm_mfma_kernel(
 // launch of three one-round contractions runs as several rounds whose
 // epilogues overlap other tiles' main loops.  The pointers come from the
 // argument buffer.
-template <int MI, int OUT>
-__global__ __launch_bounds__(256, 3) void gemm_mfma_group_kernel(int ncalls, int M, int N, int K,
+template <int MI, int OUT, int TPW = 2>
+__global__ __launch_bounds__(256, TPW == 2 ? 3 : 2) void gemm_mfma_group_kernel(int ncalls, int M, int N, int K,
                                                                  int tiles_m, int tiles_n,
                                                                  GemmCalls calls) {
   const int ntiles = tiles_m * tiles_n;
   const int tg = xcd_tile((int)blockIdx.x, ncalls * ntiles);
   const int call = __builtin_amdgcn_readfirstlane(tg / ntiles);
   const GemmCall &c = calls.c[call];
-  gemm_body<MI, OUT, false>(c.xq, c.rowsum, c.s, reinterpret_cast<const uint4 *>(c.packed), c.beta,
+  gemm_body<MI, OUT, false, TPW>(c.xq, c.rowsum, c.s, reinterpret_cast<const uint4 *>(c.packed), c.beta,
                             M, N, K, c.out, tiles_m, tiles_n, tg - call * ntiles,
                             ncalls * ntiles * (K >> 7));
 }
 
-template <int MI>
+template <int MI, int TPW = 2>
 static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N, int64_t K,
                             void *out, int out_kind, bool glu, hipStream_t stream) {
-  const int BM = 32 * MI;
+  const int BM = 32 * MI, BN = 64 * TPW;
   const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + 127) / 128);
+  const int tiles_n = (int)((N + BN - 1) / BN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
   const uint4 *pk = reinterpret_cast<const uint4 *>(packed);
 #define BL_GEMM_CASE(KIND, G)                                                \
-  gemm_mfma_kernel<MI, KIND, G><<<grid, 256, 0, stream>>>(                   \
+  gemm_mfma_kernel<MI, KIND, G, TPW><<<grid, 256, 0, stream>>>(              \
       xq, rowsum, s, pk, beta, (int)M, (int)N, (int)K, out, tiles_m, tiles_n)
   if (glu) {
     switch (out_kind) {
@@ -401,6 +406,13 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   // (measured at M = 512: 32-row tiles beat 64-row ones up to 256 tiles).
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
+  // Wide launches: 128 x 256 tiles, a wave holding 4 packed tiles, so each
+  // A operand read from LDS feeds twice the MFMAs (2 waves per SIMD: 246
+  // VGPRs).  From 1024 such tiles (gate_proj at M = 4096: 87 -> 84 us, at
+  // M = 8192: 254 -> 238 us); with fewer, the tiles do not fill the rounds
+  // (2048-wide projections at M = 4096: 20.4 -> 22.7 us) and 128 x 128 stays.
+  if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) >= kWideTiles)
+    return launch_mi<4, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 64 && tiles(128) >= 256)
     return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 32 && tiles(64) >= 256)
@@ -408,15 +420,15 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
 }
 
-template <int MI>
+template <int MI, int TPW = 2>
 static hipError_t launch_group_mi(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
                                   int64_t K, int out_kind, hipStream_t stream) {
-  const int BM = 32 * MI;
+  const int BM = 32 * MI, BN = 64 * TPW;
   const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + 127) / 128);
+  const int tiles_n = (int)((N + BN - 1) / BN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * ncalls);
 #define BL_GEMMG_CASE(KIND)                                                     \
-  gemm_mfma_group_kernel<MI, KIND><<<grid, 256, 0, stream>>>(ncalls, (int)M, (int)N, (int)K, \
+  gemm_mfma_group_kernel<MI, KIND, TPW><<<grid, 256, 0, stream>>>(ncalls, (int)M, (int)N, (int)K, \
                                                              tiles_m, tiles_n, calls)
   switch (out_kind) {
     case BL_F32: BL_GEMMG_CASE(BL_F32); break;
@@ -432,6 +444,8 @@ hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M,
   // tile height as for one call, over the tiles of all the calls
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn * ncalls; };
+  if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) * ncalls >= kWideTiles)
+    return launch_group_mi<4, 4>(calls, ncalls, M, N, K, out_kind, stream);
   if (M > 64 && tiles(128) >= 256) return launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
   if (M > 32 && tiles(64) >= 256) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
   return launch_group_mi<1>(calls, ncalls, M, N, K, out_kind, stream);
