@@ -394,15 +394,17 @@ def test_gemm_i32_largest_k(path):
     np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
 
 
-@pytest.mark.parametrize("ydt", ["bf16", "fp16"])
-def test_long_launch_epilogue_bitwise(ydt):
-    """A launch long enough for the MFMA kernel to stage its output tiles
-    through LDS (2000 x 11264 x 2048: 1408 tiles of 16 k-blocks), with a
-    ragged last tile row that stores directly.  Every output element must
-    equal the exact int32 contraction rescaled by fl32(beta / s) in fp32 and
-    rounded to the output dtype -- the epilogue's arithmetic, done on the
-    host from the int32 result -- and sampled rows must match the oracle."""
-    M, N, K = 2000, 11264, 2048
+@pytest.mark.parametrize("ydt,M", [("bf16", 2000), ("fp16", 2000), ("bf16", 4000), ("fp16", 4000)])
+def test_long_launch_epilogue_bitwise(ydt, M):
+    """Long launches of the MFMA kernel: 2000 x 11264 x 2048 (1408 tiles of
+    128 x 128, 16 k-blocks each: output tiles staged through LDS) and 4000 x
+    11264 x 2048 (1408 tiles of 128 x 256, waves of 4 packed tiles, stored
+    directly), each with a ragged last tile row.  Every
+    output element must equal the exact int32 contraction rescaled by
+    fl32(beta / s) in fp32 and rounded to the output dtype -- the epilogue's
+    arithmetic, done on the host from the int32 result -- and sampled rows
+    must match the oracle."""
+    N, K = 11264, 2048
     say(f"long-launch epilogue M={M} N={N} K={K} y={ydt}")
     xq = _random_codes(M, K, 11)
     r = np.random.default_rng(12)
