@@ -62,7 +62,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "034b2927e1318052", 656004),
     "c3": ("skinny", "9499134eac5521a3", 3129943),
-    "c4": ("gemm", "53fde9a7ac417c10", 85885377),
+    "c4": ("gemm", "712a04b2006ac279", 87507246),
     "c5-M1": ("decode", "034b2927e1318052", 5279000),
 }
 

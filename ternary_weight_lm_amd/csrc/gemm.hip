@@ -102,7 +102,7 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
 }
 
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
-constexpr int64_t kWideTiles = 1024;  // 128 x 256 tiles from which a launch takes them
+constexpr int64_t kWideTiles = 768;  // 128 x 256 tiles from which a launch takes them
 
 // Tile t of the XCD-aware order for workgroup `bid` of a launch of `ntiles`
 // tiles: workgroup ids reach the 8 XCDs round-robin, so XCD x gets the
@@ -408,9 +408,11 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
   // Wide launches: 128 x 256 tiles, a wave holding 4 packed tiles, so each
   // A operand read from LDS feeds twice the MFMAs (2 waves per SIMD: 246
-  // VGPRs).  From 1024 such tiles (gate_proj at M = 4096: 87 -> 84 us, at
-  // M = 8192: 254 -> 238 us); with fewer, the tiles do not fill the rounds
-  // (2048-wide projections at M = 4096: 20.4 -> 22.7 us) and 128 x 128 stays.
+  // VGPRs).  From 768 such tiles (gate_proj at M = 4096: 87 -> 84 us, at
+  // M = 8192: 254 -> 238 us; i/f/g grouped at M = 4096: 51 -> 49 us); with
+  // fewer, the tiles do not fill the rounds (2048-wide projections at M =
+  // 4096: 20.4 -> 22.7 us, 2560-wide at M = 8192: 49 -> 52 us) and 128 x 128
+  // stays.
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) >= kWideTiles)
     return launch_mi<4, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 64 && tiles(128) >= 256)
