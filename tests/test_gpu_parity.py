@@ -107,7 +107,7 @@ def _random_codes(M, K, seed):
                                    (17, 160, 1280), (33, 1024, 1024), (130, 96, 640),
                                    (16, 64, 7040), (200, 256, 2048), (32, 96, 2560),
                                    (48, 64, 7040), (64, 160, 1280), (40, 64, 9216),
-                                   (5, 8192, 4224)])
+                                   (5, 8192, 4224), (20, 8224, 1024), (64, 8224, 2560)])
 def test_gemm_i32_bit_exact(path, M, N, K):
     if path == tw.BL_PATH_SKINNY and M > 64:
         pytest.skip("skinny path is for M <= 64")
