@@ -160,6 +160,47 @@ __global__ __launch_bounds__(256) void act_quant_split_group_kernel(int K, float
 constexpr bool split_fits(int64_t M, int64_t K) { return K <= 8192 && (M <= 1024 || K > 4096); }
 constexpr int split_nr(int64_t K) { return (int)((((K + 511) >> 9) + 3) >> 2); }
 
+// Many rows read by up to three projections (HGRN's i/f/g share their
+// block input): one wave per row loads the row once, computes its r once
+// (row_rms) and runs the gain-dependent passes per call (quantize_scaled),
+// with the bits of one call per launch.
+template <int DT, int NC>
+__global__ __launch_bounds__(256) void act_quant_shared_kernel(int64_t M, int K, float eps,
+                                                               int ncalls, AqCalls calls) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // a whole wave leaves; nothing below synchronizes
+  constexpr int EB = dtype_bytes(DT);
+  const int lane = threadIdx.x & 63;
+  const auto kof = [&](int c) { return 8 * lane + 512 * c; };
+  const rsrc_t xr = make_rsrc(static_cast<const char *>(calls.c[0].x) + row * K * EB,
+                              (uint32_t)(K * EB));
+  Chunk8<DT> xraw[NC], graw[kGroupCalls][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) xraw[c] = bload_chunk<DT>(xr, (uint32_t)(kof(c) * EB));
+#pragma unroll
+  for (int j = 0; j < kGroupCalls; ++j) {
+    const rsrc_t gr = make_rsrc(calls.c[j].gain, j < ncalls ? (uint32_t)(K * EB) : 0u);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) graw[j][c] = bload_chunk<DT>(gr, (uint32_t)(kof(c) * EB));
+  }
+  const float r = row_rms<DT, NC>(xraw, K, eps);
+#pragma unroll
+  for (int j = 0; j < kGroupCalls; ++j) {
+    if (j >= ncalls) break;
+    const AqCall &cj = calls.c[j];
+    int8_t *qr = cj.xq + row * K;
+    float sc;
+    int rs;
+    quantize_scaled<DT, NC>(xraw, graw[j], K, r,
+                            [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(qr + k) = codes; },
+                            sc, rs);
+    if (lane == 0) {
+      cj.s[row] = sc;
+      cj.rowsum[row] = rs;
+    }
+  }
+}
+
 template <int DT>
 static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, float eps,
                       int8_t *xq, float *s, int32_t *rowsum, hipStream_t stream) {
@@ -192,9 +233,28 @@ static void launch_dt(const void *x, const void *gain, int64_t M, int64_t K, flo
 #undef BL_AQ
 }
 
+// Below this many rows one wave per row per call fills the chip better
+// than one wave per row running every call.
+constexpr int64_t kSharedMinRows = 3072;
+
 template <int DT>
 static void launch_group_dt(const AqCalls &calls, int ncalls, int64_t M, int64_t K, float eps,
                             hipStream_t stream) {
+  bool shared = ncalls > 1;
+  for (int j = 1; j < ncalls; ++j) shared = shared && calls.c[j].x == calls.c[0].x;
+  if (shared && M >= kSharedMinRows && !split_fits(M, K) && K <= 4096) {
+    const unsigned blocks = (unsigned)((M + 3) / 4);
+#define BL_AQX(NC) \
+  act_quant_shared_kernel<DT, NC><<<blocks, 256, 0, stream>>>(M, (int)K, eps, ncalls, calls)
+    switch (row_cache((int)K)) {
+      case 2: BL_AQX(2); break;
+      case 4: BL_AQX(4); break;
+      case 6: BL_AQX(6); break;
+      default: BL_AQX(8); break;
+    }
+#undef BL_AQX
+    return;
+  }
   if (split_fits(M, K)) {
     const dim3 g((unsigned)M, (unsigned)ncalls);
 #define BL_AQSG(NR) act_quant_split_group_kernel<DT, NR><<<g, 256, 0, stream>>>((int)K, eps, calls)

@@ -64,6 +64,72 @@ __host__ __device__ constexpr int row_mode(int K) {
   return K <= 512 * kRowCache ? kRowFloat : (K <= 512 * kRowRawCache ? kRowRaw : kRowReload);
 }
 
+// Pass 1 of the float mode on a row already in registers (chunk c of the
+// lane: elements 8 lane + 512 c .. +7, c < NC, in xraw[c]; chunks past K read
+// as zero): r = 1 / sqrt(fp32(sum x^2 / K) + eps), the sum in the library's
+// association.
+template <int DT, int NC>
+__device__ __forceinline__ float row_rms(const Chunk8<DT> (&xraw)[NC], int K, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int nch = (K + 511) >> 9;  // chunk rounds (some lanes idle in the last)
+  double ss[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (c < nch && 8 * lane + 512 * c < K) {
+      float v[8];
+      widen<DT>(xraw[c], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss[c & 3] = __builtin_fma((double)v[e], (double)v[e], ss[c & 3]);
+    }
+  return rms_inv(group_sum(ss), K, eps);
+}
+
+// Passes 2 and 3 of the float mode for one gain (its matching chunks in
+// graw[c]) and the row's r: xn = (x r) g, s = 127 / max(max |xn|, 1e-5),
+// codes.  `sink(k, codes)` receives the 8 codes of elements k..k+7 as two
+// dwords; on return every lane holds s and the row sum.  row_rms followed by
+// quantize_scaled runs exactly the operations of quantize_loaded below (kept
+// separate for the kernels that quantize one row under several gains, so
+// the one-row kernels keep their register allocation); a test holds the two
+// to the same bits.
+template <int DT, int NC, class Sink>
+__device__ __forceinline__ void quantize_scaled(const Chunk8<DT> (&xraw)[NC],
+                                                const Chunk8<DT> (&graw)[NC], int K, float r,
+                                                Sink sink, float &s_out, int &rowsum_out) {
+  const int lane = threadIdx.x & 63;
+  const int nch = (K + 511) >> 9;
+  const auto kof = [&](int c) { return 8 * lane + 512 * c; };
+  float v[NC][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (c < nch && kof(c) < K) {
+      float g[8];
+      widen<DT>(xraw[c], v[c]);
+      widen<DT>(graw[c], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[c][e] = (v[c][e] * r) * g[e];
+        amax = fmaxf(amax, fabsf(v[c][e]));
+      }
+    }
+  const float sc = act_scale(wave_max(amax));
+  int rs = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (c < nch && kof(c) < K) {
+      int q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = quant8(v[c][e], sc);
+      const uint2 codes = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      rs = __builtin_amdgcn_sdot4((int)codes.x, 0x01010101, rs, false);
+      rs = __builtin_amdgcn_sdot4((int)codes.y, 0x01010101, rs, false);
+      sink(kof(c), codes);
+    }
+  s_out = sc;
+  rowsum_out = wave_sum(rs);
+}
+
 // The three passes of the float mode on a row already in registers: chunk
 // c of the lane (elements 8 lane + 512 c .. +7, c < NC) in xraw[c],
 // the gain's matching chunk in graw[c] (chunks past K read as zero).

@@ -251,24 +251,30 @@ def test_grouped_shared_input(xdt):
                 assert torch.equal(y, ref), (M, N, K, n, shared)
 
 
-@pytest.mark.parametrize("case", ["mixed", "prefill_1p3b"])
+@pytest.mark.parametrize("case", ["mixed", "prefill_1p3b", "prefill_shared_x"])
 def test_grouped_ws_matches_single_calls(case):
     """bitlinear_forward_grouped_ws gives bitlinear_forward's result on every
     call, bit for bit: runs of three same-shape MFMA-path calls sharing an
     act-quant and a GEMM launch (ragged M, partial output tiles, a run of
     four split 3 + 1), an MFMA call of another shape, a skinny-path call and
     calls the fused kernels take -- and, full size, the 1.3B i/f/g triple at
-    prefill."""
+    prefill, also with one x shared by the triple (one act-quant pass per row
+    for all three calls, which must still give each call's own bits)."""
+    shared = case == "prefill_shared_x"
     if case == "mixed":
         shapes = [(300, 384, 640)] * 4 + [(100, 96, 256), (20, 160, 512), (1, 64, 1024),
                                           (3, 96, 384), (0, 64, 256), (65, 160, 1280),
                                           (65, 160, 1280)] + [(40, 96, 512)] * 3
-    else:
+    elif case == "prefill_1p3b":
         shapes = [(4096, 2048, 2048)] * 3
+    else:
+        shapes = [(4096, 2048, 2048)] * 3 + [(3101, 384, 2944)] * 3
     say(f"grouped_ws {case}")
     items, singles = [], []
     for i, (M, N, K) in enumerate(shapes):
         x = synth.make_x(950 + i, 0, 0, M, K, "bf16").to(DEV)
+        if shared and i % 3:
+            x = items[i - 1][0]   # the same tensor as the run's first call
         g = synth.make_gain(950 + i, 0, 0, K, "bf16").to(DEV)
         packed, beta = tw.pack(synth.make_w(950 + i, 0, 0, N, K).to(DEV))
         y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
