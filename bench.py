@@ -60,10 +60,10 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "034b2927e1318052", 656004),
-    "c3": ("skinny", "9499134eac5521a3", 3129943),
-    "c4": ("gemm", "712a04b2006ac279", 87507246),
-    "c5-M1": ("decode", "034b2927e1318052", 5279000),
+    "c2": ("decode", "a0400cf502a0437a", 647830),
+    "c3": ("skinny", "dc7f9d5a0921c5cb", 3126358),
+    "c4": ("gemm", "83a3dee71bd062db", 87437350),
+    "c5-M1": ("decode", "a0400cf502a0437a", 5250590),
 }
 
 
