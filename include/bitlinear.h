@@ -208,6 +208,9 @@ int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
  * launch; on the MFMA path also one GEMM launch (three 2048-wide
  * projections of 4096 tokens fill the GPU for several rounds instead of one
  * each), on the skinny path (M <= 64) each keeps its contraction launch.
+ * When such a run's calls all pass the same x pointer and the rows are many
+ * (M >= 3072, K <= 4096), the shared act-quant reads each row once and
+ * quantizes it under every call's gain; the results are the same bits.
  *   calls    HOST array of ncalls descriptors (read during the call only);
  *            shapes, pointers and alignment as for bitlinear_forward, all
  *            sharing x_dtype, y_dtype and eps; calls with M == 0 skipped.
