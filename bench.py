@@ -62,7 +62,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "a0400cf502a0437a", 647830),
     "c3": ("skinny", "dc7f9d5a0921c5cb", 3126358),
-    "c4": ("gemm", "83a3dee71bd062db", 87437350),
+    "c4": ("gemm", "f09c37220f1bdc87", 87518951),
     "c5-M1": ("decode", "a0400cf502a0437a", 5250590),
 }
 

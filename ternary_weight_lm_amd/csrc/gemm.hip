@@ -395,6 +395,20 @@ static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
   return hipGetLastError();
 }
 
+// Tile height among 128 and 96 rows (32 MI, MI = 4 or 3) for a launch of
+// t128 resp. t96 tiles of either: the CUs take the tiles in turn, so the
+// busiest one runs ceil(tiles / 256) of them, and the height with fewer
+// rows on it wins.  96 rows win where 128-row tiles leave half the CUs a
+// tile short (M = 3072, N = 2048: 384 tiles of 128 rows against 512 of 96,
+// two per CU: 18.5 -> 16.1 us; M = 3000, K = 5632: 38.2 -> 33.8 us); a tie
+// keeps 128 rows, whose unpacked weight operands feed four MFMAs instead of
+// three (M = 4096, N = 2048: 512 tiles, two per CU, against 688 of 96 rows:
+// 20.6 vs 21.6 us).
+constexpr int64_t kCUs = 256;
+constexpr int tall_mi(int64_t t128, int64_t t96) {
+  return ((t96 + kCUs - 1) / kCUs) * 3 < ((t128 + kCUs - 1) / kCUs) * 4 ? 3 : 4;
+}
+
 hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N,
@@ -416,7 +430,9 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) >= kWideTiles)
     return launch_mi<4, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 64 && tiles(128) >= 256)
-    return launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+    return tall_mi(tiles(128), tiles(96)) == 3
+               ? launch_mi<3>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream)
+               : launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 32 && tiles(64) >= 256)
     return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
@@ -448,7 +464,10 @@ hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M,
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn * ncalls; };
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) * ncalls >= kWideTiles)
     return launch_group_mi<4, 4>(calls, ncalls, M, N, K, out_kind, stream);
-  if (M > 64 && tiles(128) >= 256) return launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
+  if (M > 64 && tiles(128) >= 256)
+    return tall_mi(tiles(128), tiles(96)) == 3
+               ? launch_group_mi<3>(calls, ncalls, M, N, K, out_kind, stream)
+               : launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
   if (M > 32 && tiles(64) >= 256) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
   return launch_group_mi<1>(calls, ncalls, M, N, K, out_kind, stream);
 }

@@ -107,7 +107,8 @@ def _random_codes(M, K, seed):
                                    (17, 160, 1280), (33, 1024, 1024), (130, 96, 640),
                                    (16, 64, 7040), (200, 256, 2048), (32, 96, 2560),
                                    (48, 64, 7040), (64, 160, 1280), (40, 64, 9216),
-                                   (5, 8192, 4224), (20, 8224, 1024), (64, 8224, 2560)])
+                                   (5, 8192, 4224), (20, 8224, 1024), (64, 8224, 2560),
+                                   (1100, 4096, 384)])   # 96-row tiles
 def test_gemm_i32_bit_exact(path, M, N, K):
     if path == tw.BL_PATH_SKINNY and M > 64:
         pytest.skip("skinny path is for M <= 64")
@@ -400,17 +401,19 @@ def test_gemm_i32_largest_k(path):
     np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
 
 
-@pytest.mark.parametrize("ydt,M", [("bf16", 2000), ("fp16", 2000), ("bf16", 4000), ("fp16", 4000)])
-def test_long_launch_epilogue_bitwise(ydt, M):
+@pytest.mark.parametrize("ydt,M,N,K", [("bf16", 2000, 11264, 2048), ("fp16", 2000, 11264, 2048),
+                                        ("bf16", 4000, 11264, 2048), ("fp16", 4000, 11264, 2048),
+                                        ("bf16", 3000, 2048, 5632), ("fp16", 3000, 2048, 2048)])
+def test_long_launch_epilogue_bitwise(ydt, M, N, K):
     """Long launches of the MFMA kernel: 2000 x 11264 x 2048 (1408 tiles of
-    128 x 128, 16 k-blocks each: output tiles staged through LDS) and 4000 x
+    128 x 128, 16 k-blocks each: output tiles staged through LDS), 4000 x
     11264 x 2048 (1408 tiles of 128 x 256, waves of 4 packed tiles, stored
-    directly), each with a ragged last tile row.  Every
+    directly) and 3000 x 2048 (512 tiles of 96 x 128; at K = 5632 staged,
+    at K = 2048 stored directly), each with a ragged last tile row.  Every
     output element must equal the exact int32 contraction rescaled by
     fl32(beta / s) in fp32 and rounded to the output dtype -- the epilogue's
     arithmetic, done on the host from the int32 result -- and sampled rows
     must match the oracle."""
-    N, K = 11264, 2048
     say(f"long-launch epilogue M={M} N={N} K={K} y={ydt}")
     xq = _random_codes(M, K, 11)
     r = np.random.default_rng(12)
