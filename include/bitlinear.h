@@ -98,7 +98,7 @@ enum {
     BL_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required  */
     BL_ERR_EPS = -6,         /* eps not finite or not > 0                   */
     BL_ERR_HIP = -7,         /* a HIP launch or query failed                */
-    BL_ERR_UNSUPPORTED = -8, /* valid request this build does not implement */
+    BL_ERR_UNSUPPORTED = -8, /* valid request the library does not implement */
     BL_ERR_PATH = -9         /* unknown execution path code                 */
 };
 
