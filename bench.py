@@ -67,6 +67,17 @@ TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
 }
 
 
+def launch_kinds(wl):
+    """What one launch group of the workload runs, from the paths its calls take."""
+    import ternary_weight_lm_amd as tw
+    fused = {tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) == tw.BL_PATH_FUSED for c in wl.calls}
+    if fused == {True}:
+        return "one fused decode launch per group"
+    if fused == {False}:
+        return "two-kernel paths: act-quant + contraction per group"
+    return "one fused decode launch per group where the row length allows, else act-quant + contraction"
+
+
 def sources_sha(family):
     import hashlib
     h = hashlib.sha256()
@@ -695,7 +706,7 @@ def main():
                        weight_copies=inp["copies"],
                        launch=f"hipGraph; {len(inp['groups'])} launch groups per step "
                               f"({'i/f/g grouped' if any(len(g) > 1 for g in inp['groups']) else 'one per projection'}; "
-                              "two-kernel paths: act-quant + contraction per group)",
+                              f"{launch_kinds(wl)})",
                        parallelism="single GPU"),
         "roofline": roof,
     }
