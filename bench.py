@@ -22,7 +22,9 @@ Method
     with events on the replay stream, bracketed by device synchronization.
   * Roofline of the dominant kernel: a second graph holding only that
     kernel's launches is timed the same way, giving its average duration
-    (this matches rocprofv3's per-kernel average); algorithmic bytes (packed
+    (rocprofv3's per-dispatch average reads higher, by about 10 % on the
+    long launches and up to a third on the 2-3 us decode launches: the
+    tracer stamps and signals each dispatch on its own); algorithmic bytes (packed
     weights + x + gain + y + beta) or ops (2 M N K) per launch over it give
     `achieved`.
   * cpu_baseline: the plain C oracle, single-threaded, on the same inputs,
