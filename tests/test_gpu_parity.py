@@ -257,15 +257,18 @@ def test_grouped_ws_matches_single_calls(case):
     """bitlinear_forward_grouped_ws gives bitlinear_forward's result on every
     call, bit for bit: runs of three same-shape MFMA-path calls sharing an
     act-quant and a GEMM launch (ragged M, partial output tiles, a run of
-    four split 3 + 1), an MFMA call of another shape, a skinny-path call and
-    calls the fused kernels take -- and, full size, the 1.3B i/f/g triple at
-    prefill, also with one x shared by the triple (one act-quant pass per row
-    for all three calls, which must still give each call's own bits)."""
+    four split 3 + 1), an MFMA call of another shape, a skinny-path call,
+    calls the fused kernels take and a triple whose grouped GEMM takes 96-row
+    tiles (single calls of that shape take 32-row ones) -- and, full size,
+    the 1.3B i/f/g triple at prefill, also with one x shared by the triple
+    (one act-quant pass per row for all three calls, which must still give
+    each call's own bits)."""
     shared = case == "prefill_shared_x"
     if case == "mixed":
         shapes = [(300, 384, 640)] * 4 + [(100, 96, 256), (20, 160, 512), (1, 64, 1024),
                                           (3, 96, 384), (0, 64, 256), (65, 160, 1280),
-                                          (65, 160, 1280)] + [(40, 96, 512)] * 3
+                                          (65, 160, 1280)] + [(40, 96, 512)] * 3 \
+            + [(1100, 1408, 1024)] * 3   # grouped GEMM in 96-row tiles
     elif case == "prefill_1p3b":
         shapes = [(4096, 2048, 2048)] * 3
     else:
