@@ -129,11 +129,13 @@ def test_glu_pairing_matches_unfused_projection():
 
 @pytest.mark.parametrize("M,F,K,path", [(4096, 5632, 2048, tw.BL_PATH_AUTO),
                                          (1, 7040, 2560, tw.BL_PATH_AUTO),
-                                         (64, 7040, 2560, tw.BL_PATH_AUTO)])
+                                         (64, 7040, 2560, tw.BL_PATH_AUTO),
+                                         (1100, 2048, 1024, tw.BL_PATH_AUTO)])
 def test_forward_glu_full_size_sampled(M, F, K, path):
     """The MLP gate of the 1.3B layer at prefill and the 2.7B one at decode,
-    full size, in the launch configuration the benchmark uses; every packed
-    byte is checked, h on sampled rows."""
+    full size, in the launch configuration the benchmark uses, and a gate
+    whose GEMM takes 96-row tiles (1100 x 4096 packed rows: 384 of them);
+    every packed byte is checked, h on sampled rows."""
     say(f"glu full size M={M} F={F} K={K}")
     x = synth.make_x(77, 0, 1, M, K, "bf16", outlier_p=0.01)
     g = synth.make_gain(77, 0, 1, K, "bf16")
