@@ -66,6 +66,7 @@ TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c3": ("skinny", "dc7f9d5a0921c5cb", 3126358),
     "c4": ("gemm", "f09c37220f1bdc87", 87518951),
     "c5-M1": ("decode", "a0400cf502a0437a", 5250590),
+    "c5-M8192": ("gemm", "f09c37220f1bdc87", 260669374),
 }
 
 
