@@ -63,7 +63,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "a0400cf502a0437a", 647830),
-    "c3": ("skinny", "dc7f9d5a0921c5cb", 3126358),
+    "c3": ("skinny", "f48b47180f28191b", 3130625),
     "c4": ("gemm", "f09c37220f1bdc87", 87518951),
     "c5-M1": ("decode", "a0400cf502a0437a", 5250590),
     "c5-M8192": ("gemm", "f09c37220f1bdc87", 260669374),
