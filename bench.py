@@ -1,34 +1,40 @@
 #!/usr/bin/env python3
 """FusedBitLinear benchmark on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--steps K] [--warmup W] [--workload c5]
 
 A step is one pass of the whole hot path -- RMSNorm, per-token int8
 quantization, ternary contraction against pre-packed 2-bit weights and the
 rescale -- over every projection of the workload, on seeded synthetic inputs
-already resident in HBM.  Default workload: the 370M-shaped attention
-projections at decode (M = 1 token, four 1024 -> 1024 FusedBitLinear layers,
-fp16 activations).  Other workloads (--workload c1 | c3 | c4 | c5-M<M>) are
-the parity configurations, measurable the same way; <config>-mlp runs the
-block's MLP instead (gate_proj with the SiLU gate fused into its epilogue,
-then down_proj on the gated output).
+already resident in HBM.
+
+Default workload (c5): the 2.7B-shaped stack, 32 layers of six projections
+(i/f/g/o_proj 2560 -> 2560, gate_proj 2560 -> 2 x 7040 with its SiLU gate,
+down_proj 7040 -> 2560), bf16 activations, swept over M in {1, 8, 64, 512,
+8192} tokens, all in one JSON line: `value` and `roofline` are those of the
+largest M (prefill), `sweep` holds every M.  The layers are chained as the
+model chains them: i/f/g read the layer input, o_proj reads g_proj's output,
+gate_proj (GLU-fused) reads o_proj's output, down_proj reads the gated h and
+writes the next layer's input.  Other workloads: c5-M<M> (one M of the
+stack), c1..c4 (the single-layer configurations, independent projections,
+i/f/g on one shared input), and <c3|c4|c5-M<M>>-mlp (the MLP pair alone).
 
 Method
   * Weights come from a rotating pool of distinct packed copies of at least
     --pool-mib MiB (default 1024 MiB, four times the 256 MiB Infinity Cache),
     so every step streams its weights from HBM.
-  * Steps are captured into HIP graphs (chunks of at most 512 steps);
-    W warm-up steps are replayed untimed, then exactly K steps are timed
-    with events on the replay stream, bracketed by device synchronization.
-  * Roofline of the dominant kernel: a second graph holding only that
-    kernel's launches is timed the same way, giving its average duration
-    (rocprofv3's per-dispatch average reads higher, by about 10 % on the
-    long launches and up to a third on the 2-3 us decode launches: the
-    tracer stamps and signals each dispatch on its own); algorithmic bytes (packed
-    weights + x + gain + y + beta) or ops (2 M N K) per launch over it give
-    `achieved`.
-  * cpu_baseline: the plain C oracle, single-threaded, on the same inputs,
-    timed for about --cpu-seconds on the host.
+  * Steps are captured into HIP graphs; W warm-up steps are replayed untimed,
+    then exactly K steps are timed with events on the replay stream,
+    bracketed by device synchronization.
+  * Roofline of the dominant kernel (the path most of the step's calls take):
+    a second graph holding only that kernel's launches, as the step issues
+    them, is timed the same way, giving its average duration; when every
+    launch of a step is that kernel, the timed steps themselves give it.
+    Algorithmic bytes (packed weights + x + gain + y + beta) or ops (2 M N K)
+    per launch over that duration give `achieved`.
+  * cpu_baseline: the plain C oracle, single-threaded and pinned to one host
+    core, on a fixed row sample of the largest M, timed for about
+    --cpu-seconds and scaled to tokens/s.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -37,7 +43,6 @@ import argparse
 import json
 import math
 import os
-import platform
 import sys
 import time
 
@@ -50,6 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA
 GRAPH_CHUNK = 512             # at most this many steps per captured graph
 GRAPH_MAX_LAUNCHES = 8192     # and about this many kernel launches
+C5_SWEEP = (1, 8, 64, 512, 8192)
 
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (one run each) and scaled by what the same
@@ -62,23 +68,7 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c2": ("decode", "a0400cf502a0437a", 647830),
-    "c3": ("skinny", "f48b47180f28191b", 3130625),
-    "c4": ("gemm", "f09c37220f1bdc87", 87518951),
-    "c5-M1": ("decode", "a0400cf502a0437a", 5250590),
-    "c5-M8192": ("gemm", "f09c37220f1bdc87", 260669374),
 }
-
-
-def launch_kinds(wl):
-    """What one launch group of the workload runs, from the paths its calls take."""
-    import ternary_weight_lm_amd as tw
-    fused = {tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) == tw.BL_PATH_FUSED for c in wl.calls}
-    if fused == {True}:
-        return "one fused decode launch per group"
-    if fused == {False}:
-        return "two-kernel paths: act-quant + contraction per group"
-    return "one fused decode launch per group where the row length allows, else act-quant + contraction"
 
 
 def sources_sha(family):
@@ -99,15 +89,14 @@ def traffic(key):
     return byt if sources_sha(family) == sha else None
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c2",
-                    help="c1 | c2 | c3 | c4 | c5-M1 | c5-M8 | c5-M64 | c5-M512 | c5-M8192, "
-                         "or an MLP workload c3-mlp | c4-mlp | c5-M<M>-mlp (gate_proj with the fused "
-                         "GLU gate, then down_proj)")
+    ap.add_argument("--workload", default="c5",
+                    help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, or an MLP "
+                         "workload c3-mlp | c4-mlp | c5-M<M>-mlp")
     ap.add_argument("--pool-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -115,7 +104,7 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
                          "(reference for the HBM byte counters) and exit")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def calibrate_copy():
@@ -135,308 +124,345 @@ def calibrate_copy():
 
 # ---------------------------------------------------------------- workload
 
+class Call:
+    """One FusedBitLinear call of a step.  x / y name the activation buffers
+    it reads and writes; N is the packed row count (2F for a GLU gate_proj,
+    whose output h is F wide)."""
+
+    def __init__(self, idx, layer, pi, name, K, N, glu, x, y):
+        self.idx, self.layer, self.pi, self.name = idx, layer, pi, name
+        self.K, self.N, self.glu, self.x, self.y = K, N, glu, x, y
+
+    @property
+    def n_out(self):
+        return self.N // 2 if self.glu else self.N
+
+
 class Workload:
-    def __init__(self, key: str):
+    """The calls of one step and how they are grouped into launches."""
+
+    def __init__(self, key: str, M: int | None = None):
         from ternary_weight_lm_amd import synth
-        if key.startswith("c5"):
-            cfg = synth.CONFIGS["c5"]
-            M = int(key.split("-M")[1]) if "-M" in key else 1
-            assert M in cfg.M_list, f"c5 runs at M in {cfg.M_list}"
-            layers = cfg.layers
-        else:
-            cfg = synth.CONFIGS[key]
-            M = cfg.M_list[0]
-            layers = cfg.layers
-        self.key, self.cfg, self.M, self.layers = key, cfg, M, layers
-        # (layer, projection index) for every call of a step
-        self.calls = [(l, i) for l in range(layers) for i in range(len(cfg.projs))]
+        base = key.split("-M")[0]
+        cfg = synth.CONFIGS[base]
+        if M is None:
+            M = int(key.split("-M")[1]) if "-M" in key else cfg.M_list[0]
+        assert M in cfg.M_list, f"{base} runs at M in {cfg.M_list}"
+        self.key, self.cfg, self.M, self.layers = base, cfg, M, cfg.layers
+        self.chained = cfg.layers > 1
+        names = [p.name for p in cfg.projs]
+        self.calls = []
+        for layer in range(cfg.layers):
+            for pi, p in enumerate(cfg.projs):
+                glu = self.chained and p.name == "gate_proj"
+                if not self.chained:
+                    # independent projections: i/f/g share the block input,
+                    # every other projection reads an input of its own
+                    src = names.index(synth.SHARED_INPUT[0]) if p.name in synth.SHARED_INPUT else pi
+                    x, y = ("in", src), ("y", pi)
+                elif p.name in synth.SHARED_INPUT:
+                    x, y = ("x", layer), ("y", pi)
+                elif p.name == "o_proj":
+                    x, y = ("y", names.index("g_proj")), ("y", pi)
+                elif p.name == "gate_proj":
+                    x, y = ("y", names.index("o_proj")), ("h",)
+                else:  # down_proj
+                    x, y = ("h",), ("x", layer + 1)
+                self.calls.append(Call(len(self.calls), layer, pi, p.name, p.K, p.N, glu, x, y))
+
+    def path(self, c):
+        import ternary_weight_lm_amd as tw
+        return tw.bitlinear_select_path(self.M, c.K)
 
     def groups(self):
-        """Launch groups of a step.  HGRNBit's i/f/g projections of one layer
-        read the same block input, so when they take the fused decode path
-        they go out as one grouped decode launch; on the two-kernel paths they
-        share one act-quant launch (and on the MFMA path one GEMM launch:
-        bitlinear_forward_grouped_ws); every other projection (o_proj after
-        the recurrence, the MLP pair) is launched on its own."""
-        import ternary_weight_lm_amd as tw
-        out, cur, cur_path = [], [], None
-        for j, (layer, pi) in enumerate(self.calls):
-            name = self.cfg.projs[pi].name
-            path = tw.bitlinear_select_path(self.M, self.cfg.projs[pi].K)
-            groupable = name in ("i_proj", "f_proj", "g_proj")
-            if groupable and cur and self.calls[cur[0]][0] == layer and path == cur_path:
-                cur.append(j)
+        """Launch groups of a step: a layer's i/f/g (one input) go out as one
+        grouped call -- one fused decode launch, or on the two-kernel paths
+        one shared act-quant launch (and on the MFMA path one GEMM launch);
+        every other projection is launched on its own."""
+        from ternary_weight_lm_amd import synth
+        out, cur = [], []
+        for c in self.calls:
+            if c.name in synth.SHARED_INPUT and cur and cur[0].layer == c.layer \
+                    and self.path(cur[0]) == self.path(c):
+                cur.append(c)
                 continue
             if cur:
                 out.append(cur)
                 cur = []
-            if groupable:
-                cur, cur_path = [j], path
+            if c.name in synth.SHARED_INPUT:
+                cur = [c]
             else:
-                out.append([j])
+                out.append([c])
         if cur:
             out.append(cur)
         return out
 
-    def shape(self, call):
-        p = self.cfg.projs[call[1]]
-        return p.K, p.N
-
-    def xkey(self, call):
-        """The activation tensor a call reads: one per (layer, input), where
-        i/f/g share their block input (synth.SHARED_INPUT) and the 2.7B
-        stack reuses one per projection type across layers."""
-        from ternary_weight_lm_amd import synth
-        layer, pi = call
-        names = [q.name for q in self.cfg.projs]
-        if names[pi] in synth.SHARED_INPUT:
-            pi = names.index(synth.SHARED_INPUT[0])
-        return (0 if self.layers > 1 else layer, pi)
+    def name(self):
+        base = self.cfg.name
+        if self.chained:
+            base = base.replace("_Msweep", "") + "_chained"
+            return f"{base}_M{self.M}"
+        return base
 
     def describe(self):
-        projs = [f"{p.name} {p.K}->{p.N}" for p in self.cfg.projs]
-        return {"workload": self.cfg.name + ("" if not self.key.startswith("c5") else f"_M{self.M}"),
-                "tokens_per_step": self.M, "layers": self.layers, "projections": projs,
-                "x_dtype": self.cfg.dtype, "y_dtype": self.cfg.y_dtype}
+        projs = [f"{p.name} {p.K}->{p.N}" + (" + SiLU gate (GLU, fused)" if self.chained and
+                                              p.name == "gate_proj" else "")
+                 for p in self.cfg.projs]
+        d = {"workload": self.name(), "tokens_per_step": self.M, "layers": self.layers,
+             "projections": projs, "x_dtype": self.cfg.dtype, "y_dtype": self.cfg.y_dtype}
+        if self.chained:
+            d["dataflow"] = ("per layer: i/f/g_proj(x_l); o_proj(g_proj output); gate_proj + GLU "
+                             "(o_proj output) -> h; down_proj(h) -> x_(l+1)")
+        return d
 
 
-def build_inputs(wl: Workload, pool_bytes: int, dev):
-    """Device inputs: x and gain per (layer-shared) projection, a pool of
-    packed weight copies, per-call beta, outputs and workspaces."""
-    import torch
-    import ternary_weight_lm_amd as tw
-    from ternary_weight_lm_amd import synth
-
-    cfg, M = wl.cfg, wl.M
-    xs, gs, host = {}, {}, {}
-    packed, betas = [], []
-    for call in wl.calls:
-        layer, pi = call
-        x, g, W = synth.config_inputs(cfg, M, layer, pi)
-        key = wl.xkey(call)
-        if key not in xs:
-            xs[key] = x.to(dev)
-        gs[call] = g.to(dev)
-        pk, beta = tw.pack(W.to(dev))
-        packed.append(pk)
-        betas.append(beta)
-        if wl.layers == 1 or layer in (0, wl.layers - 1):
-            host[("W",) + call] = (x, g, W)       # oracle sample
-        del W
-    set_bytes = sum(p.numel() for p in packed)
-    copies = max(1, math.ceil(pool_bytes / set_bytes))
-    pool = []
-    for c in range(copies):
-        pool.append([p if c == 0 else p.clone() for p in packed])
-    # outputs and workspaces are shared by the layers of a projection type:
-    # each layer's output is consumed before the next layer runs
-    ydt = synth.DTYPES[cfg.y_dtype]
-    per_type_y = {pi: torch.empty(M, p.N, dtype=ydt, device=dev) for pi, p in enumerate(cfg.projs)}
-    per_type_ws = {pi: tw.workspace(M, p.K, p.N, device=dev) for pi, p in enumerate(cfg.projs)}
-    ys = [per_type_y[c[1]] for c in wl.calls]
-    wss = [per_type_ws[c[1]] for c in wl.calls]
-    groups = wl.groups()
-    # one workspace for the grouped two-kernel launches (they run one after
-    # another on the stream)
-    gws_bytes = 0
-    for grp in groups:
-        if len(grp) > 1:
-            items = [(xs[wl.xkey(wl.calls[j])],
-                      gs[wl.calls[j]], pool[0][j], betas[j], ys[j]) for j in grp]
-            gws_bytes = max(gws_bytes, tw.bitlinear_grouped_workspace_bytes(
-                items, synth.DTYPES[cfg.dtype]))
-    gws = torch.empty(max(gws_bytes, 256), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    return {"xs": xs, "gs": gs, "pool": pool, "betas": betas, "ys": ys, "wss": wss, "gws": gws,
-            "set_bytes": set_bytes, "copies": copies, "host": host, "groups": groups}
+def algorithmic(wl, c):
+    """Bytes (packed W + x + gain + y + beta) and ops (2 M N K) of one call."""
+    xb = 4 if wl.cfg.dtype == "fp32" else 2
+    yb = 4 if wl.cfg.y_dtype == "fp32" else 2
+    M = wl.M
+    byt = c.N * c.K // 4 + M * c.K * xb + c.K * xb + M * c.n_out * yb + 4
+    return byt, 2 * M * c.N * c.K
 
 
-def step_fn(wl, inp, s, keep):
-    """Enqueue one step (weights from pool copy s).  `keep` collects the
+class Weights:
+    """Packed weights of every call of the stack (GLU order for a chained
+    gate_proj), a pool of copies of at least pool_bytes, and the host copies
+    the oracle needs (layer 0 and the last layer)."""
+
+    def __init__(self, wl, pool_bytes, dev, keep_host_layers=None):
+        import torch
+        import ternary_weight_lm_amd as tw
+        from concurrent.futures import ThreadPoolExecutor
+        from ternary_weight_lm_amd import synth
+
+        cfg = wl.cfg
+        keep = set(keep_host_layers if keep_host_layers is not None else (0, wl.layers - 1))
+        self.packed, self.betas, self.host = [], [], {}
+
+        def gen(c):
+            _, g, W = synth.config_inputs(cfg, 1, c.layer, c.pi)
+            return g, W
+
+        with ThreadPoolExecutor(8) as ex:
+            for c, (g, W) in zip(wl.calls, ex.map(gen, wl.calls)):
+                Wd = W.to(dev)
+                pk, beta = tw.pack_glu(Wd) if c.glu else tw.pack(Wd)
+                del Wd
+                self.packed.append(pk)
+                self.betas.append(beta)
+                if c.layer in keep:
+                    self.host[c.idx] = W
+        self.gains = {}
+        for c in wl.calls:
+            self.gains[c.idx] = synth.make_gain(cfg.seed, c.layer, c.pi, c.K, cfg.dtype,
+                                                kind=cfg.gain).to(dev)
+        self.set_bytes = sum(p.numel() for p in self.packed)
+        self.copies = max(1, math.ceil(pool_bytes / self.set_bytes))
+        self.pool = [self.packed] + [[p.clone() for p in self.packed]
+                                     for _ in range(self.copies - 1)]
+        torch.cuda.synchronize()
+
+
+class Buffers:
+    """Activation buffers of one M: the synthetic inputs and every call's
+    output, plus the workspaces."""
+
+    def __init__(self, wl, weights, dev):
+        import torch
+        import ternary_weight_lm_amd as tw
+        from ternary_weight_lm_amd import synth
+
+        cfg, M = wl.cfg, wl.M
+        xdt, ydt = synth.DTYPES[cfg.dtype], synth.DTYPES[cfg.y_dtype]
+        self.t = {}
+        for c in wl.calls:
+            if c.x[0] == "in" and c.x not in self.t:
+                x, _, _ = synth.config_inputs(cfg, M, c.layer, c.x[1])
+                self.t[c.x] = x.to(dev)
+            if c.x == ("x", 0) and c.x not in self.t:
+                x, _, _ = synth.config_inputs(cfg, M, 0, 0)
+                self.t[c.x] = x.to(dev)
+        # chained: x_l for l >= 1 alternates between two buffers, so the
+        # step's input x_0 is never overwritten
+        dt_of = {("x",): xdt, ("y",): ydt, ("h",): xdt}
+        for c in wl.calls:
+            if c.y in self.t:
+                continue
+            if c.y[0] == "x":
+                alias = ("x", 1 + (c.y[1] - 1) % 2)
+                if alias not in self.t:
+                    self.t[alias] = torch.empty(M, c.n_out, dtype=xdt, device=dev)
+                self.t[c.y] = self.t[alias]
+            else:
+                self.t[c.y] = torch.empty(M, c.n_out, dtype=dt_of[(c.y[0],)], device=dev)
+        self.ws = {}
+        for c in wl.calls:
+            key = (c.K, c.N)
+            if key not in self.ws:
+                self.ws[key] = tw.workspace(M, c.K, c.N, device=dev)
+        gws = 256
+        for grp in wl.groups():
+            if len(grp) > 1:
+                items = [self.item(c, weights, weights.pool[0]) for c in grp]
+                gws = max(gws, tw.bitlinear_grouped_workspace_bytes(items, xdt))
+        self.gws = torch.empty(gws, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def item(self, c, weights, pool):
+        return (self.t[c.x], weights.gains[c.idx], pool[c.idx], weights.betas[c.idx], self.t[c.y])
+
+
+def launch_group(wl, grp, weights, bufs, pool, keep):
+    """Enqueue one launch group as the step issues it.  `keep` collects the
     ctypes descriptor arrays so they outlive graph capture."""
     import ternary_weight_lm_amd as tw
     from ternary_weight_lm_amd import synth
-    pool = inp["pool"][s % inp["copies"]]
-    for grp in inp["groups"]:
-        if len(grp) > 1:
-            items = []
-            for j in grp:
-                call = wl.calls[j]
-                x = inp["xs"][wl.xkey(call)]
-                items.append((x, inp["gs"][call], pool[j], inp["betas"][j], inp["ys"][j]))
-            arr = tw.make_calls(items)
-            keep.append(arr)
-            call = wl.calls[grp[0]]
-            if tw.bitlinear_select_path(wl.M, wl.shape(call)[0]) == tw.BL_PATH_FUSED:
-                tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
-                                             synth.DTYPES[wl.cfg.y_dtype])
-            else:
-                tw.bitlinear_forward_grouped_ws(arr, synth.DTYPES[wl.cfg.dtype],
-                                                synth.DTYPES[wl.cfg.y_dtype], inp["gws"])
-            continue
-        j = grp[0]
-        call = wl.calls[j]
-        K, N = wl.shape(call)
-        x = inp["xs"][wl.xkey(call)]
-        tw.bitlinear_forward(x, inp["gs"][call], pool[j], inp["betas"][j], N, inp["ys"][j],
-                             inp["wss"][j])
+    xdt, ydt = synth.DTYPES[wl.cfg.dtype], synth.DTYPES[wl.cfg.y_dtype]
+    if len(grp) > 1:
+        arr = tw.make_calls([bufs.item(c, weights, pool) for c in grp])
+        keep.append(arr)
+        if wl.path(grp[0]) == tw.BL_PATH_FUSED:
+            tw.bitlinear_forward_grouped(arr, xdt, ydt)
+        else:
+            tw.bitlinear_forward_grouped_ws(arr, xdt, ydt, bufs.gws)
+        return
+    c = grp[0]
+    x, g, pk, beta, y = bufs.item(c, weights, pool)
+    ws = bufs.ws[(c.K, c.N)]
+    if c.glu:
+        tw.bitlinear_forward_glu(x, g, pk, beta, c.n_out, y, ws)
+    else:
+        tw.bitlinear_forward(x, g, pk, beta, c.N, y, ws)
 
 
-def capture(wl, inp, first, count):
+def step_fn(wl, weights, bufs, s, keep):
+    """Enqueue one step (weights from pool copy s)."""
+    pool = weights.pool[s % weights.copies]
+    for grp in wl.groups():
+        launch_group(wl, grp, weights, bufs, pool, keep)
+
+
+def capture(fn, first, count, launches_per_step):
     import torch
     graphs = []
     s = first
-    per_step = sum(1 if len(grp) > 1 else 2 for grp in inp["groups"])  # upper bound
-    chunk = max(1, min(GRAPH_CHUNK, GRAPH_MAX_LAUNCHES // per_step))
+    chunk = max(1, min(GRAPH_CHUNK, GRAPH_MAX_LAUNCHES // max(1, launches_per_step)))
     while count > 0:
         n = min(count, chunk)
         g = torch.cuda.CUDAGraph()
         keep = []
         with torch.cuda.graph(g):
             for k in range(n):
-                step_fn(wl, inp, s + k, keep)
-        graphs.append((g, n))
+                fn(s + k, keep)
+        graphs.append((g, keep))
         s += n
         count -= n
     return graphs
 
 
+def timed_replay(graphs):
+    import torch
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for g, _ in graphs:
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 # ---------------------------------------------------------------- roofline
 
-def algorithmic(wl, call):
-    """Bytes (packed W + x + gain + y + beta) and ops (2 M N K) of one call."""
-    from ternary_weight_lm_amd import synth
-    import torch
-    K, N = wl.shape(call)
-    xb = torch.tensor([], dtype=synth.DTYPES[wl.cfg.dtype]).element_size()
-    yb = torch.tensor([], dtype=synth.DTYPES[wl.cfg.y_dtype]).element_size()
-    M = wl.M
-    byt = N * K // 4 + M * K * xb + K * xb + M * N * yb + 4
-    return byt, 2 * M * N * K
+KERNEL_NAME = {1: "bl::decode_kernel (norm+quant+contract+rescale in one launch)",
+               2: "bl::skinny_kernel<pre-quantized> (contract+rescale)",
+               3: "bl::gemm_mfma_kernel (contract+rescale)"}
 
 
-def roofline_from_steps(wl, inp, steps, ms):
-    """Fused decode path: every launch of a step is the dominant kernel, so
-    the timed steps themselves give its average duration."""
-    import ternary_weight_lm_amd as tw
-    launches = steps * len(inp["groups"])
-    sec = ms / 1e3
-    byt = sum(algorithmic(wl, c)[0] for c in wl.calls) * steps
-    ops = sum(algorithmic(wl, c)[1] for c in wl.calls) * steps
-    ach = byt / sec / 1e9
-    grouped = any(len(g) > 1 for g in inp["groups"])
-    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 5), "traffic": None,
-            "kernel": "bl::decode_kernel (norm+quant+contract+rescale in one launch)"
-                      + (", i/f/g grouped per launch" if grouped else ""),
-            "launches": launches, "avg_kernel_us": round(sec * 1e6 / launches, 3),
-            "algorithmic_bytes_per_launch": round(byt / launches, 1),
-            "ops_per_launch": round(ops / launches, 1),
-            "timed_region": "the benchmark steps themselves (one kernel per launch)"}
+def dominant_path(wl):
+    """The path most of the step's calls take (ties: the one carrying more
+    algorithmic bytes)."""
+    paths = {}
+    for c in wl.calls:
+        p = wl.path(c)
+        n, b = paths.get(p, (0, 0))
+        paths[p] = (n + 1, b + algorithmic(wl, c)[0])
+    return max(paths, key=lambda p: paths[p])
 
 
-def roofline(wl, inp, reps):
-    """Average duration of the dominant kernel: a HIP graph holding only its
-    launches (reps passes over every call, weights rotating through the
-    pool) is timed with events on the replay stream.  For the two-kernel
-    paths the activations are quantized once beforehand, so the graph holds
-    nothing but contraction launches."""
+def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
+    """Average duration of the dominant kernel's launches and the roofline
+    fraction it reaches.  If every launch of a step is that kernel, the
+    timed steps give it; otherwise a graph of only its launches (issued as
+    in a step, reps passes, weights rotating through the pool) is timed.
+    On the two-kernel paths the activations are quantized beforehand, so
+    that graph holds nothing but contraction launches."""
     import torch
     import ternary_weight_lm_amd as tw
-    from ternary_weight_lm_amd import synth
-    # the dominant kernel: the path most of the step's calls take
-    paths = [tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) for c in wl.calls]
-    path = max(set(paths), key=paths.count)
-    sel = [j for j, p in enumerate(paths) if p == path]
+
+    path = dominant_path(wl)
+    sel = [c for c in wl.calls if wl.path(c) == path]
     bound = "hbm" if path in (tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY) else "mfma"
-    ncalls = len(sel)
-    stage = {}
-    if path != tw.BL_PATH_FUSED:
-        for j in sel:
-            call = wl.calls[j]
-            K, N = wl.shape(call)
-            # per call: calls that share x still quantize it with their own gain
-            if j not in stage:
-                xq = torch.empty(wl.M, K, dtype=torch.int8, device="cuda")
-                sc = torch.empty(wl.M, dtype=torch.float32, device="cuda")
-                rs = torch.empty(wl.M, dtype=torch.int32, device="cuda")
-                tw.bitlinear_act_quant(inp["xs"][wl.xkey(call)], inp["gs"][call], xq, sc, rs)
-                stage[j] = (xq, sc, rs)
-
-    # the step's launch groups restricted to the dominant path: grouped i/f/g
-    # calls are one grouped launch (decode kernel, resp. contraction), as in
-    # a step
     units = []
-    for grp in inp["groups"]:
-        mine = [j for j in grp if j in sel]
+    for grp in wl.groups():
+        mine = [c for c in grp if wl.path(c) == path]
         if not mine:
             continue
         if len(mine) > 1 and path in (tw.BL_PATH_MFMA, tw.BL_PATH_FUSED):
             units.append(mine)
         else:
-            units.extend([j] for j in mine)
-    nunits = len(units)
-    keep = []
+            units.extend([c] for c in mine)
+    if len(sel) == len(wl.calls) and path == tw.BL_PATH_FUSED and step_ms is not None:
+        passes, ms = steps, step_ms * steps
+        timed_region = "the benchmark steps themselves (every launch is this kernel)"
+    else:
+        stage = {}
+        if path != tw.BL_PATH_FUSED:
+            for c in sel:
+                x = bufs.t[c.x]
+                xq = torch.empty(wl.M, c.K, dtype=torch.int8, device=x.device)
+                sc = torch.empty(wl.M, dtype=torch.float32, device=x.device)
+                rs = torch.empty(wl.M, dtype=torch.int32, device=x.device)
+                tw.bitlinear_act_quant(x, weights.gains[c.idx], xq, sc, rs)
+                stage[c.idx] = (xq, sc, rs)
+        nunits = len(units)
 
-    def launch(r):
-        s, uu = divmod(r, nunits)
-        unit = units[uu]
-        items = []
-        for j in unit:
-            call = wl.calls[j]
-            K, N = wl.shape(call)
-            pk = inp["pool"][(s + 7) % inp["copies"]][j]
-            xkey = wl.xkey(call)
-            if path == tw.BL_PATH_FUSED and len(unit) == 1:
-                tw.bitlinear_forward_path(inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j],
-                                          N, inp["ys"][j], inp["wss"][j], path)
-            elif path == tw.BL_PATH_FUSED:
-                items.append((inp["xs"][xkey], inp["gs"][call], pk, inp["betas"][j], inp["ys"][j]))
-            elif len(unit) == 1:
-                xq, sc, rs = stage[j]
-                tw.bitlinear_contract(xq, sc, rs, pk, inp["betas"][j], N, inp["ys"][j], path=path)
+        def launch(r, keep):
+            s, u = divmod(r, nunits)
+            unit = units[u]
+            pool = weights.pool[(s + 7) % weights.copies]
+            if path == tw.BL_PATH_FUSED:
+                launch_group(wl, unit, weights, bufs, pool, keep)
+                return
+            if len(unit) > 1:
+                items = []
+                for c in unit:
+                    xq, sc, rs = stage[c.idx]
+                    items.append((xq, sc, rs, pool[c.idx], weights.betas[c.idx], bufs.t[c.y]))
+                arr = tw.make_contract_calls(items)
+                keep.append(arr)
+                tw.bitlinear_contract_grouped(arr, bufs.t[unit[0].y].dtype)
+                return
+            c = unit[0]
+            xq, sc, rs = stage[c.idx]
+            if c.glu:
+                tw.bitlinear_contract_glu(xq, sc, rs, pool[c.idx], weights.betas[c.idx], c.n_out,
+                                          bufs.t[c.y], path=path)
             else:
-                xq, sc, rs = stage[j]
-                items.append((xq, sc, rs, pk, inp["betas"][j], inp["ys"][j]))
-        if items and path == tw.BL_PATH_FUSED:
-            arr = tw.make_calls(items)
-            keep.append(arr)
-            tw.bitlinear_forward_grouped(arr, synth.DTYPES[wl.cfg.dtype],
-                                         synth.DTYPES[wl.cfg.y_dtype])
-        elif items:
-            arr = tw.make_contract_calls(items)
-            keep.append(arr)
-            tw.bitlinear_contract_grouped(arr, synth.DTYPES[wl.cfg.y_dtype])
+                tw.bitlinear_contract(xq, sc, rs, pool[c.idx], weights.betas[c.idx], c.N,
+                                      bufs.t[c.y], path=path)
 
-    total = reps * nunits
-    graphs = []
-    r = 0
-    while r < total:
-        n = min(total - r, GRAPH_MAX_LAUNCHES)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for q in range(r, r + n):
-                launch(q)
-        graphs.append(g)
-        r += n
-    graphs[0].replay()                      # warm the replay path
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for g in graphs:
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    sec = a.elapsed_time(b) / 1e3
-    byt = ops = 0
-    for j in sel:
-        cb, co = algorithmic(wl, wl.calls[j])
-        byt += cb * reps
-        ops += co * reps
-    kernel = {tw.BL_PATH_FUSED: "bl::decode_kernel (norm+quant+contract+rescale)",
-              tw.BL_PATH_SKINNY: "bl::skinny_kernel<fused=false> (contract+rescale)",
-              tw.BL_PATH_MFMA: "bl::gemm_mfma_kernel (contract+rescale)"}[path]
+        graphs = capture(launch, 0, reps * nunits, 1)
+        graphs[0][0].replay()                      # warm the replay path
+        torch.cuda.synchronize()
+        passes, ms = reps, timed_replay(graphs)
+        timed_region = "a graph of the dominant kernel's launches only"
+    total = passes * len(units)
+    byt = sum(algorithmic(wl, c)[0] for c in sel) * passes
+    ops = sum(algorithmic(wl, c)[1] for c in sel) * passes
+    sec = ms / 1e3
     if bound == "hbm":
         ach = byt / sec / 1e9
         out = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -446,23 +472,136 @@ def roofline(wl, inp, reps):
         out = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
                "frac": round(ach / I8_PEAK_TOPS, 5)}
     out["traffic"] = None
-    out["kernel"] = kernel
-    out["calls_timed"] = (f"{len(sel)} of {len(wl.calls)} calls per step (those on this path) in "
-                          f"{nunits} launches")
+    out["kernel"] = KERNEL_NAME[path] + (" (i/f/g grouped per launch; GLU gate variant for "
+                                         "gate_proj)" if wl.chained else "")
+    out["calls_timed"] = f"{len(sel)} of {len(wl.calls)} calls per step (those on this path)"
     out["launches"] = total
     out["avg_kernel_us"] = round(sec * 1e6 / total, 3)
     out["algorithmic_bytes_per_launch"] = round(byt / total, 1)
     out["ops_per_launch"] = round(ops / total, 1)
+    out["timed_region"] = timed_region
     return out
+
+
+# --------------------------------------------------------------- one M
+
+def run_m(wl, weights, dev, args):
+    """Time one workload at one M; returns (summary dict, bufs)."""
+    import torch
+    bufs = Buffers(wl, weights, dev)
+    big = wl.M >= 512
+    steps = args.steps if args.steps is not None else (20 if big else 100)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 10)
+    reps = args.roofline_reps if args.roofline_reps is not None else (2 if big else 10)
+    groups = wl.groups()
+    per_step = sum(1 if len(g) > 1 and wl.path(g[0]) == 1 else 2 for g in groups)
+
+    def fn(s, keep):
+        step_fn(wl, weights, bufs, s, keep)
+
+    if warmup > 0:
+        for g, _ in capture(fn, 0, warmup, per_step):
+            g.replay()
+    timed = capture(fn, warmup, steps, per_step)
+    ms = timed_replay(timed)
+    del timed
+    roof = roofline(wl, weights, bufs, reps, step_ms=ms / steps, steps=steps)
+    roof["traffic"] = traffic(wl.key if not wl.chained else f"c5-M{wl.M}")
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    torch.cuda.synchronize()
+    return {"M": wl.M, "tokens_per_s": round(wl.M * steps / (ms / 1e3), 2), "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+            "launch_groups_per_step": len(groups), "roofline": roof}, bufs
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def host_facts():
+    """nproc, the CPU model and the core the oracle is pinned to."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = sorted(os.sched_getaffinity(0))
+    return {"nproc": len(avail), "cpu_count": os.cpu_count(), "model": model,
+            "pinned_core": avail[-1] if avail else None}
+
+
+def cpu_baseline(wl, weights, seconds):
+    """The oracle, as it stands, on one pinned host core: a fixed sample of
+    token rows (all rows up to 8, else 8 spread over M) through one layer's
+    calls (every call of a single-layer workload; layer 0 of the stack,
+    chained through the oracle's own outputs), tokens/s scaled to every
+    layer.  Every row and layer costs the same in the oracle."""
+    import numpy as np
+    import oracle
+    from ternary_weight_lm_amd import synth
+
+    facts = host_facts()
+    cfg = wl.cfg
+    rows = min(wl.M, 8)
+    sel = np.linspace(0, wl.M - 1, rows).round().astype(int)
+    layer_calls = [c for c in wl.calls if c.layer == 0]
+    prep = {}
+    for c in layer_calls:
+        W = weights.host[c.idx].numpy()
+        g = synth.widen(synth.make_gain(cfg.seed, c.layer, c.pi, c.K, cfg.dtype, kind=cfg.gain))
+        if c.glu:
+            _, beta, Wq = oracle.pack_glu_weights(W)
+        else:
+            _, beta, Wq = oracle.pack_weights(W)
+        prep[c.idx] = (g, Wq, beta)
+    inputs = {}
+    for c in layer_calls:
+        if c.x[0] in ("in", "x") and c.x not in inputs:
+            x, _, _ = synth.config_inputs(cfg, wl.M, 0, c.x[1] if c.x[0] == "in" else 0)
+            inputs[c.x] = synth.widen(x)[sel]
+
+    def one_layer():
+        vals = dict(inputs)
+        for c in layer_calls:
+            g, Wq, beta = prep[c.idx]
+            if c.glu:
+                out = oracle.forward_glu(vals[c.x], g, Wq, beta)["h"]
+            else:
+                out = oracle.forward(vals[c.x], g, Wq, beta)["y"]
+            vals[c.y] = out.astype(np.float32)
+
+    old = os.sched_getaffinity(0)
+    if facts["pinned_core"] is not None:
+        os.sched_setaffinity(0, {facts["pinned_core"]})
+    try:
+        t0, n = time.perf_counter(), 0
+        while True:
+            one_layer()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        os.sched_setaffinity(0, old)
+    per_token = el / n / rows * wl.layers
+    return {"value": round(1.0 / per_token, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{n} passes of {rows} of {wl.M} token rows through the {len(layer_calls)} "
+                       f"projections of one layer ({el:.1f} s single-threaded), scaled to "
+                       f"{wl.layers} layer(s)"),
+            "host": {"nproc": facts["nproc"], "os_cpu_count": facts["cpu_count"],
+                     "cpu_model": facts["model"],
+                     "pinned": f"core {facts['pinned_core']} (sched_setaffinity, 1 thread)"}}
 
 
 # ------------------------------------------------------------- MLP (GLU)
 
 def run_mlp(args):
-    """The HGRNBit MLP: gate_proj with the SiLU gate fused into its
+    """The HGRNBit MLP alone: gate_proj with the SiLU gate fused into its
     epilogue (bitlinear_forward_glu, GLU-packed weights), then down_proj on
-    the gated output -- the real dependency chain.  Workloads <config>-mlp:
-    c3-mlp (M = 32), c4-mlp (M = 4096), c5-M<M>-mlp (2.7B, 32 layers)."""
+    the gated output.  Workloads <config>-mlp: c3-mlp (M = 32), c4-mlp
+    (M = 4096), c5-M<M>-mlp (2.7B, 32 layers)."""
     import numpy as np
     import torch
     import ternary_weight_lm_amd as tw
@@ -494,7 +633,7 @@ def run_mlp(args):
     ws_d = tw.workspace(M, F, N)
     torch.cuda.synchronize()
 
-    def step(s):
+    def step(s, keep):
         for l in range(layers):
             pg, pd = pool[(s * layers + l) % copies]
             tw.bitlinear_forward_glu(xd, ggd, pg, b_g, F, h, ws_g)
@@ -503,44 +642,17 @@ def run_mlp(args):
     big = M >= 512
     steps = args.steps if args.steps is not None else (20 if big else (100 if layers > 1 else 2000))
     warmup = args.warmup if args.warmup is not None else (3 if big else 10)
-    per_graph = max(1, min(GRAPH_CHUNK, GRAPH_MAX_LAUNCHES // (4 * layers)))
-
-    def capture(first, count, fn, per):
-        graphs, s0 = [], first
-        while count > 0:
-            n = min(count, per)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for k in range(n):
-                    fn(s0 + k)
-            graphs.append(g)
-            s0 += n
-            count -= n
-        return graphs
-
-    def timed(graphs):
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for g in graphs:
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
-
-    for g in capture(0, warmup, step, per_graph):
+    for g, _ in capture(step, 0, warmup, 4 * layers):
         g.replay()
-    ms = timed(capture(warmup, steps, step, per_graph))
+    ms = timed_replay(capture(step, warmup, steps, 4 * layers))
 
-    # roofline of the fused gate_proj + GLU launches alone
     reps = 2 if big else (10 if layers > 1 else 200)
 
-    def glu_only(r):
+    def glu_only(r, keep):
         pg, _ = pool[(r + 3) % copies]
         tw.bitlinear_forward_glu(xd, ggd, pg, b_g, F, h, ws_g)
 
-    gms = timed(capture(0, reps * layers, glu_only, GRAPH_MAX_LAUNCHES // 2))
+    gms = timed_replay(capture(glu_only, 0, reps * layers, 2))
     launches = reps * layers
     sec = gms / 1e3
     ops = 2 * M * F2 * K
@@ -578,66 +690,35 @@ def run_mlp(args):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        rows = M if M <= 32 else 8
+        facts = host_facts()
+        rows = min(M, 8)
         sel = np.linspace(0, M - 1, rows).round().astype(int)
         xw = synth.widen(x)[sel]
         _, beta_g, Wq_g = oracle.pack_glu_weights(W_gate.numpy())
         _, beta_d, Wq_d = oracle.pack_weights(W_down.numpy())
         gw, dw = synth.widen(g_gate), synth.widen(g_down)
-        t0, n = time.perf_counter(), 0
-        while True:
-            hh = oracle.forward_glu(xw, gw, Wq_g, beta_g)["h"].astype(np.float32)
-            oracle.forward(hh, dw, Wq_d, beta_d)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+        old = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {facts["pinned_core"]})
+        try:
+            t0, n = time.perf_counter(), 0
+            while True:
+                hh = oracle.forward_glu(xw, gw, Wq_g, beta_g)["h"].astype(np.float32)
+                oracle.forward(hh, dw, Wq_d, beta_d)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        finally:
+            os.sched_setaffinity(0, old)
         out["cpu_baseline"] = {
             "value": round(rows * n / el / layers, 4), "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{n} passes of {rows} of {M} token rows through one layer's MLP "
-                      f"({el:.1f} s single-threaded; scaled to {layers} layer(s))"}
+                      f"({el:.1f} s single-threaded; scaled to {layers} layer(s))",
+            "host": {"nproc": facts["nproc"], "os_cpu_count": facts["cpu_count"],
+                     "cpu_model": facts["model"],
+                     "pinned": f"core {facts['pinned_core']} (sched_setaffinity, 1 thread)"}}
     print(json.dumps(out), flush=True)
-
-
-# ------------------------------------------------------------ CPU baseline
-
-def cpu_baseline(wl, inp, seconds):
-    """The oracle, as it stands, on one host core: full steps for the small
-    workloads, a fixed row sample for the large ones (tokens/s scaled by the
-    sampled row count; every row costs the same in the oracle)."""
-    import numpy as np
-    import oracle
-    from ternary_weight_lm_amd import synth
-
-    host = inp["host"]
-    rows = wl.M if wl.M <= 32 else 8
-    sample_calls = [c for c in wl.calls if ("W",) + c in host]
-    prepared = []
-    for call in sample_calls:
-        x, g, W = host[("W",) + call]
-        W = W.numpy()
-        _, beta, Wq = oracle.pack_weights(W)
-        xw = synth.widen(x)
-        sel = np.linspace(0, wl.M - 1, rows).round().astype(int)
-        prepared.append((xw[sel], synth.widen(g), Wq, beta))
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        for xw, gw, Wq, beta in prepared:
-            oracle.forward(xw, gw, Wq, beta)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per_pass = el / n                               # seconds for `rows` rows of sample_calls
-    per_token_all_calls = per_pass / rows * (len(wl.calls) / len(sample_calls))
-    return {"value": round(1.0 / per_token_all_calls, 4), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"{n} passes of {rows} of {wl.M} token rows through "
-                       f"{len(sample_calls)} of {len(wl.calls)} projections "
-                       f"({el:.1f} s single-threaded on {platform.processor() or 'host'}; "
-                       f"scaled to every projection of a step)")}
 
 
 # -------------------------------------------------------------------- main
@@ -663,58 +744,50 @@ def main():
         run_mlp(args)
         return
 
-    wl = Workload(args.workload)
-    big = wl.M >= 512 or wl.key == "c5-M64"
-    stack = wl.layers > 1
-    steps = args.steps if args.steps is not None else (20 if big else (100 if stack else 2000))
-    warmup = args.warmup if args.warmup is not None else (3 if big else (10 if stack else 100))
-    reps = args.roofline_reps if args.roofline_reps is not None else (
-        2 if big else (10 if stack else 200))
-
-    inp = build_inputs(wl, args.pool_mib << 20, dev)
-
-    warm_graphs = capture(wl, inp, 0, warmup) if warmup > 0 else []
-    timed_graphs = capture(wl, inp, warmup, steps)
-    for g, _ in warm_graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for g, _ in timed_graphs:
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / steps
-    tokens_per_s = wl.M * steps / (ms / 1e3)
-
-    import ternary_weight_lm_amd as tw
-    paths = {tw.bitlinear_select_path(wl.M, wl.shape(c)[0]) for c in wl.calls}
-    if paths == {tw.BL_PATH_FUSED}:
-        roof = roofline_from_steps(wl, inp, steps, ms)
-    else:
-        roof = roofline(wl, inp, reps)
-        roof["timed_region"] = "a graph of the dominant kernel's launches only"
-
-    roof["traffic"] = traffic(wl.key)
-    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    sweep = args.workload == "c5"
+    Ms = list(C5_SWEEP) if sweep else [None]
+    t_setup = time.perf_counter()
+    wl0 = Workload(args.workload, M=Ms[0])
+    weights = Weights(wl0, args.pool_mib << 20, dev)
+    setup_s = time.perf_counter() - t_setup
+    results, last = [], None
+    for M in Ms:
+        wl = Workload(args.workload, M=M)
+        print(f"# timing {wl.name()}", file=sys.stderr, flush=True)
+        res, bufs = run_m(wl, weights, dev, args)
+        del bufs
+        torch.cuda.empty_cache()
+        results.append(res)
+        last = wl
+    head = results[-1]
+    wl = last
+    cfgd = dict(wl.describe(),
+                weight_pool_MiB=round(weights.set_bytes * weights.copies / 2**20, 1),
+                weight_copies=weights.copies,
+                launch=(f"hipGraph; {head['launch_groups_per_step']} launch groups per step "
+                        "(a layer's i/f/g grouped on one input: one fused decode launch, or one "
+                        "shared act-quant launch + one GEMM launch on the MFMA path; every other "
+                        "projection one fused launch or act-quant + contraction)"),
+                parallelism="single GPU", setup_s=round(setup_s, 1))
+    if sweep:
+        cfgd["workload"] = wl.name().rsplit("_M", 1)[0] + "_Msweep"
+        cfgd["value_at_M"] = wl.M
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8", "data": "synthetic",
-        "config": dict(wl.describe(), weight_pool_MiB=round(inp["set_bytes"] * inp["copies"] / 2**20, 1),
-                       weight_copies=inp["copies"],
-                       launch=f"hipGraph; {len(inp['groups'])} launch groups per step "
-                              f"({'i/f/g grouped' if any(len(g) > 1 for g in inp['groups']) else 'one per projection'}; "
-                              f"{launch_kinds(wl)})",
-                       parallelism="single GPU"),
-        "roofline": roof,
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": head["steps"], "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic", "config": cfgd,
+        "roofline": head["roofline"],
     }
+    if sweep:
+        out["sweep"] = [{"M": r["M"], "tokens_per_s": r["tokens_per_s"],
+                         "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+                         "bound": r["roofline"]["bound"], "frac": r["roofline"]["frac"],
+                         "achieved": r["roofline"]["achieved"], "unit": r["roofline"]["unit"],
+                         "avg_kernel_us": r["roofline"]["avg_kernel_us"],
+                         "kernel": r["roofline"]["kernel"]} for r in results]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

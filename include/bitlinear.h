@@ -116,7 +116,12 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K);
 /* Workspace bytes bitlinear_pack_weights needs (0 for a bad shape). */
 size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 
-/* Offline weight packing (absmean ternarization + 2-bit tile layout).
+/* Offline weight packing (absmean ternarization + 2-bit tile layout): the
+ * matrix is divided by its mean absolute value and each entry rounded to
+ * the nearest of -1, 0, +1 (datacamp page, section "MatMul durch ternäre
+ * Operationen ersetzen"); fewer bits per weight mean less memory and
+ * bandwidth (aidev bluegarage page, section "量子化とは何か"), hence the
+ * 2-bit codes.
  *   W       device fp32 [N, K] latent weights (read only)
  *   packed  device, bitlinear_packed_bytes(N, K) bytes (written)
  *   beta    device fp32 scalar: the per-tensor scale (written)
@@ -132,6 +137,14 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, void *packed,
 size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /* One FusedBitLinear forward: y = rescale(contract(quant(rmsnorm(x)), Wq)).
+ * The layer as the pages state it: FusedBitLinear(in_features, out_features,
+ * bias=False) holding its own RMSNorm(eps=1e-08) (hysenlabs fr review,
+ * section "HGRNBit : ce que la structure du modèle révèle"; hysenlabs ja
+ * review, section "HGRNBit という層構成を読む"), the norm fused with the
+ * ternary projection right before quantization (hysenlabs de review,
+ * section "HGRNBit: was in einem Block tatsächlich passiert"), the scaled
+ * ternary accumulation of datacamp "Kernkomponenten: MLGRU und GLU"
+ * (figure panels 4 and 5).
  *   x       device [M, K], dtype x_dtype (read only)
  *   gain    device [K], dtype x_dtype: the RMSNorm weight (read only)
  *   packed  device packed weights of an [N, K] matrix (read only)
@@ -265,16 +278,23 @@ const char *bitlinear_status_string(int status);
  * These expose the stages of the path one at a time so each can be checked
  * on its own (bit-exact integer outputs). */
 
-/* RMSNorm + per-token int8 quantization.
+/* RMSNorm + per-token int8 quantization: the normalization that keeps the
+ * activations in a usable range right before they are quantized (hysenlabs
+ * de review, section "HGRNBit: was in einem Block tatsächlich passiert";
+ * datacamp page, figure panel 5 of "Kernkomponenten: MLGRU und GLU").  The
+ * 8-bit width and one absmax scale per token are this library's reading.
  *   xq [M, K] int8, s [M] fp32, rowsum [M] int32 = sum_k xq[m, k]
- *   (all device, written). */
+ *   (all device, written); x, gain as for bitlinear_forward. */
 int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
                         int64_t M, int64_t K, float eps, int8_t *xq, float *s,
                         int32_t *rowsum, hipStream_t stream);
 
 /* Exact contraction acc[m, n] = sum_k xq[m, k] * Wq[n, k] from int8
  * activations and packed weights (datacamp page above, section "MatMul
- * durch ternäre Operationen ersetzen").
+ * durch ternäre Operationen ersetzen"; C_ij = sum_p A_ip B_pj as the aidev
+ * bluegarage page, section "MatMulとは具体的にどんな計算か", writes it).
+ * Beyond the plain contraction this takes a `path`, so each contraction
+ * kernel can be checked on its own.
  *   xq      device int8 [M, K] (read only)
  *   rowsum  device int32 [M] = sum_k xq[m, k] (as written by
  *           bitlinear_act_quant); the kernels use it to turn the sum over
@@ -299,6 +319,20 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
                        const float *beta, int64_t N, void *y, int y_dtype,
                        int path, hipStream_t stream);
 
+/* bitlinear_contract with the GLU gate in the epilogue: from quantized
+ * activations (xq, s, rowsum as bitlinear_act_quant writes them) and a
+ * gate_proj packed by bitlinear_pack_glu_weights (2F rows),
+ *   h[m, j] = silu(y[m, j]) * y[m, F + j],  y[m, n] = acc[m, n] * beta / s[m]
+ * -- the second half of bitlinear_forward_glu, bit for bit (datacamp page,
+ * section "Kernkomponenten: MLGRU und GLU": one BitLinear output through
+ * SiLU times the other).
+ *   h       device [M, F], dtype h_dtype (written)
+ *   path    BL_PATH_AUTO, BL_PATH_SKINNY (M <= 64) or BL_PATH_MFMA.
+ * F > 0, F % 16 == 0; everything else as bitlinear_contract. */
+int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rowsum, int64_t M,
+                           int64_t K, const void *packed, const float *beta, int64_t F, void *h,
+                           int h_dtype, int path, hipStream_t stream);
+
 /* One contraction of bitlinear_contract_grouped (device pointers as in
  * bitlinear_contract). */
 typedef struct bl_contract_call {
@@ -322,7 +356,10 @@ typedef struct bl_contract_call {
 int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
                                hipStream_t stream);
 
-/* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device). */
+/* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device):
+ * the ternary matrix of datacamp page, section "MatMul durch ternäre
+ * Operationen ersetzen", for checking a pack.  packed as written by
+ * bitlinear_pack_weights (N*K/4 bytes, read only); Wq written. */
 int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
                              int8_t *Wq, hipStream_t stream);
 

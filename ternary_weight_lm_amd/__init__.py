@@ -13,7 +13,7 @@ import torch
 from ._lib import (  # noqa: F401
     BL_BF16, BL_F16, BL_F32, BL_PATH_AUTO, BL_PATH_FUSED, BL_PATH_MFMA,
     BL_PATH_SKINNY, CODE_DTYPE, DTYPE_CODE, BitLinearError, lib,
-    bitlinear_act_quant, bitlinear_contract, bitlinear_forward, bitlinear_forward_grouped,
+    bitlinear_act_quant, bitlinear_contract, bitlinear_contract_glu, bitlinear_forward, bitlinear_forward_grouped,
     bitlinear_forward_grouped_ws, bitlinear_grouped_workspace_bytes,
     bitlinear_contract_grouped, make_contract_calls,
     bitlinear_forward_glu, bitlinear_forward_path, bitlinear_pack_glu_weights, make_calls,

@@ -75,6 +75,7 @@ SIGNATURES = {
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
     "bitlinear_contract": ([P, P, P, I64, I64, P, P, I64, P, I, I, P], I),
+    "bitlinear_contract_glu": ([P, P, P, I64, I64, P, P, I64, P, I, I, P], I),
     "bitlinear_pack_glu_weights": ([P, I64, I64, P, P, P, SZ, P], I),
     "bitlinear_forward_glu": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
@@ -96,6 +97,47 @@ def lib() -> ctypes.CDLL:
             fn.restype = res
         _lib = L
     return _lib
+
+
+def _need(t, name, dtype=None, numel=None, dims=None):
+    """Host-side size / dtype check of a tensor handed to the C ABI: the ABI
+    sees only pointers, so a tensor smaller than the call implies would let
+    the kernels read or write past its allocation.  Runs before any pointer
+    is taken."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, (tuple, list, set)) else t.dtype == dtype
+        if not ok:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimension(s), has shape {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+FLOATS = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _check_layer_io(x, gain, packed, beta, N, y, n_out):
+    """x [M, K] (any float dtype), gain [K] (x's dtype), packed >= N K / 4
+    bytes, beta fp32 [>= 1], y [M, n_out] float."""
+    _need(x, "x", FLOATS, dims=2)
+    M, K = x.shape
+    _need(gain, "gain", x.dtype, numel=K)
+    _need(packed, "packed", numel=1)
+    if _nbytes(packed) < N * K // 4:
+        raise ValueError(f"packed holds {_nbytes(packed)} bytes, an [{N}, {K}] matrix needs "
+                         f"{N * K // 4}")
+    _need(beta, "beta", torch.float32, numel=1)
+    _need(y, "y", FLOATS, numel=M * n_out)
+    return M, K
 
 
 def _ptr(t: torch.Tensor | None):
@@ -144,15 +186,27 @@ def bitlinear_status_string(status: int) -> str:
     return lib().bitlinear_status_string(status).decode()
 
 
-def bitlinear_pack_weights(W, packed, beta, ws, stream=None):
+def _check_pack(W, packed, beta, ws, rows):
+    _need(W, "W", torch.float32, dims=2)
     N, K = W.shape
+    _need(packed, "packed", numel=1)
+    if _nbytes(packed) < rows * K // 4:
+        raise ValueError(f"packed holds {_nbytes(packed)} bytes, needs {rows * K // 4}")
+    _need(beta, "beta", torch.float32, numel=1)
+    _need(ws, "ws", numel=1)
+    return N, K
+
+
+def bitlinear_pack_weights(W, packed, beta, ws, stream=None):
+    N, K = _check_pack(W, packed, beta, ws, W.shape[0] if W is not None and W.dim() == 2 else 0)
     _check("bitlinear_pack_weights", lib().bitlinear_pack_weights(
         _ptr(W), N, K, _ptr(packed), _ptr(beta), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
 
 
 def bitlinear_forward(x, gain, packed, beta, N, y, ws, eps=1e-8, stream=None):
-    M, K = x.shape
+    M, K = _check_layer_io(x, gain, packed, beta, N, y, N)
+    _need(ws, "ws", numel=1)
     _check("bitlinear_forward", lib().bitlinear_forward(
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
         _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
@@ -160,7 +214,8 @@ def bitlinear_forward(x, gain, packed, beta, N, y, ws, eps=1e-8, stream=None):
 
 
 def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stream=None):
-    M, K = x.shape
+    M, K = _check_layer_io(x, gain, packed, beta, N, y, N)
+    _need(ws, "ws", numel=1)
     _check("bitlinear_forward_path", lib().bitlinear_forward_path(
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
         _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
@@ -169,7 +224,7 @@ def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stre
 
 def bitlinear_pack_glu_weights(W, packed, beta, ws, stream=None):
     """W: gate_proj [2F, K] fp32 (rows 0..F-1 SiLU-gated, F..2F-1 multiplied)."""
-    N2, K = W.shape
+    N2, K = _check_pack(W, packed, beta, ws, W.shape[0] if W is not None and W.dim() == 2 else 0)
     _check("bitlinear_pack_glu_weights", lib().bitlinear_pack_glu_weights(
         _ptr(W), N2 // 2, K, _ptr(packed), _ptr(beta), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
@@ -177,7 +232,8 @@ def bitlinear_pack_glu_weights(W, packed, beta, ws, stream=None):
 
 def bitlinear_forward_glu(x, gain, packed, beta, F, h, ws, path=BL_PATH_AUTO, eps=1e-8,
                           stream=None):
-    M, K = x.shape
+    M, K = _check_layer_io(x, gain, packed, beta, 2 * F, h, F)
+    _need(ws, "ws", numel=1)
     _check("bitlinear_forward_glu", lib().bitlinear_forward_glu(
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), F,
         _ptr(h), DTYPE_CODE[h.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
@@ -188,7 +244,10 @@ def make_calls(items):
     """ctypes array of bl_call from (x, gain, packed, beta, y) tensor tuples."""
     arr = (BlCall * len(items))()
     for i, (x, gain, packed, beta, y) in enumerate(items):
-        M, K = x.shape
+        _need(y, "y", FLOATS, dims=2)
+        M, K = _check_layer_io(x, gain, packed, beta, y.shape[1], y, y.shape[1])
+        if y.shape[0] != M:
+            raise ValueError(f"y has {y.shape[0]} rows, x has {M}")
         arr[i] = BlCall(_ptr(x), _ptr(gain), _ptr(packed), _ptr(beta), _ptr(y), M, K,
                         y.shape[1])
     return arr
@@ -225,23 +284,52 @@ def bitlinear_forward_grouped_ws(calls, x_dtype, y_dtype, ws, eps=1e-8, stream=N
 
 
 def bitlinear_act_quant(x, gain, xq, s, rowsum, eps=1e-8, stream=None):
+    _need(x, "x", FLOATS, dims=2)
     M, K = x.shape
+    _need(gain, "gain", x.dtype, numel=K)
+    _need(xq, "xq", torch.int8, numel=M * K)
+    _need(s, "s", torch.float32, numel=M)
+    _need(rowsum, "rowsum", torch.int32, numel=M)
     _check("bitlinear_act_quant", lib().bitlinear_act_quant(
         _ptr(x), DTYPE_CODE[x.dtype], _ptr(gain), M, K, eps, _ptr(xq), _ptr(s),
         _ptr(rowsum), _stream(stream)))
 
 
-def bitlinear_gemm_i32(xq, rowsum, packed, N, acc, path=BL_PATH_AUTO, stream=None):
+def _check_codes(xq, rowsum, packed, N, s=None, beta=None):
+    _need(xq, "xq", torch.int8, dims=2)
     M, K = xq.shape
+    _need(rowsum, "rowsum", torch.int32, numel=M)
+    _need(packed, "packed", numel=1)
+    if _nbytes(packed) < N * K // 4:
+        raise ValueError(f"packed holds {_nbytes(packed)} bytes, an [{N}, {K}] matrix needs "
+                         f"{N * K // 4}")
+    if s is not None or beta is not None:
+        _need(s, "s", torch.float32, numel=M)
+        _need(beta, "beta", torch.float32, numel=1)
+    return M, K
+
+
+def bitlinear_gemm_i32(xq, rowsum, packed, N, acc, path=BL_PATH_AUTO, stream=None):
+    M, K = _check_codes(xq, rowsum, packed, N)
+    _need(acc, "acc", torch.int32, numel=M * N)
     _check("bitlinear_gemm_i32", lib().bitlinear_gemm_i32(
         _ptr(xq), _ptr(rowsum), M, K, _ptr(packed), N, _ptr(acc), path, _stream(stream)))
 
 
 def bitlinear_contract(xq, s, rowsum, packed, beta, N, y, path=BL_PATH_AUTO, stream=None):
-    M, K = xq.shape
+    M, K = _check_codes(xq, rowsum, packed, N, s, beta)
+    _need(y, "y", FLOATS, numel=M * N)
     _check("bitlinear_contract", lib().bitlinear_contract(
         _ptr(xq), _ptr(s), _ptr(rowsum), M, K, _ptr(packed), _ptr(beta), N, _ptr(y),
         DTYPE_CODE[y.dtype], path, _stream(stream)))
+
+
+def bitlinear_contract_glu(xq, s, rowsum, packed, beta, F, h, path=BL_PATH_AUTO, stream=None):
+    M, K = _check_codes(xq, rowsum, packed, 2 * F, s, beta)
+    _need(h, "h", FLOATS, numel=M * F)
+    _check("bitlinear_contract_glu", lib().bitlinear_contract_glu(
+        _ptr(xq), _ptr(s), _ptr(rowsum), M, K, _ptr(packed), _ptr(beta), F, _ptr(h),
+        DTYPE_CODE[h.dtype], path, _stream(stream)))
 
 
 def make_contract_calls(items):
@@ -249,7 +337,10 @@ def make_contract_calls(items):
     tensor tuples."""
     arr = (BlContractCall * len(items))()
     for i, (xq, s, rowsum, packed, beta, y) in enumerate(items):
-        M, K = xq.shape
+        _need(y, "y", FLOATS, dims=2)
+        M, K = _check_codes(xq, rowsum, packed, y.shape[1], s, beta)
+        if y.shape[0] != M:
+            raise ValueError(f"y has {y.shape[0]} rows, xq has {M}")
         arr[i] = BlContractCall(_ptr(xq), _ptr(s), _ptr(rowsum), _ptr(packed), _ptr(beta),
                                 _ptr(y), M, K, y.shape[1])
     return arr
@@ -264,5 +355,10 @@ def bitlinear_contract_grouped(calls, y_dtype, stream=None):
 
 
 def bitlinear_unpack_weights(packed, N, K, Wq, stream=None):
+    _need(packed, "packed", numel=1)
+    if _nbytes(packed) < N * K // 4:
+        raise ValueError(f"packed holds {_nbytes(packed)} bytes, an [{N}, {K}] matrix needs "
+                         f"{N * K // 4}")
+    _need(Wq, "Wq", torch.int8, numel=N * K)
     _check("bitlinear_unpack_weights", lib().bitlinear_unpack_weights(
         _ptr(packed), N, K, _ptr(Wq), _stream(stream)))

@@ -489,6 +489,40 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
                                          stream));
 }
 
+int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rowsum, int64_t M,
+                           int64_t K, const void *packed, const float *beta, int64_t F, void *h,
+                           int h_dtype, int path, hipStream_t stream) {
+  if (!dtype_ok(h_dtype)) return BL_ERR_DTYPE;
+  if (F <= 0 || F % 16 != 0 || !nk_ok(2 * F, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (path != BL_PATH_AUTO && path != BL_PATH_SKINNY && path != BL_PATH_MFMA) return BL_ERR_PATH;
+  if (M == 0) return BL_OK;
+  if (!xq || !s || !rowsum || !packed || !beta || !h) return BL_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(packed) || !aligned16(h) ||
+      (reinterpret_cast<uintptr_t>(s) & 3u) || (reinterpret_cast<uintptr_t>(rowsum) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
+  if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
+  if (path == BL_PATH_SKINNY) {
+    bl::SkinnyArgs a{};
+    a.fused = false;
+    a.xq = xq;
+    a.s = s;
+    a.rowsum = rowsum;
+    a.packed = packed;
+    a.beta = beta;
+    a.M = M;
+    a.N = 2 * F;
+    a.K = K;
+    a.out = h;
+    a.out_kind = h_dtype;
+    a.glu = true;
+    return hip_status(bl::launch_skinny(a, stream));
+  }
+  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, 2 * F, K, h, h_dtype,
+                                         true, stream));
+}
+
 int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
                                hipStream_t stream) {
   if (!dtype_ok(y_dtype)) return BL_ERR_DTYPE;
@@ -539,3 +573,4 @@ int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
 }
 
 }  // extern "C"
+

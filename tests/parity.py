@@ -25,8 +25,48 @@ RTOL = {"fp32": 2e-3, "fp16": 2e-3, "bf16": 2e-3 + 2.0 ** -8}
 BAND = 1e-4
 
 
+GUARD = 4096          # bytes of sentinel on each side of a guarded output
+GUARD_BYTE = 0xA5
+
+
 def say(*a):
     print(*a, flush=True)
+
+
+class Guarded:
+    """A device output with GUARD sentinel bytes on both sides: .t is the
+    contiguous [shape] view the kernels write (16-byte aligned), .check()
+    asserts that nothing was written outside it."""
+
+    def __init__(self, shape, dtype, fill=None):
+        self.shape = tuple(shape)
+        esz = torch.tensor([], dtype=dtype).element_size()
+        n = int(np.prod(self.shape)) * esz
+        self.n = n
+        self.full = torch.full((GUARD + n + GUARD,), GUARD_BYTE, dtype=torch.uint8, device=DEV)
+        self.t = self.full[GUARD:GUARD + n].view(dtype).view(self.shape)
+        if fill is not None:
+            self.t.fill_(fill)
+
+    def check(self, what="output"):
+        torch.cuda.synchronize()
+        head = self.full[:GUARD]
+        tail = self.full[GUARD + self.n:]
+        assert bool(torch.all(head == GUARD_BYTE)), f"{what}: write before the buffer"
+        assert bool(torch.all(tail == GUARD_BYTE)), f"{what}: write past the buffer"
+
+
+def contract_rows(xq, Wq, workers=16):
+    """oracle.contract over row blocks on a thread pool (rows are independent
+    and the oracle releases the GIL); the blocks are the oracle's own calls."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    M = xq.shape[0]
+    w = max(1, min(workers, len(os.sched_getaffinity(0)), M))
+    bounds = np.linspace(0, M, w + 1).round().astype(int)
+    with ThreadPoolExecutor(w) as ex:
+        parts = list(ex.map(lambda i: oracle.contract(xq[bounds[i]:bounds[i + 1]], Wq), range(w)))
+    return np.concatenate(parts, axis=0)
 
 
 def band_mask(v: np.ndarray) -> np.ndarray:
@@ -63,12 +103,13 @@ def check_pack(W_cpu: torch.Tensor):
 
 def gpu_act_quant(x_dev, g_dev, eps=1e-8):
     M, K = x_dev.shape
-    xq = torch.empty(M, K, dtype=torch.int8, device=DEV)
-    s = torch.empty(M, dtype=torch.float32, device=DEV)
-    rs = torch.empty(M, dtype=torch.int32, device=DEV)
-    tw.bitlinear_act_quant(x_dev, g_dev, xq, s, rs, eps=eps)
-    torch.cuda.synchronize()
-    return xq.cpu().numpy(), s.cpu().numpy(), rs.cpu().numpy()
+    xq = Guarded((M, K), torch.int8)
+    s = Guarded((M,), torch.float32)
+    rs = Guarded((M,), torch.int32)
+    tw.bitlinear_act_quant(x_dev, g_dev, xq.t, s.t, rs.t, eps=eps)
+    for b, name in ((xq, "xq"), (s, "s"), (rs, "rowsum")):
+        b.check(name)
+    return xq.t.cpu().numpy(), s.t.cpu().numpy(), rs.t.cpu().numpy()
 
 
 def check_xq(xq_gpu, s_gpu, ref):
@@ -108,8 +149,13 @@ def y_to_np(y: torch.Tensor) -> np.ndarray:
 
 
 def run_forward(x_cpu, g_cpu, d_packed, d_beta, N, y_dtype, path=tw.BL_PATH_AUTO, eps=1e-8):
+    """bitlinear_forward_path with the output and the workspace guarded."""
     x = x_cpu.to(DEV)
     g = g_cpu.to(DEV)
-    y = tw.forward(x, g, d_packed, d_beta, N, eps=eps, out_dtype=synth.DTYPES[y_dtype], path=path)
-    torch.cuda.synchronize()
-    return y_to_np(y), x, g
+    M, K = x.shape
+    y = Guarded((M, N), synth.DTYPES[y_dtype])
+    ws = Guarded((max(16, tw.bitlinear_workspace_bytes(M, K, N)),), torch.uint8)
+    tw.bitlinear_forward_path(x, g, d_packed, d_beta, N, y.t, ws.t, path, eps=eps)
+    y.check("y")
+    ws.check("workspace")
+    return y_to_np(y.t), x, g

@@ -308,3 +308,79 @@ def test_glu_entry_points_validation():
     assert glu(A, 1, 65, 1024, B, C, D, 48, Y, 1, 1e-8, WSP,
                L.bitlinear_workspace_bytes(65, 1024, 96), 2, None) == SHAPE
     assert glu(A, 1, 0, 1024, B, C, D, 48, None, 1, 1e-8, None, 0, 0, None) == OK
+
+
+def test_contract_glu_validation():
+    L = tw.lib()
+    cg = L.bitlinear_contract_glu
+    assert cg(A, B, C, 8, 1024, D, E, 48, Y, 9, 0, None) == DTYPE
+    assert cg(A, B, C, 8, 1024, D, E, 40, Y, 1, 0, None) == SHAPE      # F % 16
+    assert cg(A, B, C, 8, 1000, D, E, 48, Y, 1, 0, None) == SHAPE      # K % 128
+    assert cg(A, B, C, 8, 1024, D, E, 48, Y, 1, 1, None) == PATH       # fused is not a contraction path
+    assert cg(A, B, C, 65, 1024, D, E, 48, Y, 1, 2, None) == SHAPE     # skinny is M <= 64
+    assert cg(A, None, C, 8, 1024, D, E, 48, Y, 1, 0, None) == NULL
+    assert cg(A, B, C, 8, 1024, D, E, 48, Y + 8, 1, 0, None) == ALIGN
+    assert cg(A, B + 2, C, 8, 1024, D, E, 48, Y, 1, 0, None) == ALIGN
+    assert cg(None, None, None, 0, 1024, None, None, 48, None, 1, 0, None) == OK
+
+
+def test_binding_checks_sizes_before_pointers():
+    """The binding checks dtype and element counts of every tensor against
+    the call's shape before it takes a pointer (the C ABI cannot see sizes):
+    mis-sized host tensors are refused for their size, well-sized ones get as
+    far as the device check."""
+    import torch
+    f16, i8, i32, f32 = torch.float16, torch.int8, torch.int32, torch.float32
+    M, K, N = 4, 256, 64
+    x = torch.zeros(M, K, dtype=f16)
+    g = torch.zeros(K, dtype=f16)
+    pk = torch.zeros(N * K // 4, dtype=torch.uint8)
+    beta = torch.zeros(1, dtype=f32)
+    y = torch.zeros(M, N, dtype=f16)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+
+    def refused(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    # well-sized: reaches the pointer check
+    refused(tw.bitlinear_forward, x, g, pk, beta, N, y, ws, match="GPU")
+    refused(tw.bitlinear_forward, x, g[:K - 8], pk, beta, N, y, ws, match="gain")
+    refused(tw.bitlinear_forward, x, g.float(), pk, beta, N, y, ws, match="gain")
+    refused(tw.bitlinear_forward, x, g, pk[:100], beta, N, y, ws, match="packed")
+    refused(tw.bitlinear_forward, x, g, pk, beta.half(), N, y, ws, match="beta")
+    refused(tw.bitlinear_forward, x, g, pk, beta, N, y[:, :N - 1].contiguous(), ws, match="y")
+    refused(tw.bitlinear_forward, x.view(-1), g, pk, beta, N, y, ws, match="x")
+    refused(tw.bitlinear_forward_path, x, g, pk, beta, N, y[:2], ws, 0, match="y")
+    F = N // 2
+    h = torch.zeros(M, F, dtype=f16)
+    refused(tw.bitlinear_forward_glu, x, g, pk, beta, F, h, ws, match="GPU")
+    refused(tw.bitlinear_forward_glu, x, g, pk, beta, F, h[:3], ws, match="h|y")
+    refused(tw.bitlinear_forward_glu, x, g, pk[:N * K // 8], beta, F, h, ws, match="packed")
+    xq = torch.zeros(M, K, dtype=i8)
+    s = torch.zeros(M, dtype=f32)
+    rs = torch.zeros(M, dtype=i32)
+    refused(tw.bitlinear_act_quant, x, g, xq, s, rs, match="GPU")
+    refused(tw.bitlinear_act_quant, x, g, xq[:3], s, rs, match="xq")
+    refused(tw.bitlinear_act_quant, x, g, xq, s[:3], rs, match="s ")
+    refused(tw.bitlinear_act_quant, x, g, xq, s, rs.float(), match="rowsum")
+    acc = torch.zeros(M, N, dtype=i32)
+    refused(tw.bitlinear_gemm_i32, xq, rs, pk, N, acc, match="GPU")
+    refused(tw.bitlinear_gemm_i32, xq, rs, pk, N, acc[:2], match="acc")
+    refused(tw.bitlinear_gemm_i32, xq, rs, pk, 2 * N, acc, match="packed")
+    refused(tw.bitlinear_contract, xq, s, rs, pk, beta, N, y, match="GPU")
+    refused(tw.bitlinear_contract, xq, s[:1], rs, pk, beta, N, y, match="s ")
+    refused(tw.bitlinear_contract_glu, xq, s, rs, pk, beta, F, h, match="GPU")
+    refused(tw.bitlinear_contract_glu, xq, s, rs, pk, beta, F, h[:1], match="h")
+    refused(tw.make_calls, [(x, g, pk, beta, y)], match="GPU")
+    refused(tw.make_calls, [(x, g, pk, beta, y[:2])], match="y")
+    refused(tw.make_contract_calls, [(xq, s, rs, pk, beta, y)], match="GPU")
+    refused(tw.make_contract_calls, [(xq, s, rs, pk[:8], beta, y)], match="packed")
+    Wf = torch.zeros(N, K, dtype=f32)
+    refused(tw.bitlinear_pack_weights, Wf, pk, beta, ws, match="GPU")
+    refused(tw.bitlinear_pack_weights, Wf.half(), pk, beta, ws, match="W")
+    refused(tw.bitlinear_pack_weights, Wf, pk[:N * K // 8], beta, ws, match="packed")
+    Wq = torch.zeros(N, K, dtype=i8)
+    refused(tw.bitlinear_unpack_weights, pk, N, K, Wq, match="GPU")
+    refused(tw.bitlinear_unpack_weights, pk, N, K, Wq[:2], match="Wq")
+

@@ -2,11 +2,12 @@
 SiLU gate fused into the projection's epilogue) against the oracle.
 
 Bar: packed bytes and beta bit-exact (as for any pack).  h is held to the
-bound that the y bar implies through the gate: with tol(v) = 1e-3 + r |v|
-the y tolerance (r per output dtype), and |silu'| <= 1.1,
-  |h_gpu - h| <= 1.1 tol(g) (|u| + tol(u)) + |silu(g)| tol(u),
-g, u the oracle's fp64 gated and multiplied outputs.  Rows whose int8 codes
-differ under the .5-band rule are re-checked from the GPU's own codes.
+stated output tolerance itself, |h_gpu - h| <= 1e-3 + r |h| (r per output
+dtype, as for y), h the oracle's fp64 silu(y_gate) * y_up: the kernels form
+h in fp32 from the exact int32 accumulators, so only the fp32 rescale, the
+SiLU evaluation (~1e-6 relative) and the output rounding separate the two.
+Rows whose int8 codes differ under the .5-band rule are re-checked from the
+GPU's own codes.  Outputs and workspaces carry guard bands.
 """
 import numpy as np
 import pytest
@@ -15,26 +16,19 @@ import torch
 import oracle
 import ternary_weight_lm_amd as tw
 from ternary_weight_lm_amd import synth
-from tests.parity import ATOL, DEV, RTOL, check_xq, gpu_act_quant, say, y_to_np
+from tests.parity import ATOL, DEV, RTOL, Guarded, check_xq, gpu_act_quant, say, y_to_np
 
 pytestmark = pytest.mark.gpu
 
 
-def _silu(a):
-    return a / (1.0 + np.exp(-a))
-
-
-def h_tolerance(y, F, dtype):
-    g, u = y[:, :F], y[:, F:]
-    tg = ATOL + RTOL[dtype] * np.abs(g)
-    tu = ATOL + RTOL[dtype] * np.abs(u)
-    return 1.1 * tg * (np.abs(u) + tu) + np.abs(_silu(g)) * tu
+def h_tolerance(h, dtype):
+    return ATOL + RTOL[dtype] * np.abs(h)
 
 
 def check_h(h_gpu, ref, F, dtype, Wq, beta, xq_gpu, s_gpu, rows=None):
     y = ref["y"] if rows is None else ref["y"][rows]
     h = oracle.glu(y)
-    bad = np.abs(h_gpu - h) > h_tolerance(y, F, dtype)
+    bad = np.abs(h_gpu - h) > h_tolerance(h, dtype)
     if not bad.any():
         return
     xo = ref["xq"] if rows is None else ref["xq"][rows]
@@ -44,7 +38,7 @@ def check_h(h_gpu, ref, F, dtype, Wq, beta, xq_gpu, s_gpu, rows=None):
             f"{float(np.max(np.abs(h_gpu[r] - h[r])))}")
         y_r = oracle.epilogue(oracle.contract(xq_gpu[r:r + 1], Wq), s_gpu[r:r + 1], beta)
         h_r = oracle.glu(y_r)
-        assert np.all(np.abs(h_gpu[r] - h_r[0]) <= h_tolerance(y_r, F, dtype)[0])
+        assert np.all(np.abs(h_gpu[r] - h_r[0]) <= h_tolerance(h_r, dtype)[0])
 
 
 def check_pack_glu(W_cpu):
@@ -94,12 +88,15 @@ def test_forward_glu_matches_oracle(path, M, F, K, xdt, hdt):
     W = synth.make_w(seed, 0, 0, 2 * F, K, zero_row_frac=0.05)
     o_Wq, o_beta, d_packed, d_beta = check_pack_glu(W)
     xd, gd = x.to(DEV), g.to(DEV)
-    h = tw.forward_glu(xd, gd, d_packed, d_beta, F, out_dtype=synth.DTYPES[hdt], path=path)
-    torch.cuda.synchronize()
+    h = Guarded((M, F), synth.DTYPES[hdt])
+    ws = Guarded((max(16, tw.bitlinear_workspace_bytes(M, K, 2 * F)),), torch.uint8)
+    tw.bitlinear_forward_glu(xd, gd, d_packed, d_beta, F, h.t, ws.t, path=path)
+    h.check("h")
+    ws.check("workspace")
     ref = oracle.forward_glu(synth.widen(x), synth.widen(g), o_Wq, o_beta)
     xq_gpu, s_gpu, _ = gpu_act_quant(xd, gd)
     check_xq(xq_gpu, s_gpu, ref)
-    check_h(y_to_np(h), ref, F, hdt, o_Wq, o_beta, xq_gpu, s_gpu)
+    check_h(y_to_np(h.t), ref, F, hdt, o_Wq, o_beta, xq_gpu, s_gpu)
 
 
 def test_glu_pairing_matches_unfused_projection():
@@ -142,8 +139,12 @@ def test_forward_glu_full_size_sampled(M, F, K, path):
     W = synth.make_w(77, 0, 1, 2 * F, K, zero_row_frac=0.05)
     o_Wq, o_beta, d_packed, d_beta = check_pack_glu(W)
     xd, gd = x.to(DEV), g.to(DEV)
-    h = tw.forward_glu(xd, gd, d_packed, d_beta, F, path=path)
-    torch.cuda.synchronize()
+    hg = Guarded((M, F), torch.bfloat16)
+    ws = Guarded((max(16, tw.bitlinear_workspace_bytes(M, K, 2 * F)),), torch.uint8)
+    tw.bitlinear_forward_glu(xd, gd, d_packed, d_beta, F, hg.t, ws.t, path=path)
+    hg.check("h")
+    ws.check("workspace")
+    h = hg.t
     rows = np.unique(np.linspace(0, M - 1, min(M, 6)).round().astype(int))
     ref = oracle.forward_glu(synth.widen(x)[rows], synth.widen(g), o_Wq, o_beta)
     xq_gpu, s_gpu, _ = gpu_act_quant(xd, gd)

@@ -9,8 +9,8 @@ import torch
 import oracle
 import ternary_weight_lm_amd as tw
 from ternary_weight_lm_amd import synth
-from tests.parity import (DEV, check_pack, check_xq, check_y, gpu_act_quant,
-                          run_forward, say, y_to_np)
+from tests.parity import (DEV, Guarded, check_pack, check_xq, check_y, contract_rows,
+                          gpu_act_quant, run_forward, say, y_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,10 +121,65 @@ def test_gemm_i32_bit_exact(path, M, N, K):
     packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
     d_xq = torch.from_numpy(xq).to(DEV)
     d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
-    acc = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
-    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc, path=path)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.contract(xq, Wq))
+    acc = Guarded((M, N), torch.int32, fill=-7)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc.t, path=path)
+    acc.check("acc")
+    np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
+
+
+@pytest.mark.parametrize("M,N,K", [(3072, 8192, 128), (3000, 8224, 128), (4096, 2560, 256)])
+def test_gemm_i32_wide_tile_launches_full(M, N, K):
+    """Launches of at least 768 tiles of 128 x 256, the ones whose waves each
+    hold four packed tiles (3072 x 8192: exactly 768; 3000 x 8224: 792 with a
+    ragged last tile row and tile column; 4096 x 2560: 320 tiles, below the
+    threshold, for contrast), every element of the int32 result against the
+    oracle's contraction, with guard bands around the output."""
+    say(f"gemm_i32 wide tiles M={M} N={N} K={K}")
+    xq = _random_codes(M, K, M + N + K)
+    r = np.random.default_rng(M * 3 + N)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wq[N - 1] = 1
+    Wq[N - 2] = -1
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = Guarded((M, N), torch.int32, fill=-7)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc.t, path=tw.BL_PATH_MFMA)
+    acc.check("acc")
+    np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
+
+
+@pytest.mark.parametrize("ydt", ["bf16", "fp16"])
+def test_contract_grouped_wide_full(ydt):
+    """A grouped launch of three 3072 x 4096 x 128 contractions (1152 tiles of
+    128 x 256 across the calls: the grouped kernel's 4-tile waves, as i/f/g
+    at prefill), every output element against the oracle's int32
+    contraction rescaled as the epilogue does it (fp32 acc times the
+    correctly rounded fp32 beta / s, rounded once to the output dtype), each
+    output guarded."""
+    say(f"contract_grouped wide tiles y={ydt}")
+    M, N, K = 3072, 4096, 128
+    items, refs, outs = [], [], []
+    for j in range(3):
+        xq = _random_codes(M, K, 500 + j)
+        r = np.random.default_rng(600 + j)
+        Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+        s = r.uniform(0.5, 40.0, size=M).astype(np.float32)
+        beta = np.float32(0.0155 + 0.001 * j)
+        d_xq = torch.from_numpy(xq).to(DEV)
+        d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+        y = Guarded((M, N), synth.DTYPES[ydt])
+        items.append((d_xq, torch.from_numpy(s).to(DEV), d_rs,
+                      torch.from_numpy(oracle.pack(Wq)).to(DEV),
+                      torch.tensor([beta], dtype=torch.float32, device=DEV), y.t))
+        outs.append(y)
+        refs.append((contract_rows(xq, Wq), s, beta))
+    tw.bitlinear_contract_grouped(items, synth.DTYPES[ydt])
+    for j, (y, (acc, s, beta)) in enumerate(zip(outs, refs)):
+        y.check(f"y[{j}]")
+        scale = (torch.tensor(beta) / torch.from_numpy(s)).to(torch.float32)
+        want = (torch.from_numpy(acc).to(torch.float32) * scale[:, None]).to(y.t.dtype)
+        assert torch.equal(y.t.cpu().view(torch.int16), want.view(torch.int16)), f"call {j}"
 
 
 FWD_CASES = [
