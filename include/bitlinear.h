@@ -99,7 +99,8 @@ enum {
     BL_ERR_EPS = -6,         /* eps not finite or not > 0                   */
     BL_ERR_HIP = -7,         /* a HIP launch or query failed                */
     BL_ERR_UNSUPPORTED = -8, /* valid request the library does not implement */
-    BL_ERR_PATH = -9         /* unknown execution path code                 */
+    BL_ERR_PATH = -9,        /* unknown execution path code                 */
+    BL_ERR_SCRATCH = -10     /* beyond bitlinear_forward_noalloc's scratch  */
 };
 
 /* execution paths for bitlinear_forward_path / bitlinear_gemm_i32 */
@@ -270,6 +271,28 @@ int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, cons
                           const void *packed, const float *beta, int64_t F, void *h,
                           int h_dtype, float eps, void *ws, size_t ws_bytes, int path,
                           hipStream_t stream);
+
+/* ------------------------------------------------- no-allocation forward
+ * For callers that cannot allocate device memory at all -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc --
+ * bitlinear_forward without the workspace argument: the int8 activations,
+ * per-row scales and row sums that pass between its act-quant and
+ * contraction launches live in a static device array of
+ * bitlinear_noalloc_max_scratch_bytes() bytes (32 MiB) inside the library,
+ * one per GPU, held until the process ends.  Nothing is allocated per call
+ * (no hipMalloc / hipFree); the first call on a device looks the array's
+ * address up once.
+ *   Arguments, results and errors as bitlinear_forward (same kernels, same
+ *   bits), except: a call whose workspace would exceed the scratch (M * K +
+ *   8 M bytes, 256-byte aligned pieces, more than 32 MiB) is rejected with
+ *   BL_ERR_SCRATCH before anything is launched.
+ *   Every call on one GPU shares that GPU's array and overwrites it before
+ *   reading it; calls that overlap in time on one GPU (different streams,
+ *   host threads) race on it and must be ordered by the caller. */
+size_t bitlinear_noalloc_max_scratch_bytes(void);
+int bitlinear_forward_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, const void *gain,
+                              const void *packed, const float *beta, int64_t N, void *y,
+                              int y_dtype, float eps, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(int status);

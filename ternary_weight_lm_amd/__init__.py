@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     bitlinear_forward_glu, bitlinear_forward_path, bitlinear_pack_glu_weights, make_calls,
     bitlinear_gemm_i32, bitlinear_pack_weights, bitlinear_pack_workspace_bytes,
     bitlinear_packed_bytes, bitlinear_select_path, bitlinear_status_string, bitlinear_unpack_weights,
-    bitlinear_workspace_bytes,
+    bitlinear_workspace_bytes, bitlinear_forward_noalloc, bitlinear_noalloc_max_scratch_bytes,
 )
 
 

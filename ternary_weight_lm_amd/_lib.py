@@ -21,7 +21,7 @@ BL_PATH_AUTO, BL_PATH_FUSED, BL_PATH_SKINNY, BL_PATH_MFMA = 0, 1, 2, 3
 STATUS = {
     0: "BL_OK", -1: "BL_ERR_NULL", -2: "BL_ERR_DTYPE", -3: "BL_ERR_SHAPE",
     -4: "BL_ERR_ALIGN", -5: "BL_ERR_WORKSPACE", -6: "BL_ERR_EPS",
-    -7: "BL_ERR_HIP", -8: "BL_ERR_UNSUPPORTED", -9: "BL_ERR_PATH",
+    -7: "BL_ERR_HIP", -8: "BL_ERR_UNSUPPORTED", -9: "BL_ERR_PATH", -10: "BL_ERR_SCRATCH",
 }
 
 DTYPE_CODE = {torch.float32: BL_F32, torch.float16: BL_F16, torch.bfloat16: BL_BF16}
@@ -79,6 +79,8 @@ SIGNATURES = {
     "bitlinear_pack_glu_weights": ([P, I64, I64, P, P, P, SZ, P], I),
     "bitlinear_forward_glu": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
+    "bitlinear_noalloc_max_scratch_bytes": ([], SZ),
+    "bitlinear_forward_noalloc": ([P, I, I64, I64, P, P, P, I64, P, I, F, P], I),
 }
 
 
@@ -220,6 +222,19 @@ def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stre
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
         _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
         path, _stream(stream)))
+
+
+def bitlinear_noalloc_max_scratch_bytes() -> int:
+    return int(lib().bitlinear_noalloc_max_scratch_bytes())
+
+
+def bitlinear_forward_noalloc(x, gain, packed, beta, N, y, eps=1e-8, stream=None):
+    """bitlinear_forward with the library's static scratch instead of a
+    workspace (no device allocation anywhere in the call)."""
+    M, K = _check_layer_io(x, gain, packed, beta, N, y, N)
+    _check("bitlinear_forward_noalloc", lib().bitlinear_forward_noalloc(
+        _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
+        _ptr(y), DTYPE_CODE[y.dtype], eps, _stream(stream)))
 
 
 def bitlinear_pack_glu_weights(W, packed, beta, ws, stream=None):

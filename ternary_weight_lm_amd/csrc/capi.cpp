@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "bitlinear.h"
@@ -91,6 +92,7 @@ const char *bitlinear_status_string(int status) {
     case BL_ERR_HIP: return "HIP launch failed";
     case BL_ERR_UNSUPPORTED: return "unsupported request";
     case BL_ERR_PATH: return "unknown or inapplicable execution path";
+    case BL_ERR_SCRATCH: return "request needs more than the library's static scratch (32 MiB)";
     default: return "unknown status";
   }
 }
@@ -574,3 +576,55 @@ int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
 
 }  // extern "C"
 
+namespace {
+
+// Scratch of bitlinear_forward_noalloc: the int8 activations, per-row scales
+// and row sums its act-quant launch writes and its contraction launch reads,
+// held in a file-scope device array instead of a caller workspace.  Every
+// GPU the library runs on holds its own copy until the process ends.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of each device's copy of `scratch`, looked up once per
+// device (the host-side name is only a stand-in for the symbol).
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+int bitlinear_forward_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, const void *gain,
+                              const void *packed, const float *beta, int64_t N, void *y,
+                              int y_dtype, float eps, hipStream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (M == 0) return BL_OK;
+  if (!x || !gain || !packed || !beta || !y) return BL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(packed) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  if (fwd_ws_bytes(M, K) > kScratchBytes) return BL_ERR_SCRATCH;
+  void *ws = scratch_address();
+  if (!ws) return BL_ERR_HIP;
+  return forward_impl(x, x_dtype, M, K, gain, packed, beta, N, y, y_dtype, eps, ws,
+                      kScratchBytes, BL_PATH_AUTO, false, stream);
+}
+
+}  // extern "C"

@@ -384,3 +384,20 @@ def test_binding_checks_sizes_before_pointers():
     refused(tw.bitlinear_unpack_weights, pk, N, K, Wq, match="GPU")
     refused(tw.bitlinear_unpack_weights, pk, N, K, Wq[:2], match="Wq")
 
+
+def test_noalloc_validation():
+    """The no-allocation forward validates like bitlinear_forward and rejects
+    a request beyond its static scratch before touching any device."""
+    L = tw.lib()
+    cap = L.bitlinear_noalloc_max_scratch_bytes()
+    assert cap == 32 << 20
+    na = L.bitlinear_forward_noalloc
+    assert na(A, 9, 4, 1024, B, C, D, 1024, Y, 1, 1e-8, None) == DTYPE
+    assert na(A, 1, 4, 1000, B, C, D, 1024, Y, 1, 1e-8, None) == SHAPE
+    assert na(A, 1, 4, 1024, B, C, D, 1024, Y, 1, -1.0, None) == EPS
+    assert na(A, 1, 4, 1024, None, C, D, 1024, Y, 1, 1e-8, None) == NULL
+    assert na(A + 8, 1, 4, 1024, B, C, D, 1024, Y, 1, 1e-8, None) == ALIGN
+    assert na(None, 1, 0, 1024, None, None, None, 1024, None, 1, 1e-8, None) == OK
+    K = 8192
+    assert na(A, 1, cap // K + 1, K, B, C, D, 1024, Y, 1, 1e-8, None) == -10
+    assert L.bitlinear_status_string(-10).decode().startswith("request needs more")
