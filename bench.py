@@ -97,6 +97,10 @@ def parse(argv=None):
     ap.add_argument("--workload", default="c5",
                     help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, or an MLP "
                          "workload c3-mlp | c4-mlp | c5-M<M>-mlp")
+    ap.add_argument("--launch", choices=["per-call", "chain"], default="per-call",
+                    help="per-call: one launch group per projection (default); chain: a "
+                         "chained stack at 1..4 tokens runs as one persistent launch per step "
+                         "(bitlinear_chain_run)")
     ap.add_argument("--pool-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,7 +145,7 @@ class Call:
 class Workload:
     """The calls of one step and how they are grouped into launches."""
 
-    def __init__(self, key: str, M: int | None = None):
+    def __init__(self, key: str, M: int | None = None, launch: str = "per-call"):
         from ternary_weight_lm_amd import synth
         base = key.split("-M")[0]
         cfg = synth.CONFIGS[base]
@@ -169,6 +173,13 @@ class Workload:
                 else:  # down_proj
                     x, y = ("h",), ("x", layer + 1)
                 self.calls.append(Call(len(self.calls), layer, pi, p.name, p.K, p.N, glu, x, y))
+        # launch == "chain": a chained stack at 1..4 tokens (16-bit
+        # activations) runs as one persistent launch per step
+        # (bitlinear_chain_run); otherwise (the default) one launch group per
+        # projection, which measures faster on MI355X (see the design notes)
+        chain_ok = self.chained and M <= 4 and cfg.dtype in ("fp16", "bf16") \
+            and max(p.K for p in cfg.projs) <= 8192
+        self.launch = "chain" if chain_ok and launch == "chain" else "per-call"
 
     def path(self, c):
         import ternary_weight_lm_amd as tw
@@ -266,9 +277,14 @@ class Weights:
 
 class Buffers:
     """Activation buffers of one M: the synthetic inputs and every call's
-    output, plus the workspaces."""
+    output, plus the workspaces.  inp[i] / out[i] are the tensors call i
+    reads and writes.  distinct=False (the benchmark): outputs of one kind
+    share a buffer across layers (each is consumed before the next layer
+    writes it; x_l alternates between two buffers so the step input x_0 is
+    never overwritten); distinct=True (tests): every call writes a buffer of
+    its own, so every output survives the step."""
 
-    def __init__(self, wl, weights, dev):
+    def __init__(self, wl, weights, dev, distinct=False):
         import torch
         import ternary_weight_lm_amd as tw
         from ternary_weight_lm_amd import synth
@@ -283,19 +299,19 @@ class Buffers:
             if c.x == ("x", 0) and c.x not in self.t:
                 x, _, _ = synth.config_inputs(cfg, M, 0, 0)
                 self.t[c.x] = x.to(dev)
-        # chained: x_l for l >= 1 alternates between two buffers, so the
-        # step's input x_0 is never overwritten
-        dt_of = {("x",): xdt, ("y",): ydt, ("h",): xdt}
+        dt_of = {"x": xdt, "y": ydt, "h": xdt}
+        self.inp, self.out = {}, {}
+        writer = {}
         for c in wl.calls:
-            if c.y in self.t:
-                continue
-            if c.y[0] == "x":
-                alias = ("x", 1 + (c.y[1] - 1) % 2)
-                if alias not in self.t:
-                    self.t[alias] = torch.empty(M, c.n_out, dtype=xdt, device=dev)
-                self.t[c.y] = self.t[alias]
+            self.inp[c.idx] = self.out[writer[c.x]] if c.x in writer else self.t[c.x]
+            if distinct:
+                self.out[c.idx] = torch.empty(M, c.n_out, dtype=dt_of[c.y[0]], device=dev)
             else:
-                self.t[c.y] = torch.empty(M, c.n_out, dtype=dt_of[(c.y[0],)], device=dev)
+                key = ("x", 1 + (c.y[1] - 1) % 2) if c.y[0] == "x" else c.y
+                if key not in self.t:
+                    self.t[key] = torch.empty(M, c.n_out, dtype=dt_of[c.y[0]], device=dev)
+                self.out[c.idx] = self.t[key]
+            writer[c.y] = c.idx
         self.ws = {}
         for c in wl.calls:
             key = (c.K, c.N)
@@ -307,10 +323,31 @@ class Buffers:
                 items = [self.item(c, weights, weights.pool[0]) for c in grp]
                 gws = max(gws, tw.bitlinear_grouped_workspace_bytes(items, xdt))
         self.gws = torch.empty(gws, dtype=torch.uint8, device=dev)
+        self.plans = None
         torch.cuda.synchronize()
 
     def item(self, c, weights, pool):
-        return (self.t[c.x], weights.gains[c.idx], pool[c.idx], weights.betas[c.idx], self.t[c.y])
+        return (self.inp[c.idx], weights.gains[c.idx], pool[c.idx], weights.betas[c.idx],
+                self.out[c.idx])
+
+    def chain_plans(self, wl, weights):
+        """One planned chain per weight-pool copy (each in a workspace of its
+        own): a step runs the chain of its copy in one launch."""
+        import torch
+        import ternary_weight_lm_amd as tw
+        from ternary_weight_lm_amd import synth
+        if self.plans is None:
+            self.plans = []
+            for pool in weights.pool:
+                arr = tw.make_chain_calls([self.item(c, weights, pool) + (c.glu,)
+                                           for c in wl.calls])
+                nbytes = tw.bitlinear_chain_workspace_bytes(arr, wl.M)
+                raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.gws.device)
+                off = (-raw.data_ptr()) % 256
+                ws = raw[off:off + nbytes]
+                plan = tw.bitlinear_chain_plan(arr, wl.M, synth.DTYPES[wl.cfg.dtype], ws)
+                self.plans.append((plan, raw, arr))
+        return self.plans
 
 
 def launch_group(wl, grp, weights, bufs, pool, keep):
@@ -338,6 +375,10 @@ def launch_group(wl, grp, weights, bufs, pool, keep):
 
 def step_fn(wl, weights, bufs, s, keep):
     """Enqueue one step (weights from pool copy s)."""
+    import ternary_weight_lm_amd as tw
+    if wl.launch == "chain":
+        tw.bitlinear_chain_run(bufs.chain_plans(wl, weights)[s % weights.copies][0])
+        return
     pool = weights.pool[s % weights.copies]
     for grp in wl.groups():
         launch_group(wl, grp, weights, bufs, pool, keep)
@@ -376,7 +417,9 @@ def timed_replay(graphs):
 
 # ---------------------------------------------------------------- roofline
 
-KERNEL_NAME = {1: "bl::decode_kernel (norm+quant+contract+rescale in one launch)",
+KERNEL_NAME = {0: "bl::chain_kernel (the whole stack's calls in one persistent launch: "
+                  "norm+quant+contract+rescale per tile column, inputs handed on in-kernel)",
+               1: "bl::decode_kernel (norm+quant+contract+rescale in one launch)",
                2: "bl::skinny_kernel<pre-quantized> (contract+rescale)",
                3: "bl::gemm_mfma_kernel (contract+rescale)"}
 
@@ -402,9 +445,9 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
     import torch
     import ternary_weight_lm_amd as tw
 
-    path = dominant_path(wl)
-    sel = [c for c in wl.calls if wl.path(c) == path]
-    bound = "hbm" if path in (tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY) else "mfma"
+    path = 0 if wl.launch == "chain" else dominant_path(wl)
+    sel = [c for c in wl.calls if path == 0 or wl.path(c) == path]
+    bound = "hbm" if path in (0, tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY) else "mfma"
     units = []
     for grp in wl.groups():
         mine = [c for c in grp if wl.path(c) == path]
@@ -414,14 +457,16 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
             units.append(mine)
         else:
             units.extend([c] for c in mine)
-    if len(sel) == len(wl.calls) and path == tw.BL_PATH_FUSED and step_ms is not None:
+    if path == 0:
+        units = [wl.calls]
+    if len(sel) == len(wl.calls) and path in (0, tw.BL_PATH_FUSED) and step_ms is not None:
         passes, ms = steps, step_ms * steps
         timed_region = "the benchmark steps themselves (every launch is this kernel)"
     else:
         stage = {}
         if path != tw.BL_PATH_FUSED:
             for c in sel:
-                x = bufs.t[c.x]
+                x = bufs.inp[c.idx]
                 xq = torch.empty(wl.M, c.K, dtype=torch.int8, device=x.device)
                 sc = torch.empty(wl.M, dtype=torch.float32, device=x.device)
                 rs = torch.empty(wl.M, dtype=torch.int32, device=x.device)
@@ -440,19 +485,19 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
                 items = []
                 for c in unit:
                     xq, sc, rs = stage[c.idx]
-                    items.append((xq, sc, rs, pool[c.idx], weights.betas[c.idx], bufs.t[c.y]))
+                    items.append((xq, sc, rs, pool[c.idx], weights.betas[c.idx], bufs.out[c.idx]))
                 arr = tw.make_contract_calls(items)
                 keep.append(arr)
-                tw.bitlinear_contract_grouped(arr, bufs.t[unit[0].y].dtype)
+                tw.bitlinear_contract_grouped(arr, bufs.out[unit[0].idx].dtype)
                 return
             c = unit[0]
             xq, sc, rs = stage[c.idx]
             if c.glu:
                 tw.bitlinear_contract_glu(xq, sc, rs, pool[c.idx], weights.betas[c.idx], c.n_out,
-                                          bufs.t[c.y], path=path)
+                                          bufs.out[c.idx], path=path)
             else:
                 tw.bitlinear_contract(xq, sc, rs, pool[c.idx], weights.betas[c.idx], c.N,
-                                      bufs.t[c.y], path=path)
+                                      bufs.out[c.idx], path=path)
 
         graphs = capture(launch, 0, reps * nunits, 1)
         graphs[0][0].replay()                      # warm the replay path
@@ -473,7 +518,7 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
                "frac": round(ach / I8_PEAK_TOPS, 5)}
     out["traffic"] = None
     out["kernel"] = KERNEL_NAME[path] + (" (i/f/g grouped per launch; GLU gate variant for "
-                                         "gate_proj)" if wl.chained else "")
+                                         "gate_proj)" if wl.chained and path != 0 else "")
     out["calls_timed"] = f"{len(sel)} of {len(wl.calls)} calls per step (those on this path)"
     out["launches"] = total
     out["avg_kernel_us"] = round(sec * 1e6 / total, 3)
@@ -494,7 +539,10 @@ def run_m(wl, weights, dev, args):
     warmup = args.warmup if args.warmup is not None else (3 if big else 10)
     reps = args.roofline_reps if args.roofline_reps is not None else (2 if big else 10)
     groups = wl.groups()
-    per_step = sum(1 if len(g) > 1 and wl.path(g[0]) == 1 else 2 for g in groups)
+    per_step = 1 if wl.launch == "chain" else \
+        sum(1 if len(g) > 1 and wl.path(g[0]) == 1 else 2 for g in groups)
+    if wl.launch == "chain":
+        bufs.chain_plans(wl, weights)
 
     def fn(s, keep):
         step_fn(wl, weights, bufs, s, keep)
@@ -510,7 +558,8 @@ def run_m(wl, weights, dev, args):
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     torch.cuda.synchronize()
     return {"M": wl.M, "tokens_per_s": round(wl.M * steps / (ms / 1e3), 2), "steps": steps,
-            "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+            "warmup": warmup, "ms_per_step": round(ms / steps, 6), "launch": wl.launch,
+            "launches_per_step": 1 if wl.launch == "chain" else per_step,
             "launch_groups_per_step": len(groups), "roofline": roof}, bufs
 
 
@@ -747,13 +796,13 @@ def main():
     sweep = args.workload == "c5"
     Ms = list(C5_SWEEP) if sweep else [None]
     t_setup = time.perf_counter()
-    wl0 = Workload(args.workload, M=Ms[0])
+    wl0 = Workload(args.workload, M=Ms[0], launch=args.launch)
     weights = Weights(wl0, args.pool_mib << 20, dev)
     setup_s = time.perf_counter() - t_setup
     results, last = [], None
     for M in Ms:
-        wl = Workload(args.workload, M=M)
-        print(f"# timing {wl.name()}", file=sys.stderr, flush=True)
+        wl = Workload(args.workload, M=M, launch=args.launch)
+        print(f"# timing {wl.name()} ({wl.launch})", file=sys.stderr, flush=True)
         res, bufs = run_m(wl, weights, dev, args)
         del bufs
         torch.cuda.empty_cache()
@@ -764,10 +813,15 @@ def main():
     cfgd = dict(wl.describe(),
                 weight_pool_MiB=round(weights.set_bytes * weights.copies / 2**20, 1),
                 weight_copies=weights.copies,
-                launch=(f"hipGraph; {head['launch_groups_per_step']} launch groups per step "
-                        "(a layer's i/f/g grouped on one input: one fused decode launch, or one "
-                        "shared act-quant launch + one GEMM launch on the MFMA path; every other "
-                        "projection one fused launch or act-quant + contraction)"),
+                launch=(("hipGraph; the whole step as one persistent chained launch "
+                         "(bitlinear_chain_run)" if wl.launch == "chain" else
+                         "hipGraph; per layer i/f/g grouped on one input (one fused decode "
+                         "launch, or one shared act-quant launch + one GEMM launch on the MFMA "
+                         "path), every other projection one fused launch or act-quant + "
+                         "contraction") if wl.chained else
+                        f"hipGraph; {head['launch_groups_per_step']} launch groups per step (i/f/g "
+                        "grouped on one input; every other projection one fused launch or "
+                        "act-quant + contraction)"),
                 parallelism="single GPU", setup_s=round(setup_s, 1))
     if sweep:
         cfgd["workload"] = wl.name().rsplit("_M", 1)[0] + "_Msweep"
@@ -782,6 +836,7 @@ def main():
     if sweep:
         out["sweep"] = [{"M": r["M"], "tokens_per_s": r["tokens_per_s"],
                          "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+                         "launch": r["launch"], "launches_per_step": r["launches_per_step"],
                          "bound": r["roofline"]["bound"], "frac": r["roofline"]["frac"],
                          "achieved": r["roofline"]["achieved"], "unit": r["roofline"]["unit"],
                          "avg_kernel_us": r["roofline"]["avg_kernel_us"],

@@ -100,7 +100,8 @@ enum {
     BL_ERR_HIP = -7,         /* a HIP launch or query failed                */
     BL_ERR_UNSUPPORTED = -8, /* valid request the library does not implement */
     BL_ERR_PATH = -9,        /* unknown execution path code                 */
-    BL_ERR_SCRATCH = -10     /* beyond bitlinear_forward_noalloc's scratch  */
+    BL_ERR_SCRATCH = -10,    /* beyond bitlinear_forward_noalloc's scratch  */
+    BL_ERR_TIMEOUT = -11     /* a chained launch's bounded wait gave up     */
 };
 
 /* execution paths for bitlinear_forward_path / bitlinear_gemm_i32 */
@@ -271,6 +272,84 @@ int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, cons
                           const void *packed, const float *beta, int64_t F, void *h,
                           int h_dtype, float eps, void *ws, size_t ws_bytes, int path,
                           hipStream_t stream);
+
+/* ------------------------------------------------------ chained decode
+ * A decode step of an HGRNBit stack is a chain of FusedBitLinear calls: per
+ * block i/f/g_proj on the block input, o_proj, the MLP's gate_proj (GLU)
+ * and down_proj, whose output the next block reads (hysenlabs ja review,
+ * section "HGRNBit という層構成を読む"; hysenlabs de review, section "Die
+ * drei vortrainierten Modelle und ihre Trainingsdaten" for the 24- and
+ * 32-block stacks).  At 1..4 tokens each call is too small to fill the GPU
+ * and a launch per call costs more than its weights take to stream, so the
+ * chain runs as ONE persistent launch: workgroups claim the calls' output
+ * tile columns in call order, fetch their weights ahead, and wait (bounded)
+ * only for the call whose output they read.  Every call's y equals
+ * bitlinear_forward's (or bitlinear_forward_glu's) on the same input, bit
+ * for bit.
+ *
+ * Plan once, run every step: bitlinear_chain_plan validates the calls,
+ * works out which earlier call each call reads, and writes a call table and
+ * counters into the workspace (it copies from the host and synchronizes the
+ * stream: not for graph capture); bitlinear_chain_run is one kernel launch
+ * (capturable, allocation-free, replayable any number of times). */
+typedef struct bl_chain_call {
+    const void *x;        /* [M, K]: an earlier call's y (that call's output
+                             is then read inside the launch), or an input
+                             no call of the chain writes                   */
+    const void *gain;     /* [K]                                          */
+    const void *packed;   /* packed [N, K] (GLU order when glu)            */
+    const float *beta;    /* per-tensor weight scale                       */
+    void *y;              /* [M, N], or h [M, N / 2] when glu (written)    */
+    int64_t K, N;         /* N = packed rows (2F for a GLU gate_proj)      */
+    int32_t glu;          /* 1: y = silu(gate half) * up half, as
+                             bitlinear_forward_glu                         */
+    int32_t reserved;     /* 0                                             */
+} bl_chain_call;
+
+/* A planned chain (filled by bitlinear_chain_plan; plain data, copyable). */
+typedef struct bl_chain {
+    void *ws;
+    int64_t M, items, kmax, grid, lds;
+    int32_t dtype, ncalls;
+} bl_chain;
+
+/* Workspace bytes of a chain (0 if the calls are invalid). */
+size_t bitlinear_chain_workspace_bytes(const bl_chain_call *calls, int ncalls, int64_t M);
+
+/* Validate and plan a chain.
+ *   calls   HOST array of ncalls (1..4096) descriptors, read during the call
+ *   M       token rows, 1..4; dtype BL_F16 or BL_BF16 (x, gain and y of
+ *           every call); eps the RMSNorm epsilon of every call
+ *   ws      device workspace of >= bitlinear_chain_workspace_bytes bytes,
+ *           256-byte aligned, owned by this plan until it is re-planned
+ *   plan    HOST struct, written
+ * A call whose x pointer equals an earlier call's y reads that call's
+ * output (the latest such call; its output width must equal K).  Any other
+ * x is read as it is and must not overlap a y of the chain.  When y buffers
+ * of two calls overlap, the later call's values remain only if it depends,
+ * directly or through other calls, on the earlier one.  Shapes, alignment
+ * and pointers as for bitlinear_forward; K <= 8192.
+ * Returns BL_OK, BL_ERR_* for an invalid request (nothing touched), or
+ * BL_ERR_UNSUPPORTED for an x that overlaps a y without equalling it, or
+ * fp32 activations. */
+int bitlinear_chain_plan(const bl_chain_call *calls, int ncalls, int64_t M, int dtype, float eps,
+                         void *ws, size_t ws_bytes, bl_chain *plan, hipStream_t stream);
+
+/* Run a planned chain once: one launch on `stream`.  Runs of one plan must
+ * be ordered (same stream); each leaves the workspace ready for the next. */
+int bitlinear_chain_run(const bl_chain *plan, hipStream_t stream);
+
+/* bitlinear_chain_run with the bounded wait set to wait_us microseconds of
+ * wall clock (bitlinear_chain_run uses two seconds; 0 gives up at the
+ * first wait that is not already satisfied).  A wait that gives up sets the
+ * plan's error word; every other wait then gives up at once, items whose
+ * input never came are skipped, and the launch still ends normally. */
+int bitlinear_chain_run_ex(const bl_chain *plan, uint32_t wait_us, hipStream_t stream);
+
+/* Synchronize `stream`, then BL_OK, or BL_ERR_TIMEOUT if a run since the
+ * last check gave up waiting (its outputs are then incomplete); clears the
+ * error word. */
+int bitlinear_chain_status(const bl_chain *plan, hipStream_t stream);
 
 /* ------------------------------------------------- no-allocation forward
  * For callers that cannot allocate device memory at all -- code under HIP

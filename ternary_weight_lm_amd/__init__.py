@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     bitlinear_gemm_i32, bitlinear_pack_weights, bitlinear_pack_workspace_bytes,
     bitlinear_packed_bytes, bitlinear_select_path, bitlinear_status_string, bitlinear_unpack_weights,
     bitlinear_workspace_bytes, bitlinear_forward_noalloc, bitlinear_noalloc_max_scratch_bytes,
+    BL_ERR_TIMEOUT, BlChain, make_chain_calls, bitlinear_chain_workspace_bytes,
+    bitlinear_chain_plan, bitlinear_chain_run, bitlinear_chain_run_ex, bitlinear_chain_status,
 )
 
 

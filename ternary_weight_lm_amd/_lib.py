@@ -22,7 +22,9 @@ STATUS = {
     0: "BL_OK", -1: "BL_ERR_NULL", -2: "BL_ERR_DTYPE", -3: "BL_ERR_SHAPE",
     -4: "BL_ERR_ALIGN", -5: "BL_ERR_WORKSPACE", -6: "BL_ERR_EPS",
     -7: "BL_ERR_HIP", -8: "BL_ERR_UNSUPPORTED", -9: "BL_ERR_PATH", -10: "BL_ERR_SCRATCH",
+    -11: "BL_ERR_TIMEOUT",
 }
+BL_ERR_TIMEOUT = -11
 
 DTYPE_CODE = {torch.float32: BL_F32, torch.float16: BL_F16, torch.bfloat16: BL_BF16}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
@@ -54,6 +56,20 @@ class BlCall(ctypes.Structure):
                 ("N", ctypes.c_int64)]
 
 
+class BlChainCall(ctypes.Structure):
+    """struct bl_chain_call of bitlinear.h"""
+    _fields_ = [("x", ctypes.c_void_p), ("gain", ctypes.c_void_p), ("packed", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("y", ctypes.c_void_p), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("glu", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class BlChain(ctypes.Structure):
+    """struct bl_chain of bitlinear.h (a planned chain)"""
+    _fields_ = [("ws", ctypes.c_void_p), ("M", ctypes.c_int64), ("items", ctypes.c_int64),
+                ("kmax", ctypes.c_int64), ("grid", ctypes.c_int64), ("lds", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("ncalls", ctypes.c_int32)]
+
+
 I64 = ctypes.c_int64
 SZ = ctypes.c_size_t
 I = ctypes.c_int
@@ -80,6 +96,11 @@ SIGNATURES = {
     "bitlinear_forward_glu": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
     "bitlinear_noalloc_max_scratch_bytes": ([], SZ),
+    "bitlinear_chain_workspace_bytes": ([P, I, I64], SZ),
+    "bitlinear_chain_plan": ([P, I, I64, I, F, P, SZ, P, P], I),
+    "bitlinear_chain_run": ([P, P], I),
+    "bitlinear_chain_run_ex": ([P, ctypes.c_uint32, P], I),
+    "bitlinear_chain_status": ([P, P], I),
     "bitlinear_forward_noalloc": ([P, I, I64, I64, P, P, P, I64, P, I, F, P], I),
 }
 
@@ -377,3 +398,55 @@ def bitlinear_unpack_weights(packed, N, K, Wq, stream=None):
     _need(Wq, "Wq", torch.int8, numel=N * K)
     _check("bitlinear_unpack_weights", lib().bitlinear_unpack_weights(
         _ptr(packed), N, K, _ptr(Wq), _stream(stream)))
+
+
+# ------------------------------------------------------------ chained decode
+
+def make_chain_calls(items):
+    """ctypes array of bl_chain_call from (x, gain, packed, beta, y, glu)
+    tuples: x [M, K] and y [M, n_out] 16-bit; N = n_out, or 2 n_out when glu.
+    A call whose x is an earlier call's y reads that call's output."""
+    arr = (BlChainCall * len(items))()
+    for i, (x, gain, packed, beta, y, glu) in enumerate(items):
+        _need(y, "y", (torch.float16, torch.bfloat16), dims=2)
+        N = 2 * y.shape[1] if glu else y.shape[1]
+        M, K = _check_layer_io(x, gain, packed, beta, N, y, y.shape[1])
+        if y.shape[0] != M:
+            raise ValueError(f"y has {y.shape[0]} rows, x has {M}")
+        arr[i] = BlChainCall(_ptr(x), _ptr(gain), _ptr(packed), _ptr(beta), _ptr(y), K, N,
+                             1 if glu else 0, 0)
+    return arr
+
+
+def bitlinear_chain_workspace_bytes(calls, M: int) -> int:
+    return int(lib().bitlinear_chain_workspace_bytes(ctypes.cast(calls, ctypes.c_void_p),
+                                                     len(calls), M))
+
+
+def bitlinear_chain_plan(calls, M, dtype, ws, eps=1e-8, stream=None) -> BlChain:
+    """Plan a chain (calls: a make_chain_calls() array) into the workspace
+    tensor ws; returns the plan (keep ws alive as long as the plan)."""
+    _need(ws, "ws", numel=1)
+    plan = BlChain()
+    _check("bitlinear_chain_plan", lib().bitlinear_chain_plan(
+        ctypes.cast(calls, ctypes.c_void_p), len(calls), M, DTYPE_CODE[dtype], eps, _ptr(ws),
+        _nbytes(ws), ctypes.byref(plan), _stream(stream)))
+    return plan
+
+
+def bitlinear_chain_run(plan: BlChain, stream=None):
+    _check("bitlinear_chain_run", lib().bitlinear_chain_run(ctypes.byref(plan), _stream(stream)))
+
+
+def bitlinear_chain_run_ex(plan: BlChain, wait_us: int, stream=None):
+    _check("bitlinear_chain_run_ex", lib().bitlinear_chain_run_ex(
+        ctypes.byref(plan), int(wait_us), _stream(stream)))
+
+
+def bitlinear_chain_status(plan: BlChain, stream=None) -> int:
+    """BL_OK (0) or BL_ERR_TIMEOUT after synchronizing the stream (clears the
+    error word); any other failure raises."""
+    st = int(lib().bitlinear_chain_status(ctypes.byref(plan), _stream(stream)))
+    if st not in (0, BL_ERR_TIMEOUT):
+        _check("bitlinear_chain_status", st)
+    return st

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "bitlinear.h"
 
 namespace bl {
@@ -142,6 +144,27 @@ inline bool decode_split_fits(int64_t M, int64_t K, int x_dtype) {
 inline bool decode_fits(int64_t M, int64_t K, int x_dtype) {
   return decode_split_fits(M, K, x_dtype) || decode_rows_fits(M, K, x_dtype);
 }
+
+// Chained decode (chain.hip): dependent calls of 1..4 token rows, 16-bit
+// activations, in one persistent launch.  The C ABI layer validates the
+// calls and works out which earlier call (if any) each call reads.
+struct ChainPlanIn {
+  const bl_chain_call *calls;
+  int ncalls;
+  int64_t M;
+  int dtype;
+  float eps;
+  std::vector<int> dep;        // call whose y is this call's x, or -1
+  std::vector<char> consumed;  // a later call reads this call's y
+  std::vector<int64_t> n_out;  // output columns (N, or N / 2 for GLU)
+};
+constexpr int64_t kChainMaxM = 4;
+constexpr int kChainMaxCalls = 4096;
+size_t chain_workspace_bytes(const ChainPlanIn &in);
+hipError_t chain_plan(const ChainPlanIn &in, void *ws, bl_chain &out, hipStream_t stream);
+hipError_t chain_run(const bl_chain &p, uint32_t wait_us, hipStream_t stream);
+// synchronizes the stream, returns the chain's error word and clears it
+hipError_t chain_error(const bl_chain &p, uint32_t *err, hipStream_t stream);
 
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;

@@ -93,6 +93,7 @@ const char *bitlinear_status_string(int status) {
     case BL_ERR_UNSUPPORTED: return "unsupported request";
     case BL_ERR_PATH: return "unknown or inapplicable execution path";
     case BL_ERR_SCRATCH: return "request needs more than the library's static scratch (32 MiB)";
+    case BL_ERR_TIMEOUT: return "a chained launch gave up waiting for an input";
     default: return "unknown status";
   }
 }
@@ -625,6 +626,101 @@ int bitlinear_forward_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, 
   if (!ws) return BL_ERR_HIP;
   return forward_impl(x, x_dtype, M, K, gain, packed, beta, N, y, y_dtype, eps, ws,
                       kScratchBytes, BL_PATH_AUTO, false, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Validation and dependency analysis of a chain (host only).
+int chain_analyse(const bl_chain_call *calls, int ncalls, int64_t M, int dtype,
+                  bl::ChainPlanIn &in) {
+  if (dtype != BL_F16 && dtype != BL_BF16) return dtype == BL_F32 ? BL_ERR_UNSUPPORTED : BL_ERR_DTYPE;
+  if (ncalls < 1 || ncalls > bl::kChainMaxCalls) return BL_ERR_SHAPE;
+  if (M < 1 || M > bl::kChainMaxM) return BL_ERR_SHAPE;
+  if (!calls) return BL_ERR_NULL;
+  in.calls = calls;
+  in.ncalls = ncalls;
+  in.M = M;
+  in.dtype = dtype;
+  in.dep.assign(ncalls, -1);
+  in.consumed.assign(ncalls, 0);
+  in.n_out.assign(ncalls, 0);
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_chain_call &c = calls[i];
+    if (c.glu != 0 && c.glu != 1) return BL_ERR_SHAPE;
+    if (!nk_ok(c.N, c.K) || c.K > bl::kFusedMaxK) return BL_ERR_SHAPE;
+    if (c.glu && c.N % 64 != 0) return BL_ERR_SHAPE;
+    if (!c.x || !c.gain || !c.packed || !c.beta || !c.y) return BL_ERR_NULL;
+    if (!aligned16(c.x) || !aligned16(c.gain) || !aligned16(c.packed) || !aligned16(c.y) ||
+        (reinterpret_cast<uintptr_t>(c.beta) & 3u))
+      return BL_ERR_ALIGN;
+    in.n_out[i] = c.glu ? c.N / 2 : c.N;
+  }
+  const size_t eb = 2;
+  for (int i = 0; i < ncalls; ++i) {
+    const bl_chain_call &c = calls[i];
+    for (int j = i - 1; j >= 0; --j)
+      if (calls[j].y == c.x) {
+        if (in.n_out[j] != c.K) return BL_ERR_SHAPE;
+        in.dep[i] = j;
+        in.consumed[j] = 1;
+        break;
+      }
+    if (in.dep[i] >= 0) continue;
+    // a plain input must not be written by any call of the chain
+    for (int j = 0; j < ncalls; ++j)
+      if (overlaps(c.x, (size_t)(M * c.K) * eb, calls[j].y, (size_t)(M * in.n_out[j]) * eb))
+        return BL_ERR_UNSUPPORTED;
+  }
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_chain_workspace_bytes(const bl_chain_call *calls, int ncalls, int64_t M) {
+  bl::ChainPlanIn in;
+  if (chain_analyse(calls, ncalls, M, BL_BF16, in) != BL_OK) return 0;
+  return bl::chain_workspace_bytes(in);
+}
+
+int bitlinear_chain_plan(const bl_chain_call *calls, int ncalls, int64_t M, int dtype, float eps,
+                         void *ws, size_t ws_bytes, bl_chain *plan, hipStream_t stream) {
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (!plan) return BL_ERR_NULL;
+  bl::ChainPlanIn in;
+  const int st = chain_analyse(calls, ncalls, M, dtype, in);
+  if (st != BL_OK) return st;
+  in.eps = eps;
+  if (!ws || ws_bytes < bl::chain_workspace_bytes(in)) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  return hip_status(bl::chain_plan(in, ws, *plan, stream));
+}
+
+int bitlinear_chain_run_ex(const bl_chain *plan, uint32_t wait_us, hipStream_t stream) {
+  if (!plan || !plan->ws) return BL_ERR_NULL;
+  if (plan->M < 1 || plan->M > bl::kChainMaxM || plan->ncalls < 1 || plan->grid < 1 ||
+      (plan->dtype != BL_F16 && plan->dtype != BL_BF16))
+    return BL_ERR_SHAPE;
+  return hip_status(bl::chain_run(*plan, wait_us, stream));
+}
+
+int bitlinear_chain_run(const bl_chain *plan, hipStream_t stream) {
+  return bitlinear_chain_run_ex(plan, 2000000u, stream);
+}
+
+int bitlinear_chain_status(const bl_chain *plan, hipStream_t stream) {
+  if (!plan || !plan->ws) return BL_ERR_NULL;
+  uint32_t err = 0;
+  if (bl::chain_error(*plan, &err, stream) != hipSuccess) return BL_ERR_HIP;
+  return err ? BL_ERR_TIMEOUT : BL_OK;
 }
 
 }  // extern "C"

@@ -401,3 +401,57 @@ def test_noalloc_validation():
     K = 8192
     assert na(A, 1, cap // K + 1, K, B, C, D, 1024, Y, 1, 1e-8, None) == -10
     assert L.bitlinear_status_string(-10).decode().startswith("request needs more")
+
+
+def test_chain_plan_validation():
+    """Chain planning: validation and dependency analysis are host-only, so
+    every rejection comes back before any HIP call (made-up pointers)."""
+    from ternary_weight_lm_amd._lib import BlChainCall, BlChain
+    L = tw.lib()
+    X0, G, PK, BE = 0x7F0000010000, 0x7F0000020000, 0x7F0000030000, 0x7F0000040000
+    Y1, Y2, Y3 = 0x7F0000050000, 0x7F0000060000, 0x7F0000070000
+
+    def arr(calls):
+        a = (BlChainCall * len(calls))(*calls)
+        return ctypes.cast(a, ctypes.c_void_p), len(calls), a
+
+    good = [BlChainCall(X0, G, PK, BE, Y1, 1024, 1024, 0, 0),      # reads the chain input
+            BlChainCall(Y1, G, PK, BE, Y2, 1024, 2048, 1, 0),      # reads call 0; GLU -> 1024 wide
+            BlChainCall(Y2, G, PK, BE, Y3, 1024, 512, 0, 0)]       # reads call 1's h
+    p, n, keep = arr(good)
+    ws = L.bitlinear_chain_workspace_bytes(p, n, 1)
+    # header, 3 descriptors, item0 table, done counters, tagged outputs of calls 0 and 1
+    assert ws == 256 + 512 + 256 + 256 + 1024 * 4 + 1024 * 4
+    assert L.bitlinear_chain_workspace_bytes(p, n, 4) == 256 + 512 + 256 + 256 + 2 * 4 * 4096
+    plan = BlChain()
+    pl = L.bitlinear_chain_plan
+    WSD = 0x7F0001000000
+    assert pl(p, n, 1, 2, 1e-8, WSD, ws - 1, ctypes.byref(plan), None) == WS
+    assert pl(p, n, 1, 2, 1e-8, WSD + 16, ws, ctypes.byref(plan), None) == ALIGN
+    assert pl(p, n, 1, 0, 1e-8, WSD, ws, ctypes.byref(plan), None) == UNSUP    # fp32 chains
+    assert pl(p, n, 1, 7, 1e-8, WSD, ws, ctypes.byref(plan), None) == DTYPE
+    assert pl(p, n, 5, 2, 1e-8, WSD, ws, ctypes.byref(plan), None) == SHAPE    # M <= 4
+    assert pl(p, n, 0, 2, 1e-8, WSD, ws, ctypes.byref(plan), None) == SHAPE
+    assert pl(p, n, 1, 2, 0.0, WSD, ws, ctypes.byref(plan), None) == EPS
+    assert pl(p, n, 1, 2, 1e-8, WSD, ws, None, None) == NULL
+    assert pl(p, 0, 1, 2, 1e-8, WSD, ws, ctypes.byref(plan), None) == SHAPE
+    assert pl(None, 3, 1, 2, 1e-8, WSD, ws, ctypes.byref(plan), None) == NULL
+
+    def one(bad):
+        q, m, k = arr(bad)
+        return pl(q, m, 1, 2, 1e-8, WSD, 1 << 30, ctypes.byref(plan), None)
+
+    assert one([good[0], BlChainCall(Y1, G, PK, BE, Y2, 2048, 1024, 0, 0)]) == SHAPE   # width
+    assert one([BlChainCall(X0, G, PK, BE, Y1, 9216, 1024, 0, 0)]) == SHAPE           # K > 8192
+    assert one([BlChainCall(X0, G, PK, BE, Y1, 1024, 1056, 1, 0)]) == SHAPE           # GLU N % 64
+    assert one([BlChainCall(X0, G, PK, BE, Y1, 1024, 1024, 2, 0)]) == SHAPE
+    assert one([BlChainCall(X0, None, PK, BE, Y1, 1024, 1024, 0, 0)]) == NULL
+    assert one([BlChainCall(X0 + 8, G, PK, BE, Y1, 1024, 1024, 0, 0)]) == ALIGN
+    # a plain input that a call of the chain writes (here: the later call's y)
+    assert one([BlChainCall(X0, G, PK, BE, Y1, 1024, 1024, 0, 0),
+                BlChainCall(Y3, G, PK, BE, X0 + 512, 1024, 1024, 0, 0)]) == UNSUP
+    # the status entry points need a plan
+    assert L.bitlinear_chain_run(None, None) == NULL
+    assert L.bitlinear_chain_status(None, None) == NULL
+    assert L.bitlinear_chain_run_ex(ctypes.byref(BlChain()), 0, None) == NULL
+    assert L.bitlinear_status_string(-11).decode().startswith("a chained launch")

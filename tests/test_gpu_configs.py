@@ -3,6 +3,9 @@ bench.py times: its Workload / Weights / Buffers and launch_group build and
 issue every launch group exactly as a benchmark step does (i/f/g grouped on
 one input through bitlinear_forward_grouped or bitlinear_forward_grouped_ws;
 in the 2.7B stack the layers chained, gate_proj through the fused GLU gate).
+The 2.7B stack is also run at one token as the single chained launch of
+bitlinear_chain_run (bench.py --launch chain), over per-call output buffers
+so every output survives.
 
 Every packed byte and beta of every projection (all 192 of the 2.7B stack)
 is compared with the oracle's packer.  Every call's output is compared with
@@ -19,6 +22,7 @@ import torch
 
 import bench
 import oracle
+import ternary_weight_lm_amd as tw
 from ternary_weight_lm_amd import synth
 from tests.parity import DEV, check_xq, check_y, gpu_act_quant, say, y_to_np
 from tests.test_gpu_glu import check_h
@@ -60,22 +64,31 @@ def check_call(c, cfg, d_packed, d_beta, samples):
     return c.idx
 
 
-def run_config(key, Ms, rows_of):
+def run_config(key, Ms, rows_of, launch="per-call"):
     dev = torch.device(DEV)
-    wls = {M: bench.Workload(key, M=M) for M in Ms}
+    wls = {M: bench.Workload(key, M=M, launch=launch) for M in Ms}
     wl0 = wls[Ms[0]]
     cfg = wl0.cfg
     say(f"{key}: packing {len(wl0.calls)} projections")
     weights = bench.Weights(wl0, 0, dev, keep_host_layers=())
-    bufs = {M: bench.Buffers(wls[M], weights, dev) for M in Ms}
+    bufs = {M: bench.Buffers(wls[M], weights, dev, distinct=wls[M].launch == "chain")
+            for M in Ms}
     groups = {M: wls[M].groups() for M in Ms}
     pool = weights.pool[0]
+    for M in Ms:
+        if wls[M].launch == "chain":
+            say(f"{key}: M={M} as one chained launch of {len(wls[M].calls)} calls")
+            plan = bufs[M].chain_plans(wls[M], weights)[0][0]
+            tw.bitlinear_chain_run(plan)
+            assert tw.bitlinear_chain_status(plan) == 0
     done = set()
     futures = []
     with ThreadPoolExecutor(WORKERS) as ex:
         for layer in range(cfg.layers):
             calls = [c for c in wl0.calls if c.layer == layer]
             for M in Ms:
+                if wls[M].launch == "chain":
+                    continue
                 for grp in groups[M]:
                     if grp[0].layer == layer:
                         bench.launch_group(wls[M], grp, weights, bufs[M], pool, [])
@@ -86,9 +99,9 @@ def run_config(key, Ms, rows_of):
                     rows = sample_rows(M, rows_of(M))
                     ridx = torch.from_numpy(rows).to(dev)
                     b = bufs[M]
-                    x = b.t[c.x][ridx].contiguous()
+                    x = b.inp[c.idx][ridx].contiguous()
                     xq, s, _ = gpu_act_quant(x, weights.gains[c.idx])
-                    samples.append((M, synth.widen(x), y_to_np(b.t[c.y][ridx]), xq, s))
+                    samples.append((M, synth.widen(x), y_to_np(b.out[c.idx][ridx]), xq, s))
                 d_packed = weights.packed[c.idx].cpu().numpy()
                 d_beta = np.float32(weights.betas[c.idx].cpu().item())
                 futures.append(ex.submit(check_call, c, cfg, d_packed, d_beta, samples))
@@ -110,3 +123,9 @@ def test_config_2p7b_stack_chained():
     grouped 4-tile-wave GEMM).  Rows: all of M = 1, first and last of M = 8,
     first, middle and last of M >= 64."""
     run_config("c5", list(bench.C5_SWEEP), lambda M: 1 if M == 1 else (2 if M <= 8 else 3))
+
+
+def test_config_2p7b_stack_one_chained_launch():
+    """The 2.7B stack at one token as one persistent chained launch
+    (bitlinear_chain_run over all 192 calls), every call against the oracle."""
+    run_config("c5", [1], lambda M: 1, launch="chain")
