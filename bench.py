@@ -68,6 +68,11 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
+    "c5-M1": ("decode", "aab3e6752836bbc9", 5247143),
+    "c5-M8": ("decode", "aab3e6752836bbc9", 5795187),
+    "c5-M64": ("skinny", "1c40f81eaaa887df", 5572923),
+    "c5-M512": ("gemm", "53b5e7bfa9ea7e07", 23237509),
+    "c5-M8192": ("gemm", "53b5e7bfa9ea7e07", 222642006),
 }
 
 
@@ -104,7 +109,9 @@ def parse(argv=None):
     ap.add_argument("--pool-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--roofline-reps", type=int, default=None)
+    ap.add_argument("--roofline-reps", type=int, default=None,
+                    help="passes of the dominant kernel's roofline graph; 0 skips it where "
+                         "the steps do not give it (for kernel traces of the steps alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
                          "(reference for the HBM byte counters) and exit")
@@ -553,9 +560,13 @@ def run_m(wl, weights, dev, args):
     timed = capture(fn, warmup, steps, per_step)
     ms = timed_replay(timed)
     del timed
-    roof = roofline(wl, weights, bufs, reps, step_ms=ms / steps, steps=steps)
-    roof["traffic"] = traffic(wl.key if not wl.chained else f"c5-M{wl.M}")
-    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    if reps > 0 or wl.launch == "chain" or all(wl.path(c) == 1 for c in wl.calls):
+        roof = roofline(wl, weights, bufs, max(reps, 1), step_ms=ms / steps, steps=steps)
+        roof["traffic"] = traffic(wl.key if not wl.chained else f"c5-M{wl.M}")
+        roof["traffic_unit"] = ("HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "copy-calibrated)")
+    else:
+        roof = None    # --roofline-reps 0: only the steps run (kernel traces of a step)
     torch.cuda.synchronize()
     return {"M": wl.M, "tokens_per_s": round(wl.M * steps / (ms / 1e3), 2), "steps": steps,
             "warmup": warmup, "ms_per_step": round(ms / steps, 6), "launch": wl.launch,
@@ -834,13 +845,12 @@ def main():
         "roofline": head["roofline"],
     }
     if sweep:
-        out["sweep"] = [{"M": r["M"], "tokens_per_s": r["tokens_per_s"],
-                         "ms_per_step": r["ms_per_step"], "steps": r["steps"],
-                         "launch": r["launch"], "launches_per_step": r["launches_per_step"],
-                         "bound": r["roofline"]["bound"], "frac": r["roofline"]["frac"],
-                         "achieved": r["roofline"]["achieved"], "unit": r["roofline"]["unit"],
-                         "avg_kernel_us": r["roofline"]["avg_kernel_us"],
-                         "kernel": r["roofline"]["kernel"]} for r in results]
+        out["sweep"] = [dict({"M": r["M"], "tokens_per_s": r["tokens_per_s"],
+                              "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+                              "launch": r["launch"], "launches_per_step": r["launches_per_step"]},
+                             **({k: r["roofline"][k] for k in ("bound", "frac", "achieved", "unit",
+                                                              "avg_kernel_us", "traffic", "kernel")}
+                                if r["roofline"] else {})) for r in results]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, weights, args.cpu_seconds)
     print(json.dumps(out), flush=True)
