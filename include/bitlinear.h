@@ -373,6 +373,12 @@ int bitlinear_forward_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, 
                               const void *packed, const float *beta, int64_t N, void *y,
                               int y_dtype, float eps, hipStream_t stream);
 
+/* Test hook, for callers' failure-path tests: the next n kernel launches the
+ * library would issue (any entry point) return BL_ERR_HIP instead, as a
+ * failed HIP launch does, without launching or touching memory; n <= 0
+ * clears it.  Process-wide; launches that are not forced are unaffected. */
+void bitlinear_test_fail_launches(int n);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(int status);
 

@@ -35,8 +35,14 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle; ORACLE_LIB names another build of oracle.c to load
+    instead (the sanitizer run of the pin suite uses it)."""
     global _lib
     if _lib is None:
+        alt = os.environ.get("ORACLE_LIB")
+        if alt:
+            _lib = load(alt)
+            return _lib
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(
                 f"oracle library {_LIB_PATH} is not built; run "

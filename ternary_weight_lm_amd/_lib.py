@@ -96,6 +96,7 @@ SIGNATURES = {
     "bitlinear_forward_glu": ([P, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, I, P], I),
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
     "bitlinear_noalloc_max_scratch_bytes": ([], SZ),
+    "bitlinear_test_fail_launches": ([I], None),
     "bitlinear_chain_workspace_bytes": ([P, I, I64], SZ),
     "bitlinear_chain_plan": ([P, I, I64, I, F, P, SZ, P, P], I),
     "bitlinear_chain_run": ([P, P], I),
@@ -243,6 +244,12 @@ def bitlinear_forward_path(x, gain, packed, beta, N, y, ws, path, eps=1e-8, stre
         _ptr(x), DTYPE_CODE[x.dtype], M, K, _ptr(gain), _ptr(packed), _ptr(beta), N,
         _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), ws.numel() * ws.element_size(),
         path, _stream(stream)))
+
+
+def bitlinear_test_fail_launches(n: int):
+    """Test hook: the next n kernel launches of the library fail with
+    BL_ERR_HIP without launching (0 clears)."""
+    lib().bitlinear_test_fail_launches(int(n))
 
 
 def bitlinear_noalloc_max_scratch_bytes() -> int:

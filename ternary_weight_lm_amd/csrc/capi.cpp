@@ -5,6 +5,7 @@
 // then dispatches to the kernel launchers in bl_launch.h.  No exception
 // crosses the boundary; every failure is a negative status code.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -37,6 +38,20 @@ bool m_ok(int64_t M) { return M >= 0 && M <= kMaxM; }
 bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+// Test hook (bitlinear_test_fail_launches): the next n launcher calls report
+// a launch failure instead of launching, so the path of a failed HIP launch
+// to the caller can be driven from the host without a GPU.
+std::atomic<int> g_fail_launches{0};
+
+bool forced_failure() {
+  int n = g_fail_launches.load(std::memory_order_relaxed);
+  while (n > 0)
+    if (g_fail_launches.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) return true;
+  return false;
+}
+
+#define BL_LAUNCH(call) (forced_failure() ? hipErrorLaunchFailure : (call))
 
 // Forward workspace: xq [M, K] int8 | s [M] fp32 | rowsum [M] int32.
 struct FwdWs {
@@ -80,6 +95,8 @@ int auto_path(int64_t M, int64_t K, int x_dtype) {
 
 extern "C" {
 
+void bitlinear_test_fail_launches(int n) { g_fail_launches.store(n > 0 ? n : 0); }
+
 const char *bitlinear_status_string(int status) {
   switch (status) {
     case BL_OK: return "ok";
@@ -120,7 +137,7 @@ int bitlinear_pack_weights(const float *W, int64_t N, int64_t K, void *packed,
   if (!aligned16(W) || !aligned16(packed) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
-  return hip_status(bl::launch_pack(W, N, K, packed, beta, ws, 0, stream));
+  return hip_status(BL_LAUNCH(bl::launch_pack(W, N, K, packed, beta, ws, 0, stream)));
 }
 
 int bitlinear_pack_glu_weights(const float *W, int64_t F, int64_t K, void *packed, float *beta,
@@ -131,7 +148,7 @@ int bitlinear_pack_glu_weights(const float *W, int64_t F, int64_t K, void *packe
   if (!aligned16(W) || !aligned16(packed) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
-  return hip_status(bl::launch_pack(W, 2 * F, K, packed, beta, ws, F, stream));
+  return hip_status(BL_LAUNCH(bl::launch_pack(W, 2 * F, K, packed, beta, ws, F, stream)));
 }
 
 size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -181,10 +198,10 @@ int forward_impl(const void *x, int x_dtype, int64_t M, int64_t K, const void *g
     a.out = y;
     a.out_kind = y_dtype;
     a.glu = glu;
-    return hip_status(bl::launch_skinny(a, stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
   }
   const FwdWs w = carve(ws, M, K);
-  hipError_t e = bl::launch_act_quant(x, x_dtype, gain, M, K, eps, w.xq, w.s, w.rowsum, stream);
+  hipError_t e = BL_LAUNCH(bl::launch_act_quant(x, x_dtype, gain, M, K, eps, w.xq, w.s, w.rowsum, stream));
   if (e != hipSuccess) return BL_ERR_HIP;
   if (path == BL_PATH_SKINNY) {
     bl::SkinnyArgs a{};
@@ -200,10 +217,10 @@ int forward_impl(const void *x, int x_dtype, int64_t M, int64_t K, const void *g
     a.out = y;
     a.out_kind = y_dtype;
     a.glu = glu;
-    return hip_status(bl::launch_skinny(a, stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
   }
-  return hip_status(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
-                                         y_dtype, glu, stream));
+  return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
+                                         y_dtype, glu, stream)));
 }
 
 }  // namespace
@@ -270,7 +287,7 @@ int bitlinear_forward_grouped(const bl_call *calls, int ncalls, int x_dtype,
     args.push_back(a);
   }
   if (args.empty()) return BL_OK;
-  return hip_status(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream));
+  return hip_status(BL_LAUNCH(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream)));
 }
 
 }  // extern "C"
@@ -368,10 +385,10 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
       aq.c[j] = bl::AqCall{c.x, c.gain, w.xq, w.s, w.rowsum};
       gm.c[j] = bl::GemmCall{w.xq, w.rowsum, w.s, c.packed, c.beta, c.y};
     }
-    if (bl::launch_act_quant_group(aq, r.n, x_dtype, c0.M, c0.K, eps, stream) != hipSuccess)
+    if (BL_LAUNCH(bl::launch_act_quant_group(aq, r.n, x_dtype, c0.M, c0.K, eps, stream)) != hipSuccess)
       return BL_ERR_HIP;
     if (r.path == BL_PATH_MFMA) {
-      if (bl::launch_gemm_mfma_group(gm, r.n, c0.M, c0.N, c0.K, y_dtype, stream) != hipSuccess)
+      if (BL_LAUNCH(bl::launch_gemm_mfma_group(gm, r.n, c0.M, c0.N, c0.K, y_dtype, stream)) != hipSuccess)
         return BL_ERR_HIP;
       continue;
     }
@@ -388,7 +405,7 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
       a.K = c0.K;
       a.out = gm.c[j].out;
       a.out_kind = y_dtype;
-      if (bl::launch_skinny(a, stream) != hipSuccess) return BL_ERR_HIP;
+      if (BL_LAUNCH(bl::launch_skinny(a, stream)) != hipSuccess) return BL_ERR_HIP;
     }
   }
   if (!fused.empty()) {
@@ -410,7 +427,7 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
       a.out_kind = y_dtype;
       args.push_back(a);
     }
-    return hip_status(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny_grouped(args.data(), (int)args.size(), stream)));
   }
   return BL_OK;
 }
@@ -426,7 +443,7 @@ int bitlinear_act_quant(const void *x, int x_dtype, const void *gain,
   if (!aligned16(x) || !aligned16(gain) || !aligned16(xq) ||
       (reinterpret_cast<uintptr_t>(s) & 3u) || (reinterpret_cast<uintptr_t>(rowsum) & 3u))
     return BL_ERR_ALIGN;
-  return hip_status(bl::launch_act_quant(x, x_dtype, gain, M, K, eps, xq, s, rowsum, stream));
+  return hip_status(BL_LAUNCH(bl::launch_act_quant(x, x_dtype, gain, M, K, eps, xq, s, rowsum, stream)));
 }
 
 int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
@@ -452,10 +469,10 @@ int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
     a.K = K;
     a.out = acc;
     a.out_kind = bl::kOutI32;
-    return hip_status(bl::launch_skinny(a, stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
   }
-  return hip_status(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
-                                         bl::kOutI32, false, stream));
+  return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
+                                         bl::kOutI32, false, stream)));
 }
 
 int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
@@ -486,10 +503,10 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
     a.K = K;
     a.out = y;
     a.out_kind = y_dtype;
-    return hip_status(bl::launch_skinny(a, stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
   }
-  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, false,
-                                         stream));
+  return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, false,
+                                         stream)));
 }
 
 int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rowsum, int64_t M,
@@ -520,10 +537,10 @@ int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rows
     a.out = h;
     a.out_kind = h_dtype;
     a.glu = true;
-    return hip_status(bl::launch_skinny(a, stream));
+    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
   }
-  return hip_status(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, 2 * F, K, h, h_dtype,
-                                         true, stream));
+  return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, 2 * F, K, h, h_dtype,
+                                         true, stream)));
 }
 
 int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
@@ -558,9 +575,9 @@ int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_
       gm.c[j] = bl::GemmCall{c.xq, c.rowsum, c.s, c.packed, c.beta, c.y};
     }
     const hipError_t e =
-        n == 1 ? bl::launch_gemm_mfma(c0.xq, c0.rowsum, c0.s, c0.packed, c0.beta, c0.M, c0.N,
-                                      c0.K, c0.y, y_dtype, false, stream)
-               : bl::launch_gemm_mfma_group(gm, n, c0.M, c0.N, c0.K, y_dtype, stream);
+        n == 1 ? BL_LAUNCH(bl::launch_gemm_mfma(c0.xq, c0.rowsum, c0.s, c0.packed, c0.beta, c0.M, c0.N,
+                                      c0.K, c0.y, y_dtype, false, stream))
+               : BL_LAUNCH(bl::launch_gemm_mfma_group(gm, n, c0.M, c0.N, c0.K, y_dtype, stream));
     if (e != hipSuccess) return BL_ERR_HIP;
     i += n;
   }
@@ -572,7 +589,7 @@ int bitlinear_unpack_weights(const void *packed, int64_t N, int64_t K,
   if (!nk_ok(N, K)) return BL_ERR_SHAPE;
   if (!packed || !Wq) return BL_ERR_NULL;
   if (!aligned16(packed) || !aligned16(Wq)) return BL_ERR_ALIGN;
-  return hip_status(bl::launch_unpack(packed, N, K, Wq, stream));
+  return hip_status(BL_LAUNCH(bl::launch_unpack(packed, N, K, Wq, stream)));
 }
 
 }  // extern "C"
@@ -701,7 +718,7 @@ int bitlinear_chain_plan(const bl_chain_call *calls, int ncalls, int64_t M, int 
   in.eps = eps;
   if (!ws || ws_bytes < bl::chain_workspace_bytes(in)) return BL_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
-  return hip_status(bl::chain_plan(in, ws, *plan, stream));
+  return hip_status(BL_LAUNCH(bl::chain_plan(in, ws, *plan, stream)));
 }
 
 int bitlinear_chain_run_ex(const bl_chain *plan, uint32_t wait_us, hipStream_t stream) {
@@ -709,7 +726,7 @@ int bitlinear_chain_run_ex(const bl_chain *plan, uint32_t wait_us, hipStream_t s
   if (plan->M < 1 || plan->M > bl::kChainMaxM || plan->ncalls < 1 || plan->grid < 1 ||
       (plan->dtype != BL_F16 && plan->dtype != BL_BF16))
     return BL_ERR_SHAPE;
-  return hip_status(bl::chain_run(*plan, wait_us, stream));
+  return hip_status(BL_LAUNCH(bl::chain_run(*plan, wait_us, stream)));
 }
 
 int bitlinear_chain_run(const bl_chain *plan, hipStream_t stream) {

@@ -455,3 +455,27 @@ def test_chain_plan_validation():
     assert L.bitlinear_chain_status(None, None) == NULL
     assert L.bitlinear_chain_run_ex(ctypes.byref(BlChain()), 0, None) == NULL
     assert L.bitlinear_status_string(-11).decode().startswith("a chained launch")
+
+
+def test_forced_launch_failure_reaches_the_caller():
+    """The launch-failure hook: a valid call whose launch is forced to fail
+    returns BL_ERR_HIP from every kind of entry point (no GPU involved: the
+    forced launch never happens), and a rejected call does not consume it."""
+    from ternary_weight_lm_amd._lib import BlCall
+    L = tw.lib()
+    try:
+        L.bitlinear_test_fail_launches(1)
+        assert fwd(M=0) == OK                      # nothing to launch: not consumed
+        assert fwd(eps=0.0) == EPS                 # rejected: not consumed
+        assert fwd() == HIP                        # consumed here
+        L.bitlinear_test_fail_launches(3)
+        assert L.bitlinear_pack_weights(A, 64, 256, C, D, WSP,
+                                        L.bitlinear_pack_workspace_bytes(64, 256), None) == HIP
+        assert L.bitlinear_forward_path(A, 1, 300, 1024, B, C, D, 1024, Y, 1, 1e-8, WSP,
+                                        L.bitlinear_workspace_bytes(300, 1024, 1024), 3, None) == HIP
+        calls = (BlCall * 3)(*[BlCall(A, B, C, D, Y, 4096, 2048, 2048)] * 3)
+        gws = L.bitlinear_grouped_workspace_bytes(ctypes.cast(calls, ctypes.c_void_p), 3, 2)
+        assert L.bitlinear_forward_grouped_ws(ctypes.cast(calls, ctypes.c_void_p), 3, 2, 2, 1e-8,
+                                              WSP, gws, None) == HIP
+    finally:
+        L.bitlinear_test_fail_launches(0)
