@@ -84,6 +84,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_forward.argtypes = [P, P, I64, I64, P, F, I64, F, P, P, P, P, P]
     L.oracle_silu.restype = ctypes.c_double
     L.oracle_silu.argtypes = [ctypes.c_double]
+    L.oracle_rmsnorm_swish_gate.argtypes = [P, P, P, I64, I64, ctypes.c_double, P]
+    L.oracle_rmsnorm_swish_gate.restype = None
     L.oracle_glu.restype = None
     L.oracle_glu.argtypes = [P, I64, I64, P]
     L.oracle_glu_rows.restype = ctypes.c_int
@@ -271,3 +273,18 @@ def forward_glu(x, g, Wq, beta, eps=1e-8):
     out = forward(x, g, Wq, beta, eps)
     out["h"] = glu(out["y"])
     return out
+
+
+# ------------------------------------------- FusedRMSNormSwishGate (reading)
+
+def rmsnorm_swish_gate(o, g, w, eps=1e-6) -> np.ndarray:
+    """z [M,K] (fp64) = (o * r) * w * silu(g), r = 1/sqrt(mean(o^2) + eps):
+    the reading of FusedRMSNormSwishGate (oracle.c)."""
+    o = _c(np.atleast_2d(o), np.float32)
+    g = _c(np.atleast_2d(g), np.float32)
+    w = _c(w, np.float32)
+    M, K = o.shape
+    assert g.shape == (M, K) and w.shape == (K,)
+    z = np.empty((M, K), np.float64)
+    lib().oracle_rmsnorm_swish_gate(_p(o), _p(g), _p(w), M, K, float(eps), _p(z))
+    return z

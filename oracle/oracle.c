@@ -264,3 +264,31 @@ int oracle_glu_rows(int64_t F, int64_t *src)
     }
     return 0;
 }
+
+/* ------------------------------------- FusedRMSNormSwishGate (a reading) */
+
+/* The gate in front of o_proj.  The pages name the module and its role only:
+ * the gate part of the block is FusedRMSNormSwishGate, a layer of its own
+ * that fuses an RMSNorm with the gate (hysenlabs ja review, sections
+ * "HGRNBit という層構成を読む" and "代替手段との違い").  The reading is what the
+ * name says: the RMSNorm of the token mixer's output o (gain w, epsilon eps)
+ * multiplied elementwise by the Swish of the gate input g, Swish with unit
+ * slope being the SiLU a / (1 + e^-a) of the GLU (datacamp "MatMul-freie
+ * LLMs: Zentrale Konzepte erklärt", section "Kernkomponenten: MLGRU und GLU"):
+ *   z[m,k] = (o[m,k] * r_m) * w[k] * silu(g[m,k]),
+ *   r_m    = 1 / sqrt(sum_k o[m,k]^2 / K + eps).
+ * Everything in fp64; z is a floating-point value held to a tolerance. */
+void oracle_rmsnorm_swish_gate(const float *o, const float *g, const float *w, int64_t M,
+                               int64_t K, double eps, double *z)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const float *orow = o + m * K;
+        const float *grow = g + m * K;
+        double sumsq = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            sumsq += (double)orow[k] * (double)orow[k];
+        const double r = 1.0 / sqrt(sumsq / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            z[m * K + k] = ((double)orow[k] * r) * (double)w[k] * oracle_silu((double)grow[k]);
+    }
+}

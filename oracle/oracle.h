@@ -145,6 +145,12 @@ void oracle_glu(const double *y, int64_t M, int64_t F, double *h);
  * Returns 0, or -1 unless F > 0 and F % 16 == 0. */
 int oracle_glu_rows(int64_t F, int64_t *src);
 
+/* FusedRMSNormSwishGate, as the module's name reads (see oracle.c):
+ * z [M, K] (fp64) = (o * r_m) * w * silu(g), r_m = 1/sqrt(mean_k o^2 + eps).
+ * o, g [M, K] and w [K] fp32 (exact widening of the stored dtype). */
+void oracle_rmsnorm_swish_gate(const float *o, const float *g, const float *w, int64_t M,
+                               int64_t K, double eps, double *z);
+
 #ifdef __cplusplus
 }
 #endif

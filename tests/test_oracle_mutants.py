@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_gate as gate_pins
 from tests import test_oracle_glu as glu_pins
 from tests import test_oracle_pins as pins
 
@@ -45,13 +46,23 @@ MUTANTS = {
                                  "y[m * 2 * F + j] * oracle_silu(y[m * 2 * F + F + j])"),
     "glu_rows_halves_swapped": ("(half == 0 ? 0 : F) + 16 * t + c", "(half == 0 ? F : 0) + 16 * t + c"),
     "glu_rows_tile_of_32": ("(half == 0 ? 0 : F) + 16 * t + c", "(half == 0 ? 0 : F) + 32 * t + c"),
+    "gate_normalizes_g": ("sumsq += (double)orow[k] * (double)orow[k];",
+                          "sumsq += (double)grow[k] * (double)grow[k];"),
+    "gate_sigmoid_not_swish": ("(double)w[k] * oracle_silu((double)grow[k]);",
+                               "(double)w[k] / (1.0 + exp(-(double)grow[k]));"),
+    "gate_eps_outside_sqrt": ("1.0 / sqrt(sumsq / (double)K + eps);",
+                              "1.0 / (sqrt(sumsq / (double)K) + eps);"),
+    "gate_without_1_over_K": ("1.0 / sqrt(sumsq / (double)K + eps);", "1.0 / sqrt(sumsq + eps);"),
+    "gate_drops_gain": ("((double)orow[k] * r) * (double)w[k] * oracle_silu",
+                        "((double)orow[k] * r) * oracle_silu"),
+    "gate_unnormalized": ("((double)orow[k] * r) * (double)w[k]", "((double)orow[k]) * (double)w[k]"),
 }
 
 
 def _pin_tests():
-    return [f for mod in (pins, glu_pins)
+    return [f for mod in (pins, glu_pins, gate_pins)
             for name, f in inspect.getmembers(mod, inspect.isfunction)
-            if name.startswith("test_")]
+            if name.startswith("test_") and not hasattr(f, "pytestmark")]
 
 
 def _run_pins(mod):
