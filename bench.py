@@ -100,8 +100,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c5",
-                    help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, or an MLP "
-                         "workload c3-mlp | c4-mlp | c5-M<M>-mlp")
+                    help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, an MLP "
+                         "workload c3-mlp | c4-mlp | c5-M<M>-mlp, or the gated o_proj c5-M<M>-gate")
     ap.add_argument("--launch", choices=["per-call", "chain"], default="per-call",
                     help="per-call: one launch group per projection (default); chain: a "
                          "chained stack at 1..4 tokens runs as one persistent launch per step "
@@ -574,6 +574,125 @@ def run_m(wl, weights, dev, args):
             "launch_groups_per_step": len(groups), "roofline": roof}, bufs
 
 
+# ------------------------------------------------ o_proj with its swish gate
+
+GATE_EPS = 1e-6   # the gate's RMSNorm epsilon (a reading: the pages give none)
+
+
+def run_gate(args):
+    """o_proj with FusedRMSNormSwishGate as its prologue (bitlinear_forward_gated):
+    per layer, the gate of the token mixer's output o and the gate input g
+    (both synthetic, bf16) feeds the 2.7B o_proj (2560 -> 2560), the gate's z
+    never leaving registers.  Workloads c5-M<M>-gate (32 layers)."""
+    import numpy as np
+    import torch
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+    import oracle
+
+    base = args.workload[:-len("-gate")]
+    cfg = synth.CONFIGS["c5"]
+    M = int(base.split("-M")[1])
+    layers = cfg.layers
+    names = [p.name for p in cfg.projs]
+    oi = names.index("o_proj")
+    K, N = cfg.projs[oi].K, cfg.projs[oi].N
+    dev = torch.device("cuda:0")
+    xdt = synth.DTYPES[cfg.dtype]
+    o = synth.make_x(cfg.seed, 0, oi, M, K, cfg.dtype).to(dev)
+    g = (synth.make_x(cfg.seed, 1, oi, M, K, cfg.dtype) * 2).to(dev)
+    gw = synth.make_gain(cfg.seed, 1, oi, K, cfg.dtype).to(dev)
+    packed, betas, gains, host_W = [], [], [], None
+    for layer in range(layers):
+        _, gn, W = synth.config_inputs(cfg, M, layer, oi)
+        if layer == 0:
+            host_W = W
+        pk, b = tw.pack(W.to(dev))
+        packed.append(pk)
+        betas.append(b)
+        gains.append(gn.to(dev))
+    set_bytes = sum(p.numel() for p in packed)
+    copies = max(1, math.ceil((args.pool_mib << 20) / set_bytes))
+    pool = [packed] + [[p.clone() for p in packed] for _ in range(copies - 1)]
+    y = torch.empty(M, N, dtype=xdt, device=dev)
+    ws = tw.workspace(M, K, N, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, keep):
+        pl = pool[s % copies]
+        for layer in range(layers):
+            tw.bitlinear_forward_gated(o, g, gw, gains[layer], pl[layer], betas[layer], N, y, ws,
+                                       gate_eps=GATE_EPS)
+
+    big = M >= 512
+    steps = args.steps if args.steps is not None else (20 if big else 100)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 10)
+    for gr, _ in capture(step, 0, warmup, 2 * layers):
+        gr.replay()
+    ms = timed_replay(capture(step, warmup, steps, 2 * layers))
+    launches = steps * layers
+    sec = ms / 1e3
+    ops = 2 * M * N * K
+    byt = N * K // 4 + 2 * M * K * 2 + 2 * K * 2 + M * N * 2 + 4   # W + o, g + gate and o_proj gains + y
+    path_mfma = M > 64
+    if path_mfma:
+        ach = ops * launches / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(ach / I8_PEAK_TOPS, 5)}
+    else:
+        ach = byt * launches / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 5)}
+    roof.update({"traffic": None,
+                 "kernel": "gated act-quant (gate + norm + quant) + "
+                           + ("bl::gemm_mfma_kernel" if path_mfma else "bl::skinny_kernel<pre-quantized>"),
+                 "launches": launches, "avg_call_us": round(sec * 1e6 / launches, 3),
+                 "algorithmic_bytes_per_call": byt, "ops_per_call": ops,
+                 "timed_region": "the benchmark steps (each call: the gated act-quant launch and the "
+                                 "contraction launch)"})
+    out = {
+        "metric": METRIC, "value": round(M * steps / sec, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name.replace('_Msweep', '')}_M{M}_o_proj_swish_gate",
+                   "tokens_per_step": M, "layers": layers,
+                   "projections": [f"FusedRMSNormSwishGate({K}) -> o_proj {K}->{N} (fused prologue)"],
+                   "x_dtype": cfg.dtype, "y_dtype": cfg.dtype, "gate_eps": GATE_EPS,
+                   "weight_pool_MiB": round(set_bytes * copies / 2**20, 1),
+                   "launch": "hipGraph; per layer bitlinear_forward_gated", "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        facts = host_facts()
+        rows = min(M, 8)
+        sel = np.linspace(0, M - 1, rows).round().astype(int)
+        ow, gw_, ww = synth.widen(o.cpu())[sel], synth.widen(g.cpu())[sel], synth.widen(gw.cpu())
+        _, beta, Wq = oracle.pack_weights(host_W.numpy())
+        gn0 = synth.widen(gains[0].cpu())
+        old = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {facts["pinned_core"]})
+        try:
+            t0, n = time.perf_counter(), 0
+            while True:
+                z = oracle.rmsnorm_swish_gate(ow, gw_, ww, eps=GATE_EPS).astype(np.float32)
+                oracle.forward(z, gn0, Wq, beta)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        finally:
+            os.sched_setaffinity(0, old)
+        out["cpu_baseline"] = {
+            "value": round(rows * n / el / layers, 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} passes of {rows} of {M} token rows through one layer's gate + o_proj "
+                      f"({el:.1f} s single-threaded; scaled to {layers} layers)",
+            "host": {"nproc": facts["nproc"], "cpu_model": facts["model"],
+                     "pinned": f"core {facts['pinned_core']}"}}
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def host_facts():
@@ -802,6 +921,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload.endswith("-mlp"):
         run_mlp(args)
+        return
+    if args.workload.endswith("-gate"):
+        run_gate(args)
         return
 
     sweep = args.workload == "c5"

@@ -273,6 +273,40 @@ int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, cons
                           int h_dtype, float eps, void *ws, size_t ws_bytes, int path,
                           hipStream_t stream);
 
+/* ------------------------------------------- FusedRMSNormSwishGate
+ * The gate in front of o_proj.  The pages name it -- the gate part of an
+ * HGRNBit block is FusedRMSNormSwishGate, a layer of its own fusing an
+ * RMSNorm with the gate (hysenlabs ja review, sections "HGRNBit という層構成を
+ * 読む" and "代替手段との違い") -- but give no formula; this library reads the
+ * name as the RMSNorm of the token mixer's output o times the Swish of the
+ * gate input g, Swish with unit slope being the SiLU of the GLU (datacamp
+ * page, section "Kernkomponenten: MLGRU und GLU"):
+ *   z[m,k] = ((o[m,k] * r_m) * w[k]) * silu(g[m,k]),
+ *   r_m = 1 / sqrt(mean_k o[m,k]^2 + eps)
+ * (sum of squares in fp64, the rest fp32, silu from the hardware exp2 and
+ * reciprocal, ~1e-6 relative), z rounded to the activation dtype. */
+
+/* z [M, K] (dtype, written) from o, g [M, K] and the gate gain w [K] (all
+ * dtype, device, read only).  K % 128 == 0, K <= 4096 (else
+ * BL_ERR_UNSUPPORTED); eps > 0 (this library's workloads use 1e-6). */
+int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, int dtype,
+                                 int64_t M, int64_t K, float eps, void *z, hipStream_t stream);
+
+/* o_proj with the gate as its prologue: y = FusedBitLinear(z) for the z of
+ * bitlinear_rmsnorm_swish_gate(o, g, gate_w, gate_eps), without z going
+ * through memory: the act-quant launch computes z in registers and
+ * quantizes it (codes, scales and row sums identical to running the gate
+ * and then bitlinear_forward on the stored z), then the contraction runs on
+ * the skinny path (M <= 64) or the MFMA path.  gain, packed, beta, N, y,
+ * y_dtype, eps, ws and ws_bytes as for bitlinear_forward (workspace
+ * bitlinear_workspace_bytes(M, K, N)); x_dtype is the dtype of o, g, gate_w
+ * and gain; K <= 4096. */
+int bitlinear_forward_gated(const void *o, const void *g, const void *gate_w, float gate_eps,
+                            int x_dtype, int64_t M, int64_t K, const void *gain,
+                            const void *packed, const float *beta, int64_t N, void *y,
+                            int y_dtype, float eps, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* ------------------------------------------------------ chained decode
  * A decode step of an HGRNBit stack is a chain of FusedBitLinear calls: per
  * block i/f/g_proj on the block input, o_proj, the MLP's gate_proj (GLU)

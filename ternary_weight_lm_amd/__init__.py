@@ -22,7 +22,7 @@ from ._lib import (  # noqa: F401
     bitlinear_workspace_bytes, bitlinear_forward_noalloc, bitlinear_noalloc_max_scratch_bytes,
     BL_ERR_TIMEOUT, BlChain, make_chain_calls, bitlinear_chain_workspace_bytes,
     bitlinear_chain_plan, bitlinear_chain_run, bitlinear_chain_run_ex, bitlinear_chain_status,
-    bitlinear_test_fail_launches,
+    bitlinear_test_fail_launches, bitlinear_rmsnorm_swish_gate, bitlinear_forward_gated,
 )
 
 

@@ -97,6 +97,8 @@ SIGNATURES = {
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
     "bitlinear_noalloc_max_scratch_bytes": ([], SZ),
     "bitlinear_test_fail_launches": ([I], None),
+    "bitlinear_rmsnorm_swish_gate": ([P, P, P, I, I64, I64, F, P, P], I),
+    "bitlinear_forward_gated": ([P, P, P, F, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, P], I),
     "bitlinear_chain_workspace_bytes": ([P, I, I64], SZ),
     "bitlinear_chain_plan": ([P, I, I64, I, F, P, SZ, P, P], I),
     "bitlinear_chain_run": ([P, P], I),
@@ -457,3 +459,30 @@ def bitlinear_chain_status(plan: BlChain, stream=None) -> int:
     if st not in (0, BL_ERR_TIMEOUT):
         _check("bitlinear_chain_status", st)
     return st
+
+
+# ------------------------------------------------------ swish gate (o_proj)
+
+def bitlinear_rmsnorm_swish_gate(o, g, w, z, eps=1e-6, stream=None):
+    """z = ((o * r) * w) * silu(g), r = 1/sqrt(mean(o^2) + eps), per row."""
+    _need(o, "o", FLOATS, dims=2)
+    M, K = o.shape
+    _need(g, "g", o.dtype, numel=M * K)
+    _need(w, "w", o.dtype, numel=K)
+    _need(z, "z", o.dtype, numel=M * K)
+    _check("bitlinear_rmsnorm_swish_gate", lib().bitlinear_rmsnorm_swish_gate(
+        _ptr(o), _ptr(g), _ptr(w), DTYPE_CODE[o.dtype], M, K, eps, _ptr(z), _stream(stream)))
+
+
+def bitlinear_forward_gated(o, g, gate_w, gain, packed, beta, N, y, ws, gate_eps=1e-6, eps=1e-8,
+                            stream=None):
+    """y = FusedBitLinear(z) with z = the swish gate of (o, g) (o_proj with
+    the gate as its prologue)."""
+    M, K = _check_layer_io(o, gain, packed, beta, N, y, N)
+    _need(g, "g", o.dtype, numel=M * K)
+    _need(gate_w, "gate_w", o.dtype, numel=K)
+    _need(ws, "ws", numel=1)
+    _check("bitlinear_forward_gated", lib().bitlinear_forward_gated(
+        _ptr(o), _ptr(g), _ptr(gate_w), gate_eps, DTYPE_CODE[o.dtype], M, K, _ptr(gain),
+        _ptr(packed), _ptr(beta), N, _ptr(y), DTYPE_CODE[y.dtype], eps, _ptr(ws), _nbytes(ws),
+        _stream(stream)))

@@ -166,6 +166,25 @@ hipError_t chain_run(const bl_chain &p, uint32_t wait_us, hipStream_t stream);
 // synchronizes the stream, returns the chain's error word and clears it
 hipError_t chain_error(const bl_chain &p, uint32_t *err, hipStream_t stream);
 
+// FusedRMSNormSwishGate (gate.hip), one wave per row, K <= kGateMaxK:
+// z = ((o r) w) silu(g) rounded to dtype.  xq == nullptr: store z [M, K];
+// else quantize z for the following projection (gain, eps) into xq / s /
+// rowsum, as the act-quant kernel would from the stored z.
+struct GateArgs {
+  const void *o, *g, *w;
+  float gate_eps;
+  int dtype;
+  int64_t M, K;
+  void *z;
+  const void *gain;
+  float eps;
+  int8_t *xq;
+  float *s;
+  int32_t *rowsum;
+};
+constexpr int64_t kGateMaxK = 4096;
+hipError_t launch_gate(const GateArgs &a, hipStream_t stream);
+
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;
 constexpr int64_t kFusedMaxK = 8192;

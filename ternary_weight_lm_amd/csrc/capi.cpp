@@ -741,3 +741,78 @@ int bitlinear_chain_status(const bl_chain *plan, hipStream_t stream) {
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, int dtype,
+                                 int64_t M, int64_t K, float eps, void *z, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BL_ERR_DTYPE;
+  if (!m_ok(M) || K < 128 || K % 128 != 0) return BL_ERR_SHAPE;
+  if (K > bl::kGateMaxK) return BL_ERR_UNSUPPORTED;
+  if (!eps_ok(eps)) return BL_ERR_EPS;
+  if (M == 0) return BL_OK;
+  if (!o || !g || !w || !z) return BL_ERR_NULL;
+  if (!aligned16(o) || !aligned16(g) || !aligned16(w) || !aligned16(z)) return BL_ERR_ALIGN;
+  bl::GateArgs a{};
+  a.o = o;
+  a.g = g;
+  a.w = w;
+  a.gate_eps = eps;
+  a.dtype = dtype;
+  a.M = M;
+  a.K = K;
+  a.z = z;
+  return hip_status(BL_LAUNCH(bl::launch_gate(a, stream)));
+}
+
+int bitlinear_forward_gated(const void *o, const void *g, const void *gate_w, float gate_eps,
+                            int x_dtype, int64_t M, int64_t K, const void *gain,
+                            const void *packed, const float *beta, int64_t N, void *y,
+                            int y_dtype, float eps, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (!nk_ok(N, K) || !m_ok(M)) return BL_ERR_SHAPE;
+  if (K > bl::kGateMaxK) return BL_ERR_UNSUPPORTED;
+  if (!eps_ok(eps) || !eps_ok(gate_eps)) return BL_ERR_EPS;
+  if (M == 0) return BL_OK;
+  if (!o || !g || !gate_w || !gain || !packed || !beta || !y) return BL_ERR_NULL;
+  if (!ws || ws_bytes < fwd_ws_bytes(M, K)) return BL_ERR_WORKSPACE;
+  if (!aligned16(o) || !aligned16(g) || !aligned16(gate_w) || !aligned16(gain) ||
+      !aligned16(packed) || !aligned16(y) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return BL_ERR_ALIGN;
+  const FwdWs w = carve(ws, M, K);
+  bl::GateArgs a{};
+  a.o = o;
+  a.g = g;
+  a.w = gate_w;
+  a.gate_eps = gate_eps;
+  a.dtype = x_dtype;
+  a.M = M;
+  a.K = K;
+  a.gain = gain;
+  a.eps = eps;
+  a.xq = w.xq;
+  a.s = w.s;
+  a.rowsum = w.rowsum;
+  if (BL_LAUNCH(bl::launch_gate(a, stream)) != hipSuccess) return BL_ERR_HIP;
+  if (M <= bl::kSkinnyMaxM) {
+    bl::SkinnyArgs sa{};
+    sa.fused = false;
+    sa.xq = w.xq;
+    sa.s = w.s;
+    sa.rowsum = w.rowsum;
+    sa.packed = packed;
+    sa.beta = beta;
+    sa.M = M;
+    sa.N = N;
+    sa.K = K;
+    sa.out = y;
+    sa.out_kind = y_dtype;
+    return hip_status(BL_LAUNCH(bl::launch_skinny(sa, stream)));
+  }
+  return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
+                                                   y_dtype, false, stream)));
+}
+
+}  // extern "C"

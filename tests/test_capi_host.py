@@ -479,3 +479,34 @@ def test_forced_launch_failure_reaches_the_caller():
                                               WSP, gws, None) == HIP
     finally:
         L.bitlinear_test_fail_launches(0)
+
+
+def test_gate_entry_points_validation():
+    L = tw.lib()
+    gt = L.bitlinear_rmsnorm_swish_gate
+    assert gt(A, B, C, 9, 4, 1024, 1e-6, Y, None) == DTYPE
+    assert gt(A, B, C, 2, 4, 1000, 1e-6, Y, None) == SHAPE
+    assert gt(A, B, C, 2, 4, 8192, 1e-6, Y, None) == UNSUP      # K > 4096
+    assert gt(A, B, C, 2, 4, 1024, 0.0, Y, None) == EPS
+    assert gt(A, None, C, 2, 4, 1024, 1e-6, Y, None) == NULL
+    assert gt(A, B, C + 4, 2, 4, 1024, 1e-6, Y, None) == ALIGN
+    assert gt(None, None, None, 2, 0, 1024, 1e-6, None, None) == OK
+    fg = L.bitlinear_forward_gated
+    wsb = L.bitlinear_workspace_bytes(4, 1024, 512)
+    args = lambda **k: dict(dict(o=A, g=B, w=C, ge=1e-6, xdt=2, M=4, K=1024, gain=D, pk=E, beta=D,
+                                 N=512, y=Y, ydt=2, eps=1e-8, ws=WSP, wsb=wsb), **k)
+
+    def call(**k):
+        a = args(**k)
+        return fg(a["o"], a["g"], a["w"], a["ge"], a["xdt"], a["M"], a["K"], a["gain"], a["pk"],
+                  a["beta"], a["N"], a["y"], a["ydt"], a["eps"], a["ws"], a["wsb"], None)
+
+    assert call(xdt=5) == DTYPE
+    assert call(N=100) == SHAPE
+    assert call(K=8192, wsb=1 << 20) == UNSUP
+    assert call(ge=-1.0) == EPS
+    assert call(eps=float("nan")) == EPS
+    assert call(g=None) == NULL
+    assert call(wsb=16) == WS
+    assert call(o=A + 2) == ALIGN
+    assert call(M=0, o=None, g=None) == OK
