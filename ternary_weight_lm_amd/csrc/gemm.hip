@@ -23,12 +23,20 @@
 // Epilogue: subtract rowsum, multiply by beta / s_m, round to the output
 // dtype (or store the exact int32 accumulator); long launches stage 2-byte
 // output tiles through LDS for whole-row-segment stores.
+// Launches with few tiles split K inside the workgroup: KG groups of 4
+// waves (KG = 2 or 4) each run the whole tile over a contiguous range of
+// k-blocks with their own A stage, then the groups' int32 accumulators are
+// added through LDS into group 0, which runs the epilogue.  Integer sums do
+// not depend on the order, so the result is the same bits; the serial chain
+// of k-blocks per wave (the latency that bounds a one-round launch) shrinks
+// KG-fold and each CU holds KG times the waves.
 // Workgroup ids are remapped so each of the 8 XCDs (which receive ids
 // round-robin) works on a contiguous range of a banded column-major tile
 // order, keeping the A rows and B columns of the tiles it runs together in
 // that XCD's L2.  A grouped launch (gemm_mfma_group_kernel) runs up to three
 // same-shape contractions as one tile sequence.
 #include <algorithm>
+#include <type_traits>
 
 #include "bl_common.h"
 #include "bl_launch.h"
@@ -43,14 +51,17 @@ namespace bl {
 // Loads are buffer loads: a per-lane offset fixed for the whole loop plus a
 // k-block offset in a scalar register, so no vector address arithmetic runs
 // per k-block; rows and tiles past the matrix read as zero.
-template <int MI, int TPW>
-__device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, uint8_t *next,
+// kb: the k-block multiplied now; kend: one past the last k-block of this
+// wave's range (loads clamp to it, k-blocks at or past it are trips that
+// only keep the barriers in step with the other groups: CHECK = KG > 1).
+template <int MI, int TPW, bool CHECK>
+__device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur, uint8_t *next,
                                             v4i (&acc)[MI][2 * TPW], v4i (&a_store)[MI],
                                             v4i (&a_load)[MI], v4i (&b)[TPW],
                                             rsrc_t ars, const int (&a_voff)[MI],
                                             const int (&a_dst)[MI], rsrc_t brs, int b_voff,
                                             int b_tile_bytes, int arow0, int lane) {
-  const int k2 = min(kb + 2, KB - 1);  // the tail re-reads the last block (unused)
+  const int k2 = min(kb + 2, kend - 1);  // the tail re-reads the last block (unused)
   // scheduling fences keep each k-block's work in its own slot: without
   // them the scheduler pulls the next block's unpack (and so its wait for
   // the B loads) forward, shortening the prefetch distance
@@ -79,6 +90,7 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
   // scheduler reads two operands at a time and waits for each pair, which
   // exposes the LDS latency 2*MI/2 times per k-block
   __builtin_amdgcn_sched_barrier(0);
+  if (!CHECK || kb < kend) {
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -93,6 +105,7 @@ __device__ __forceinline__ void gemm_kblock(int kb, int KB, const uint8_t *cur, 
         acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
       }
     }
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -117,7 +130,8 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 // contraction's tiles; work: tiles x k-blocks of the whole launch (picks the
 // epilogue).  GLU: the packed rows are a gate_proj in GLU order (each 32-row
 // tile = 16 gated rows + the 16 rows they multiply) and out is h [M, N/2].
-template <int MI, int OUT, bool GLU, int TPW>
+// KG: groups of 4 waves splitting K (256 KG threads).
+template <int MI, int OUT, bool GLU, int TPW, int KG>
 __device__ __forceinline__ void gemm_body(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
@@ -125,11 +139,16 @@ __device__ __forceinline__ void gemm_body(
     void *__restrict__ out, int tiles_m, int tiles_n, int t, int work) {
   constexpr int BM = 32 * MI;
   constexpr int BN = 64 * TPW;  // a wave: 16 MI rows x 32 TPW outputs (TPW packed tiles)
-  __shared__ __align__(16) uint8_t lds[2][BM * 128];
+  static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
+  static_assert(KG == 1 || TPW == 2, "the K-group reduction fits 2-tile waves only");
+  __shared__ __align__(16) uint8_t lds[KG][2][BM * 128];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
+  const int kg = KG == 1 ? 0 : wave >> 2;                    // K group
+  const int wq = wave & 3;                                    // wave in its group
+  const int gtid = tid & 255;                                 // thread in its group
+  const int wm = wq >> 1, wn = wq & 1;
 
   // Inside the sequence, tiles go column by column through bands of
   // kBandRows tile rows, so the ~64 workgroups an XCD runs at once share a
@@ -141,6 +160,12 @@ __device__ __forceinline__ void gemm_body(
   const int m0 = tm * BM, n0 = tn * BN;
   const int KB = K >> 7;
   const int NT = N >> 5;
+  // this group's k-blocks [kb0, kend); every group runs `trips` k-blocks so
+  // the barriers stay in step (the surplus trips multiply nothing)
+  const int trips = KG == 1 ? KB : (KB + KG - 1) / KG;
+  const int kb0 = KG == 1 ? 0 : min(kg * trips, KB);
+  const int kend = KG == 1 ? KB : min(KB, kb0 + trips);
+  const int klast = max(kend - 1, 0);
 
   // ---- A tile: BM rows x 8 chunks of 16 B, MI chunks per thread; thread
   // chunk j covers row (tid + 256 j) / 8, chunk (tid + 256 j) % 8.  The
@@ -150,7 +175,7 @@ __device__ __forceinline__ void gemm_body(
   int a_voff[MI], a_dst[MI];
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
-    const int c = tid + 256 * j;
+    const int c = gtid + 256 * j;
     const int row = c >> 3, ch = c & 7;
     a_voff[j] = row * K + ch * 16;
     a_dst[j] = row * 128 + (swz(row, ch) << 4);
@@ -179,40 +204,85 @@ __device__ __forceinline__ void gemm_body(
   // copies are lowered to memcpy through private memory.)
   v4i P[MI], Q[MI];     // A staging sets
   v4i X[TPW], Y[TPW];   // B of even / odd k-blocks
+  uint8_t *const st0 = lds[kg][0];
+  uint8_t *const st1 = lds[kg][1];
   {
-    const int k1 = min(1, KB - 1);
+    const int k0 = min(kb0, klast), k1 = min(kb0 + 1, klast);
 #pragma unroll
     for (int j = 0; j < MI; ++j)
-      Q[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], 0, 0));
+      Q[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k0 * 128, 0));
 #pragma unroll
     for (int j = 0; j < MI; ++j)
       P[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k1 * 128, 0));
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
       X[t] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, 0, 0));
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k0 * 1024, 0));
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
       Y[t] = __builtin_bit_cast(
           v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k1 * 1024, 0));
 #pragma unroll
-    for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(&lds[0][a_dst[j]]) = Q[j];
+    for (int j = 0; j < MI; ++j) *reinterpret_cast<v4i *>(st0 + a_dst[j]) = Q[j];
   }
   __syncthreads();
 
   const int arow0 = wm * 16 * MI + (lane & 15);
   // Both halves of a trip are unconditional: a conditional second half would
   // let the compiler sink the first half's prefetch loads into it.
-  int kb = 0;
-  for (; kb + 1 < KB; kb += 2) {
-    gemm_kblock<MI, TPW>(kb, KB, lds[0], lds[1], acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
-                         tile_bytes, arow0, lane);
-    gemm_kblock<MI, TPW>(kb + 1, KB, lds[1], lds[0], acc, Q, P, Y, ars, a_voff, a_dst, brs,
-                         b_voff, tile_bytes, arow0, lane);
+  constexpr bool CHECK = KG > 1;
+  const int kstop = kb0 + trips;
+  int kb = kb0;
+  for (; kb + 1 < kstop; kb += 2) {
+    gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+                                tile_bytes, arow0, lane);
+    gemm_kblock<MI, TPW, CHECK>(kb + 1, kend, st1, st0, acc, Q, P, Y, ars, a_voff, a_dst, brs,
+                                b_voff, tile_bytes, arow0, lane);
   }
-  if (kb < KB)
-    gemm_kblock<MI, TPW>(kb, KB, lds[0], lds[1], acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
-                         tile_bytes, arow0, lane);
+  if (kb < kstop)
+    gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+                                tile_bytes, arow0, lane);
+
+  if constexpr (KG > 1) {
+    // Add the groups' accumulators into group 0 through the A stages (free:
+    // the last k-block ended with a barrier).  A slot holds one group's
+    // accumulators, lane-contiguous per register; KG = 4 uses two slots and
+    // a two-level tree (2 -> 0 and 3 -> 1, then 1 -> 0).  Every wave passes
+    // every barrier.
+    constexpr int NREG = MI * 2 * TPW;
+    static_assert(KG * 2 * BM * 128 >= (KG / 2) * 4 * NREG * 64 * 16, "reduction slots fit");
+    v4i *const red = reinterpret_cast<v4i *>(&lds[0][0][0]);
+    const auto slot = [&](int gs, int mi, int nb) -> v4i * {
+      return red + ((gs * 4 + wq) * NREG + mi * 2 * TPW + nb) * 64 + lane;
+    };
+    const auto put_acc = [&](int gs) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 2 * TPW; ++nb) *slot(gs, mi, nb) = acc[mi][nb];
+    };
+    const auto add_acc = [&](int gs) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] += *slot(gs, mi, nb);
+    };
+    if constexpr (KG == 2) {
+      if (kg == 1) put_acc(0);
+      __syncthreads();
+      if (kg == 1) return;
+      add_acc(0);
+    } else {
+      if (kg >= 2) put_acc(kg - 2);
+      __syncthreads();
+      if (kg < 2) add_acc(kg);
+      __syncthreads();
+      if (kg == 1) put_acc(0);
+      __syncthreads();
+      if (kg != 0) return;
+      add_acc(0);
+    }
+  }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
   // row sums and rescale factors of the wave's 16*MI rows go through a small
@@ -224,8 +294,8 @@ __device__ __forceinline__ void gemm_body(
   const int wrow0 = m0 + wm * 16 * MI;
   if (lane < 16 * MI) {
     const int mrow = min(wrow0 + lane, M - 1);
-    e_rs[wave][lane] = rowsum[mrow];
-    if constexpr (OUT != kOutI32) e_sc[wave][lane] = div_rn(*beta, s[mrow]);
+    e_rs[wq][lane] = rowsum[mrow];
+    if constexpr (OUT != kOutI32) e_sc[wq][lane] = div_rn(*beta, s[mrow]);
   }
   wave_lds_sync();
   const int q4 = 4 * (lane >> 4);
@@ -234,8 +304,8 @@ __device__ __forceinline__ void gemm_body(
   float sc4[MI][4];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    rs4[mi] = *reinterpret_cast<const v4i *>(&e_rs[wave][16 * mi + q4]);
-    const v4i t = *reinterpret_cast<const v4i *>(&e_sc[wave][16 * mi + q4]);
+    rs4[mi] = *reinterpret_cast<const v4i *>(&e_rs[wq][16 * mi + q4]);
+    const v4i t = *reinterpret_cast<const v4i *>(&e_sc[wq][16 * mi + q4]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc4[mi][i] = __int_as_float(t[i]);
   }
@@ -268,7 +338,7 @@ __device__ __forceinline__ void gemm_body(
       }
     return;
   }
-  if constexpr ((OUT == BL_F16 || OUT == BL_BF16) && TPW == 2) {
+  if constexpr ((OUT == BL_F16 || OUT == BL_BF16) && TPW == 2 && KG == 1) {
     // Whole tile of 2-byte outputs in a long launch: the wave's 16 MI x 64
     // block goes through the A buffers (idle since the barrier that ended
     // the last k-block), row-major with each row's 16-byte chunks XOR-
@@ -279,7 +349,7 @@ __device__ __forceinline__ void gemm_body(
     // other tile overlaps, so short launches store directly (measured
     // threshold: tiles x k-blocks > 16384).
     if (m0 + BM <= M && n0 + BN <= N && work > 16384) {
-      uint8_t *st = &lds[0][0] + wave * (16 * MI * 128);
+      uint8_t *st = &lds[0][0][0] + wq * (16 * MI * 128);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -335,15 +405,18 @@ __device__ __forceinline__ void gemm_body(
   }
 }
 
-template <int MI, int OUT, bool GLU, int TPW = 2>
-__global__ __launch_bounds__(256, TPW == 2 ? 3 : 2) void gemm_mfma_kernel(
+// workgroups per CU the register budget is set for
+constexpr int gemm_occupancy(int TPW, int KG) { return TPW == 4 ? 2 : KG == 1 ? 3 : KG == 2 ? 2 : 1; }
+
+template <int MI, int OUT, bool GLU, int TPW = 2, int KG = 1>
+__global__ __launch_bounds__(256 * KG, gemm_occupancy(TPW, KG)) void gemm_mfma_kernel(
     const int8_t *__restrict__ xq, const int32_t *__restrict__ rowsum,
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
     void *__restrict__ out, int tiles_m, int tiles_n) {
   const int ntiles = tiles_m * tiles_n;
-  gemm_body<MI, OUT, GLU, TPW>(xq, rowsum, s, packed, beta, M, N, K, out, tiles_m, tiles_n,
-                               xcd_tile((int)blockIdx.x, ntiles), ntiles * (K >> 7));
+  gemm_body<MI, OUT, GLU, TPW, KG>(xq, rowsum, s, packed, beta, M, N, K, out, tiles_m, tiles_n,
+                                   xcd_tile((int)blockIdx.x, ntiles), ntiles * (K >> 7));
 }
 
 // Up to kGemmCalls contractions of one shape in one launch (HGRN's i/f/g at
@@ -351,20 +424,19 @@ __global__ __launch_bounds__(256, TPW == 2 ? 3 : 2) void gemm_mfma_kernel(
 // launch of three one-round contractions runs as several rounds whose
 // epilogues overlap other tiles' main loops.  The pointers come from the
 // argument buffer.
-template <int MI, int OUT, int TPW = 2>
-__global__ __launch_bounds__(256, TPW == 2 ? 3 : 2) void gemm_mfma_group_kernel(int ncalls, int M, int N, int K,
-                                                                 int tiles_m, int tiles_n,
-                                                                 GemmCalls calls) {
+template <int MI, int OUT, int TPW = 2, int KG = 1>
+__global__ __launch_bounds__(256 * KG, gemm_occupancy(TPW, KG)) void gemm_mfma_group_kernel(
+    int ncalls, int M, int N, int K, int tiles_m, int tiles_n, GemmCalls calls) {
   const int ntiles = tiles_m * tiles_n;
   const int tg = xcd_tile((int)blockIdx.x, ncalls * ntiles);
   const int call = __builtin_amdgcn_readfirstlane(tg / ntiles);
   const GemmCall &c = calls.c[call];
-  gemm_body<MI, OUT, false, TPW>(c.xq, c.rowsum, c.s, reinterpret_cast<const uint4 *>(c.packed), c.beta,
-                            M, N, K, c.out, tiles_m, tiles_n, tg - call * ntiles,
-                            ncalls * ntiles * (K >> 7));
+  gemm_body<MI, OUT, false, TPW, KG>(c.xq, c.rowsum, c.s, reinterpret_cast<const uint4 *>(c.packed),
+                                     c.beta, M, N, K, c.out, tiles_m, tiles_n, tg - call * ntiles,
+                                     ncalls * ntiles * (K >> 7));
 }
 
-template <int MI, int TPW = 2>
+template <int MI, int TPW = 2, int KG = 1>
 static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N, int64_t K,
@@ -375,7 +447,7 @@ static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
   const uint4 *pk = reinterpret_cast<const uint4 *>(packed);
 #define BL_GEMM_CASE(KIND, G)                                                \
-  gemm_mfma_kernel<MI, KIND, G, TPW><<<grid, 256, 0, stream>>>(              \
+  gemm_mfma_kernel<MI, KIND, G, TPW, KG><<<grid, 256 * KG, 0, stream>>>(     \
       xq, rowsum, s, pk, beta, (int)M, (int)N, (int)K, out, tiles_m, tiles_n)
   if (glu) {
     switch (out_kind) {
@@ -409,6 +481,37 @@ constexpr int tall_mi(int64_t t128, int64_t t96) {
   return ((t96 + kCUs - 1) / kCUs) * 3 < ((t128 + kCUs - 1) / kCUs) * 4 ? 3 : 4;
 }
 
+// K groups per workgroup for a launch of `tiles` workgroups of 32 MI rows
+// over KB k-blocks of 128.  A split pays while the launch leaves a CU about
+// one workgroup (its waves then wait on every k-block's loads): 4 groups
+// while every tile fits one 16-wave workgroup per CU, 2 groups while the
+// 8-wave workgroups still all fit at once (3 per CU at MI = 1, ~2 at MI =
+// 2), at least 4 k-blocks per group.  Measured on 2.7B shapes (us, K groups
+// 1 / 2 / 4): M = 128 o_proj 9.2 / 7.0 / 6.8, down_proj 20.4 / 13.8 / 11.6;
+// M = 256 down_proj 20.3 / 13.9 / 11.6, gate_proj 16.6 / 15.4 / 18.6; M =
+// 512 o_proj 10.3 / 9.5 / 11.9, down_proj 22.3 / 19.0 / 21.5, i/f/g grouped
+// (480 tiles of 64 rows) 13.9 / 14.5.  Taller tiles (MI >= 3, 440 and more
+// of them) measured 2-15 % slower split, and never split.
+constexpr int k_groups(int64_t tiles, int64_t KB, int MI) {
+  return MI > 2                                                      ? 1
+         : tiles <= kCUs && KB >= 16                                 ? 4
+         : tiles <= (MI == 1 ? 3 * kCUs : 7 * kCUs / 4) && KB >= 8 ? 2
+                                                                     : 1;
+}
+
+template <int MI>
+static hipError_t launch_mi_kg(int kg, const int8_t *xq, const int32_t *rowsum, const float *s,
+                               const void *packed, const float *beta, int64_t M, int64_t N,
+                               int64_t K, void *out, int out_kind, bool glu, hipStream_t stream) {
+  if constexpr (MI <= 2) {
+    if (kg == 4)
+      return launch_mi<MI, 2, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+    if (kg == 2)
+      return launch_mi<MI, 2, 2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+  }
+  return launch_mi<MI, 2, 1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+}
+
 hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N,
@@ -433,21 +536,24 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
     return tall_mi(tiles(128), tiles(96)) == 3
                ? launch_mi<3>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream)
                : launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+  const int64_t KB = K / 128;
   if (M > 32 && tiles(64) >= 256)
-    return launch_mi<2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
-  return launch_mi<1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+    return launch_mi_kg<2>(k_groups(tiles(64), KB, 2), xq, rowsum, s, packed, beta, M, N, K, out,
+                           out_kind, glu, stream);
+  return launch_mi_kg<1>(k_groups(tiles(32), KB, 1), xq, rowsum, s, packed, beta, M, N, K, out,
+                         out_kind, glu, stream);
 }
 
-template <int MI, int TPW = 2>
+template <int MI, int TPW = 2, int KG = 1>
 static hipError_t launch_group_mi(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
                                   int64_t K, int out_kind, hipStream_t stream) {
   const int BM = 32 * MI, BN = 64 * TPW;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * ncalls);
-#define BL_GEMMG_CASE(KIND)                                                     \
-  gemm_mfma_group_kernel<MI, KIND, TPW><<<grid, 256, 0, stream>>>(ncalls, (int)M, (int)N, (int)K, \
-                                                             tiles_m, tiles_n, calls)
+#define BL_GEMMG_CASE(KIND)                                                         \
+  gemm_mfma_group_kernel<MI, KIND, TPW, KG><<<grid, 256 * KG, 0, stream>>>(         \
+      ncalls, (int)M, (int)N, (int)K, tiles_m, tiles_n, calls)
   switch (out_kind) {
     case BL_F32: BL_GEMMG_CASE(BL_F32); break;
     case BL_F16: BL_GEMMG_CASE(BL_F16); break;
@@ -468,8 +574,16 @@ hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M,
     return tall_mi(tiles(128), tiles(96)) == 3
                ? launch_group_mi<3>(calls, ncalls, M, N, K, out_kind, stream)
                : launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
-  if (M > 32 && tiles(64) >= 256) return launch_group_mi<2>(calls, ncalls, M, N, K, out_kind, stream);
-  return launch_group_mi<1>(calls, ncalls, M, N, K, out_kind, stream);
+  const int64_t KB = K / 128;
+  const auto go = [&](auto mi_tag, int kg) {
+    constexpr int MI = decltype(mi_tag)::value;
+    if (kg == 4) return launch_group_mi<MI, 2, 4>(calls, ncalls, M, N, K, out_kind, stream);
+    if (kg == 2) return launch_group_mi<MI, 2, 2>(calls, ncalls, M, N, K, out_kind, stream);
+    return launch_group_mi<MI, 2, 1>(calls, ncalls, M, N, K, out_kind, stream);
+  };
+  if (M > 32 && tiles(64) >= 256)
+    return go(std::integral_constant<int, 2>{}, k_groups(tiles(64), KB, 2));
+  return go(std::integral_constant<int, 1>{}, k_groups(tiles(32), KB, 1));
 }
 
 }  // namespace bl

@@ -149,16 +149,51 @@ def test_gemm_i32_wide_tile_launches_full(M, N, K):
     np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
 
 
-@pytest.mark.parametrize("ydt", ["bf16", "fp16"])
-def test_contract_grouped_wide_full(ydt):
-    """A grouped launch of three 3072 x 4096 x 128 contractions (1152 tiles of
-    128 x 256 across the calls: the grouped kernel's 4-tile waves, as i/f/g
-    at prefill), every output element against the oracle's int32
-    contraction rescaled as the epilogue does it (fp32 acc times the
-    correctly rounded fp32 beta / s, rounded once to the output dtype), each
-    output guarded."""
-    say(f"contract_grouped wide tiles y={ydt}")
-    M, N, K = 3072, 4096, 128
+# (M, N, K) -> (tile height, K groups) under the launch rule in gemm.hip:
+# (20, 992, 2176) 32 rows, 4 groups over 17 k-blocks (5/5/5/2);
+# (100, 2560, 7040) 32, 4 over 55 (14/14/14/13); (512, 2560, 2560) 32, 2;
+# (400, 2560, 7040) 32, 2 over 55 (28/27); (40, 3072, 1280) 32, 2 over 10;
+# (300, 1024, 1024) 32, 2 over 8; (700, 2976, 1152) 64, 2 over 9 (5/4);
+# (1000, 2560, 7040) 64, 2; (1000, 2048, 2560) 64, 4; (64, 512, 512) 32, 1
+# (too few k-blocks to split); (2048, 2560, 7040) 96 rows, not split.
+K_GROUP_SHAPES = [(20, 992, 2176), (100, 2560, 7040), (512, 2560, 2560), (400, 2560, 7040),
+                  (40, 3072, 1280), (300, 1024, 1024), (700, 2976, 1152), (1000, 2560, 7040),
+                  (1000, 2048, 2560), (64, 512, 512), (2048, 2560, 7040)]
+
+
+@pytest.mark.parametrize("M,N,K", K_GROUP_SHAPES)
+def test_gemm_i32_k_groups_full(M, N, K):
+    """Launches with few tiles split K over 2 or 4 wave groups of one
+    workgroup and add the groups' int32 accumulators in LDS: every element
+    against the oracle's contraction (ragged M, N and uneven k-block shares
+    included), guard bands around the output."""
+    say(f"gemm_i32 k-groups M={M} N={N} K={K}")
+    xq = _random_codes(M, K, 5 * M + N + K)
+    r = np.random.default_rng(M + 11 * N + K)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wq[0] = 1
+    Wq[N - 1] = -1
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = Guarded((M, N), torch.int32, fill=-7)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc.t, path=tw.BL_PATH_MFMA)
+    acc.check("acc")
+    np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
+
+
+@pytest.mark.parametrize("ydt,M,N,K", [("bf16", 3072, 4096, 128), ("fp16", 3072, 4096, 128),
+                                         ("bf16", 256, 2560, 2560), ("fp16", 100, 1024, 2176)])
+def test_contract_grouped_full(ydt, M, N, K):
+    """A grouped launch of three same-shape contractions, every output
+    element against the oracle's int32 contraction rescaled as the epilogue
+    does it (fp32 acc times the correctly rounded fp32 beta / s, rounded once
+    to the output dtype), each output guarded.  3072 x 4096 x 128: 1152 tiles
+    of 128 x 256 across the calls (the grouped kernel's 4-tile waves, as
+    i/f/g at prefill); 256 x 2560 x 2560: 480 tiles of 32 rows, K split over
+    2 wave groups (i/f/g of the 2.7B layer at 256 tokens); 100 x 1024 x
+    2176: 96 tiles, K split over 4 groups with uneven shares."""
+    say(f"contract_grouped M={M} N={N} K={K} y={ydt}")
     items, refs, outs = [], [], []
     for j in range(3):
         xq = _random_codes(M, K, 500 + j)
