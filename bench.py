@@ -460,7 +460,7 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
         mine = [c for c in grp if wl.path(c) == path]
         if not mine:
             continue
-        if len(mine) > 1 and path in (tw.BL_PATH_MFMA, tw.BL_PATH_FUSED):
+        if len(mine) > 1 and path in (tw.BL_PATH_MFMA, tw.BL_PATH_FUSED, tw.BL_PATH_SKINNY):
             units.append(mine)
         else:
             units.extend([c] for c in mine)
@@ -495,7 +495,7 @@ def roofline(wl, weights, bufs, reps, step_ms=None, steps=None):
                     items.append((xq, sc, rs, pool[c.idx], weights.betas[c.idx], bufs.out[c.idx]))
                 arr = tw.make_contract_calls(items)
                 keep.append(arr)
-                tw.bitlinear_contract_grouped(arr, bufs.out[unit[0].idx].dtype)
+                tw.bitlinear_contract_grouped(arr, bufs.out[unit[0].idx].dtype, path=path)
                 return
             c = unit[0]
             xq, sc, rs = stage[c.idx]
@@ -546,8 +546,10 @@ def run_m(wl, weights, dev, args):
     warmup = args.warmup if args.warmup is not None else (3 if big else 10)
     reps = args.roofline_reps if args.roofline_reps is not None else (2 if big else 10)
     groups = wl.groups()
+    # fused groups are one launch; the two-kernel paths an act-quant launch
+    # and one contraction launch per group (grouped MFMA or grouped skinny)
     per_step = 1 if wl.launch == "chain" else \
-        sum(1 if len(g) > 1 and wl.path(g[0]) == 1 else 2 for g in groups)
+        sum(1 if wl.path(g[0]) == 1 else 2 for g in groups)
     if wl.launch == "chain":
         bufs.chain_plans(wl, weights)
 

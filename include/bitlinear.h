@@ -498,6 +498,17 @@ typedef struct bl_contract_call {
 int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
                                hipStream_t stream);
 
+/* bitlinear_contract_grouped with a path, as bitlinear_contract takes it:
+ * BL_PATH_MFMA is bitlinear_contract_grouped; BL_PATH_SKINNY (every call
+ * M <= 64, else BL_ERR_SHAPE) runs each group of up to three same-shape
+ * calls as one launch of the skinny kernel (the contraction
+ * bitlinear_forward_grouped_ws runs for HGRN's i/f/g at 9..64 tokens);
+ * BL_PATH_AUTO takes SKINNY for groups with M <= 64, else MFMA.  Each
+ * call's y equals bitlinear_contract(..., same path) bit for bit.  Unknown
+ * path: BL_ERR_PATH before anything is launched. */
+int bitlinear_contract_grouped_path(const bl_contract_call *calls, int ncalls, int y_dtype,
+                                    int path, hipStream_t stream);
+
 /* Decode packed weights back to int8 Wq [N, K] in {-1, 0, +1} (device):
  * the ternary matrix of datacamp page, section "MatMul durch ternäre
  * Operationen ersetzen", for checking a pack.  packed as written by

@@ -87,6 +87,7 @@ SIGNATURES = {
     "bitlinear_select_path": ([I64, I64], I),
     "bitlinear_grouped_workspace_bytes": ([P, I, I], SZ),
     "bitlinear_contract_grouped": ([P, I, I, P], I),
+    "bitlinear_contract_grouped_path": ([P, I, I, I, P], I),
     "bitlinear_forward_grouped_ws": ([P, I, I, I, F, P, SZ, P], I),
     "bitlinear_act_quant": ([P, I, P, I64, I64, F, P, P, P, P], I),
     "bitlinear_gemm_i32": ([P, P, I64, I64, P, I64, P, I, P], I),
@@ -391,12 +392,19 @@ def make_contract_calls(items):
     return arr
 
 
-def bitlinear_contract_grouped(calls, y_dtype, stream=None):
-    """calls: a make_contract_calls() array or a list of tuples for it."""
+def bitlinear_contract_grouped(calls, y_dtype, path=BL_PATH_MFMA, stream=None):
+    """calls: a make_contract_calls() array or a list of tuples for it.
+    path BL_PATH_MFMA calls bitlinear_contract_grouped, any other path
+    bitlinear_contract_grouped_path."""
     if not isinstance(calls, ctypes.Array):
         calls = make_contract_calls(calls)
-    _check("bitlinear_contract_grouped", lib().bitlinear_contract_grouped(
-        ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[y_dtype], _stream(stream)))
+    if path == BL_PATH_MFMA:
+        _check("bitlinear_contract_grouped", lib().bitlinear_contract_grouped(
+            ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[y_dtype], _stream(stream)))
+    else:
+        _check("bitlinear_contract_grouped_path", lib().bitlinear_contract_grouped_path(
+            ctypes.cast(calls, ctypes.c_void_p), len(calls), DTYPE_CODE[y_dtype], path,
+            _stream(stream)))
 
 
 def bitlinear_unpack_weights(packed, N, K, Wq, stream=None):

@@ -95,6 +95,10 @@ struct SkinnyArgs {
 };
 hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream);
 
+// Up to kGroupCalls pre-quantized, non-GLU calls of one shape (M <= 64) in
+// one launch of the skinny kernel; each output as launch_skinny computes it.
+hipError_t launch_skinny_pre_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream);
+
 // Up to kGroupMax fused skinny calls per launch (more are split into several
 // launches).  Every call must be fused-eligible and share x / out dtypes.
 constexpr int kGroupMax = 16;

@@ -392,8 +392,10 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
         return BL_ERR_HIP;
       continue;
     }
+    bl::SkinnyArgs sk[bl::kGroupCalls];
     for (int j = 0; j < r.n; ++j) {
-      bl::SkinnyArgs a{};
+      bl::SkinnyArgs &a = sk[j];
+      a = bl::SkinnyArgs{};
       a.fused = false;
       a.xq = gm.c[j].xq;
       a.s = gm.c[j].s;
@@ -405,8 +407,8 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
       a.K = c0.K;
       a.out = gm.c[j].out;
       a.out_kind = y_dtype;
-      if (BL_LAUNCH(bl::launch_skinny(a, stream)) != hipSuccess) return BL_ERR_HIP;
     }
+    if (BL_LAUNCH(bl::launch_skinny_pre_grouped(sk, r.n, stream)) != hipSuccess) return BL_ERR_HIP;
   }
   if (!fused.empty()) {
     std::vector<bl::SkinnyArgs> args;
@@ -545,13 +547,20 @@ int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rows
 
 int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_dtype,
                                hipStream_t stream) {
+  return bitlinear_contract_grouped_path(calls, ncalls, y_dtype, BL_PATH_MFMA, stream);
+}
+
+int bitlinear_contract_grouped_path(const bl_contract_call *calls, int ncalls, int y_dtype,
+                                    int path, hipStream_t stream) {
   if (!dtype_ok(y_dtype)) return BL_ERR_DTYPE;
+  if (path != BL_PATH_AUTO && path != BL_PATH_SKINNY && path != BL_PATH_MFMA) return BL_ERR_PATH;
   if (ncalls < 0 || ncalls > 4096) return BL_ERR_SHAPE;
   if (ncalls == 0) return BL_OK;
   if (!calls) return BL_ERR_NULL;
   for (int i = 0; i < ncalls; ++i) {
     const bl_contract_call &c = calls[i];
     if (!nk_ok(c.N, c.K) || !m_ok(c.M)) return BL_ERR_SHAPE;
+    if (path == BL_PATH_SKINNY && c.M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
     if (c.M == 0) continue;
     if (!c.xq || !c.s || !c.rowsum || !c.packed || !c.beta || !c.y) return BL_ERR_NULL;
     if (!aligned16(c.xq) || !aligned16(c.packed) || !aligned16(c.y) ||
@@ -569,15 +578,34 @@ int bitlinear_contract_grouped(const bl_contract_call *calls, int ncalls, int y_
     while (n < bl::kGroupCalls && i + n < ncalls && calls[i + n].M == c0.M &&
            calls[i + n].K == c0.K && calls[i + n].N == c0.N)
       ++n;
+    const bool skinny =
+        path == BL_PATH_SKINNY || (path == BL_PATH_AUTO && c0.M <= bl::kSkinnyMaxM);
     bl::GemmCalls gm{};
+    bl::SkinnyArgs sk[bl::kGroupCalls];
     for (int j = 0; j < n; ++j) {
       const bl_contract_call &c = calls[i + j];
       gm.c[j] = bl::GemmCall{c.xq, c.rowsum, c.s, c.packed, c.beta, c.y};
+      sk[j] = bl::SkinnyArgs{};
+      sk[j].fused = false;
+      sk[j].xq = c.xq;
+      sk[j].s = c.s;
+      sk[j].rowsum = c.rowsum;
+      sk[j].packed = c.packed;
+      sk[j].beta = c.beta;
+      sk[j].M = c.M;
+      sk[j].N = c.N;
+      sk[j].K = c.K;
+      sk[j].out = c.y;
+      sk[j].out_kind = y_dtype;
     }
-    const hipError_t e =
-        n == 1 ? BL_LAUNCH(bl::launch_gemm_mfma(c0.xq, c0.rowsum, c0.s, c0.packed, c0.beta, c0.M, c0.N,
-                                      c0.K, c0.y, y_dtype, false, stream))
-               : BL_LAUNCH(bl::launch_gemm_mfma_group(gm, n, c0.M, c0.N, c0.K, y_dtype, stream));
+    hipError_t e;
+    if (skinny)
+      e = n == 1 ? BL_LAUNCH(bl::launch_skinny(sk[0], stream))
+                 : BL_LAUNCH(bl::launch_skinny_pre_grouped(sk, n, stream));
+    else
+      e = n == 1 ? BL_LAUNCH(bl::launch_gemm_mfma(c0.xq, c0.rowsum, c0.s, c0.packed, c0.beta, c0.M,
+                                                 c0.N, c0.K, c0.y, y_dtype, false, stream))
+                 : BL_LAUNCH(bl::launch_gemm_mfma_group(gm, n, c0.M, c0.N, c0.K, y_dtype, stream));
     if (e != hipSuccess) return BL_ERR_HIP;
     i += n;
   }

@@ -482,6 +482,71 @@ hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Pre-quantized calls of one shape (HGRN's i/f/g at 9..64 tokens) as one
+// launch: the calls' 16-row blocks (or the whole calls, when the launch
+// already has a tile column per CU or M <= 16) are the sub-calls of the
+// launch, numbered call after call, each computed exactly as launch_skinny
+// computes it alone.  One launch instead of three: the 2.7B i/f/g at M = 64
+// take one launch of 960 workgroups.
+constexpr int kPreSub = kGroupCalls * 4;
+
+template <int MB, int TB, int NW>
+static void launch_pre_sub(const SkinnyLaunch<kPreSub> &R, int out_kind, unsigned grid,
+                           hipStream_t stream) {
+  launch_out<false, BL_F32, kPreSub, kRowFloat, MB, TB, NW>(R, out_kind, grid, 0, false, stream);
+}
+
+template <int MB>
+static void launch_pre_mb(const SkinnyLaunch<kPreSub> &R, int out_kind, unsigned grid, int64_t K,
+                          hipStream_t stream) {
+  if (K >= 2048 && grid < 256) {
+    if (K <= 4096) launch_pre_sub<MB, 4, 8>(R, out_kind, grid, stream);
+    else launch_pre_sub<MB, 8, 8>(R, out_kind, grid, stream);
+  } else {
+    switch (skinny_tb(K)) {
+      case 4: launch_pre_sub<MB, 4, 4>(R, out_kind, grid, stream); break;
+      case 8: launch_pre_sub<MB, 8, 4>(R, out_kind, grid, stream); break;
+      default: launch_pre_sub<MB, 16, 4>(R, out_kind, grid, stream); break;
+    }
+  }
+}
+
+hipError_t launch_skinny_pre_grouped(const SkinnyArgs *calls, int ncalls, hipStream_t stream) {
+  const SkinnyArgs &a = calls[0];
+  const int nt = (int)(a.N / 32);
+  const int nrb = (int)((a.M + 15) / 16);
+  const bool split = a.M > 16 && nt * ncalls < 256;  // as launch_skinny, over the launch
+  const size_t esz = (a.out_kind == BL_F16 || a.out_kind == BL_BF16) ? 2 : 4;
+  SkinnyLaunch<kPreSub> R;
+  int sub = 0, blocks = 0;
+  for (int j = 0; j < ncalls; ++j) {
+    const int parts = split ? nrb : 1;
+    for (int r = 0; r < parts; ++r) {
+      SkinnyCall c = to_call(calls[j]);
+      if (split) {
+        c.xq += (int64_t)16 * r * a.K;
+        c.s += 16 * r;
+        c.rowsum += 16 * r;
+        c.out = static_cast<char *>(c.out) + (size_t)16 * r * (size_t)a.N * esz;
+        c.M = (int)(a.M - 16 * r < 16 ? a.M - 16 * r : 16);
+      }
+      R.call[sub] = c;
+      R.first_block[sub] = blocks;
+      blocks += nt;
+      ++sub;
+    }
+  }
+  for (int i = sub; i <= kPreSub; ++i) R.first_block[i] = blocks;
+  R.ncalls = sub;
+  R.eps = a.eps;
+  const unsigned grid = (unsigned)blocks;
+  const int64_t M = split ? 16 : a.M;
+  if (M <= 16) launch_pre_mb<1>(R, a.out_kind, grid, a.K, stream);
+  else if (M <= 32) launch_pre_mb<2>(R, a.out_kind, grid, a.K, stream);
+  else launch_pre_mb<4>(R, a.out_kind, grid, a.K, stream);
+  return hipGetLastError();
+}
+
 // Consecutive calls of one shape that the decode kernel takes go out in
 // launches of up to kDecodeCalls; the others are gathered into launches of
 // the skinny kernel of up to kGroupMax calls.

@@ -272,6 +272,35 @@ def test_contract_grouped_validation():
     assert grp([BlContractCall(None, None, None, None, None, None, 0, 2048, 2048)] * 3) == OK
 
 
+def test_contract_grouped_path_validation():
+    """The path-taking grouped contraction: unknown paths and BL_PATH_FUSED
+    are refused, BL_PATH_SKINNY refuses any call of more than 64 rows, and
+    everything bitlinear_contract_grouped checks is still checked -- all
+    before a launch (no GPU here)."""
+    from ternary_weight_lm_amd._lib import BlContractCall
+    L = tw.lib()
+    PATH = -9
+
+    def grp(calls, path, ydt=2):
+        arr = (BlContractCall * max(1, len(calls)))(*calls)
+        return L.bitlinear_contract_grouped_path(ctypes.cast(arr, ctypes.c_void_p), len(calls),
+                                                 ydt, path, None)
+    small = BlContractCall(A, B, C, D, E, Y, 64, 2560, 2560)
+    big = BlContractCall(A, B, C, D, E, Y, 65, 2560, 2560)
+    assert grp([small], 7) == PATH
+    assert grp([small], tw.BL_PATH_FUSED) == PATH
+    assert grp([small], -1) == PATH
+    assert grp([small, big], tw.BL_PATH_SKINNY) == SHAPE
+    assert grp([small], tw.BL_PATH_SKINNY, ydt=9) == DTYPE
+    assert grp([small, BlContractCall(A, None, C, D, E, Y, 64, 2560, 2560)], tw.BL_PATH_AUTO) == NULL
+    assert grp([small, BlContractCall(A + 4, B, C, D, E, Y, 64, 2560, 2560)],
+               tw.BL_PATH_SKINNY) == ALIGN
+    assert grp([BlContractCall(None, None, None, None, None, None, 0, 2560, 2560)] * 3,
+               tw.BL_PATH_SKINNY) == OK
+    assert L.bitlinear_contract_grouped_path(None, 0, 2, tw.BL_PATH_AUTO, None) == OK
+    assert L.bitlinear_contract_grouped_path(None, 1, 2, tw.BL_PATH_AUTO, None) == NULL
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.float16)

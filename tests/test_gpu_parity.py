@@ -342,7 +342,7 @@ def test_grouped_shared_input(xdt):
                 assert torch.equal(y, ref), (M, N, K, n, shared)
 
 
-@pytest.mark.parametrize("case", ["mixed", "prefill_1p3b", "prefill_shared_x"])
+@pytest.mark.parametrize("case", ["mixed", "prefill_1p3b", "prefill_shared_x", "skinny_runs"])
 def test_grouped_ws_matches_single_calls(case):
     """bitlinear_forward_grouped_ws gives bitlinear_forward's result on every
     call, bit for bit: runs of three same-shape MFMA-path calls sharing an
@@ -352,7 +352,9 @@ def test_grouped_ws_matches_single_calls(case):
     tiles (single calls of that shape take 32-row ones) -- and, full size,
     the 1.3B i/f/g triple at prefill, also with one x shared by the triple
     (one act-quant pass per row for all three calls, which must still give
-    each call's own bits)."""
+    each call's own bits).  skinny_runs: triples that go out as one skinny
+    launch (the 2.7B i/f/g at 64 tokens, 12 sub-calls of 16 rows; 20 tokens
+    over 288 tile columns, not split; 33 tokens at K = 7040)."""
     shared = case == "prefill_shared_x"
     if case == "mixed":
         shapes = [(300, 384, 640)] * 4 + [(100, 96, 256), (20, 160, 512), (1, 64, 1024),
@@ -361,6 +363,8 @@ def test_grouped_ws_matches_single_calls(case):
             + [(1100, 1408, 1024)] * 3   # grouped GEMM in 96-row tiles
     elif case == "prefill_1p3b":
         shapes = [(4096, 2048, 2048)] * 3
+    elif case == "skinny_runs":
+        shapes = [(64, 2560, 2560)] * 3 + [(20, 3072, 1024)] * 3 + [(33, 2560, 7040)] * 3
     else:
         shapes = [(4096, 2048, 2048)] * 3 + [(3101, 384, 2944)] * 3
     say(f"grouped_ws {case}")
@@ -383,11 +387,21 @@ def test_grouped_ws_matches_single_calls(case):
         assert torch.equal(y, ref)
 
 
-def test_contract_grouped_matches_single_calls():
+@pytest.mark.parametrize("path", [tw.BL_PATH_MFMA, tw.BL_PATH_SKINNY, tw.BL_PATH_AUTO])
+def test_contract_grouped_matches_single_calls(path):
     """bitlinear_contract_grouped (runs of up to three same-shape calls per
-    MFMA launch) gives bitlinear_contract(..., BL_PATH_MFMA) bit for bit."""
-    say("contract_grouped")
-    shapes = [(300, 384, 640)] * 4 + [(40, 96, 256), (300, 384, 640), (0, 64, 256)]
+    launch) gives bitlinear_contract(..., same path) bit for bit: on the MFMA
+    kernel, and on the skinny kernel (the 2.7B i/f/g at 64 tokens as 12
+    sub-calls of 16 rows, a run of four split 3 + 1, a run over 288 tile
+    columns that is not split), and with the path chosen per run."""
+    say(f"contract_grouped path={path}")
+    if path == tw.BL_PATH_MFMA:
+        shapes = [(300, 384, 640)] * 4 + [(40, 96, 256), (300, 384, 640), (0, 64, 256)]
+    else:
+        shapes = [(64, 2560, 2560)] * 3 + [(40, 96, 256)] * 4 + [(20, 3072, 1024)] * 3 \
+            + [(0, 64, 256), (7, 160, 1280)]
+        if path == tw.BL_PATH_AUTO:
+            shapes += [(300, 384, 640)] * 3
     items, singles = [], []
     for i, (M, N, K) in enumerate(shapes):
         xq = (torch.from_numpy(_random_codes(M, K, 70 + i)) if M else
@@ -397,10 +411,10 @@ def test_contract_grouped_matches_single_calls():
         packed, beta = tw.pack(synth.make_w(970 + i, 0, 0, N, K).to(DEV))
         y = torch.full((M, N), 7.0, dtype=torch.float16, device=DEV)
         ref = torch.empty_like(y)
-        tw.bitlinear_contract(xq, sc, rs, packed, beta, N, ref, path=tw.BL_PATH_MFMA)
+        tw.bitlinear_contract(xq, sc, rs, packed, beta, N, ref, path=path)
         items.append((xq, sc, rs, packed, beta, y))
         singles.append(ref)
-    tw.bitlinear_contract_grouped(items, torch.float16)
+    tw.bitlinear_contract_grouped(items, torch.float16, path=path)
     torch.cuda.synchronize()
     for it, ref in zip(items, singles):
         assert torch.equal(it[5], ref)
