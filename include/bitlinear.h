@@ -413,6 +413,25 @@ int bitlinear_forward_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, 
  * clears it.  Process-wide; launches that are not forced are unaffected. */
 void bitlinear_test_fail_launches(int n);
 
+/* The unit that contracts the decode kernels' 1-token (split mode) and
+ * 2-token (row mode) calls -- bitlinear_forward, _forward_glu, _grouped and
+ * _grouped_ws on BL_PATH_FUSED.  The datacamp page (section "MatMul durch
+ * ternäre Operationen ersetzen") reduces the ternary product to additions
+ * and subtractions of activations.  The MFMA path multiplies 16-row blocks
+ * of which 1 or 2 rows are live; the VALU path dots each lane's unpacked
+ * codes with the activation codes (v_dot4_i32_i8).  Both compute the same
+ * exact int32 sums, so outputs are identical bit for bit; only speed
+ * differs (the VALU path measured 2-7 % slower on the 2.7B decode calls).
+ *   BL_DECODE_AUTO  the library's choice (the MFMA path)
+ *   BL_DECODE_MFMA  matrix cores
+ *   BL_DECODE_VALU  vector ALU
+ * Process-wide, read when a launch is issued (a captured graph keeps the
+ * unit it was captured with).  Returns BL_OK, or BL_ERR_PATH for an unknown
+ * unit (the setting is then unchanged). */
+enum { BL_DECODE_AUTO = 0, BL_DECODE_MFMA = 1, BL_DECODE_VALU = 2 };
+int bitlinear_set_decode_contraction(int unit);
+int bitlinear_get_decode_contraction(void);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(int status);
 

@@ -98,6 +98,8 @@ SIGNATURES = {
     "bitlinear_unpack_weights": ([P, I64, I64, P, P], I),
     "bitlinear_noalloc_max_scratch_bytes": ([], SZ),
     "bitlinear_test_fail_launches": ([I], None),
+    "bitlinear_set_decode_contraction": ([I], I),
+    "bitlinear_get_decode_contraction": ([], I),
     "bitlinear_rmsnorm_swish_gate": ([P, P, P, I, I64, I64, F, P, P], I),
     "bitlinear_forward_gated": ([P, P, P, F, I, I64, I64, P, P, P, I64, P, I, F, P, SZ, P], I),
     "bitlinear_chain_workspace_bytes": ([P, I, I64], SZ),
@@ -253,6 +255,20 @@ def bitlinear_test_fail_launches(n: int):
     """Test hook: the next n kernel launches of the library fail with
     BL_ERR_HIP without launching (0 clears)."""
     lib().bitlinear_test_fail_launches(int(n))
+
+
+BL_DECODE_AUTO, BL_DECODE_MFMA, BL_DECODE_VALU = 0, 1, 2
+
+
+def bitlinear_set_decode_contraction(unit: int):
+    """Matrix cores (BL_DECODE_MFMA) or vector ALU (BL_DECODE_VALU) for the
+    decode kernels' 1- and 2-token contractions; BL_DECODE_AUTO restores the
+    library's choice.  Outputs are identical either way."""
+    _check("bitlinear_set_decode_contraction", lib().bitlinear_set_decode_contraction(int(unit)))
+
+
+def bitlinear_get_decode_contraction() -> int:
+    return int(lib().bitlinear_get_decode_contraction())
 
 
 def bitlinear_noalloc_max_scratch_bytes() -> int:

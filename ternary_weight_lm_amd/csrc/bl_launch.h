@@ -124,6 +124,10 @@ struct DecodeArgs {
   bool glu;  // one call only: out = h [M, N/2] = silu(y_gate) * y_up
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Contraction unit of the decode kernels at 1 token (split mode) and 2
+// tokens (row mode): BL_DECODE_MFMA or BL_DECODE_VALU, from the process-wide
+// setting of bitlinear_set_decode_contraction (capi.cpp).
+bool decode_use_valu();
 // the kernels for one activation dtype (decode_f32.hip, decode_f16.hip,
 // decode_bf16.hip); launch_decode picks one
 void launch_decode_f32(const DecodeArgs &a, hipStream_t stream);

@@ -93,9 +93,36 @@ int auto_path(int64_t M, int64_t K, int x_dtype) {
 
 }  // namespace
 
+namespace {
+
+// bitlinear_set_decode_contraction's process-wide setting.  BL_DECODE_AUTO
+// takes the matrix cores: on the 2.7B decode calls the VALU contraction ran
+// 2-3 % slower at 1 token and 5-7 % at 2 (it adds 16 v_dot4 per tile to the
+// unpack both units pay, while the MFMAs overlap that VALU stream).
+std::atomic<int> g_decode_unit{BL_DECODE_AUTO};
+constexpr bool kAutoDecodeValu = false;
+
+}  // namespace
+
+namespace bl {
+bool decode_use_valu() {
+  const int u = g_decode_unit.load(std::memory_order_relaxed);
+  return u == BL_DECODE_VALU || (u == BL_DECODE_AUTO && kAutoDecodeValu);
+}
+}  // namespace bl
+
 extern "C" {
 
 void bitlinear_test_fail_launches(int n) { g_fail_launches.store(n > 0 ? n : 0); }
+
+int bitlinear_set_decode_contraction(int unit) {
+  if (unit != BL_DECODE_AUTO && unit != BL_DECODE_MFMA && unit != BL_DECODE_VALU)
+    return BL_ERR_PATH;
+  g_decode_unit.store(unit, std::memory_order_relaxed);
+  return BL_OK;
+}
+
+int bitlinear_get_decode_contraction(void) { return g_decode_unit.load(std::memory_order_relaxed); }
 
 const char *bitlinear_status_string(int status) {
   switch (status) {

@@ -37,6 +37,10 @@
 //     barrier), then the waves share the contraction.
 // Up to kDecodeCalls projections of the same shape (HGRN's i/f/g) can share
 // one launch in either mode: workgroup b works on call b / tiles.
+// At 1 token (split mode) and 2 tokens (row mode) the contraction can run on
+// the vector ALU instead (v_dot4_i32_i8 on the unpacked codes, valu_contract)
+// -- same integers, same output bits; bitlinear_set_decode_contraction
+// picks the unit.
 //
 // The templates are instantiated once per activation dtype (decode_f32.hip,
 // decode_f16.hip, decode_bf16.hip), so the three compile in parallel.
@@ -71,7 +75,55 @@ constexpr int dec_nw(int64_t K) { return K <= 1024 ? 4 : 8; }
 // the activation loads are issued: in the three-call kernel some of them are
 // not preloaded and must first be fetched from the argument buffer, and that
 // wait must not hold up the first loads.
-template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU, int KC, int NW>
+// The contraction on the vector ALU, for VR <= 2 token rows (the MFMA path
+// multiplies 16-row blocks of which VR rows are live).  Lane l holds, per
+// tile and k-step s2, the 16 codes of output rows 16 h + l % 16 at k = 32
+// (l / 16) + 16 s2 + 0..15 -- the MFMA B operand -- and dots each with the
+// same 16 activation codes of every token row (LDS, one broadcast 16-byte
+// read per row) by v_dot4_i32_i8, four int8 products per instruction, exact
+// in int32.  The four lane groups l / 16 hold disjoint k, so two cross-lane
+// additions leave lanes 0..15 with the wave's sums: out[m][h] of output row
+// 16 h + lane.  Same integers as the MFMA path, so the same output bits.
+template <int VR, int TPW, int NW>
+__device__ __forceinline__ void valu_contract(const v4i (&wt)[TPW], const int8_t *xs,
+                                              int lds_stride, int w, int nmine, int lane,
+                                              int (&out)[VR][2]) {
+  int acc[VR][2];
+#pragma unroll
+  for (int m = 0; m < VR; ++m) acc[m][0] = acc[m][1] = 0;
+  const int8_t *abase = xs + 32 * (lane >> 4);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (t >= nmine) break;
+    const v4i u = wt[t];
+    const int kofs = (w + NW * t) * 128;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const v4i c0 = unpack_codes((uint32_t)(s2 ? u.y : u.x));  // output rows 0..15
+      const v4i c1 = unpack_codes((uint32_t)(s2 ? u.w : u.z));  // output rows 16..31
+#pragma unroll
+      for (int m = 0; m < VR; ++m) {
+        const v4i a = *reinterpret_cast<const v4i *>(abase + m * lds_stride + kofs + 16 * s2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[m][0] = __builtin_amdgcn_sdot4(c0[i], a[i], acc[m][0], false);
+          acc[m][1] = __builtin_amdgcn_sdot4(c1[i], a[i], acc[m][1], false);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < VR; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int v = acc[m][h];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      out[m][h] = v;
+    }
+}
+
+template <int DT, int OUT, int MR, bool GAIN_LATE, bool GLU, int KC, int NW, bool VALU = false>
 __device__ __forceinline__ void decode_body(
     const void *x, int K, int M, int tiles, int nt, float eps, int call, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
@@ -245,6 +297,18 @@ __device__ __forceinline__ void decode_body(
 
   // ---- 5. contraction: the wave's tiles kb = w + NW t
   const int nmine = w < KB ? (KB - w + NW - 1) / NW : 0;
+  if constexpr (VALU) {
+    static_assert(MR <= 2, "the VALU contraction takes 1 or 2 rows");
+    int vs[MR][2];
+    valu_contract<MR, TPW, NW>(wt, xs, lds_stride, w, nmine, lane, vs);
+    if (lane < 16) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        red[w][m][0][lane] = vs[m][0];
+        red[w][m][1][lane] = vs[m][1];
+      }
+    }
+  } else {
   const int arow = lane & 15;
   const bool arow_ok = arow < M;
   const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
@@ -285,6 +349,7 @@ __device__ __forceinline__ void decode_body(
       red[w][m][0][lane] = acc0[0][m] + acc0[1][m];
       red[w][m][1][lane] = acc1[0][m] + acc1[1][m];
     }
+  }
   }
   __syncthreads();
   const auto tile_sum = [&](int m, int h, int l) {
@@ -330,20 +395,20 @@ __device__ __forceinline__ void decode_body(
 // One call.  Every argument fits the 14 preloaded SGPRs.
 // shape = K/128 | M << 7 | tiles << 10.  GLU: the packed rows are a
 // gate_proj in GLU order and out is h [M, tiles * 16].
-template <int DT, int OUT, int MR, bool GLU, int KC, int NW>
+template <int DT, int OUT, int MR, bool GLU, int KC, int NW, bool VALU = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(const void *x, uint32_t shape,
                                                                  float eps, const uint4 *packed,
                                                                  const void *gain,
                                                                  const float *beta, void *out) {
   const int K = (int)(shape & 127u) << 7, M = (int)(shape >> 7) & 7;
-  decode_body<DT, OUT, MR, false, GLU, KC, NW>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0,
+  decode_body<DT, OUT, MR, false, GLU, KC, NW, VALU>(x, K, M, (int)(shape >> 10), (int)blockIdx.x, eps, 0,
                                                packed, packed, packed, gain, gain, gain, beta, beta,
                                                beta, out, out, out);
 }
 
 // Up to three calls of one shape; workgroup b works on call b / tiles.  The
 // activation and weight pointers are preloaded, the rest is fetched.
-template <int DT, int OUT, int MR, int KC, int NW>
+template <int DT, int OUT, int MR, int KC, int NW, bool VALU = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
     const void *x0, const void *x1, const void *x2, uint32_t shape, float eps,
     const uint4 *p0, const uint4 *p1, const uint4 *p2, const void *g0, const void *g1,
@@ -354,7 +419,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
   const int bid = (int)blockIdx.x;
   const int call = (bid >= tiles) + (bid >= 2 * tiles);
   const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
-  decode_body<DT, OUT, MR, true, false, KC, NW>(x, K, M, tiles, bid - call * tiles, eps, call, p0,
+  decode_body<DT, OUT, MR, true, false, KC, NW, VALU>(x, K, M, tiles, bid - call * tiles, eps, call, p0,
                                                 p1, p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
 }
 
@@ -368,7 +433,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
 // of its row.
 // GAIN_LATE (three-call kernel): the gain pointer comes from the argument
 // buffer, so the weights are issued before waiting for it.
-template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool GAIN_LATE>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool GAIN_LATE, bool VALU = false>
 __device__ __forceinline__ void decode_rows_body(
     const void *x, uint32_t shape, float eps, int nt, int call, const uint4 *p0, const uint4 *p1,
     const uint4 *p2, const void *g0, const void *g1, const void *g2, const float *b0,
@@ -444,7 +509,20 @@ __device__ __forceinline__ void decode_rows_body(
   __syncthreads();
 
   // ---- 3. contraction: tiles kb = w + NW t, rows 0..15 as one MFMA block
+  // (VALU: the 2 rows of a 2-token call on the vector ALU)
   const int nmine = w < KB ? (KB - w + NW - 1) / NW : 0;
+  if constexpr (VALU) {
+    int vs[2][2];
+    valu_contract<2, TPW, NW>(wt, xs, lds_stride, w, nmine, lane, vs);
+    // red[w][4 h + i][L] holds row 4 (L / 16) + i: rows 0, 1 at L = 0..15
+    if (lane < 16) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        red[w][m][lane] = vs[m][0];
+        red[w][4 + m][lane] = vs[m][1];
+      }
+    }
+  } else {
   const int arow = lane & 15;
   const int8_t *abase = xs + arow * lds_stride + 32 * (lane >> 4);
   v4i acc0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, acc1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -480,6 +558,7 @@ __device__ __forceinline__ void decode_rows_body(
     red[w][i][lane] = acc0[0][i] + acc0[1][i];
     red[w][4 + i][lane] = acc1[0][i] + acc1[1][i];
   }
+  }
   __syncthreads();
   const auto wsum = [&](int j, int L) {
     int v = red[0][j][L];
@@ -511,13 +590,13 @@ __device__ __forceinline__ void decode_rows_body(
   }
 }
 
-template <int DT, int OUT, bool GLU, int KC, int NW, int RPW>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool VALU = false>
 __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows_kernel(const void *x, uint32_t shape,
                                                                       float eps,
                                                                       const uint4 *packed,
                                                                       const void *gain,
                                                                       const float *bp, void *out) {
-  decode_rows_body<DT, OUT, GLU, KC, NW, RPW, false>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
+  decode_rows_body<DT, OUT, GLU, KC, NW, RPW, false, VALU>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
                                                 packed, gain, gain, gain, bp, bp, bp, out, out,
                                                 out);
 }
@@ -525,7 +604,7 @@ __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows_ker
 // Up to three row-mode calls of one shape; workgroup b works on call
 // b / tiles.  The activation and weight pointers are preloaded, the rest is
 // fetched.
-template <int DT, int OUT, int KC, int NW, int RPW>
+template <int DT, int OUT, int KC, int NW, int RPW, bool VALU = false>
 __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows3_kernel(
     const void *x0, const void *x1, const void *x2, uint32_t shape, float eps, const uint4 *p0,
     const uint4 *p1, const uint4 *p2, const void *g0, const void *g1, const void *g2,
@@ -534,7 +613,7 @@ __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows3_ke
   const int bid = (int)blockIdx.x;
   const int call = (bid >= tiles) + (bid >= 2 * tiles);
   const void *x = call == 0 ? x0 : (call == 1 ? x1 : x2);
-  decode_rows_body<DT, OUT, false, KC, NW, RPW, true>(x, shape, eps, bid - call * tiles, call, p0, p1,
+  decode_rows_body<DT, OUT, false, KC, NW, RPW, true, VALU>(x, shape, eps, bid - call * tiles, call, p0, p1,
                                                  p2, g0, g1, g2, b0, b1, b2, o0, o1, o2);
 }
 
@@ -543,7 +622,7 @@ __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows3_ke
 // 16 from 13 rows.
 constexpr int kRowsNW = 8;
 
-template <int DT, int OUT, bool GLU, int KC, int NW, int RPW>
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool VALU = false>
 static void launch_rows_rpw(const DecodeArgs &a, hipStream_t stream) {
   const unsigned tiles = (unsigned)(a.N / 32);
   const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
@@ -553,12 +632,12 @@ static void launch_rows_rpw(const DecodeArgs &a, hipStream_t stream) {
     const uint4 *p[3];
     for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
     const unsigned grid = tiles * (unsigned)a.ncalls;
-    decode_rows3_kernel<DT, OUT, KC, NW, RPW><<<grid, 64 * NW, lds, stream>>>(
+    decode_rows3_kernel<DT, OUT, KC, NW, RPW, VALU><<<grid, 64 * NW, lds, stream>>>(
         a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1], a.gain[2],
         a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2]);
     return;
   }
-  decode_rows_kernel<DT, OUT, GLU, KC, NW, RPW><<<tiles, 64 * NW, lds, stream>>>(
+  decode_rows_kernel<DT, OUT, GLU, KC, NW, RPW, VALU><<<tiles, 64 * NW, lds, stream>>>(
       a.x[0], shape, a.eps, pk, a.gain[0], a.beta[0], a.out[0]);
 }
 
@@ -570,7 +649,8 @@ static void launch_rows_t(const DecodeArgs &a, hipStream_t stream) {
   // at 9 rows the wider workgroup was 5 % slower).  fp32 rows past K = 2048
   // do not fit 16 waves' registers; decode_rows_fits never sends them more
   // than 8 rows, and the 8-wave kernel stands in for that instance.
-  if (a.M <= kRowsNW) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 1>(a, stream);
+  if (a.M == 2 && decode_use_valu()) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 1, true>(a, stream);
+  else if (a.M <= kRowsNW) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 1>(a, stream);
   else if (a.M <= 12) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 2>(a, stream);
   else if constexpr (DT == BL_F32 && KC > 2) launch_rows_rpw<DT, OUT, GLU, KC, kRowsNW, 2>(a, stream);
   else launch_rows_rpw<DT, OUT, GLU, KC, 2 * kRowsNW, 1>(a, stream);
@@ -598,23 +678,28 @@ static void launch_mr_t(const DecodeArgs &a, hipStream_t stream) {
   for (int i = 0; i < 3; ++i) p[i] = reinterpret_cast<const uint4 *>(a.packed[i]);
   // fp32 activations decode one row per launch (decode_fits)
   constexpr int MR4 = DT == BL_F32 ? 1 : (int)kDecodeMaxM;
+  const bool valu = a.M == 1 && decode_use_valu();
   if (a.ncalls == 1) {
-#define BL_DECODE1(MR_, G)                                                                  \
-  decode_kernel<DT, OUT, MR_, G, KC, NW><<<grid, 64 * NW, lds, stream>>>(                    \
+#define BL_DECODE1(MR_, G, V)                                                               \
+  decode_kernel<DT, OUT, MR_, G, KC, NW, V><<<grid, 64 * NW, lds, stream>>>(                 \
       a.x[0], shape, a.eps, p[0], a.gain[0], a.beta[0], a.out[0])
-    if (a.M == 1) {
-      if (a.glu) BL_DECODE1(1, true); else BL_DECODE1(1, false);
+    if (valu) {
+      if (a.glu) BL_DECODE1(1, true, true); else BL_DECODE1(1, false, true);
+    } else if (a.M == 1) {
+      if (a.glu) BL_DECODE1(1, true, false); else BL_DECODE1(1, false, false);
     } else {
-      if (a.glu) BL_DECODE1(MR4, true); else BL_DECODE1(MR4, false);
+      if (a.glu) BL_DECODE1(MR4, true, false); else BL_DECODE1(MR4, false, false);
     }
 #undef BL_DECODE1
     return;
   }
-#define BL_DECODE3(MR_)                                                                     \
-  decode3_kernel<DT, OUT, MR_, KC, NW><<<grid, 64 * NW, lds, stream>>>(                      \
+#define BL_DECODE3(MR_, V)                                                                  \
+  decode3_kernel<DT, OUT, MR_, KC, NW, V><<<grid, 64 * NW, lds, stream>>>(                   \
       a.x[0], a.x[1], a.x[2], shape, a.eps, p[0], p[1], p[2], a.gain[0], a.gain[1],          \
       a.gain[2], a.beta[0], a.beta[1], a.beta[2], a.out[0], a.out[1], a.out[2])
-  if (a.M == 1) BL_DECODE3(1); else BL_DECODE3(MR4);
+  if (valu) BL_DECODE3(1, true);
+  else if (a.M == 1) BL_DECODE3(1, false);
+  else BL_DECODE3(MR4, false);
 #undef BL_DECODE3
 }
 

@@ -486,6 +486,22 @@ def test_chain_plan_validation():
     assert L.bitlinear_status_string(-11).decode().startswith("a chained launch")
 
 
+def test_decode_contraction_setting():
+    """bitlinear_set_decode_contraction accepts the three units, refuses any
+    other value with BL_ERR_PATH and leaves the setting unchanged then."""
+    L = tw.lib()
+    try:
+        for u in (tw.BL_DECODE_VALU, tw.BL_DECODE_MFMA, tw.BL_DECODE_AUTO):
+            assert L.bitlinear_set_decode_contraction(u) == OK
+            assert L.bitlinear_get_decode_contraction() == u
+        assert L.bitlinear_set_decode_contraction(tw.BL_DECODE_VALU) == OK
+        for bad in (-1, 3, 99):
+            assert L.bitlinear_set_decode_contraction(bad) == -9
+            assert L.bitlinear_get_decode_contraction() == tw.BL_DECODE_VALU
+    finally:
+        L.bitlinear_set_decode_contraction(tw.BL_DECODE_AUTO)
+
+
 def test_forced_launch_failure_reaches_the_caller():
     """The launch-failure hook: a valid call whose launch is forced to fail
     returns BL_ERR_HIP from every kind of entry point (no GPU involved: the
