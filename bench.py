@@ -68,11 +68,11 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c5-M1": ("decode", "aab3e6752836bbc9", 5247143),
-    "c5-M8": ("decode", "aab3e6752836bbc9", 5795187),
-    "c5-M64": ("skinny", "1c40f81eaaa887df", 5572923),
-    "c5-M512": ("gemm", "53b5e7bfa9ea7e07", 23237509),
-    "c5-M8192": ("gemm", "53b5e7bfa9ea7e07", 222642006),
+    "c5-M1": ("decode", "72b9082c5f954c25", 5255272),
+    "c5-M8": ("decode", "72b9082c5f954c25", 5795828),
+    "c5-M64": ("skinny", "dd142e5815c10966", 8318092),
+    "c5-M512": ("gemm", "1602ce43042cddbb", 23230424),
+    "c5-M8192": ("gemm", "1602ce43042cddbb", 225956157),
 }
 
 
