@@ -73,6 +73,9 @@ TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c5-M64": ("skinny", "dd142e5815c10966", 8318092),
     "c5-M512": ("gemm", "1602ce43042cddbb", 23230424),
     "c5-M8192": ("gemm", "1602ce43042cddbb", 225956157),
+    "c2": ("decode", "72b9082c5f954c25", 639930),
+    "c3": ("skinny", "dd142e5815c10966", 4661966),
+    "c4": ("gemm", "1602ce43042cddbb", 87419221),
 }
 
 
