@@ -72,6 +72,11 @@ CASES = [
     (tw.BL_PATH_MFMA, 17, 80, 1280, "bf16", "bf16"),
     (tw.BL_PATH_MFMA, 130, 176, 1024, "fp16", "fp16"),
     (tw.BL_PATH_MFMA, 257, 48, 2048, "bf16", "fp32"),
+    # K split over wave groups inside the workgroup: the 2.7B gate_proj at
+    # 128 tokens (440 tiles of 32 rows, 2 groups of 10 k-blocks) and 4
+    # groups over 17 k-blocks (5/5/5/2)
+    (tw.BL_PATH_MFMA, 128, 7040, 2560, "bf16", "bf16"),
+    (tw.BL_PATH_MFMA, 40, 2048, 2176, "fp16", "fp16"),
     (tw.BL_PATH_FUSED, 9, 80, 1024, "bf16", "bf16"),   # row mode, two rows per wave
     (tw.BL_PATH_FUSED, 16, 48, 2048, "fp32", "fp32"),
     (tw.BL_PATH_FUSED, 13, 80, 2560, "bf16", "fp16"),
