@@ -648,13 +648,17 @@ def run_gate(args):
         ach = byt * launches / sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 5)}
+    one_launch = M <= 8   # the decode kernel's gated row mode (16-bit activations)
     roof.update({"traffic": None,
-                 "kernel": "gated act-quant (gate + norm + quant) + "
-                           + ("bl::gemm_mfma_kernel" if path_mfma else "bl::skinny_kernel<pre-quantized>"),
+                 "kernel": ("bl::decode_rows_gated_kernel (gate + norm + quant + contract + rescale "
+                            "in one launch)" if one_launch else
+                            "gated act-quant (gate + norm + quant) + "
+                            + ("bl::gemm_mfma_kernel" if path_mfma else "bl::skinny_kernel<pre-quantized>")),
                  "launches": launches, "avg_call_us": round(sec * 1e6 / launches, 3),
                  "algorithmic_bytes_per_call": byt, "ops_per_call": ops,
-                 "timed_region": "the benchmark steps (each call: the gated act-quant launch and the "
-                                 "contraction launch)"})
+                 "timed_region": "the benchmark steps (each call: " +
+                                 ("one launch)" if one_launch else
+                                  "the gated act-quant launch and the contraction launch)")})
     out = {
         "metric": METRIC, "value": round(M * steps / sec, 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
@@ -665,7 +669,8 @@ def run_gate(args):
                    "projections": [f"FusedRMSNormSwishGate({K}) -> o_proj {K}->{N} (fused prologue)"],
                    "x_dtype": cfg.dtype, "y_dtype": cfg.dtype, "gate_eps": GATE_EPS,
                    "weight_pool_MiB": round(set_bytes * copies / 2**20, 1),
-                   "launch": "hipGraph; per layer bitlinear_forward_gated", "parallelism": "single GPU"},
+                   "launch": "hipGraph; per layer bitlinear_forward_gated (one launch up to 8 tokens)",
+                   "parallelism": "single GPU"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -294,10 +294,13 @@ int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, in
 
 /* o_proj with the gate as its prologue: y = FusedBitLinear(z) for the z of
  * bitlinear_rmsnorm_swish_gate(o, g, gate_w, gate_eps), without z going
- * through memory: the act-quant launch computes z in registers and
- * quantizes it (codes, scales and row sums identical to running the gate
- * and then bitlinear_forward on the stored z), then the contraction runs on
- * the skinny path (M <= 64) or the MFMA path.  gain, packed, beta, N, y,
+ * through memory.  1..8 tokens of 16-bit activations (M (K + 16) <= 45056):
+ * one launch of the decode kernel's row mode, each wave gating, normalizing
+ * and quantizing its row in registers before the contraction; otherwise the
+ * act-quant launch computes z in registers and quantizes it, then the
+ * contraction runs on the skinny path (M <= 64) or the MFMA path.  Either
+ * way the codes, scales, row sums and y are identical to running the gate
+ * and then bitlinear_forward on the stored z.  gain, packed, beta, N, y,
  * y_dtype, eps, ws and ws_bytes as for bitlinear_forward (workspace
  * bitlinear_workspace_bytes(M, K, N)); x_dtype is the dtype of o, g, gate_w
  * and gain; K <= 4096. */

@@ -193,6 +193,28 @@ struct GateArgs {
 constexpr int64_t kGateMaxK = 4096;
 hipError_t launch_gate(const GateArgs &a, hipStream_t stream);
 
+// o_proj behind FusedRMSNormSwishGate in one launch of the decode kernel's
+// row mode: 1..8 rows of 16-bit activations, K <= 4096, the codes within the
+// row mode's LDS budget.
+struct DecodeGateArgs {
+  const void *o, *g, *gate_w;
+  float gate_eps;
+  int x_dtype;
+  int64_t M, N, K;
+  const void *gain;
+  float eps;
+  const void *packed;
+  const float *beta;
+  void *out;
+  int out_kind;
+};
+inline bool decode_gated_fits(int64_t M, int64_t K, int x_dtype) {
+  return x_dtype != BL_F32 && M >= 1 && M <= 8 && K <= kGateMaxK && M * (K + 16) <= kDecodeRowsLds;
+}
+hipError_t launch_decode_gated(const DecodeGateArgs &a, hipStream_t stream);
+void launch_decode_gated_f16(const DecodeGateArgs &a, hipStream_t stream);
+void launch_decode_gated_bf16(const DecodeGateArgs &a, hipStream_t stream);
+
 // Largest M and K the fused skinny kernel accepts.
 constexpr int64_t kFusedMaxM = 16;
 constexpr int64_t kFusedMaxK = 8192;

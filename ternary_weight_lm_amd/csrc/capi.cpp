@@ -836,6 +836,25 @@ int bitlinear_forward_gated(const void *o, const void *g, const void *gate_w, fl
       !aligned16(packed) || !aligned16(y) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u))
     return BL_ERR_ALIGN;
+  if (bl::decode_gated_fits(M, K, x_dtype)) {
+    // one launch: the decode kernel's row mode with the gate in front
+    bl::DecodeGateArgs d{};
+    d.o = o;
+    d.g = g;
+    d.gate_w = gate_w;
+    d.gate_eps = gate_eps;
+    d.x_dtype = x_dtype;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    d.gain = gain;
+    d.eps = eps;
+    d.packed = packed;
+    d.beta = beta;
+    d.out = y;
+    d.out_kind = y_dtype;
+    return hip_status(BL_LAUNCH(bl::launch_decode_gated(d, stream)));
+  }
   const FwdWs w = carve(ws, M, K);
   bl::GateArgs a{};
   a.o = o;

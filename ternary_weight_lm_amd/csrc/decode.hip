@@ -13,4 +13,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// 16-bit activations only (decode_gated_fits)
+hipError_t launch_decode_gated(const DecodeGateArgs &a, hipStream_t stream) {
+  if (a.x_dtype == BL_F16) launch_decode_gated_f16(a, stream);
+  else launch_decode_gated_bf16(a, stream);
+  return hipGetLastError();
+}
+
 }  // namespace bl

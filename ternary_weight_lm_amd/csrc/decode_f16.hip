@@ -4,5 +4,8 @@
 namespace bl {
 
 void launch_decode_f16(const DecodeArgs &a, hipStream_t stream) { launch_decode_dt<BL_F16>(a, stream); }
+void launch_decode_gated_f16(const DecodeGateArgs &a, hipStream_t stream) {
+  launch_decode_gated_dt<BL_F16>(a, stream);
+}
 
 }  // namespace bl

@@ -433,11 +433,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode3_kernel(
 // of its row.
 // GAIN_LATE (three-call kernel): the gain pointer comes from the argument
 // buffer, so the weights are issued before waiting for it.
-template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool GAIN_LATE, bool VALU = false>
+// GATE (one call): x is the token mixer's output o, and each row is first
+// put through FusedRMSNormSwishGate with the gate input gin, the gate's gain
+// gw and epsilon gate_eps (gate_row, as the gated act-quant kernel does).
+template <int DT, int OUT, bool GLU, int KC, int NW, int RPW, bool GAIN_LATE, bool VALU = false,
+          bool GATE = false>
 __device__ __forceinline__ void decode_rows_body(
     const void *x, uint32_t shape, float eps, int nt, int call, const uint4 *p0, const uint4 *p1,
     const uint4 *p2, const void *g0, const void *g1, const void *g2, const float *b0,
-    const float *b1, const float *b2, void *o0, void *o1, void *o2) {
+    const float *b1, const float *b2, void *o0, void *o1, void *o2,
+    const void *gin = nullptr, const void *gw = nullptr, float gate_eps = 0.0f) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K + 16] int8 codes
   __shared__ int red[NW][8][64];
   __shared__ float f_row[16];
@@ -464,6 +469,23 @@ __device__ __forceinline__ void decode_rows_body(
       const int k = 8 * lane + 512 * c;
       xraw[j][c] = bload_chunk<DT>(xr, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
     }
+  }
+  // GATE: the rows' gate inputs and the gate's gain, right behind o
+  Chunk8<DT> gate_in[GATE ? RPW : 1][GATE ? RC : 1], gate_w[GATE ? RC : 1];
+  if constexpr (GATE) {
+    const rsrc_t gir = make_rsrc(gin, (uint32_t)(M * K * EB));
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int m = w + NW * j;
+#pragma unroll
+      for (int c = 0; c < RC; ++c) {
+        const int k = 8 * lane + 512 * c;
+        gate_in[j][c] = bload_chunk<DT>(gir, m < M && k < K ? (uint32_t)((m * K + k) * EB) : kOob);
+      }
+    }
+    const rsrc_t gwr = make_rsrc(gw, (uint32_t)(K * EB));
+#pragma unroll
+    for (int c = 0; c < RC; ++c) gate_w[c] = bload_chunk<DT>(gwr, (uint32_t)((8 * lane + 512 * c) * EB));
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint4 *packed = call == 0 ? p0 : (call == 1 ? p1 : p2);
@@ -498,9 +520,14 @@ __device__ __forceinline__ void decode_rows_body(
     int8_t *dst = xs + m * lds_stride;
     float sc;
     int rs;
-    quantize_loaded<DT, RC>(xraw[j], graw, K, eps,
-                            [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; },
-                            sc, rs);
+    const auto sink = [&](int k, uint2 codes) { *reinterpret_cast<uint2 *>(dst + k) = codes; };
+    if constexpr (GATE) {
+      Chunk8<DT> z[RC];
+      gate_row<DT, RC>(xraw[j], gate_in[j], gate_w, K, gate_eps, z);
+      quantize_loaded<DT, RC>(z, graw, K, eps, sink, sc, rs);
+    } else {
+      quantize_loaded<DT, RC>(xraw[j], graw, K, eps, sink, sc, rs);
+    }
     if (lane == 0) {
       f_row[m] = div_rn(beta, sc);
       rs_row[m] = rs;
@@ -599,6 +626,18 @@ __global__ __launch_bounds__(64 * NW, NW <= 8 ? 8 / NW : 4) void decode_rows_ker
   decode_rows_body<DT, OUT, GLU, KC, NW, RPW, false, VALU>(x, shape, eps, (int)blockIdx.x, 0, packed, packed,
                                                 packed, gain, gain, gain, bp, bp, bp, out, out,
                                                 out);
+}
+
+// One gated call (o_proj behind FusedRMSNormSwishGate) in row mode, 1..8
+// rows: the gate, o_proj's norm, quantization, contraction and rescale in
+// one launch.
+template <int DT, int OUT, int KC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_rows_gated_kernel(
+    const void *o, const void *gin, const void *gw, float gate_eps, uint32_t shape, float eps,
+    const uint4 *packed, const void *gain, const float *bp, void *out) {
+  decode_rows_body<DT, OUT, false, KC, NW, 1, false, false, true>(
+      o, shape, eps, (int)blockIdx.x, 0, packed, packed, packed, gain, gain, gain, bp, bp, bp,
+      out, out, out, gin, gw, gate_eps);
 }
 
 // Up to three row-mode calls of one shape; workgroup b works on call
@@ -713,6 +752,36 @@ static void launch_mr(const DecodeArgs &a, hipStream_t stream) {
     case 4: launch_mr_t<DT, OUT, 4>(a, stream); break;
     case 6: launch_mr_t<DT, OUT, 6>(a, stream); break;
     default: launch_mr_t<DT, OUT, 8>(a, stream); break;
+  }
+}
+
+// The gated row mode (decode_gated_fits): 8 waves, one row per wave.
+template <int DT, int OUT, int KC>
+static void launch_rows_gated_t(const DecodeGateArgs &a, hipStream_t stream) {
+  const unsigned tiles = (unsigned)(a.N / 32);
+  const size_t lds = (size_t)a.M * (size_t)(a.K + 16);
+  const uint32_t shape = (uint32_t)(a.K >> 7) | ((uint32_t)a.M << 7) | (tiles << 12);
+  decode_rows_gated_kernel<DT, OUT, KC, kRowsNW><<<tiles, 64 * kRowsNW, lds, stream>>>(
+      a.o, a.g, a.gate_w, a.gate_eps, shape, a.eps, reinterpret_cast<const uint4 *>(a.packed),
+      a.gain, a.beta, a.out);
+}
+
+template <int DT, int OUT>
+static void launch_rows_gated(const DecodeGateArgs &a, hipStream_t stream) {
+  switch (dec_kc(a.K)) {
+    case 1: launch_rows_gated_t<DT, OUT, 1>(a, stream); break;
+    case 2: launch_rows_gated_t<DT, OUT, 2>(a, stream); break;
+    case 3: launch_rows_gated_t<DT, OUT, 3>(a, stream); break;
+    default: launch_rows_gated_t<DT, OUT, 4>(a, stream); break;
+  }
+}
+
+template <int DT>
+static void launch_decode_gated_dt(const DecodeGateArgs &a, hipStream_t stream) {
+  switch (a.out_kind) {
+    case BL_F32: launch_rows_gated<DT, BL_F32>(a, stream); break;
+    case BL_F16: launch_rows_gated<DT, BL_F16>(a, stream); break;
+    default: launch_rows_gated<DT, BL_BF16>(a, stream); break;
   }
 }
 

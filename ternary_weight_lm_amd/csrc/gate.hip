@@ -29,35 +29,6 @@ namespace {
 
 constexpr int kGateWaves = 4;  // rows (waves) per workgroup
 
-// z chunks of one row from the loaded o, g and gate-gain chunks.
-template <int DT, int NC>
-__device__ __forceinline__ void gate_row(const Chunk8<DT> (&o)[NC], const Chunk8<DT> (&g)[NC],
-                                         const Chunk8<DT> (&w)[NC], int K, float eps,
-                                         Chunk8<DT> (&z)[NC]) {
-  const float r = row_rms<DT, NC>(o, K, eps);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float fo[8], fg[8], fw[8], v[8];
-    widen<DT>(o[c], fo);
-    widen<DT>(g[c], fg);
-    widen<DT>(w[c], fw);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = ((fo[e] * r) * fw[e]) * silu(fg[e]);
-    if constexpr (DT == BL_F32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[c].u[0][i] = __float_as_int(v[i]);
-        z[c].u[1][i] = __float_as_int(v[4 + i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        z[c].u[0][i] = (int)((uint32_t)out_bits<DT>(v[2 * i]) |
-                             ((uint32_t)out_bits<DT>(v[2 * i + 1]) << 16));
-    }
-  }
-}
-
 template <int DT, int NC>
 __device__ __forceinline__ void load_rows(const void *o, const void *g, const void *w, int m,
                                           int K, Chunk8<DT> (&oc)[NC], Chunk8<DT> (&gc)[NC],

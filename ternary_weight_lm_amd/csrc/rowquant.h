@@ -84,6 +84,40 @@ __device__ __forceinline__ float row_rms(const Chunk8<DT> (&xraw)[NC], int K, fl
   return rms_inv(group_sum(ss), K, eps);
 }
 
+// FusedRMSNormSwishGate of one row held in registers (chunk c of the lane:
+// elements 8 lane + 512 c .. +7): z = ((o r) w) silu(g), r = 1 / sqrt(fp32(sum
+// o^2 / K) + eps) in the library's association, every product in fp32, z
+// rounded to the activation dtype -- the value a gate layer hands on.  Used by
+// the gate kernels and by the decode kernel's gated row mode, so the two give
+// the same bits.
+template <int DT, int NC>
+__device__ __forceinline__ void gate_row(const Chunk8<DT> (&o)[NC], const Chunk8<DT> (&g)[NC],
+                                         const Chunk8<DT> (&w)[NC], int K, float eps,
+                                         Chunk8<DT> (&z)[NC]) {
+  const float r = row_rms<DT, NC>(o, K, eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float fo[8], fg[8], fw[8], v[8];
+    widen<DT>(o[c], fo);
+    widen<DT>(g[c], fg);
+    widen<DT>(w[c], fw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ((fo[e] * r) * fw[e]) * silu(fg[e]);
+    if constexpr (DT == BL_F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[c].u[0][i] = __float_as_int(v[i]);
+        z[c].u[1][i] = __float_as_int(v[4 + i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        z[c].u[0][i] = (int)((uint32_t)out_bits<DT>(v[2 * i]) |
+                             ((uint32_t)out_bits<DT>(v[2 * i + 1]) << 16));
+    }
+  }
+}
+
 // Passes 2 and 3 of the float mode for one gain (its matching chunks in
 // graw[c]) and the row's r: xn = (x r) g, s = 127 / max(max |xn|, 1e-5),
 // codes.  `sink(k, codes)` receives the 8 codes of elements k..k+7 as two

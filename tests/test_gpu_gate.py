@@ -51,9 +51,14 @@ def test_gate_matches_oracle(dt, M, K):
         assert np.all(y_to_np(z.t)[1:3] == 0.0)
 
 
+# 1..8 rows of 16-bit activations take one launch (the decode kernel's row
+# mode with the gate in front; every K capacity 1024 KC, KC = 1..4, 1 and 8
+# rows); more rows or fp32 the gated act-quant launch and the contraction.
 @pytest.mark.parametrize("M,K,N,dt", [(1, 2560, 2560, "bf16"), (4, 1024, 1024, "fp16"),
+                                      (8, 4096, 512, "bf16"), (3, 2048, 160, "fp16"),
+                                      (5, 128, 96, "bf16"), (8, 2560, 2560, "fp16"),
                                       (40, 2048, 512, "bf16"), (300, 2560, 2560, "bf16"),
-                                      (130, 1024, 160, "fp32")])
+                                      (130, 1024, 160, "fp32"), (2, 1024, 1024, "fp32")])
 def test_gated_forward(M, K, N, dt):
     """o_proj with the gate as its prologue: bit-identical to gate then
     bitlinear_forward, and y within tolerance of the oracle on the GPU's z."""
