@@ -75,6 +75,27 @@ FwdWs carve(void *ws, int64_t M, int64_t K) {
   return w;
 }
 
+// The contraction half of the two-kernel path on the skinny kernel: a call
+// from pre-quantized activations (xq, s, rowsum as the act-quant writes them).
+bl::SkinnyArgs pre_call(const int8_t *xq, const float *s, const int32_t *rowsum,
+                        const void *packed, const float *beta, int64_t M, int64_t N, int64_t K,
+                        void *out, int out_kind, bool glu = false) {
+  bl::SkinnyArgs a{};
+  a.fused = false;
+  a.xq = xq;
+  a.s = s;
+  a.rowsum = rowsum;
+  a.packed = packed;
+  a.beta = beta;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.out = out;
+  a.out_kind = out_kind;
+  a.glu = glu;
+  return a;
+}
+
 bool fused_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= bl::kFusedMaxM && K <= bl::kFusedMaxK && M * (K + 16) <= kFusedLdsBytes;
 }
@@ -230,22 +251,9 @@ int forward_impl(const void *x, int x_dtype, int64_t M, int64_t K, const void *g
   const FwdWs w = carve(ws, M, K);
   hipError_t e = BL_LAUNCH(bl::launch_act_quant(x, x_dtype, gain, M, K, eps, w.xq, w.s, w.rowsum, stream));
   if (e != hipSuccess) return BL_ERR_HIP;
-  if (path == BL_PATH_SKINNY) {
-    bl::SkinnyArgs a{};
-    a.fused = false;
-    a.xq = w.xq;
-    a.s = w.s;
-    a.rowsum = w.rowsum;
-    a.packed = packed;
-    a.beta = beta;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.out = y;
-    a.out_kind = y_dtype;
-    a.glu = glu;
-    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
-  }
+  if (path == BL_PATH_SKINNY)
+    return hip_status(BL_LAUNCH(bl::launch_skinny(
+        pre_call(w.xq, w.s, w.rowsum, packed, beta, M, N, K, y, y_dtype, glu), stream)));
   return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
                                          y_dtype, glu, stream)));
 }
@@ -420,21 +428,9 @@ int bitlinear_forward_grouped_ws(const bl_call *calls, int ncalls, int x_dtype, 
       continue;
     }
     bl::SkinnyArgs sk[bl::kGroupCalls];
-    for (int j = 0; j < r.n; ++j) {
-      bl::SkinnyArgs &a = sk[j];
-      a = bl::SkinnyArgs{};
-      a.fused = false;
-      a.xq = gm.c[j].xq;
-      a.s = gm.c[j].s;
-      a.rowsum = gm.c[j].rowsum;
-      a.packed = gm.c[j].packed;
-      a.beta = gm.c[j].beta;
-      a.M = c0.M;
-      a.N = c0.N;
-      a.K = c0.K;
-      a.out = gm.c[j].out;
-      a.out_kind = y_dtype;
-    }
+    for (int j = 0; j < r.n; ++j)
+      sk[j] = pre_call(gm.c[j].xq, gm.c[j].s, gm.c[j].rowsum, gm.c[j].packed, gm.c[j].beta, c0.M,
+                       c0.N, c0.K, gm.c[j].out, y_dtype);
     if (BL_LAUNCH(bl::launch_skinny_pre_grouped(sk, r.n, stream)) != hipSuccess) return BL_ERR_HIP;
   }
   if (!fused.empty()) {
@@ -487,19 +483,9 @@ int bitlinear_gemm_i32(const int8_t *xq, const int32_t *rowsum, int64_t M,
     return BL_ERR_ALIGN;
   if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
   if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
-  if (path == BL_PATH_SKINNY) {
-    bl::SkinnyArgs a{};
-    a.fused = false;
-    a.xq = xq;
-    a.rowsum = rowsum;
-    a.packed = packed;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.out = acc;
-    a.out_kind = bl::kOutI32;
-    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
-  }
+  if (path == BL_PATH_SKINNY)
+    return hip_status(BL_LAUNCH(bl::launch_skinny(
+        pre_call(xq, nullptr, rowsum, packed, nullptr, M, N, K, acc, bl::kOutI32), stream)));
   return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, nullptr, packed, nullptr, M, N, K, acc,
                                          bl::kOutI32, false, stream)));
 }
@@ -519,21 +505,9 @@ int bitlinear_contract(const int8_t *xq, const float *s, const int32_t *rowsum,
     return BL_ERR_ALIGN;
   if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
   if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
-  if (path == BL_PATH_SKINNY) {
-    bl::SkinnyArgs a{};
-    a.fused = false;
-    a.xq = xq;
-    a.s = s;
-    a.rowsum = rowsum;
-    a.packed = packed;
-    a.beta = beta;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.out = y;
-    a.out_kind = y_dtype;
-    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
-  }
+  if (path == BL_PATH_SKINNY)
+    return hip_status(BL_LAUNCH(bl::launch_skinny(
+        pre_call(xq, s, rowsum, packed, beta, M, N, K, y, y_dtype), stream)));
   return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, N, K, y, y_dtype, false,
                                          stream)));
 }
@@ -552,22 +526,9 @@ int bitlinear_contract_glu(const int8_t *xq, const float *s, const int32_t *rows
     return BL_ERR_ALIGN;
   if (path == BL_PATH_AUTO) path = M <= bl::kSkinnyMaxM ? BL_PATH_SKINNY : BL_PATH_MFMA;
   if (path == BL_PATH_SKINNY && M > bl::kSkinnyMaxM) return BL_ERR_SHAPE;
-  if (path == BL_PATH_SKINNY) {
-    bl::SkinnyArgs a{};
-    a.fused = false;
-    a.xq = xq;
-    a.s = s;
-    a.rowsum = rowsum;
-    a.packed = packed;
-    a.beta = beta;
-    a.M = M;
-    a.N = 2 * F;
-    a.K = K;
-    a.out = h;
-    a.out_kind = h_dtype;
-    a.glu = true;
-    return hip_status(BL_LAUNCH(bl::launch_skinny(a, stream)));
-  }
+  if (path == BL_PATH_SKINNY)
+    return hip_status(BL_LAUNCH(bl::launch_skinny(
+        pre_call(xq, s, rowsum, packed, beta, M, 2 * F, K, h, h_dtype, true), stream)));
   return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(xq, rowsum, s, packed, beta, M, 2 * F, K, h, h_dtype,
                                          true, stream)));
 }
@@ -612,18 +573,7 @@ int bitlinear_contract_grouped_path(const bl_contract_call *calls, int ncalls, i
     for (int j = 0; j < n; ++j) {
       const bl_contract_call &c = calls[i + j];
       gm.c[j] = bl::GemmCall{c.xq, c.rowsum, c.s, c.packed, c.beta, c.y};
-      sk[j] = bl::SkinnyArgs{};
-      sk[j].fused = false;
-      sk[j].xq = c.xq;
-      sk[j].s = c.s;
-      sk[j].rowsum = c.rowsum;
-      sk[j].packed = c.packed;
-      sk[j].beta = c.beta;
-      sk[j].M = c.M;
-      sk[j].N = c.N;
-      sk[j].K = c.K;
-      sk[j].out = c.y;
-      sk[j].out_kind = y_dtype;
+      sk[j] = pre_call(c.xq, c.s, c.rowsum, c.packed, c.beta, c.M, c.N, c.K, c.y, y_dtype);
     }
     hipError_t e;
     if (skinny)
@@ -870,21 +820,9 @@ int bitlinear_forward_gated(const void *o, const void *g, const void *gate_w, fl
   a.s = w.s;
   a.rowsum = w.rowsum;
   if (BL_LAUNCH(bl::launch_gate(a, stream)) != hipSuccess) return BL_ERR_HIP;
-  if (M <= bl::kSkinnyMaxM) {
-    bl::SkinnyArgs sa{};
-    sa.fused = false;
-    sa.xq = w.xq;
-    sa.s = w.s;
-    sa.rowsum = w.rowsum;
-    sa.packed = packed;
-    sa.beta = beta;
-    sa.M = M;
-    sa.N = N;
-    sa.K = K;
-    sa.out = y;
-    sa.out_kind = y_dtype;
-    return hip_status(BL_LAUNCH(bl::launch_skinny(sa, stream)));
-  }
+  if (M <= bl::kSkinnyMaxM)
+    return hip_status(BL_LAUNCH(bl::launch_skinny(
+        pre_call(w.xq, w.s, w.rowsum, packed, beta, M, N, K, y, y_dtype), stream)));
   return hip_status(BL_LAUNCH(bl::launch_gemm_mfma(w.xq, w.rowsum, w.s, packed, beta, M, N, K, y,
                                                    y_dtype, false, stream)));
 }
