@@ -114,6 +114,81 @@ __device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur
   __syncthreads();
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at
+// lds + 16 L (lds is wave-uniform, taken through M0).  Kept out of the
+// templates: the host pass of the compiler rejects the LDS address-space
+// cast inside a template instantiation.
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint8_t *lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds, 16, voffset, soffset, 0, 0);
+}
+
+// The k-block body of launches without K groups: A goes from global memory
+// straight into LDS (the 16-byte buffer->LDS load; lane L writes the 16
+// bytes at base + 16 L) through a ring of three stages, two k-blocks ahead,
+// so no registers stage it; the weights come three k-blocks ahead through
+// three register sets.  At k-block kb: request A(kb+2) into stage
+// (kb+2) mod 3 (last read at kb-1, before the barrier that ended it), read
+// A(kb) from stage kb mod 3, multiply by the codes in bc (then reloaded with
+// k-block kb+3), and before the closing barrier wait only for A(kb+1) --
+// the loads issued after it (B(kb+2), A(kb+2), B(kb+3)) stay in flight.
+// The barrier is a plain s_barrier: a workgroup fence would also wait for
+// every load still in flight.
+template <int MI, int TPW, bool TAIL>
+__device__ __forceinline__ void gemm_kblock_dma(int kb, int kend, const uint8_t *cur,
+                                                uint8_t *dst, v4i (&acc)[MI][2 * TPW],
+                                                v4i (&bc)[TPW], rsrc_t ars,
+                                                const int (&a_dma)[MI], int a_lds0, rsrc_t brs,
+                                                int b_voff, int b_tile_bytes, int arow0, int lane) {
+  const int k2 = min(kb + 2, kend - 1), k3 = min(kb + 3, kend - 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < MI; ++j)
+    lds_load16(ars, dst + a_lds0 + 32 * 128 * j, a_dma[j], k2 * 128);
+  __builtin_amdgcn_sched_barrier(0);
+  v4i a[MI][2];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = arow0 + 16 * mi;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ch = 2 * (lane >> 4) + s2;
+      a[mi][s2] = *reinterpret_cast<const v4i *>(cur + row * 128 + (swz(row, ch) << 4));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const v4i w0 = unpack_codes(s2 ? bc[t].y : bc[t].x);
+      const v4i w1 = unpack_codes(s2 ? bc[t].w : bc[t].z);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
+        acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
+      }
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!TAIL) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      bc[t] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * b_tile_bytes, k3 * 1024, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // A(kb+1) has landed when at most B(kb+2), A(kb+2) and B(kb+3) remain.
+  // The count holds only where all three are issued, i.e. inside the loop,
+  // whose code loads are all live; in the last k-blocks the compiler may
+  // drop or move the code loads, and only A(kb+2) is sure to follow A(kb+1).
+  constexpr int kAfter = TAIL ? MI : 2 * TPW + MI;
+  static_assert(kAfter < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(kAfter | (7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 constexpr int kBandRows = 4;  // tile rows per band of the tile order
 constexpr int64_t kWideTiles = 768;  // 128 x 256 tiles from which a launch takes them
 
@@ -141,7 +216,14 @@ __device__ __forceinline__ void gemm_body(
   constexpr int BN = 64 * TPW;  // a wave: 16 MI rows x 32 TPW outputs (TPW packed tiles)
   static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
   static_assert(KG == 1 || TPW == 2, "the K-group reduction fits 2-tile waves only");
-  __shared__ __align__(16) uint8_t lds[KG][2][BM * 128];
+  // A stages: 2 per K group (filled through registers), or without K groups
+  // a ring of 3 filled by buffer->LDS loads and kept as three separate
+  // arrays: the compiler tells LDS objects apart, not offsets inside one,
+  // so a read of one stage does not wait for the loads into another
+  constexpr int NST = KG == 1 ? 1 : 2;
+  __shared__ __align__(16) uint8_t lds[KG][NST][BM * 128];
+  __shared__ __align__(16) uint8_t lds_r1[KG == 1 ? BM * 128 : 16];
+  __shared__ __align__(16) uint8_t lds_r2[KG == 1 ? BM * 128 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -197,11 +279,89 @@ __device__ __forceinline__ void gemm_body(
 #pragma unroll
     for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
 
-  // Prefetch distance 2: the A chunks and B tiles of k-block kb+2 are
-  // requested while k-block kb is multiplied, so each load has about two
-  // iterations of MFMA work to arrive; A goes through a double-buffered LDS
-  // stage one iteration before use.  (Native int vectors, not uint4: struct
-  // copies are lowered to memcpy through private memory.)
+  // Without K groups A is loaded straight into a ring of three LDS stages,
+  // two k-blocks ahead, and the codes three k-blocks ahead (gemm_kblock_dma;
+  // measured 3-5 % faster on the prefill shapes than staging A through
+  // registers).  With K groups (where the LDS holds two stages per group)
+  // prefetch distance 2: the A chunks and B tiles of k-block kb+2 are
+  // requested while k-block kb is multiplied, and A goes through a double-
+  // buffered LDS stage one iteration before use.  (Native int vectors, not
+  // uint4: struct copies are lowered to memcpy through private memory.)
+  const int arow0 = wm * 16 * MI + (lane & 15);
+  const int kstop = kb0 + trips;
+  int kb = kb0;
+  if constexpr (KG == 1) {
+    // wave wq fills rows 8 wq + 32 j .. +7 of a stage (1 KiB per load):
+    // lane L lands at row 8 wq + 32 j + L / 8, 16-byte slot L % 8, so it
+    // fetches the row's chunk that the swizzle puts in that slot
+    int a_dma[MI];
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int row = 8 * wq + 32 * j + (lane >> 3);
+      const int ch = swz(row, lane & 7);  // the swizzle is an involution
+      a_dma[j] = row * K + ch * 16;
+    }
+    const int a_lds0 = 8 * wq * 128;
+    uint8_t *const s0 = lds[0][0];
+    uint8_t *const s1 = lds_r1;
+    uint8_t *const s2 = lds_r2;
+    v4i U[TPW], V[TPW], W[TPW];  // codes of k-blocks = 0, 1, 2 mod 3
+    {
+      // issued in the loop's own order (B(0), A(0), B(1), A(1), B(2)), so
+      // the compiler's wait counts at the loop head match the steady state
+      const int k1 = __builtin_amdgcn_readfirstlane(min(1, klast));
+      const int k2 = __builtin_amdgcn_readfirstlane(min(2, klast));
+      const auto load_b = [&](v4i(&b)[TPW], int k) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          b[t] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k * 1024, 0));
+      };
+      const auto load_a = [&](uint8_t *stage, int k) {
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+          lds_load16(ars, stage + a_lds0 + 32 * 128 * j, a_dma[j], k * 128);
+      };
+      load_b(U, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(s0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(V, k1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(s1, k1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(W, k2);
+      __builtin_amdgcn_sched_barrier(0);
+      // A(0) has landed when at most A(1) remains (the code loads may be
+      // moved past this point by the compiler: only A(1) is sure to follow
+      // A(0)); the kernel-argument loads are drained too, so no wait on
+      // them lingers into the loop
+      __builtin_amdgcn_s_waitcnt(MI | (7 << 4) | (0 << 8));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    for (; kb + 2 < kstop; kb += 3) {
+      gemm_kblock_dma<MI, TPW, false>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+                               tile_bytes, arow0, lane);
+      gemm_kblock_dma<MI, TPW, false>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+                               tile_bytes, arow0, lane);
+      gemm_kblock_dma<MI, TPW, false>(kb + 2, kend, s2, s1, acc, W, ars, a_dma, a_lds0, brs, b_voff,
+                               tile_bytes, arow0, lane);
+    }
+    if (kb < kstop)
+      gemm_kblock_dma<MI, TPW, true>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+                               tile_bytes, arow0, lane);
+    if (kb + 1 < kstop)
+      gemm_kblock_dma<MI, TPW, true>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+                               tile_bytes, arow0, lane);
+    // the loads of the last k-blocks (clamped repeats) may still be writing
+    // the stages: drain them before the epilogue reuses the LDS
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  } else {
   v4i P[MI], Q[MI];     // A staging sets
   v4i X[TPW], Y[TPW];   // B of even / odd k-blocks
   uint8_t *const st0 = lds[kg][0];
@@ -227,12 +387,9 @@ __device__ __forceinline__ void gemm_body(
   }
   __syncthreads();
 
-  const int arow0 = wm * 16 * MI + (lane & 15);
   // Both halves of a trip are unconditional: a conditional second half would
   // let the compiler sink the first half's prefetch loads into it.
   constexpr bool CHECK = KG > 1;
-  const int kstop = kb0 + trips;
-  int kb = kb0;
   for (; kb + 1 < kstop; kb += 2) {
     gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
@@ -242,6 +399,7 @@ __device__ __forceinline__ void gemm_body(
   if (kb < kstop)
     gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
+  }
 
   if constexpr (KG > 1) {
     // Add the groups' accumulators into group 0 through the A stages (free:
@@ -250,7 +408,7 @@ __device__ __forceinline__ void gemm_body(
     // a two-level tree (2 -> 0 and 3 -> 1, then 1 -> 0).  Every wave passes
     // every barrier.
     constexpr int NREG = MI * 2 * TPW;
-    static_assert(KG * 2 * BM * 128 >= (KG / 2) * 4 * NREG * 64 * 16, "reduction slots fit");
+    static_assert(KG * NST * BM * 128 >= (KG / 2) * 4 * NREG * 64 * 16, "reduction slots fit");
     v4i *const red = reinterpret_cast<v4i *>(&lds[0][0][0]);
     const auto slot = [&](int gs, int mi, int nb) -> v4i * {
       return red + ((gs * 4 + wq) * NREG + mi * 2 * TPW + nb) * 64 + lane;
@@ -349,7 +507,7 @@ __device__ __forceinline__ void gemm_body(
     // other tile overlaps, so short launches store directly (measured
     // threshold: tiles x k-blocks > 16384).
     if (m0 + BM <= M && n0 + BN <= N && work > 16384) {
-      uint8_t *st = &lds[0][0][0] + wq * (16 * MI * 128);
+      uint8_t *st = (wq < 2 ? &lds[0][0][0] : lds_r1) + (wq & 1) * (16 * MI * 128);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -524,7 +682,7 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
   // Wide launches: 128 x 256 tiles, a wave holding 4 packed tiles, so each
-  // A operand read from LDS feeds twice the MFMAs (2 waves per SIMD: 246
+  // A operand read from LDS feeds twice the MFMAs (2 waves per SIMD: 240
   // VGPRs).  From 768 such tiles (gate_proj at M = 4096: 87 -> 84 us, at
   // M = 8192: 254 -> 238 us; i/f/g grouped at M = 4096: 51 -> 49 us); with
   // fewer, the tiles do not fill the rounds (2048-wide projections at M =

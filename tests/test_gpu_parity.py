@@ -149,6 +149,26 @@ def test_gemm_i32_wide_tile_launches_full(M, N, K):
     np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640])
+def test_gemm_i32_stage_ring_tails(K):
+    """128-row tiles (2000 x 2048: 256 tiles, the last tile row ragged) whose
+    k-blocks run in steps of three with one or two left over: 1 to 5
+    k-blocks cover no full step, one step, and each remainder, every element
+    against the oracle's contraction."""
+    M, N = 2000, 2048
+    say(f"gemm_i32 stage ring M={M} N={N} K={K}")
+    xq = _random_codes(M, K, K + 5)
+    r = np.random.default_rng(K)
+    Wq = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    packed = torch.from_numpy(oracle.pack(Wq)).to(DEV)
+    d_xq = torch.from_numpy(xq).to(DEV)
+    d_rs = torch.from_numpy(xq.astype(np.int64).sum(1).astype(np.int32)).to(DEV)
+    acc = Guarded((M, N), torch.int32, fill=-7)
+    tw.bitlinear_gemm_i32(d_xq, d_rs, packed, N, acc.t, path=tw.BL_PATH_MFMA)
+    acc.check("acc")
+    np.testing.assert_array_equal(acc.t.cpu().numpy(), contract_rows(xq, Wq))
+
+
 # (M, N, K) -> (tile height, K groups) under the launch rule in gemm.hip:
 # (20, 992, 2176) 32 rows, 4 groups over 17 k-blocks (5/5/5/2);
 # (100, 2560, 7040) 32, 4 over 55 (14/14/14/13); (512, 2560, 2560) 32, 2;
