@@ -68,14 +68,14 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
-    "c5-M1": ("decode", "22a7bba0bac5f177", 5255271),
-    "c5-M8": ("decode", "22a7bba0bac5f177", 5792373),
-    "c5-M64": ("skinny", "4474cdc02a05004c", 8312451),
-    "c5-M512": ("gemm", "c271b5961390af08", 23230407),
-    "c5-M8192": ("gemm", "c271b5961390af08", 225346776),
-    "c2": ("decode", "22a7bba0bac5f177", 648121),
-    "c3": ("skinny", "4474cdc02a05004c", 4662009),
-    "c4": ("gemm", "c271b5961390af08", 87402774),
+    "c5-M1": ("decode", "22a7bba0bac5f177", 5255327),
+    "c5-M8": ("decode", "22a7bba0bac5f177", 5792459),
+    "c5-M64": ("skinny", "4474cdc02a05004c", 8312538),
+    "c5-M512": ("gemm", "3ce42a83e7adff85", 23240033),
+    "c5-M8192": ("gemm", "3ce42a83e7adff85", 231771243),
+    "c2": ("decode", "22a7bba0bac5f177", 647950),
+    "c3": ("skinny", "4474cdc02a05004c", 4662275),
+    "c4": ("gemm", "3ce42a83e7adff85", 87286944),
 }
 
 
