@@ -91,6 +91,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_glu_rows.restype = ctypes.c_int
     L.oracle_glu_rows.argtypes = [I64, P]
     L.oracle_forward.restype = ctypes.c_int
+    L.oracle_mlgru_scan.argtypes = [P, P, I64, I64, I64, P, P, P]
+    L.oracle_mlgru_scan.restype = None
     return L
 
 
@@ -288,3 +290,25 @@ def rmsnorm_swish_gate(o, g, w, eps=1e-6) -> np.ndarray:
     z = np.empty((M, K), np.float64)
     lib().oracle_rmsnorm_swish_gate(_p(o), _p(g), _p(w), M, K, float(eps), _p(z))
     return z
+
+
+def mlgru_scan(i, f, h0=None):
+    """h [B,T,D] (fp64), hT [B,D] (fp64): the reading of the MLGRU recurrence
+    (oracle.c): h_t = a h_{t-1} + (1 - a) i_t, a = sigmoid(f_t), h_{-1} = h0
+    (zeros when None).  i, f [B,T,D] (or [T,D] for one sequence), widened
+    exactly to fp32."""
+    i = np.asarray(i)
+    squeeze = i.ndim == 2
+    i = _c(i[None] if squeeze else i, np.float32)
+    f = np.asarray(f)
+    f = _c(f[None] if squeeze else f, np.float32)
+    B, T, D = i.shape
+    assert f.shape == (B, T, D)
+    h = np.empty((B, T, D), np.float64)
+    hT = np.empty((B, D), np.float64)
+    h0p = None
+    if h0 is not None:
+        h0 = _c(np.asarray(h0).reshape(B, D), np.float64)
+        h0p = _p(h0)
+    lib().oracle_mlgru_scan(_p(i), _p(f), B, T, D, h0p, _p(h), _p(hT))
+    return (h[0], hT[0]) if squeeze else (h, hT)

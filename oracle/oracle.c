@@ -292,3 +292,38 @@ void oracle_rmsnorm_swish_gate(const float *o, const float *g, const float *w, i
             z[m * K + k] = ((double)orow[k] * r) * (double)w[k] * oracle_silu((double)grow[k]);
     }
 }
+
+/* ------------------------------------------------ MLGRU scan (a reading) */
+
+/* The token mixer of the HGRNBit block.  The pages describe the MLGRU in
+ * words only (datacamp "MatMul-freie LLMs: Zentrale Konzepte erklärt",
+ * section "Kernkomponenten: MLGRU und GLU", the MLGRU paragraph and figure
+ * panel 2): it runs over the sequence token by token; each step takes the
+ * current token and the previous hidden state and updates the state with
+ * elementwise operations and gates, vectors of values between 0 and 1 that
+ * weigh which parts of the previous state and of the current token carry
+ * on.  Its projections are the block's i_proj and f_proj (hysenlabs ja
+ * review, section "HGRNBit という層構成を読む").  The reading taken here is
+ * the plainest one those words support: the forget gate is the logistic
+ * sigmoid of f_proj's output, the candidate is i_proj's output, and the new
+ * state is their gate-weighted mix,
+ *   a = 1 / (1 + e^-f[b,t,d]),
+ *   h[b,t,d] = a * h[b,t-1,d] + (1 - a) * i[b,t,d],   h[b,-1,d] = h0[b,d],
+ * per sequence b, time step t and channel d; the state starts at h0 (zero
+ * when h0 is NULL) and hT receives h[b,T-1,:].  i, f, h are [B, T, D] with
+ * the tokens of one sequence consecutive; everything in fp64. */
+void oracle_mlgru_scan(const float *i, const float *f, int64_t B, int64_t T, int64_t D,
+                       const double *h0, double *h, double *hT)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            double state = h0 ? h0[b * D + d] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t e = (b * T + t) * D + d;
+                const double a = 1.0 / (1.0 + exp(-(double)f[e]));
+                state = a * state + (1.0 - a) * (double)i[e];
+                h[e] = state;
+            }
+            if (hT) hT[b * D + d] = state;
+        }
+}

@@ -151,6 +151,13 @@ int oracle_glu_rows(int64_t F, int64_t *src);
 void oracle_rmsnorm_swish_gate(const float *o, const float *g, const float *w, int64_t M,
                                int64_t K, double eps, double *z);
 
+/* The MLGRU scan, as the pages' description reads (see oracle.c):
+ * h[b,t,d] = a h[b,t-1,d] + (1 - a) i[b,t,d], a = sigmoid(f[b,t,d]),
+ * h[b,-1,:] = h0[b,:] (zero if h0 is NULL).  i, f [B, T, D] fp32; h [B, T, D]
+ * and hT [B, D] (may be NULL) fp64. */
+void oracle_mlgru_scan(const float *i, const float *f, int64_t B, int64_t T, int64_t D,
+                       const double *h0, double *h, double *hT);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_gate as gate_pins
 from tests import test_oracle_glu as glu_pins
+from tests import test_oracle_mlgru as mlgru_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -56,11 +57,24 @@ MUTANTS = {
     "gate_drops_gain": ("((double)orow[k] * r) * (double)w[k] * oracle_silu",
                         "((double)orow[k] * r) * oracle_silu"),
     "gate_unnormalized": ("((double)orow[k] * r) * (double)w[k]", "((double)orow[k]) * (double)w[k]"),
+    "scan_gate_on_the_input": ("state = a * state + (1.0 - a) * (double)i[e];",
+                               "state = (1.0 - a) * state + a * (double)i[e];"),
+    "scan_sigmoid_sign_slip": ("1.0 / (1.0 + exp(-(double)f[e]))", "1.0 / (1.0 + exp((double)f[e]))"),
+    "scan_gate_without_sigmoid": ("1.0 / (1.0 + exp(-(double)f[e]))", "(double)f[e]"),
+    "scan_i_and_f_swapped": ("state = a * state + (1.0 - a) * (double)i[e];",
+                             "state = a * state + (1.0 - a) * (double)f[e];"),
+    "scan_stores_before_update": ("                state = a * state + (1.0 - a) * (double)i[e];\n"
+                                  "                h[e] = state;",
+                                  "                h[e] = state;\n"
+                                  "                state = a * state + (1.0 - a) * (double)i[e];"),
+    "scan_ignores_h0": ("double state = h0 ? h0[b * D + d] : 0.0;", "double state = 0.0;"),
+    "scan_time_major_layout": ("const int64_t e = (b * T + t) * D + d;",
+                               "const int64_t e = (t * B + b) * D + d;"),
 }
 
 
 def _pin_tests():
-    return [f for mod in (pins, glu_pins, gate_pins)
+    return [f for mod in (pins, glu_pins, gate_pins, mlgru_pins)
             for name, f in inspect.getmembers(mod, inspect.isfunction)
             if name.startswith("test_") and not hasattr(f, "pytestmark")]
 

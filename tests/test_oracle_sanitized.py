@@ -37,7 +37,8 @@ def test_oracle_pins_under_asan_ubsan(tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_glu.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_gate.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_gate.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_mlgru.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-4000:]
