@@ -292,6 +292,39 @@ int bitlinear_forward_glu(const void *x, int x_dtype, int64_t M, int64_t K, cons
 int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, int dtype,
                                  int64_t M, int64_t K, float eps, void *z, hipStream_t stream);
 
+/* ------------------------------------------------------- MLGRU scan
+ * The token mixer's recurrence.  The pages describe the MLGRU in words only
+ * (datacamp page, section "Kernkomponenten: MLGRU und GLU", the MLGRU
+ * paragraph and figure panel 2: token by token, gates of values in (0, 1)
+ * weigh the previous hidden state against the current token; its
+ * projections are i_proj and f_proj, hysenlabs ja review, section "HGRNBit
+ * という層構成を読む").  This library reads that as
+ *   a = 1 / (1 + e^-f[b,t,d]),  h[b,t,d] = a h[b,t-1,d] + (1 - a) i[b,t,d],
+ *   h[b,-1,d] = h0[b,d]  (zero when h0 is NULL),
+ * in fp32 (hardware exp2 and reciprocal), h rounded to dtype.  Chunks of 32
+ * steps are scanned in parallel and joined through their start states
+ * (three launches; one for T <= 32). */
+
+/* Workspace bytes bitlinear_mlgru_scan needs for [B, T, D] (0 when
+ * T <= 32, or for an invalid shape). */
+size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);
+
+/* h [B, T, D] (dtype, device, written) from i and f [B, T, D] (dtype,
+ * device, read only; a sequence's T token rows consecutive, each D wide --
+ * the row order of the i_proj and f_proj outputs).
+ *   h0  device fp32 [B, D] start state, or NULL for zeros (read only)
+ *   hT  device fp32 [B, D] written with the state after step T - 1
+ *       (bit-identical to h[:, T-1, :] before rounding), or NULL
+ *   ws  device scratch of >= bitlinear_mlgru_workspace_bytes(B, T, D) bytes
+ *       (16-byte aligned; may be NULL when that is 0)
+ * Shapes: 0 <= B <= 65535, 0 <= T <= 2^20, 0 <= D <= 65536, D % 8 == 0
+ * (else BL_ERR_SHAPE); B, T or D == 0 is a no-op.  i, f, h 16-byte aligned
+ * (BL_ERR_ALIGN); h may not overlap i or f.  Returns BL_OK or a negative
+ * BL_ERR_* code (nothing launched on error). */
+int bitlinear_mlgru_scan(const void *i, const void *f, int dtype, int64_t B, int64_t T, int64_t D,
+                         const float *h0, void *h, float *hT, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* o_proj with the gate as its prologue: y = FusedBitLinear(z) for the z of
  * bitlinear_rmsnorm_swish_gate(o, g, gate_w, gate_eps), without z going
  * through memory.  1..8 tokens of 16-bit activations (M (K + 16) <= 45056):

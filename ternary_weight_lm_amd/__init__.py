@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     BL_ERR_TIMEOUT, BlChain, make_chain_calls, bitlinear_chain_workspace_bytes,
     bitlinear_chain_plan, bitlinear_chain_run, bitlinear_chain_run_ex, bitlinear_chain_status,
     bitlinear_test_fail_launches, bitlinear_rmsnorm_swish_gate, bitlinear_forward_gated,
+    bitlinear_mlgru_scan, bitlinear_mlgru_workspace_bytes,
     bitlinear_set_decode_contraction, bitlinear_get_decode_contraction,
     BL_DECODE_AUTO, BL_DECODE_MFMA, BL_DECODE_VALU,
 )

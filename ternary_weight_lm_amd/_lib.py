@@ -108,6 +108,8 @@ SIGNATURES = {
     "bitlinear_chain_run_ex": ([P, ctypes.c_uint32, P], I),
     "bitlinear_chain_status": ([P, P], I),
     "bitlinear_forward_noalloc": ([P, I, I64, I64, P, P, P, I64, P, I, F, P], I),
+    "bitlinear_mlgru_workspace_bytes": ([I64, I64, I64], SZ),
+    "bitlinear_mlgru_scan": ([P, P, I, I64, I64, I64, P, P, P, P, SZ, P], I),
 }
 
 
@@ -496,6 +498,39 @@ def bitlinear_rmsnorm_swish_gate(o, g, w, z, eps=1e-6, stream=None):
     _need(z, "z", o.dtype, numel=M * K)
     _check("bitlinear_rmsnorm_swish_gate", lib().bitlinear_rmsnorm_swish_gate(
         _ptr(o), _ptr(g), _ptr(w), DTYPE_CODE[o.dtype], M, K, eps, _ptr(z), _stream(stream)))
+
+
+def bitlinear_mlgru_workspace_bytes(B, T, D):
+    return int(lib().bitlinear_mlgru_workspace_bytes(B, T, D))
+
+
+def bitlinear_mlgru_scan(i, f, h, h0=None, hT=None, ws=None, stream=None):
+    """h [B,T,D] = the MLGRU recurrence over i, f [B,T,D] (or [T,D] for one
+    sequence): h_t = a h_{t-1} + (1 - a) i_t, a = sigmoid(f_t), from h0
+    (fp32 [B,D], zeros when None); hT (fp32 [B,D]) receives the last state.
+    ws: scratch of bitlinear_mlgru_workspace_bytes(B, T, D) bytes (allocated
+    here when None and needed)."""
+    _need(i, "i", FLOATS)
+    if i.dim() == 2:
+        B, (T, D) = 1, i.shape
+    elif i.dim() == 3:
+        B, T, D = i.shape
+    else:
+        raise ValueError(f"i must be [T, D] or [B, T, D], got {tuple(i.shape)}")
+    _need(f, "f", i.dtype, numel=B * T * D)
+    _need(h, "h", i.dtype, numel=B * T * D)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, numel=B * D)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, numel=B * D)
+    need = bitlinear_mlgru_workspace_bytes(B, T, D)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=i.device)
+    if ws is not None:
+        _need(ws, "ws", numel=1)
+    _check("bitlinear_mlgru_scan", lib().bitlinear_mlgru_scan(
+        _ptr(i), _ptr(f), DTYPE_CODE[i.dtype], B, T, D, _ptr(h0), _ptr(h), _ptr(hT), _ptr(ws),
+        _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def bitlinear_forward_gated(o, g, gate_w, gain, packed, beta, N, y, ws, gate_eps=1e-6, eps=1e-8,

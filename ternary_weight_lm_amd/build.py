@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libbitlinear.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pack.hip", "actquant.hip", "gemm.hip", "skinny.hip", "decode.hip", "decode_f32.hip",
-           "decode_f16.hip", "decode_bf16.hip", "chain.hip", "gate.hip", "capi.cpp"]
+           "decode_f16.hip", "decode_bf16.hip", "chain.hip", "gate.hip", "mlgru.hip", "capi.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

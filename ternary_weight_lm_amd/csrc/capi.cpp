@@ -770,6 +770,43 @@ int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, in
   return hip_status(BL_LAUNCH(bl::launch_gate(a, stream)));
 }
 
+namespace {
+bool mlgru_shape_ok(int64_t B, int64_t T, int64_t D) {
+  return B >= 0 && T >= 0 && D >= 0 && D % 8 == 0 && B <= bl::kMlgruMaxB && D <= bl::kMlgruMaxD &&
+         T <= bl::kMlgruMaxT;
+}
+}  // namespace
+
+size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D) {
+  if (!mlgru_shape_ok(B, T, D)) return 0;
+  return bl::mlgru_workspace_bytes(B, T, D);
+}
+
+int bitlinear_mlgru_scan(const void *i, const void *f, int dtype, int64_t B, int64_t T, int64_t D,
+                         const float *h0, void *h, float *hT, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!dtype_ok(dtype)) return BL_ERR_DTYPE;
+  if (!mlgru_shape_ok(B, T, D)) return BL_ERR_SHAPE;
+  if (B == 0 || T == 0 || D == 0) return BL_OK;
+  if (!i || !f || !h) return BL_ERR_NULL;
+  if (!aligned16(i) || !aligned16(f) || !aligned16(h)) return BL_ERR_ALIGN;
+  const size_t need = bl::mlgru_workspace_bytes(B, T, D);
+  if (need > 0 && (!ws || ws_bytes < need)) return BL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return BL_ERR_ALIGN;
+  bl::MlgruArgs a{};
+  a.i = i;
+  a.f = f;
+  a.dtype = dtype;
+  a.B = B;
+  a.T = T;
+  a.D = D;
+  a.h0 = h0;
+  a.h = h;
+  a.hT = hT;
+  a.ws = ws;
+  return hip_status(BL_LAUNCH(bl::launch_mlgru_scan(a, stream)));
+}
+
 int bitlinear_forward_gated(const void *o, const void *g, const void *gate_w, float gate_eps,
                             int x_dtype, int64_t M, int64_t K, const void *gain,
                             const void *packed, const float *beta, int64_t N, void *y,

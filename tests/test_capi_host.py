@@ -555,3 +555,37 @@ def test_gate_entry_points_validation():
     assert call(wsb=16) == WS
     assert call(o=A + 2) == ALIGN
     assert call(M=0, o=None, g=None) == OK
+
+
+def test_mlgru_workspace_closed_form():
+    L = tw.lib()
+    # 2 B C D floats with C = ceil(T / 32) chunks; none for one chunk
+    assert L.bitlinear_mlgru_workspace_bytes(1, 32, 2560) == 0
+    assert L.bitlinear_mlgru_workspace_bytes(1, 33, 2560) == 2 * 1 * 2 * 2560 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(4, 8192, 2048) == 2 * 4 * 256 * 2048 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(1, 100, 12) == 0       # D % 8 != 0: invalid
+    assert L.bitlinear_mlgru_workspace_bytes(-1, 100, 16) == 0
+
+
+def test_mlgru_scan_validation():
+    L = tw.lib()
+    sc = L.bitlinear_mlgru_scan
+    wsb = L.bitlinear_mlgru_workspace_bytes(2, 100, 64)
+
+    def call(i=A, f=B, dt=2, Bn=2, T=100, Dn=64, h0=None, h=Y, hT=None, ws=WSP, wsb=wsb):
+        return sc(i, f, dt, Bn, T, Dn, h0, h, hT, ws, wsb, None)
+
+    assert call(dt=7) == DTYPE
+    assert call(Dn=60) == SHAPE                   # D % 8 != 0
+    assert call(Bn=70000) == SHAPE
+    assert call(T=(1 << 20) + 1) == SHAPE
+    assert call(Dn=-8) == SHAPE
+    assert call(f=None) == NULL
+    assert call(h=None) == NULL
+    assert call(i=A + 8) == ALIGN
+    assert call(ws=None) == WS
+    assert call(wsb=wsb - 1) == WS
+    assert call(ws=WSP + 4) == ALIGN
+    assert call(T=0, i=None, f=None, h=None) == OK    # empty: nothing touched
+    assert call(Bn=0, i=None, f=None, h=None) == OK
+    assert call(Dn=0, i=None, f=None, h=None) == OK
