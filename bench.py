@@ -66,8 +66,9 @@ C5_SWEEP = (1, 8, 64, 512, 8192)
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip", "decode_f16.hip",
                              "decode_bf16.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "gemm": ["gemm.hip", "bl_common.h", "bl_launch.h"],
-                  "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"]}
-TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
+                  "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
+                  "mlgru": ["mlgru.hip", "bl_common.h", "bl_launch.h"]}
+TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; per call for -mlgru)
     "c5-M1": ("decode", "22a7bba0bac5f177", 5255327),
     "c5-M8": ("decode", "22a7bba0bac5f177", 5792459),
     "c5-M64": ("skinny", "4474cdc02a05004c", 8312538),
@@ -76,6 +77,8 @@ TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch)
     "c2": ("decode", "22a7bba0bac5f177", 647950),
     "c3": ("skinny", "4474cdc02a05004c", 4662275),
     "c4": ("gemm", "3ce42a83e7adff85", 87286944),
+    "c5-M8192-mlgru": ("mlgru", "13143e5eedc14bcc", 218136958),
+    "c5-M512-mlgru": ("mlgru", "13143e5eedc14bcc", 14450799),
 }
 
 
@@ -104,7 +107,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c5",
                     help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, an MLP "
-                         "workload c3-mlp | c4-mlp | c5-M<M>-mlp, or the gated o_proj c5-M<M>-gate")
+                         "workload c3-mlp | c4-mlp | c5-M<M>-mlp, the gated o_proj c5-M<M>-gate, "
+                         "or the MLGRU scan c5-M<M>-mlgru")
     ap.add_argument("--launch", choices=["per-call", "chain"], default="per-call",
                     help="per-call: one launch group per projection (default); chain: a "
                          "chained stack at 1..4 tokens runs as one persistent launch per step "
@@ -703,6 +707,106 @@ def run_gate(args):
     print(json.dumps(out), flush=True)
 
 
+def run_mlgru(args):
+    """The MLGRU scan (bitlinear_mlgru_scan) at the 2.7B block's mixer width:
+    per layer one scan over the i_proj and f_proj outputs (synthetic, bf16,
+    a distinct pair per layer so each scan reads them from HBM).  M >= 512
+    tokens are one sequence of M steps (prefill); fewer are M sequences of
+    one step each, continuing from a start state (decode).  Workloads
+    c5-M<M>-mlgru (32 layers)."""
+    import numpy as np
+    import torch
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+    import oracle
+
+    base = args.workload[:-len("-mlgru")]
+    cfg = synth.CONFIGS["c5"]
+    M = int(base.split("-M")[1])
+    layers = cfg.layers
+    D = cfg.projs[[p.name for p in cfg.projs].index("i_proj")].N
+    B, T = (1, M) if M >= 512 else (M, 1)
+    dev = torch.device("cuda:0")
+    xdt = synth.DTYPES[cfg.dtype]
+    i_in, f_in = [], []
+    for layer in range(layers):
+        i_in.append(synth.make_x(cfg.seed, layer, 0, M, D, cfg.dtype).to(dev).view(B, T, D))
+        f_in.append((synth.make_x(cfg.seed, layer, 1, M, D, "fp32") * 3).to(xdt).to(dev).view(B, T, D))
+    h0 = [synth.make_x(cfg.seed, layer, 2, B, D, "fp32").to(dev) for layer in range(layers)]
+    h = torch.empty(B, T, D, dtype=xdt, device=dev)
+    hT = torch.empty(B, D, dtype=torch.float32, device=dev)
+    need = tw.bitlinear_mlgru_workspace_bytes(B, T, D)
+    ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, keep):
+        for layer in range(layers):
+            tw.bitlinear_mlgru_scan(i_in[layer], f_in[layer], h, h0=h0[layer], hT=hT, ws=ws)
+
+    nlaunch = 1 if T <= 32 else 3
+    big = M >= 512
+    steps = args.steps if args.steps is not None else (20 if big else 100)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 10)
+    for gr, _ in capture(step, 0, warmup, nlaunch * layers):
+        gr.replay()
+    ms = timed_replay(capture(step, warmup, steps, nlaunch * layers))
+    calls = steps * layers
+    sec = ms / 1e3
+    byt = 6 * B * T * D + 8 * B * D          # i, f, h (bf16) + h0, hT (fp32)
+    ach = byt * calls / sec / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 5), "traffic": traffic(args.workload),
+            "kernel": ("bl::mlgru_apply_kernel (one chunk per sequence: one launch per scan)"
+                       if nlaunch == 1 else
+                       "bl::mlgru_chunk_kernel + mlgru_carry_kernel + mlgru_apply_kernel "
+                       "(chunks of 32 steps joined through their start states)"),
+            "launches": calls * nlaunch, "avg_call_us": round(sec * 1e6 / calls, 3),
+            "algorithmic_bytes_per_call": byt,
+            "timed_region": f"the benchmark steps (each call: {nlaunch} launch"
+                            f"{'es' if nlaunch > 1 else ''})",
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE over its "
+                            "launches, copy-calibrated)"}
+    out = {
+        "metric": METRIC, "value": round(M * steps / sec, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name.replace('_Msweep', '')}_M{M}_mlgru_scan",
+                   "tokens_per_step": M, "layers": layers, "sequences": B, "steps_per_sequence": T,
+                   "channels": D, "x_dtype": cfg.dtype,
+                   "launch": f"hipGraph; per layer one bitlinear_mlgru_scan ({nlaunch} launch"
+                             f"{'es' if nlaunch > 1 else ''})",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        facts = host_facts()
+        iw = synth.widen(i_in[0].cpu())
+        fw = synth.widen(f_in[0].cpu())
+        hw = synth.widen(h0[0].cpu()).astype(np.float64)
+        cols = min(D, 256)                   # a channel sample: the scan is per channel
+        old = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {facts["pinned_core"]})
+        try:
+            t0, n = time.perf_counter(), 0
+            while True:
+                oracle.mlgru_scan(iw[:, :, :cols], fw[:, :, :cols], hw[:, :cols])
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        finally:
+            os.sched_setaffinity(0, old)
+        out["cpu_baseline"] = {
+            "value": round(M * n * cols / D / el / layers, 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} scans of {cols} of {D} channels over all {M} tokens of one layer "
+                      f"({el:.1f} s single-threaded; scaled to {D} channels and {layers} layers)",
+            "host": {"nproc": facts["nproc"], "cpu_model": facts["model"],
+                     "pinned": f"core {facts['pinned_core']}"}}
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def host_facts():
@@ -934,6 +1038,9 @@ def main():
         return
     if args.workload.endswith("-gate"):
         run_gate(args)
+        return
+    if args.workload.endswith("-mlgru"):
+        run_mlgru(args)
         return
 
     sweep = args.workload == "c5"

@@ -194,8 +194,8 @@ constexpr int64_t kGateMaxK = 4096;
 hipError_t launch_gate(const GateArgs &a, hipStream_t stream);
 
 // MLGRU recurrence over [B, T, D] (mlgru.hip): h_t = a h_{t-1} + (1 - a) i_t,
-// a = sigmoid(f_t), chunks of kMlgruChunk steps; ws holds 2 B C D floats
-// (C = ceil(T / kMlgruChunk)) when C > 1.
+// a = sigmoid(f_t), chunks of mlgru_chunk_len(T) steps; ws holds 2 B C D
+// floats (C = ceil(T / chunk length)) when C > 1.
 struct MlgruArgs {
   const void *i, *f;
   int dtype;
@@ -205,9 +205,9 @@ struct MlgruArgs {
   float *hT;        // [B, D] or null
   void *ws;
 };
-constexpr int kMlgruChunk = 32;
+constexpr int64_t mlgru_chunk_len(int64_t T) { return T >= 4096 ? 64 : 32; }
 constexpr int64_t kMlgruMaxB = 65535;      // launch grid z
-constexpr int64_t kMlgruMaxT = 1 << 20;    // chunks per sequence (grid y) <= 32768
+constexpr int64_t kMlgruMaxT = 1 << 20;    // chunks per sequence (grid y) <= 16384
 constexpr int64_t kMlgruMaxD = 1 << 16;
 size_t mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);
 hipError_t launch_mlgru_scan(const MlgruArgs &a, hipStream_t stream);

@@ -14,18 +14,21 @@
 //
 // The recurrence is linear in h, so a chunk of L steps maps a start state H
 // to P H + S (P the product of the chunk's gates, S the chunk run from
-// zero).  Three launches over [B, T, D]:
-//   1. per (sequence, chunk, 8 channels): P and S of the chunk;
+// zero).  L = 32, or 64 from 4096 steps: shorter chunks put more waves on
+// the two streaming launches, longer ones shorten the carry's chain (2.7B
+// width, one sequence: 8192 steps 55.8 / 49.1 / 52.7 us per scan at L = 32 /
+// 64 / 128, 512 steps 12.9 / 18.4 / 30.1 us).  Three launches over [B, T, D]:
+//   1. per (sequence, chunk, 2 channels): P and S of the chunk;
 //   2. per (sequence, channel): the chunk start states, walking the chunks
 //      in order (H_{c+1} = P_c H_c + S_c), written over S;
-//   3. per (sequence, chunk, 8 channels): the chunk run again from its start
+//   3. per (sequence, chunk, 2 channels): the chunk run again from its start
 //      state, storing h (and, in the last chunk, the final state hT).
-// A sequence of at most L steps is launch 3 alone, from h0.  Each thread
-// holds 8 consecutive channels (one 16-byte chunk of a 2-byte dtype), so a
-// wave reads 512 channels of a token row per load; the loads of a chunk do
-// not depend on the state and run ahead of the recurrence.  HBM traffic:
-// i and f twice and h once (10 bytes per element in bf16), plus 24 bytes per
-// chunk and channel of P, S and the start states.
+// A sequence of at most L steps is launch 3 alone, from h0.  A thread holds
+// two consecutive channels, so a wave reads 128 channels of a token row per
+// load and a 2560-wide row spreads over 20 waves; the loads of a chunk go
+// out in batches ahead of the recurrence, which does not feed them.  HBM
+// traffic: i and f twice and h once (10 bytes per element in bf16), plus 24
+// bytes per chunk and channel of P, S and the start states.
 #include "bl_common.h"
 #include "bl_launch.h"
 
@@ -33,79 +36,145 @@ namespace bl {
 
 namespace {
 
-constexpr int kScanThreads = 256;  // threads per workgroup, 8 channels each
+constexpr int kScanThreads = 256;  // threads per workgroup
+constexpr int kCpt = 2;            // consecutive channels per thread
 
 __device__ __forceinline__ float gate_of(float f) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-f * 1.4426950408889634f));
 }
 
+// The kCpt channels a thread holds in one token row: one dword of a 2-byte
+// dtype, two of fp32.
 template <int DT>
-__device__ __forceinline__ void load_token(const void *p, int64_t elem, float v[8]) {
-  constexpr int EB = dtype_bytes(DT);
-  const char *q = static_cast<const char *>(p) + elem * EB;
-  Chunk8<DT> c;
-  c.u[0] = *reinterpret_cast<const v4i *>(q);
-  if constexpr (DT == BL_F32) c.u[1] = *reinterpret_cast<const v4i *>(q + 16);
-  widen<DT>(c, v);
+struct Pair {
+  uint32_t w[DT == BL_F32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ Pair<DT> load_pair(const void *p, int64_t elem) {
+  Pair<DT> v;
+  if constexpr (DT == BL_F32) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(static_cast<const float *>(p) + elem);
+    v.w[0] = q.x;
+    v.w[1] = q.y;
+  } else {
+    v.w[0] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p) + elem);
+  }
+  return v;
 }
 
 template <int DT>
-__device__ __forceinline__ void store_token(void *p, int64_t elem, const float v[8]) {
-  constexpr int EB = dtype_bytes(DT);
-  char *q = static_cast<char *>(p) + elem * EB;
+__device__ __forceinline__ void widen_pair(const Pair<DT> &v, float f[2]) {
   if constexpr (DT == BL_F32) {
-    *reinterpret_cast<v4i *>(q) = v4i{__float_as_int(v[0]), __float_as_int(v[1]),
-                                      __float_as_int(v[2]), __float_as_int(v[3])};
-    *reinterpret_cast<v4i *>(q + 16) = v4i{__float_as_int(v[4]), __float_as_int(v[5]),
-                                           __float_as_int(v[6]), __float_as_int(v[7])};
+    f[0] = __uint_as_float(v.w[0]);
+    f[1] = __uint_as_float(v.w[1]);
+  } else if constexpr (DT == BL_BF16) {
+    f[0] = __uint_as_float(v.w[0] << 16);
+    f[1] = __uint_as_float(v.w[0] & 0xFFFF0000u);
   } else {
-    v4i w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (int)((uint32_t)out_bits<DT>(v[2 * j]) | ((uint32_t)out_bits<DT>(v[2 * j + 1]) << 16));
-    *reinterpret_cast<v4i *>(q) = w;
+    f[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.w[0] & 0xFFFFu));
+    f[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.w[0] >> 16));
   }
 }
 
-// 1. P and S of chunk blockIdx.y of sequence blockIdx.z.
 template <int DT>
+__device__ __forceinline__ void store_pair(void *p, int64_t elem, const float v[2]) {
+  if constexpr (DT == BL_F32) {
+    *reinterpret_cast<uint2 *>(static_cast<float *>(p) + elem) =
+        make_uint2(__float_as_uint(v[0]), __float_as_uint(v[1]));
+  } else {
+    *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p) + elem) =
+        (uint32_t)out_bits<DT>(v[0]) | ((uint32_t)out_bits<DT>(v[1]) << 16);
+  }
+}
+
+// Tokens [t0, t1) of one chunk (t1 - t0 <= L) for kCpt channels of
+// one sequence, in batches of U tokens whose 2 U loads (i and f) go out
+// together, the next batch's before the current one is computed (the loads
+// do not depend on the state).  The batch loop is unrolled over the whole
+// chunk with two buffers and no branch around the loads (rows past t1 load
+// row t1 - 1 again and are not computed): left to itself the compiler
+// waits for each token's pair before requesting the next.  step(t, a, iv)
+// receives each token in order.
+template <int DT>
+struct ScanBatch {
+  static constexpr int U = 16;  // tokens per batch
+  Pair<DT> i[U], f[U];
+};
+
+template <int DT>
+__device__ __forceinline__ void scan_load(ScanBatch<DT> &bt, const void *i, const void *f,
+                                          int64_t row0, int64_t D, int t, int t1) {
+#pragma unroll
+  for (int u = 0; u < ScanBatch<DT>::U; ++u) {
+    const int64_t r = row0 + (int64_t)min(t + u, t1 - 1) * D;
+    bt.i[u] = load_pair<DT>(i, r);
+    bt.f[u] = load_pair<DT>(f, r);
+  }
+}
+
+template <int DT, int L, class Step>
+__device__ __forceinline__ void scan_tokens(const void *i, const void *f, int64_t row0, int64_t D,
+                                            int t0, int t1, Step step) {
+  constexpr int U = ScanBatch<DT>::U;
+  static_assert(L % U == 0, "whole batches");
+  constexpr int NB = L / U;
+  ScanBatch<DT> buf[2];
+  scan_load<DT>(buf[0], i, f, row0, D, t0, t1);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int t = t0 + k * U;
+    if (k + 1 < NB) scan_load<DT>(buf[(k + 1) & 1], i, f, row0, D, t + U, t1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t + u < t1) {
+        float iv[kCpt], fv[kCpt], a[kCpt];
+        widen_pair<DT>(buf[k & 1].i[u], iv);
+        widen_pair<DT>(buf[k & 1].f[u], fv);
+#pragma unroll
+        for (int e = 0; e < kCpt; ++e) a[e] = gate_of(fv[e]);
+        step(t + u, a, iv);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// 1. P and S of chunk blockIdx.y (L steps) of sequence blockIdx.z.
+template <int DT, int L>
 __global__ __launch_bounds__(kScanThreads) void mlgru_chunk_kernel(const void *__restrict__ i,
                                                                    const void *__restrict__ f,
-                                                                   int T, int D, int L, int C,
+                                                                   int T, int D, int C,
                                                                    float *__restrict__ P,
                                                                    float *__restrict__ S) {
-  const int d0 = 8 * ((int)blockIdx.x * kScanThreads + (int)threadIdx.x);
+  const int d0 = kCpt * ((int)blockIdx.x * kScanThreads + (int)threadIdx.x);
   if (d0 >= D) return;
   const int b = (int)blockIdx.z, c = (int)blockIdx.y;
   const int t0 = c * L, t1 = min(T, t0 + L);
-  float p[8], s[8];
+  float p[kCpt], s[kCpt];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < kCpt; ++e) {
     p[e] = 1.0f;
     s[e] = 0.0f;
   }
-#pragma unroll 4
-  for (int t = t0; t < t1; ++t) {
-    const int64_t row = ((int64_t)b * T + t) * D + d0;
-    float iv[8], fv[8];
-    load_token<DT>(i, row, iv);
-    load_token<DT>(f, row, fv);
+  scan_tokens<DT, L>(i, f, (int64_t)b * T * D + d0, D, t0, t1,
+                  [&](int, const float *a, const float *iv) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float a = gate_of(fv[e]);
-      s[e] = a * s[e] + (1.0f - a) * iv[e];
-      p[e] = p[e] * a;
-    }
-  }
+                    for (int e = 0; e < kCpt; ++e) {
+                      s[e] = a[e] * s[e] + (1.0f - a[e]) * iv[e];
+                      p[e] = p[e] * a[e];
+                    }
+                  });
   const int64_t o = ((int64_t)b * C + c) * D + d0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    P[o + e] = p[e];
-    S[o + e] = s[e];
-  }
+  *reinterpret_cast<float2 *>(P + o) = make_float2(p[0], p[1]);
+  *reinterpret_cast<float2 *>(S + o) = make_float2(s[0], s[1]);
 }
 
-// 2. The chunk start states of sequence b, channel d, written over S.
+// 2. The chunk start states of sequence b, channel d, written over S.  The
+// chain is C dependent steps; the loads of each batch of kCarryBatch chunks
+// go out together (they do not depend on the state), so the chain pays one
+// memory latency per batch instead of one per chunk.
+constexpr int kCarryBatch = 32;
 __global__ __launch_bounds__(kScanThreads) void mlgru_carry_kernel(const float *__restrict__ h0,
                                                                    int B, int D, int C,
                                                                    const float *__restrict__ P,
@@ -113,74 +182,84 @@ __global__ __launch_bounds__(kScanThreads) void mlgru_carry_kernel(const float *
   const int64_t bd = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
   if (bd >= (int64_t)B * D) return;
   const int64_t b = bd / D, d = bd - b * D;
+  const float *Pb = P + b * C * D + d;
+  float *Sb = S + b * C * D + d;
   float H = h0 ? h0[bd] : 0.0f;
-  for (int c = 0; c < C; ++c) {
-    const int64_t o = (b * C + c) * D + d;
-    const float p = P[o], s = S[o];
-    S[o] = H;
-    H = p * H + s;
+  for (int c0 = 0; c0 < C; c0 += kCarryBatch) {
+    float p[kCarryBatch], s[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      const int c = min(c0 + j, C - 1);   // past the end: a repeat, never used
+      p[j] = Pb[(int64_t)c * D];
+      s[j] = Sb[(int64_t)c * D];
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j)
+      if (c0 + j < C) {
+        Sb[(int64_t)(c0 + j) * D] = H;
+        H = p[j] * H + s[j];
+      }
   }
 }
 
 // 3. The chunk run from its start state (Hs[(b C + c) D + d], or h0 / zero
 // when Hs is null -- one chunk per sequence), storing h and, in the last
 // chunk, hT.
-template <int DT>
+template <int DT, int L>
 __global__ __launch_bounds__(kScanThreads) void mlgru_apply_kernel(
-    const void *__restrict__ i, const void *__restrict__ f, int T, int D, int L, int C,
+    const void *__restrict__ i, const void *__restrict__ f, int T, int D, int C,
     const float *__restrict__ Hs, const float *__restrict__ h0, void *__restrict__ h,
     float *__restrict__ hT) {
-  const int d0 = 8 * ((int)blockIdx.x * kScanThreads + (int)threadIdx.x);
+  const int d0 = kCpt * ((int)blockIdx.x * kScanThreads + (int)threadIdx.x);
   if (d0 >= D) return;
   const int b = (int)blockIdx.z, c = (int)blockIdx.y;
   const int t0 = c * L, t1 = min(T, t0 + L);
-  float s[8];
   const float *start = Hs ? Hs + ((int64_t)b * C + c) * D + d0 : h0 ? h0 + (int64_t)b * D + d0 : nullptr;
+  float s[kCpt];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = start ? start[e] : 0.0f;
-#pragma unroll 4
-  for (int t = t0; t < t1; ++t) {
-    const int64_t row = ((int64_t)b * T + t) * D + d0;
-    float iv[8], fv[8];
-    load_token<DT>(i, row, iv);
-    load_token<DT>(f, row, fv);
+  for (int e = 0; e < kCpt; ++e) s[e] = start ? start[e] : 0.0f;
+  const int64_t row0 = (int64_t)b * T * D + d0;
+  scan_tokens<DT, L>(i, f, row0, D, t0, t1, [&](int t, const float *a, const float *iv) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float a = gate_of(fv[e]);
-      s[e] = a * s[e] + (1.0f - a) * iv[e];
-    }
-    store_token<DT>(h, row, s);
-  }
+    for (int e = 0; e < kCpt; ++e) s[e] = a[e] * s[e] + (1.0f - a[e]) * iv[e];
+    store_pair<DT>(h, row0 + (int64_t)t * D, s);
+  });
   if (hT && c == C - 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hT[(int64_t)b * D + d0 + e] = s[e];
+    for (int e = 0; e < kCpt; ++e) hT[(int64_t)b * D + d0 + e] = s[e];
   }
 }
 
-template <int DT>
-hipError_t launch_t(const MlgruArgs &a, hipStream_t stream) {
+template <int DT, int L>
+hipError_t launch_l(const MlgruArgs &a, hipStream_t stream) {
   const int T = (int)a.T, D = (int)a.D, B = (int)a.B;
-  const int C = (T + kMlgruChunk - 1) / kMlgruChunk;
-  const dim3 grid((unsigned)((D / 8 + kScanThreads - 1) / kScanThreads), (unsigned)C, (unsigned)B);
+  const int C = (T + L - 1) / L;
+  const dim3 grid((unsigned)((D / kCpt + kScanThreads - 1) / kScanThreads), (unsigned)C, (unsigned)B);
   if (C == 1) {
-    mlgru_apply_kernel<DT><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, kMlgruChunk, 1,
-                                                              nullptr, a.h0, a.h, a.hT);
+    mlgru_apply_kernel<DT, L><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, 1, nullptr, a.h0,
+                                                                 a.h, a.hT);
     return hipGetLastError();
   }
   float *P = static_cast<float *>(a.ws);
   float *S = P + (int64_t)B * C * D;
-  mlgru_chunk_kernel<DT><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, kMlgruChunk, C, P, S);
+  mlgru_chunk_kernel<DT, L><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, C, P, S);
   const unsigned cgrid = (unsigned)(((int64_t)B * D + kScanThreads - 1) / kScanThreads);
   mlgru_carry_kernel<<<cgrid, kScanThreads, 0, stream>>>(a.h0, B, D, C, P, S);
-  mlgru_apply_kernel<DT><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, kMlgruChunk, C, S,
-                                                            a.h0, a.h, a.hT);
+  mlgru_apply_kernel<DT, L><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, C, S, a.h0, a.h,
+                                                               a.hT);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_t(const MlgruArgs &a, hipStream_t stream) {
+  return mlgru_chunk_len(a.T) == 64 ? launch_l<DT, 64>(a, stream) : launch_l<DT, 32>(a, stream);
 }
 
 }  // namespace
 
 size_t mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D) {
-  const int64_t C = (T + kMlgruChunk - 1) / kMlgruChunk;
+  const int64_t L = mlgru_chunk_len(T);
+  const int64_t C = (T + L - 1) / L;
   return C <= 1 ? 0 : (size_t)(2 * B * C * D) * sizeof(float);
 }
 

@@ -559,10 +559,12 @@ def test_gate_entry_points_validation():
 
 def test_mlgru_workspace_closed_form():
     L = tw.lib()
-    # 2 B C D floats with C = ceil(T / 32) chunks; none for one chunk
+    # 2 B C D floats with C = ceil(T / L) chunks, L = 32 (64 from 4096
+    # steps); none for one chunk
     assert L.bitlinear_mlgru_workspace_bytes(1, 32, 2560) == 0
     assert L.bitlinear_mlgru_workspace_bytes(1, 33, 2560) == 2 * 1 * 2 * 2560 * 4
-    assert L.bitlinear_mlgru_workspace_bytes(4, 8192, 2048) == 2 * 4 * 256 * 2048 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(4, 4095, 2048) == 2 * 4 * 128 * 2048 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(4, 8192, 2048) == 2 * 4 * 128 * 2048 * 4
     assert L.bitlinear_mlgru_workspace_bytes(1, 100, 12) == 0       # D % 8 != 0: invalid
     assert L.bitlinear_mlgru_workspace_bytes(-1, 100, 16) == 0
 
@@ -570,9 +572,9 @@ def test_mlgru_workspace_closed_form():
 def test_mlgru_scan_validation():
     L = tw.lib()
     sc = L.bitlinear_mlgru_scan
-    wsb = L.bitlinear_mlgru_workspace_bytes(2, 100, 64)
+    wsb = L.bitlinear_mlgru_workspace_bytes(2, 300, 64)
 
-    def call(i=A, f=B, dt=2, Bn=2, T=100, Dn=64, h0=None, h=Y, hT=None, ws=WSP, wsb=wsb):
+    def call(i=A, f=B, dt=2, Bn=2, T=300, Dn=64, h0=None, h=Y, hT=None, ws=WSP, wsb=wsb):
         return sc(i, f, dt, Bn, T, Dn, h0, h, hT, ws, wsb, None)
 
     assert call(dt=7) == DTYPE

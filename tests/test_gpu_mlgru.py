@@ -57,11 +57,12 @@ def _run(i, f, h0, dt, with_h0=True, with_hT=True):
 
 
 # one chunk (T <= 32) is one launch; past it three (chunks of 32, the last
-# ragged); D covers one and several 2048-channel workgroups, ragged ones and
-# the 8-channel minimum
+# ragged; 64 from 4096 steps); D covers one and several 512-channel
+# workgroups, ragged ones and the 8-channel minimum
 CASES = [(1, 1, 8, "bf16", True), (2, 1, 2560, "fp16", True), (1, 32, 64, "fp16", False),
-         (1, 33, 520, "bf16", True), (2, 100, 2056, "fp32", True), (3, 257, 24, "bf16", False),
-         (4, 64, 2048, "fp16", True), (1, 1000, 2560, "bf16", True), (2, 96, 4104, "bf16", True)]
+         (1, 33, 520, "bf16", True), (2, 300, 1032, "fp32", True), (3, 257, 24, "bf16", False),
+         (4, 256, 2048, "fp16", True), (1, 1000, 2560, "bf16", True), (2, 400, 4104, "bf16", True),
+         (1, 4100, 136, "fp16", True)]
 
 
 @pytest.mark.parametrize("B,T,D,dt,with_h0", CASES)
@@ -103,9 +104,9 @@ def test_mlgru_scan_continues_from_its_final_state():
     """Two calls, the second from the first's hT, against one call over the
     whole sequence: the same function (both within the bar of the oracle),
     the way a decode step continues a prefill."""
-    B, T, D = 2, 77, 264
+    B, T, D = 2, 300, 264
     i, f, h0 = _inputs(5, B, T, D, "fp16")
-    t0 = 45
+    t0 = 173
     h_a, hT_a = _run(i[:, :t0].contiguous(), f[:, :t0].contiguous(), h0, "fp16")
     h_b, hT_b = _run(i[:, t0:].contiguous(), f[:, t0:].contiguous(), hT_a.cpu(), "fp16")
     ref, refT = oracle.mlgru_scan(synth.widen(i), synth.widen(f), synth.widen(h0).astype(np.float64))
