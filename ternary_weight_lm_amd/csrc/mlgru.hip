@@ -19,8 +19,9 @@
 // width, one sequence: 8192 steps 55.8 / 49.1 / 52.7 us per scan at L = 32 /
 // 64 / 128, 512 steps 12.9 / 18.4 / 30.1 us).  Three launches over [B, T, D]:
 //   1. per (sequence, chunk, 2 channels): P and S of the chunk;
-//   2. per (sequence, channel): the chunk start states, walking the chunks
-//      in order (H_{c+1} = P_c H_c + S_c), written over S;
+//   2. per (sequence, channel): the chunk start states (H_{c+1} = P_c H_c +
+//      S_c), composed over groups of 32 chunks in parallel and chained
+//      across the groups, written over S;
 //   3. per (sequence, chunk, 2 channels): the chunk run again from its start
 //      state, storing h (and, in the last chunk, the final state hT).
 // A sequence of at most L steps is launch 3 alone, from h0.  A thread holds
@@ -170,35 +171,93 @@ __global__ __launch_bounds__(kScanThreads) void mlgru_chunk_kernel(const void *_
   *reinterpret_cast<float2 *>(S + o) = make_float2(s[0], s[1]);
 }
 
-// 2. The chunk start states of sequence b, channel d, written over S.  The
-// chain is C dependent steps; the loads of each batch of kCarryBatch chunks
-// go out together (they do not depend on the state), so the chain pays one
-// memory latency per batch instead of one per chunk.
-constexpr int kCarryBatch = 32;
-__global__ __launch_bounds__(kScanThreads) void mlgru_carry_kernel(const float *__restrict__ h0,
-                                                                   int B, int D, int C,
-                                                                   const float *__restrict__ P,
-                                                                   float *__restrict__ S) {
+// 2. (at most kCarryPerGroup chunks) The chunk start states of sequence b,
+// channel d, written over S: one thread per pair walks the chunks in order,
+// their P and S loaded together first.
+constexpr int kCarryPerGroup = 32;   // chunks a thread loads at once
+__global__ __launch_bounds__(kScanThreads) void mlgru_carry_short_kernel(
+    const float *__restrict__ h0, int B, int D, int C, const float *__restrict__ P,
+    float *__restrict__ S) {
   const int64_t bd = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
   if (bd >= (int64_t)B * D) return;
   const int64_t b = bd / D, d = bd - b * D;
   const float *Pb = P + b * C * D + d;
   float *Sb = S + b * C * D + d;
   float H = h0 ? h0[bd] : 0.0f;
-  for (int c0 = 0; c0 < C; c0 += kCarryBatch) {
-    float p[kCarryBatch], s[kCarryBatch];
+  float p[kCarryPerGroup], s[kCarryPerGroup];
 #pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      const int c = min(c0 + j, C - 1);   // past the end: a repeat, never used
-      p[j] = Pb[(int64_t)c * D];
-      s[j] = Sb[(int64_t)c * D];
+  for (int j = 0; j < kCarryPerGroup; ++j) {
+    const int c = min(j, C - 1);   // past the end: a repeat, never used
+    p[j] = Pb[(int64_t)c * D];
+    s[j] = Sb[(int64_t)c * D];
+  }
+#pragma unroll
+  for (int j = 0; j < kCarryPerGroup; ++j)
+    if (j < C) {
+      Sb[(int64_t)j * D] = H;
+      H = p[j] * H + s[j];
     }
+}
+
+// 2. (more chunks) The chunk start states, written over S.  A workgroup takes 32
+// channels (of the B D sequence-channel pairs) and their chunks in windows
+// of kCarryGroups x 32: group g of its threads composes chunks
+// 32 g .. 32 g + 31 of the window into one map (their P and S loaded
+// together, one memory latency), the window's group maps are chained in
+// LDS by the first group (8 steps, carrying each channel's state from the
+// window before), and every group then walks its chunks from its start
+// state, storing each chunk's.  The carry pays a few memory latencies per
+// 256 chunks instead of one per chunk.
+constexpr int kCarryGroups = kScanThreads / 32;   // 8
+__global__ __launch_bounds__(kScanThreads) void mlgru_carry_kernel(const float *__restrict__ h0,
+                                                                   int B, int D, int C,
+                                                                   const float *__restrict__ P,
+                                                                   float *__restrict__ S) {
+  __shared__ float s_p[kCarryGroups][32], s_s[kCarryGroups][32];
+  const int g = (int)threadIdx.x >> 5, dl = (int)threadIdx.x & 31;
+  const int64_t bd = (int64_t)blockIdx.x * 32 + dl;
+  const bool live = bd < (int64_t)B * D;
+  const int64_t b = live ? bd / D : 0, d = live ? bd - b * D : 0;
+  const float *Pb = P + b * C * D + d;
+  float *Sb = S + b * C * D + d;
+  float H = (live && h0) ? h0[bd] : 0.0f;   // the running state (group 0's threads)
+  for (int w0 = 0; w0 < C; w0 += kCarryGroups * kCarryPerGroup) {
+    const int c0 = w0 + g * kCarryPerGroup;
+    float p[kCarryPerGroup], s[kCarryPerGroup];
 #pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j)
+    for (int j = 0; j < kCarryPerGroup; ++j) {
+      const int c = min(c0 + j, C - 1);   // past the end: a repeat, never used
+      p[j] = live ? Pb[(int64_t)c * D] : 1.0f;
+      s[j] = live ? Sb[(int64_t)c * D] : 0.0f;
+    }
+    // this group's map over its chunks: H -> pg H + sg
+    float pg = 1.0f, sg = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCarryPerGroup; ++j)
       if (c0 + j < C) {
-        Sb[(int64_t)(c0 + j) * D] = H;
-        H = p[j] * H + s[j];
+        sg = p[j] * sg + s[j];
+        pg = p[j] * pg;
       }
+    s_p[g][dl] = pg;
+    s_s[g][dl] = sg;
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int k = 0; k < kCarryGroups; ++k) {
+        const float pk = s_p[k][dl], sk = s_s[k][dl];
+        s_s[k][dl] = H;   // group k's start state
+        H = pk * H + sk;
+      }
+    }
+    __syncthreads();
+    float Hg = s_s[g][dl];
+#pragma unroll
+    for (int j = 0; j < kCarryPerGroup; ++j)
+      if (live && c0 + j < C) {
+        Sb[(int64_t)(c0 + j) * D] = Hg;
+        Hg = p[j] * Hg + s[j];
+      }
+    __syncthreads();   // s_s is rewritten by the next window
   }
 }
 
@@ -243,8 +302,13 @@ hipError_t launch_l(const MlgruArgs &a, hipStream_t stream) {
   float *P = static_cast<float *>(a.ws);
   float *S = P + (int64_t)B * C * D;
   mlgru_chunk_kernel<DT, L><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, C, P, S);
-  const unsigned cgrid = (unsigned)(((int64_t)B * D + kScanThreads - 1) / kScanThreads);
-  mlgru_carry_kernel<<<cgrid, kScanThreads, 0, stream>>>(a.h0, B, D, C, P, S);
+  if (C <= kCarryPerGroup) {
+    const unsigned cgrid = (unsigned)(((int64_t)B * D + kScanThreads - 1) / kScanThreads);
+    mlgru_carry_short_kernel<<<cgrid, kScanThreads, 0, stream>>>(a.h0, B, D, C, P, S);
+  } else {
+    const unsigned cgrid = (unsigned)(((int64_t)B * D + 31) / 32);
+    mlgru_carry_kernel<<<cgrid, kScanThreads, 0, stream>>>(a.h0, B, D, C, P, S);
+  }
   mlgru_apply_kernel<DT, L><<<grid, kScanThreads, 0, stream>>>(a.i, a.f, T, D, C, S, a.h0, a.h,
                                                                a.hT);
   return hipGetLastError();

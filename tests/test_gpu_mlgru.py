@@ -57,12 +57,14 @@ def _run(i, f, h0, dt, with_h0=True, with_hT=True):
 
 
 # one chunk (T <= 32) is one launch; past it three (chunks of 32, the last
-# ragged; 64 from 4096 steps); D covers one and several 512-channel
-# workgroups, ragged ones and the 8-channel minimum
+# ragged; 64 from 4096 steps), the carry in one batch up to 32 chunks, else
+# in groups of 32 chunks over windows of 256 (20000 steps: two windows); D
+# covers one and several 512-channel workgroups, ragged ones and the
+# 8-channel minimum
 CASES = [(1, 1, 8, "bf16", True), (2, 1, 2560, "fp16", True), (1, 32, 64, "fp16", False),
          (1, 33, 520, "bf16", True), (2, 300, 1032, "fp32", True), (3, 257, 24, "bf16", False),
          (4, 256, 2048, "fp16", True), (1, 1000, 2560, "bf16", True), (2, 400, 4104, "bf16", True),
-         (1, 4100, 136, "fp16", True)]
+         (1, 4100, 136, "fp16", True), (1, 2000, 40, "fp32", True), (2, 20000, 16, "bf16", True)]
 
 
 @pytest.mark.parametrize("B,T,D,dt,with_h0", CASES)
