@@ -77,8 +77,8 @@ TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; 
     "c2": ("decode", "22a7bba0bac5f177", 647950),
     "c3": ("skinny", "4474cdc02a05004c", 4662275),
     "c4": ("gemm", "3ce42a83e7adff85", 87286944),
-    "c5-M8192-mlgru": ("mlgru", "a335322fa510d238", 218206431),
-    "c5-M512-mlgru": ("mlgru", "a335322fa510d238", 14434392),
+    "c5-M8192-mlgru": ("mlgru", "4fbba9ecee82c2d9", 218206431),
+    "c5-M512-mlgru": ("mlgru", "4fbba9ecee82c2d9", 14434392),
 }
 
 

@@ -16,12 +16,14 @@
 // to P H + S (P the product of the chunk's gates, S the chunk run from
 // zero).  L = 32, or 64 from 4096 steps: shorter chunks put more waves on
 // the two streaming launches, longer ones shorten the carry's chain (2.7B
-// width, one sequence: 8192 steps 55.8 / 49.1 / 52.7 us per scan at L = 32 /
-// 64 / 128, 512 steps 12.9 / 18.4 / 30.1 us).  Three launches over [B, T, D]:
+// width, one sequence, the carry then walking the chunks in order: 8192
+// steps 55.8 / 49.1 / 52.7 us per scan at L = 32 / 64 / 128, 512 steps
+// 12.9 / 18.4 / 30.1 us).  Three launches over [B, T, D]:
 //   1. per (sequence, chunk, 2 channels): P and S of the chunk;
 //   2. per (sequence, channel): the chunk start states (H_{c+1} = P_c H_c +
-//      S_c), composed over groups of 32 chunks in parallel and chained
-//      across the groups, written over S;
+//      S_c), written over S -- up to 32 chunks walked in order, more
+//      composed over groups of 32 chunks in parallel and chained across the
+//      groups;
 //   3. per (sequence, chunk, 2 channels): the chunk run again from its start
 //      state, storing h (and, in the last chunk, the final state hT).
 // A sequence of at most L steps is launch 3 alone, from h0.  A thread holds
