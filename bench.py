@@ -108,7 +108,7 @@ def parse(argv=None):
     ap.add_argument("--workload", default="c5",
                     help="c5 (2.7B stack, M sweep) | c5-M<M> | c1 | c2 | c3 | c4, an MLP "
                          "workload c3-mlp | c4-mlp | c5-M<M>-mlp, the gated o_proj c5-M<M>-gate, "
-                         "or the MLGRU scan c5-M<M>-mlgru")
+                         "the MLGRU scan c5-M<M>-mlgru, or whole HGRNBit blocks c5-M<M>-block")
     ap.add_argument("--launch", choices=["per-call", "chain"], default="per-call",
                     help="per-call: one launch group per projection (default); chain: a "
                          "chained stack at 1..4 tokens runs as one persistent launch per step "
@@ -807,6 +807,131 @@ def run_mlgru(args):
     print(json.dumps(out), flush=True)
 
 
+def run_block(args):
+    """The 2.7B stack as whole HGRNBit blocks (ternary_weight_lm_amd.block):
+    per layer i/f/g grouped on the block input, the MLGRU scan of i and f,
+    o_proj behind the swish gate of (h, g), gate_proj + GLU and down_proj,
+    whose output is the next layer's input.  M >= 512 tokens: one sequence
+    of M steps; fewer: M sequences of one step each, the scan continuing from
+    each sequence's state.  Workloads c5-M<M>-block (32 layers)."""
+    import numpy as np
+    import torch
+    import ternary_weight_lm_amd as tw
+    from ternary_weight_lm_amd import synth
+    from ternary_weight_lm_amd.block import Block
+    import oracle
+
+    base = args.workload[:-len("-block")]
+    cfg = synth.CONFIGS["c5"]
+    M = int(base.split("-M")[1])
+    layers = cfg.layers
+    names = [p.name for p in cfg.projs]
+    D = cfg.projs[names.index("i_proj")].N
+    F = cfg.projs[names.index("down_proj")].K
+    dev = torch.device("cuda:0")
+    blocks, host = [], None
+    for layer in range(layers):
+        W, gain = {}, {}
+        for n in Block.NAMES:
+            _, gain[n], W[n] = synth.config_inputs(cfg, 1, layer, names.index(n))
+        if layer == 0:
+            host = (W, gain)
+        gate_w = synth.make_gain(cfg.seed, layer, len(names), D, cfg.dtype)
+        blocks.append(Block(W, gain, gate_w, device=dev))
+    seqs = 1 if M >= 512 else M
+    bufs = [blk.buffers(M, sequences=seqs, device=dev) for blk in blocks]
+    bufs[0]["x"].copy_(synth.make_x(cfg.seed, 0, 0, M, D, cfg.dtype).to(dev))
+    for layer in range(1, layers):          # layer l reads layer l - 1's output
+        bufs[layer]["x"] = bufs[layer - 1]["y"]
+        calls = [(bufs[layer]["x"], blocks[layer].gain[n], blocks[layer].packed[n],
+                  blocks[layer].beta[n], bufs[layer][n[0]]) for n in ("i_proj", "f_proj", "g_proj")]
+        bufs[layer]["calls"] = tw.make_calls(calls)
+    torch.cuda.synchronize()
+
+    def step(s, keep):
+        for layer in range(layers):
+            blocks[layer].step(bufs[layer])
+
+    per_layer = 12   # launches per block at most
+    big = M >= 512
+    steps = args.steps if args.steps is not None else (10 if big else 50)
+    warmup = args.warmup if args.warmup is not None else (2 if big else 5)
+    for gr, _ in capture(step, 0, warmup, per_layer * layers):
+        gr.replay()
+    ms = timed_replay(capture(step, warmup, steps, per_layer * layers))
+    sec = ms / 1e3
+    proj_nk = 4 * D * D + 2 * F * D + F * D                      # weights per layer
+    if big:
+        ops = 2 * M * proj_nk * layers * steps
+        ach = ops / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(ach / I8_PEAK_TOPS, 5), "ops_per_step": ops // steps}
+    else:
+        byt = (proj_nk // 4 + M * 2 * (3 * D + D + D + D + F + F) + 16 * M * D) * layers * steps
+        ach = byt / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 5), "algorithmic_bytes_per_step": byt // steps}
+    roof.update({"traffic": None,
+                 "kernel": "whole block step (every launch of the 32 blocks: i/f/g, scan, gated "
+                           "o_proj, gate_proj + GLU, down_proj)",
+                 "timed_region": "the benchmark steps; the roofline counts every projection's "
+                                 + ("int8 ops" if big else "weight and activation bytes")
+                                 + " against the whole step's time"})
+    out = {
+        "metric": METRIC, "value": round(M * steps / sec, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name.replace('_Msweep', '')}_M{M}_hgrn_blocks",
+                   "tokens_per_step": M, "layers": layers, "sequences": seqs,
+                   "steps_per_sequence": M // seqs, "x_dtype": cfg.dtype,
+                   "block": "i/f/g grouped -> MLGRU scan -> FusedRMSNormSwishGate + o_proj -> "
+                            "gate_proj + GLU -> down_proj",
+                   "launch": "hipGraph; per layer ternary_weight_lm_amd.block.Block.step",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        facts = host_facts()
+        W0, g0 = host
+        packs = {}
+        for n in Block.NAMES:
+            Wn = W0[n].numpy()
+            packs[n] = (oracle.pack_glu_weights(Wn) if n == "gate_proj" else oracle.pack_weights(Wn))[1:]
+        gw0 = synth.widen(synth.make_gain(cfg.seed, 0, len(names), D, cfg.dtype))
+        rows = min(M, 8)
+        x = synth.widen(synth.make_x(cfg.seed, 0, 0, rows, D, cfg.dtype))
+        gn = {n: synth.widen(g0[n]) for n in Block.NAMES}
+        old = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {facts["pinned_core"]})
+        try:
+            t0, n = time.perf_counter(), 0
+            while True:
+                y = {k: oracle.forward(x, gn[k], *packs[k][::-1])["y"].astype(np.float32)
+                     for k in ("i_proj", "f_proj", "g_proj")}
+                # the rows as one sequence of `rows` steps: the scan needs every step
+                h, _ = oracle.mlgru_scan(y["i_proj"][None], y["f_proj"][None])
+                z = oracle.rmsnorm_swish_gate(h[0].astype(np.float32), y["g_proj"], gw0,
+                                              eps=GATE_EPS).astype(np.float32)
+                o = oracle.forward(z, gn["o_proj"], *packs["o_proj"][::-1])["y"].astype(np.float32)
+                m = oracle.forward_glu(o, gn["gate_proj"], *packs["gate_proj"][::-1])["h"]
+                oracle.forward(m.astype(np.float32), gn["down_proj"], *packs["down_proj"][::-1])
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        finally:
+            os.sched_setaffinity(0, old)
+        out["cpu_baseline"] = {
+            "value": round(rows * n / el / layers, 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} passes of {rows} of {M} token rows through one block ({el:.1f} s "
+                      f"single-threaded; scaled to {layers} blocks)",
+            "host": {"nproc": facts["nproc"], "cpu_model": facts["model"],
+                     "pinned": f"core {facts['pinned_core']}"}}
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def host_facts():
@@ -1041,6 +1166,9 @@ def main():
         return
     if args.workload.endswith("-mlgru"):
         run_mlgru(args)
+        return
+    if args.workload.endswith("-block"):
+        run_block(args)
         return
 
     sweep = args.workload == "c5"

@@ -315,7 +315,8 @@ size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);
  * the row order of the i_proj and f_proj outputs).
  *   h0  device fp32 [B, D] start state, or NULL for zeros (read only)
  *   hT  device fp32 [B, D] written with the state after step T - 1
- *       (bit-identical to h[:, T-1, :] before rounding), or NULL
+ *       (bit-identical to h[:, T-1, :] before rounding), or NULL; it may
+ *       be h0 itself (the state carried from call to call in place)
  *   ws  device scratch of >= bitlinear_mlgru_workspace_bytes(B, T, D) bytes
  *       (16-byte aligned; may be NULL when that is 0)
  * Shapes: 0 <= B <= 65535, 0 <= T <= 2^20, 0 <= D <= 65536, D % 8 == 0
