@@ -54,9 +54,9 @@ namespace bl {
 // kb: the k-block multiplied now; kend: one past the last k-block of this
 // wave's range (loads clamp to it, k-blocks at or past it are trips that
 // only keep the barriers in step with the other groups: CHECK = KG > 1).
-template <int MI, int TPW, bool CHECK>
+template <int MI, int WR, int TPW, bool CHECK>
 __device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur, uint8_t *next,
-                                            v4i (&acc)[MI][2 * TPW], v4i (&a_store)[MI],
+                                            v4i (&acc)[WR][2 * TPW], v4i (&a_store)[MI],
                                             v4i (&a_load)[MI], v4i (&b)[TPW],
                                             rsrc_t ars, const int (&a_voff)[MI],
                                             const int (&a_dst)[MI], rsrc_t brs, int b_voff,
@@ -71,9 +71,9 @@ __device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur
     a_load[j] = __builtin_bit_cast(
         v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k2 * 128, 0));
   __builtin_amdgcn_sched_barrier(0);
-  v4i a[MI][2];
+  v4i a[WR][2];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mi = 0; mi < WR; ++mi) {
     const int row = arow0 + 16 * mi;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -100,7 +100,7 @@ __device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur
       const v4i w0 = unpack_codes(s2 ? b[t].y : b[t].x);
       const v4i w1 = unpack_codes(s2 ? b[t].w : b[t].z);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
+      for (int mi = 0; mi < WR; ++mi) {
         acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
         acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
       }
@@ -134,9 +134,9 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint8_t *lds, int voffset, 
 // the loads issued after it (B(kb+2), A(kb+2), B(kb+3)) stay in flight.
 // The barrier is a plain s_barrier: a workgroup fence would also wait for
 // every load still in flight.
-template <int MI, int TPW, bool TAIL>
+template <int MI, int WR, int TPW, bool TAIL>
 __device__ __forceinline__ void gemm_kblock_dma(int kb, int kend, const uint8_t *cur,
-                                                uint8_t *dst, v4i (&acc)[MI][2 * TPW],
+                                                uint8_t *dst, v4i (&acc)[WR][2 * TPW],
                                                 v4i (&bc)[TPW], rsrc_t ars,
                                                 const int (&a_dma)[MI], int a_lds0, rsrc_t brs,
                                                 int b_voff, int b_tile_bytes, int arow0, int lane) {
@@ -146,9 +146,9 @@ __device__ __forceinline__ void gemm_kblock_dma(int kb, int kend, const uint8_t 
   for (int j = 0; j < MI; ++j)
     lds_load16(ars, dst + a_lds0 + 32 * 128 * j, a_dma[j], k2 * 128);
   __builtin_amdgcn_sched_barrier(0);
-  v4i a[MI][2];
+  v4i a[WR][2];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mi = 0; mi < WR; ++mi) {
     const int row = arow0 + 16 * mi;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -164,7 +164,7 @@ __device__ __forceinline__ void gemm_kblock_dma(int kb, int kend, const uint8_t 
       const v4i w0 = unpack_codes(s2 ? bc[t].y : bc[t].x);
       const v4i w1 = unpack_codes(s2 ? bc[t].w : bc[t].z);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
+      for (int mi = 0; mi < WR; ++mi) {
         acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
         acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
       }
@@ -212,10 +212,18 @@ __device__ __forceinline__ void gemm_body(
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
     void *__restrict__ out, int tiles_m, int tiles_n, int t, int work) {
+  // Waves: WM x WN over the tile, each 16 WR rows x 32 TPW outputs (TPW
+  // packed tiles).  TPW = 2 or 4: 2 x 2 waves, WR = MI.  TPW = 1: 1 x 4
+  // waves, each over all the tile's rows and one packed tile, WR = 2 MI:
+  // every code word is unpacked by one wave instead of two (the 32- and
+  // 64-row tiles, whose k-blocks have few MFMAs per unpacked word).
+  constexpr int WN = TPW == 1 ? 4 : 2;
+  constexpr int WR = TPW == 1 ? 2 * MI : MI;
   constexpr int BM = 32 * MI;
-  constexpr int BN = 64 * TPW;  // a wave: 16 MI rows x 32 TPW outputs (TPW packed tiles)
+  constexpr int BN = 32 * TPW * WN;
   static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
-  static_assert(KG == 1 || TPW == 2, "the K-group reduction fits 2-tile waves only");
+  static_assert(KG == 1 || TPW <= 2, "the K-group reduction fits 1- and 2-tile waves only");
+  static_assert(16 * WR <= 64, "the epilogue's row table holds 64 rows per wave");
   // A stages: 2 per K group (filled through registers), or without K groups
   // a ring of 3 filled by buffer->LDS loads and kept as three separate
   // arrays: the compiler tells LDS objects apart, not offsets inside one,
@@ -230,7 +238,7 @@ __device__ __forceinline__ void gemm_body(
   const int kg = KG == 1 ? 0 : wave >> 2;                    // K group
   const int wq = wave & 3;                                    // wave in its group
   const int gtid = tid & 255;                                 // thread in its group
-  const int wm = wq >> 1, wn = wq & 1;
+  const int wm = wq / WN, wn = wq % WN;
 
   // Inside the sequence, tiles go column by column through bands of
   // kBandRows tile rows, so the ~64 workgroups an XCD runs at once share a
@@ -262,7 +270,7 @@ __device__ __forceinline__ void gemm_body(
     a_voff[j] = row * K + ch * 16;
     a_dst[j] = row * 128 + (swz(row, ch) << 4);
   }
-  // ---- B: the wave's two packed 32-row tiles (tiles past N read as zero:
+  // ---- B: the wave's TPW packed 32-row tiles (tiles past N read as zero:
   // their columns are never stored).
   const int nt0 = (n0 >> 5) + TPW * wn;
   const int tile_bytes = KB * 1024;
@@ -273,9 +281,9 @@ __device__ __forceinline__ void gemm_body(
   const rsrc_t brs = make_rsrc(packed + (int64_t)b_first * KB * 64, (uint32_t)b_bytes);
   const int b_voff = lane * 16;
 
-  v4i acc[MI][2 * TPW];
+  v4i acc[WR][2 * TPW];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
     for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
 
@@ -287,7 +295,7 @@ __device__ __forceinline__ void gemm_body(
   // requested while k-block kb is multiplied, and A goes through a double-
   // buffered LDS stage one iteration before use.  (Native int vectors, not
   // uint4: struct copies are lowered to memcpy through private memory.)
-  const int arow0 = wm * 16 * MI + (lane & 15);
+  const int arow0 = wm * 16 * WR + (lane & 15);
   const int kstop = kb0 + trips;
   int kb = kb0;
   if constexpr (KG == 1) {
@@ -342,18 +350,18 @@ __device__ __forceinline__ void gemm_body(
       asm volatile("" ::: "memory");
     }
     for (; kb + 2 < kstop; kb += 3) {
-      gemm_kblock_dma<MI, TPW, false>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TPW, false>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
-      gemm_kblock_dma<MI, TPW, false>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TPW, false>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
-      gemm_kblock_dma<MI, TPW, false>(kb + 2, kend, s2, s1, acc, W, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TPW, false>(kb + 2, kend, s2, s1, acc, W, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     }
     if (kb < kstop)
-      gemm_kblock_dma<MI, TPW, true>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TPW, true>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     if (kb + 1 < kstop)
-      gemm_kblock_dma<MI, TPW, true>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TPW, true>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     // the loads of the last k-blocks (clamped repeats) may still be writing
     // the stages: drain them before the epilogue reuses the LDS
@@ -391,13 +399,13 @@ __device__ __forceinline__ void gemm_body(
   // let the compiler sink the first half's prefetch loads into it.
   constexpr bool CHECK = KG > 1;
   for (; kb + 1 < kstop; kb += 2) {
-    gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+    gemm_kblock<MI, WR, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
-    gemm_kblock<MI, TPW, CHECK>(kb + 1, kend, st1, st0, acc, Q, P, Y, ars, a_voff, a_dst, brs,
+    gemm_kblock<MI, WR, TPW, CHECK>(kb + 1, kend, st1, st0, acc, Q, P, Y, ars, a_voff, a_dst, brs,
                                 b_voff, tile_bytes, arow0, lane);
   }
   if (kb < kstop)
-    gemm_kblock<MI, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+    gemm_kblock<MI, WR, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
   }
 
@@ -407,7 +415,7 @@ __device__ __forceinline__ void gemm_body(
     // accumulators, lane-contiguous per register; KG = 4 uses two slots and
     // a two-level tree (2 -> 0 and 3 -> 1, then 1 -> 0).  Every wave passes
     // every barrier.
-    constexpr int NREG = MI * 2 * TPW;
+    constexpr int NREG = WR * 2 * TPW;
     static_assert(KG * NST * BM * 128 >= (KG / 2) * 4 * NREG * 64 * 16, "reduction slots fit");
     v4i *const red = reinterpret_cast<v4i *>(&lds[0][0][0]);
     const auto slot = [&](int gs, int mi, int nb) -> v4i * {
@@ -415,13 +423,13 @@ __device__ __forceinline__ void gemm_body(
     };
     const auto put_acc = [&](int gs) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
         for (int nb = 0; nb < 2 * TPW; ++nb) *slot(gs, mi, nb) = acc[mi][nb];
     };
     const auto add_acc = [&](int gs) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
         for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] += *slot(gs, mi, nb);
     };
@@ -443,14 +451,14 @@ __device__ __forceinline__ void gemm_body(
   }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i of each 16x16 block.  The
-  // row sums and rescale factors of the wave's 16*MI rows go through a small
+  // row sums and rescale factors of the wave's 16*WR rows go through a small
   // LDS table (lane l fetches row l; one division per lane), from which each
   // lane reads its four consecutive rows with one 16-byte read (the table is
   // the wave's own: a wavefront fence, no barrier).
   __shared__ __align__(16) int e_rs[4][64];
   __shared__ __align__(16) float e_sc[4][64];
-  const int wrow0 = m0 + wm * 16 * MI;
-  if (lane < 16 * MI) {
+  const int wrow0 = m0 + wm * 16 * WR;
+  if (lane < 16 * WR) {
     const int mrow = min(wrow0 + lane, M - 1);
     e_rs[wq][lane] = rowsum[mrow];
     if constexpr (OUT != kOutI32) e_sc[wq][lane] = div_rn(*beta, s[mrow]);
@@ -458,10 +466,10 @@ __device__ __forceinline__ void gemm_body(
   wave_lds_sync();
   const int q4 = 4 * (lane >> 4);
   const int ncol0 = n0 + 32 * TPW * wn + (lane & 15);
-  v4i rs4[MI];
-  float sc4[MI][4];
+  v4i rs4[WR];
+  float sc4[WR][4];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mi = 0; mi < WR; ++mi) {
     rs4[mi] = *reinterpret_cast<const v4i *>(&e_rs[wq][16 * mi + q4]);
     const v4i t = *reinterpret_cast<const v4i *>(&e_sc[wq][16 * mi + q4]);
 #pragma unroll
@@ -481,7 +489,7 @@ __device__ __forceinline__ void gemm_body(
     const int64_t F = N >> 1;
     const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wrow0 + 16 * mi + q4 + i;
@@ -541,7 +549,7 @@ __device__ __forceinline__ void gemm_body(
     // whole tile (all but the ragged edges): no per-element checks, one row
     // offset per (mi, i) and constant column offsets
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t rowbase = (int64_t)(wrow0 + 16 * mi + q4 + i) * N + ncol0;
@@ -550,7 +558,7 @@ __device__ __forceinline__ void gemm_body(
       }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wrow0 + 16 * mi + q4 + i;
@@ -599,7 +607,7 @@ static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
                             const float *s, const void *packed,
                             const float *beta, int64_t M, int64_t N, int64_t K,
                             void *out, int out_kind, bool glu, hipStream_t stream) {
-  const int BM = 32 * MI, BN = 64 * TPW;
+  const int BM = 32 * MI, BN = TPW == 1 ? 128 : 64 * TPW;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
@@ -635,39 +643,47 @@ static hipError_t launch_mi(const int8_t *xq, const int32_t *rowsum,
 // three (M = 4096, N = 2048: 512 tiles, two per CU, against 688 of 96 rows:
 // 20.6 vs 21.6 us).
 constexpr int64_t kCUs = 256;
+// Packed tiles per wave of the 32- and 64-row tiles: one, the waves side by
+// side over the tile's rows (1 x 4), so each code word is unpacked once per
+// workgroup instead of twice.  Those k-blocks have few MFMAs per unpacked
+// word, and halving the unpacking measured 9-18 % faster at M = 128..1024
+// on the 2.7B and 1.3B projections (o_proj at M = 512: 9.7 -> 8.3 us,
+// down_proj 19.9 -> 16.3, i/f/g grouped 13.5 -> 12.2; c5 M = 512 +6.7 %)
+// than 2 x 2 waves of two tiles.
+constexpr int kShortTpw = 1;
 constexpr int tall_mi(int64_t t128, int64_t t96) {
   return ((t96 + kCUs - 1) / kCUs) * 3 < ((t128 + kCUs - 1) / kCUs) * 4 ? 3 : 4;
 }
 
 // K groups per workgroup for a launch of `tiles` workgroups of 32 MI rows
-// over KB k-blocks of 128.  A split pays while the launch leaves a CU about
-// one workgroup (its waves then wait on every k-block's loads): 4 groups
-// while every tile fits one 16-wave workgroup per CU, 2 groups while the
-// 8-wave workgroups still all fit at once (3 per CU at MI = 1, ~2 at MI =
-// 2), at least 4 k-blocks per group.  Measured on 2.7B shapes (us, K groups
-// 1 / 2 / 4): M = 128 o_proj 9.2 / 7.0 / 6.8, down_proj 20.4 / 13.8 / 11.6;
-// M = 256 down_proj 20.3 / 13.9 / 11.6, gate_proj 16.6 / 15.4 / 18.6; M =
-// 512 o_proj 10.3 / 9.5 / 11.9, down_proj 22.3 / 19.0 / 21.5, i/f/g grouped
-// (480 tiles of 64 rows) 13.9 / 14.5.  Taller tiles (MI >= 3, 440 and more
-// of them) measured 2-15 % slower split, and never split.
+// over KB k-blocks of 128.  A split pays only while the launch leaves a CU
+// about one workgroup (its waves then wait on every k-block's loads): up to
+// one tile per CU, 4 groups from 8 k-blocks per group, else 2 groups from
+// 4.  Past one tile per CU the unsplit waves already overlap each other's
+// loads and a split only adds the reduction.  Measured on 2.7B and 1.3B
+// shapes with the 1 x 4 wave layout (us, K groups 1 / 2 / 4): M = 128
+// down_proj (KB = 55, 80 tiles) 14.0 / 12.1 / 10.2, o_proj (KB = 20) 6.4 /
+// 6.0 / 6.2; M = 512 1.3B down_proj (KB = 44, 256 tiles) 11.2 / 10.0 / 9.2,
+// 1.3B o_proj (KB = 16) 5.8 / 5.9 / 6.0; M = 512 o_proj (320 tiles) 7.6 /
+// 8.1 / 9.1; M = 1024 o_proj (320 tiles of 64 rows) 10.2 / 12.1 / 15.9,
+// down_proj 22.2 / 25.6 / 29.0; M = 256 gate_proj (440 tiles) 12.8 / 13.9
+// / 17.9.  Taller tiles (MI >= 3) never split.
 constexpr int k_groups(int64_t tiles, int64_t KB, int MI) {
-  return MI > 2                                                      ? 1
-         : tiles <= kCUs && KB >= 16                                 ? 4
-         : tiles <= (MI == 1 ? 3 * kCUs : 7 * kCUs / 4) && KB >= 8 ? 2
-                                                                     : 1;
+  return MI > 2 || tiles > kCUs ? 1 : KB >= 32 ? 4 : KB >= 8 ? 2 : 1;
 }
 
 template <int MI>
 static hipError_t launch_mi_kg(int kg, const int8_t *xq, const int32_t *rowsum, const float *s,
                                const void *packed, const float *beta, int64_t M, int64_t N,
                                int64_t K, void *out, int out_kind, bool glu, hipStream_t stream) {
+  constexpr int TP = MI <= 2 ? kShortTpw : 2;
   if constexpr (MI <= 2) {
     if (kg == 4)
-      return launch_mi<MI, 2, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+      return launch_mi<MI, TP, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
     if (kg == 2)
-      return launch_mi<MI, 2, 2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+      return launch_mi<MI, TP, 2>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   }
-  return launch_mi<MI, 2, 1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
+  return launch_mi<MI, TP, 1>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
 }
 
 hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
@@ -675,10 +691,13 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
                             const float *beta, int64_t M, int64_t N,
                             int64_t K, void *out, int out_kind, bool glu,
                             hipStream_t stream) {
-  // The tallest tile that still gives every CU a workgroup: 128-row tiles
-  // reuse each unpacked weight operand four times, but below one tile per
-  // CU the idle CUs cost more than the extra unpacking of shorter tiles
-  // (measured at M = 512: 32-row tiles beat 64-row ones up to 256 tiles).
+  // 128-row tiles reuse each unpacked weight operand four times, but with
+  // fewer than two of them per CU the rounds run part-empty and 64-row
+  // tiles (waves side by side, each code unpacked once) win: at 256..511
+  // 128-row tiles, o_proj 2048 x 2048 at M = 2048 12.2 -> 9.6 us, down_proj
+  // 2560 x 7040 at M = 2048 36.7 -> 35.1, gate_proj 14080 x 2560 at M = 512
+  // 21.9 -> 20.6.  Below one 64-row tile per CU the same holds for 32-row
+  // tiles (measured at M = 512).
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
   // Wide launches: 128 x 256 tiles, a wave holding 4 packed tiles, so each
@@ -690,7 +709,7 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   // stays.
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) >= kWideTiles)
     return launch_mi<4, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
-  if (M > 64 && tiles(128) >= 256)
+  if (M > 64 && tiles(128) >= 512)
     return tall_mi(tiles(128), tiles(96)) == 3
                ? launch_mi<3>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream)
                : launch_mi<4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
@@ -705,7 +724,7 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
 template <int MI, int TPW = 2, int KG = 1>
 static hipError_t launch_group_mi(const GemmCalls &calls, int ncalls, int64_t M, int64_t N,
                                   int64_t K, int out_kind, hipStream_t stream) {
-  const int BM = 32 * MI, BN = 64 * TPW;
+  const int BM = 32 * MI, BN = TPW == 1 ? 128 : 64 * TPW;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * ncalls);
@@ -728,16 +747,17 @@ hipError_t launch_gemm_mfma_group(const GemmCalls &calls, int ncalls, int64_t M,
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn * ncalls; };
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) * ncalls >= kWideTiles)
     return launch_group_mi<4, 4>(calls, ncalls, M, N, K, out_kind, stream);
-  if (M > 64 && tiles(128) >= 256)
+  if (M > 64 && tiles(128) >= 512)
     return tall_mi(tiles(128), tiles(96)) == 3
                ? launch_group_mi<3>(calls, ncalls, M, N, K, out_kind, stream)
                : launch_group_mi<4>(calls, ncalls, M, N, K, out_kind, stream);
   const int64_t KB = K / 128;
   const auto go = [&](auto mi_tag, int kg) {
     constexpr int MI = decltype(mi_tag)::value;
-    if (kg == 4) return launch_group_mi<MI, 2, 4>(calls, ncalls, M, N, K, out_kind, stream);
-    if (kg == 2) return launch_group_mi<MI, 2, 2>(calls, ncalls, M, N, K, out_kind, stream);
-    return launch_group_mi<MI, 2, 1>(calls, ncalls, M, N, K, out_kind, stream);
+    constexpr int TP = MI <= 2 ? kShortTpw : 2;
+    if (kg == 4) return launch_group_mi<MI, TP, 4>(calls, ncalls, M, N, K, out_kind, stream);
+    if (kg == 2) return launch_group_mi<MI, TP, 2>(calls, ncalls, M, N, K, out_kind, stream);
+    return launch_group_mi<MI, TP, 1>(calls, ncalls, M, N, K, out_kind, stream);
   };
   if (M > 32 && tiles(64) >= 256)
     return go(std::integral_constant<int, 2>{}, k_groups(tiles(64), KB, 2));
