@@ -69,14 +69,14 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "mlgru": ["mlgru.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; per call for -mlgru)
-    "c5-M1": ("decode", "22a7bba0bac5f177", 5255327),
-    "c5-M8": ("decode", "22a7bba0bac5f177", 5792459),
-    "c5-M64": ("skinny", "4474cdc02a05004c", 8312538),
-    "c5-M512": ("gemm", "3ce42a83e7adff85", 23240033),
-    "c5-M8192": ("gemm", "3ce42a83e7adff85", 231771243),
-    "c2": ("decode", "22a7bba0bac5f177", 647950),
-    "c3": ("skinny", "4474cdc02a05004c", 4662275),
-    "c4": ("gemm", "3ce42a83e7adff85", 87286944),
+    "c5-M1": ("decode", "cd86cdfcb0546931", 5255335),
+    "c5-M8": ("decode", "cd86cdfcb0546931", 5792433),
+    "c5-M64": ("skinny", "c65ec570e0cdc386", 8312541),
+    "c5-M512": ("gemm", "9dd3cdb4cda39b67", 24119058),
+    "c5-M8192": ("gemm", "9dd3cdb4cda39b67", 231755787),
+    "c2": ("decode", "cd86cdfcb0546931", 648128),
+    "c3": ("skinny", "c65ec570e0cdc386", 4662064),
+    "c4": ("gemm", "9dd3cdb4cda39b67", 87401968),
     "c5-M8192-mlgru": ("mlgru", "4fbba9ecee82c2d9", 218206431),
     "c5-M512-mlgru": ("mlgru", "4fbba9ecee82c2d9", 14434392),
 }
