@@ -9,17 +9,20 @@
 // are fed to it as int8 and the signed sum is recovered exactly as
 //   sum_k xq * Wq = sum_k xq * c - sum_k xq      (rowsum from act-quant).
 //
-// Workgroup tile: BM = 32*MI token rows x BN = 128 output rows, K in blocks
-// of 128 (one packed tile column).  4 waves as 2 x 2; wave (wm, wn) owns
-// 16*MI rows x 64 outputs = MI x 4 MFMA blocks of 16 x 16.
-//   A (xq): global -> registers -> LDS, double-buffered, 16-byte chunks of a
-//           128-byte row XOR-swizzled (swz) so the lanes that read one column
-//           of chunks hit distinct banks.
-//   B (packed codes): each wave loads its two 1 KiB tiles per k-block
-//           straight into registers (one 16-byte load per lane per tile, the
-//           layout was built for exactly this) and unpacks them with
-//           shift + mask; no LDS traffic for weights.
-//   Loads run two k-blocks ahead of the MFMAs.
+// Workgroup tile: BM = 32*MI token rows x BN = 128 (or 256) output rows, K
+// in blocks of 128 (one packed tile column).  4 waves, either side by side
+// over all the tile's rows, each owning one (or, in 256-wide tiles, two)
+// packed 32-row tiles -- so every code word is unpacked once per workgroup
+// -- or, for 128 x 128 tiles, as 2 x 2 waves of 16*MI rows x two packed
+// tiles each.
+//   A (xq): global -> LDS (straight, by the buffer->LDS load, or through
+//           registers), 16-byte chunks of a 128-byte row XOR-swizzled (swz)
+//           so the lanes that read one column of chunks hit distinct banks.
+//   B (packed codes): each wave loads its 1 KiB tiles per k-block straight
+//           into registers (one 16-byte load per lane per tile, the layout
+//           was built for exactly this) and unpacks them with shift + mask;
+//           no LDS traffic for weights.
+//   Loads run two (A) or three (B) k-blocks ahead of the MFMAs.
 // Epilogue: subtract rowsum, multiply by beta / s_m, round to the output
 // dtype (or store the exact int32 accumulator); long launches stage 2-byte
 // output tiles through LDS for whole-row-segment stores.
@@ -42,6 +45,25 @@
 #include "bl_launch.h"
 
 namespace bl {
+
+// Unpack two consecutive code words of a lane slot (the same 16 output
+// rows, both 64-wide k halves) at once: one 64-bit shift moves both words,
+// and the bits the low word takes in from the high one land outside the
+// mask, so 3 shifts and 8 masks replace 6 shifts and 8 masks.  (Written as
+// inline shifts: left to itself the compiler splits a 64-bit shift by a
+// constant into two 32-bit ones.)  The unpack is the contraction's VALU
+// work; taking a fifth of it off measured 2-4 % faster prefill launches.
+__device__ __forceinline__ void unpack_pair(uint32_t x, uint32_t y, v4i &ux, v4i &uy) {
+  const uint64_t p = ((uint64_t)y << 32) | x;
+  uint64_t p2, p4, p6;
+  asm("v_lshrrev_b64 %0, 2, %1" : "=v"(p2) : "v"(p));
+  asm("v_lshrrev_b64 %0, 4, %1" : "=v"(p4) : "v"(p));
+  asm("v_lshrrev_b64 %0, 6, %1" : "=v"(p6) : "v"(p));
+  constexpr uint32_t M = 0x03030303u;
+  ux = v4i{(int)(x & M), (int)((uint32_t)p2 & M), (int)((uint32_t)p4 & M), (int)((uint32_t)p6 & M)};
+  uy = v4i{(int)(y & M), (int)((uint32_t)(p2 >> 32) & M), (int)((uint32_t)(p4 >> 32) & M),
+           (int)((uint32_t)(p6 >> 32) & M)};
+}
 
 // One k-block of 128: request k-block kb+2 (A into a_load, B into b0/b1
 // once they are consumed), stage k-block kb+1 (a_store) into `next`, and
@@ -92,18 +114,19 @@ __device__ __forceinline__ void gemm_kblock(int kb, int kend, const uint8_t *cur
   __builtin_amdgcn_sched_barrier(0);
   if (!CHECK || kb < kend) {
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
     for (int t = 0; t < TPW; ++t) {
       // word (h, s2) of a lane slot sits at dword 2h + s2: h = 0 is the
       // tile's first 16 rows (block 2t), h = 1 its last 16 (block 2t + 1)
-      const v4i w0 = unpack_codes(s2 ? b[t].y : b[t].x);
-      const v4i w1 = unpack_codes(s2 ? b[t].w : b[t].z);
+      v4i w[2][2];
+      unpack_pair(b[t].x, b[t].y, w[0][0], w[1][0]);
+      unpack_pair(b[t].z, b[t].w, w[0][1], w[1][1]);
 #pragma unroll
-      for (int mi = 0; mi < WR; ++mi) {
-        acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
-        acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
-      }
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mi = 0; mi < WR; ++mi) {
+          acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w[s2][0], acc[mi][2 * t]);
+          acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w[s2][1], acc[mi][2 * t + 1]);
+        }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -158,17 +181,18 @@ __device__ __forceinline__ void gemm_kblock_dma(int kb, int kend, const uint8_t 
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
+  for (int t = 0; t < TPW; ++t) {
+    v4i w[2][2];
+    unpack_pair(bc[t].x, bc[t].y, w[0][0], w[1][0]);
+    unpack_pair(bc[t].z, bc[t].w, w[0][1], w[1][1]);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const v4i w0 = unpack_codes(s2 ? bc[t].y : bc[t].x);
-      const v4i w1 = unpack_codes(s2 ? bc[t].w : bc[t].z);
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mi = 0; mi < WR; ++mi) {
-        acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w0, acc[mi][2 * t]);
-        acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w1, acc[mi][2 * t + 1]);
+        acc[mi][2 * t] = mfma16x16x64(a[mi][s2], w[s2][0], acc[mi][2 * t]);
+        acc[mi][2 * t + 1] = mfma16x16x64(a[mi][s2], w[s2][1], acc[mi][2 * t + 1]);
       }
-    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!TAIL) {
 #pragma unroll
@@ -212,18 +236,25 @@ __device__ __forceinline__ void gemm_body(
     const float *__restrict__ s, const uint4 *__restrict__ packed,
     const float *__restrict__ beta, int M, int N, int K,
     void *__restrict__ out, int tiles_m, int tiles_n, int t, int work) {
-  // Waves: WM x WN over the tile, each 16 WR rows x 32 TPW outputs (TPW
-  // packed tiles).  TPW = 2 or 4: 2 x 2 waves, WR = MI.  TPW = 1: 1 x 4
-  // waves, each over all the tile's rows and one packed tile, WR = 2 MI:
-  // every code word is unpacked by one wave instead of two (the 32- and
-  // 64-row tiles, whose k-blocks have few MFMAs per unpacked word).
-  constexpr int WN = TPW == 1 ? 4 : 2;
-  constexpr int WR = TPW == 1 ? 2 * MI : MI;
+  // Waves: WM x WN over the tile, each 16 WR rows x 32 TW outputs (TW
+  // packed tiles).  TPW = 2 (128 x 128 tiles): 2 x 2 waves of two tiles,
+  // WR = MI.  TPW = 1 (32- and 64-row tiles) and TPW = 4 (128 x 256 tiles):
+  // 1 x 4 waves side by side, each over all the tile's rows and one resp.
+  // two packed tiles, WR = 2 MI: every code word is unpacked by one wave
+  // instead of two, for twice the LDS reads of A.  The unpack is VALU work
+  // beside the MFMAs, and halving it measured faster wherever the LDS keeps
+  // up: the 32- and 64-row tiles (M = 128..1024, 9-18 %) and the 128 x 256
+  // tiles (2.7B prefill launches at M = 8192 2.3 %, the 1.3B layer at
+  // M = 4096 1.9 %, on top of the paired unpack).
+  constexpr bool SIDE = TPW == 1 || TPW == 4;  // waves side by side (1 x 4)
+  constexpr int TW = TPW == 4 ? 2 : TPW;        // packed tiles per wave
+  constexpr int WN = SIDE ? 4 : 2;
+  constexpr int WR = SIDE ? 2 * MI : MI;
   constexpr int BM = 32 * MI;
-  constexpr int BN = 32 * TPW * WN;
+  constexpr int BN = 32 * TW * WN;
   static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
   static_assert(KG == 1 || TPW <= 2, "the K-group reduction fits 1- and 2-tile waves only");
-  static_assert(16 * WR <= 64, "the epilogue's row table holds 64 rows per wave");
+  static_assert(16 * WR <= 128, "the epilogue's row table holds 128 rows per wave");
   // A stages: 2 per K group (filled through registers), or without K groups
   // a ring of 3 filled by buffer->LDS loads and kept as three separate
   // arrays: the compiler tells LDS objects apart, not offsets inside one,
@@ -270,22 +301,22 @@ __device__ __forceinline__ void gemm_body(
     a_voff[j] = row * K + ch * 16;
     a_dst[j] = row * 128 + (swz(row, ch) << 4);
   }
-  // ---- B: the wave's TPW packed 32-row tiles (tiles past N read as zero:
+  // ---- B: the wave's TW packed 32-row tiles (tiles past N read as zero:
   // their columns are never stored).
-  const int nt0 = (n0 >> 5) + TPW * wn;
+  const int nt0 = (n0 >> 5) + TW * wn;
   const int tile_bytes = KB * 1024;
   // (readfirstlane: tell the compiler these are wave-uniform, so the buffer
   // descriptor lives in scalar registers)
   const int b_first = __builtin_amdgcn_readfirstlane(min(nt0, NT));
-  const int b_bytes = __builtin_amdgcn_readfirstlane(max(0, min(TPW, NT - nt0)) * tile_bytes);
+  const int b_bytes = __builtin_amdgcn_readfirstlane(max(0, min(TW, NT - nt0)) * tile_bytes);
   const rsrc_t brs = make_rsrc(packed + (int64_t)b_first * KB * 64, (uint32_t)b_bytes);
   const int b_voff = lane * 16;
 
-  v4i acc[WR][2 * TPW];
+  v4i acc[WR][2 * TW];
 #pragma unroll
   for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < 2 * TW; ++nb) acc[mi][nb] = v4i{0, 0, 0, 0};
 
   // Without K groups A is loaded straight into a ring of three LDS stages,
   // two k-blocks ahead, and the codes three k-blocks ahead (gemm_kblock_dma;
@@ -313,15 +344,15 @@ __device__ __forceinline__ void gemm_body(
     uint8_t *const s0 = lds[0][0];
     uint8_t *const s1 = lds_r1;
     uint8_t *const s2 = lds_r2;
-    v4i U[TPW], V[TPW], W[TPW];  // codes of k-blocks = 0, 1, 2 mod 3
+    v4i U[TW], V[TW], W[TW];  // codes of k-blocks = 0, 1, 2 mod 3
     {
       // issued in the loop's own order (B(0), A(0), B(1), A(1), B(2)), so
       // the compiler's wait counts at the loop head match the steady state
       const int k1 = __builtin_amdgcn_readfirstlane(min(1, klast));
       const int k2 = __builtin_amdgcn_readfirstlane(min(2, klast));
-      const auto load_b = [&](v4i(&b)[TPW], int k) {
+      const auto load_b = [&](v4i(&b)[TW], int k) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TW; ++t)
           b[t] = __builtin_bit_cast(
               v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k * 1024, 0));
       };
@@ -350,18 +381,18 @@ __device__ __forceinline__ void gemm_body(
       asm volatile("" ::: "memory");
     }
     for (; kb + 2 < kstop; kb += 3) {
-      gemm_kblock_dma<MI, WR, TPW, false>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TW, false>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
-      gemm_kblock_dma<MI, WR, TPW, false>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TW, false>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
-      gemm_kblock_dma<MI, WR, TPW, false>(kb + 2, kend, s2, s1, acc, W, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TW, false>(kb + 2, kend, s2, s1, acc, W, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     }
     if (kb < kstop)
-      gemm_kblock_dma<MI, WR, TPW, true>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TW, true>(kb, kend, s0, s2, acc, U, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     if (kb + 1 < kstop)
-      gemm_kblock_dma<MI, WR, TPW, true>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
+      gemm_kblock_dma<MI, WR, TW, true>(kb + 1, kend, s1, s0, acc, V, ars, a_dma, a_lds0, brs, b_voff,
                                tile_bytes, arow0, lane);
     // the loads of the last k-blocks (clamped repeats) may still be writing
     // the stages: drain them before the epilogue reuses the LDS
@@ -371,7 +402,7 @@ __device__ __forceinline__ void gemm_body(
     asm volatile("" ::: "memory");
   } else {
   v4i P[MI], Q[MI];     // A staging sets
-  v4i X[TPW], Y[TPW];   // B of even / odd k-blocks
+  v4i X[TW], Y[TW];   // B of even / odd k-blocks
   uint8_t *const st0 = lds[kg][0];
   uint8_t *const st1 = lds[kg][1];
   {
@@ -383,11 +414,11 @@ __device__ __forceinline__ void gemm_body(
     for (int j = 0; j < MI; ++j)
       P[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, a_voff[j], k1 * 128, 0));
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TW; ++t)
       X[t] = __builtin_bit_cast(
           v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k0 * 1024, 0));
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TW; ++t)
       Y[t] = __builtin_bit_cast(
           v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, b_voff + t * tile_bytes, k1 * 1024, 0));
 #pragma unroll
@@ -399,13 +430,13 @@ __device__ __forceinline__ void gemm_body(
   // let the compiler sink the first half's prefetch loads into it.
   constexpr bool CHECK = KG > 1;
   for (; kb + 1 < kstop; kb += 2) {
-    gemm_kblock<MI, WR, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+    gemm_kblock<MI, WR, TW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
-    gemm_kblock<MI, WR, TPW, CHECK>(kb + 1, kend, st1, st0, acc, Q, P, Y, ars, a_voff, a_dst, brs,
+    gemm_kblock<MI, WR, TW, CHECK>(kb + 1, kend, st1, st0, acc, Q, P, Y, ars, a_voff, a_dst, brs,
                                 b_voff, tile_bytes, arow0, lane);
   }
   if (kb < kstop)
-    gemm_kblock<MI, WR, TPW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
+    gemm_kblock<MI, WR, TW, CHECK>(kb, kend, st0, st1, acc, P, Q, X, ars, a_voff, a_dst, brs, b_voff,
                                 tile_bytes, arow0, lane);
   }
 
@@ -415,23 +446,23 @@ __device__ __forceinline__ void gemm_body(
     // accumulators, lane-contiguous per register; KG = 4 uses two slots and
     // a two-level tree (2 -> 0 and 3 -> 1, then 1 -> 0).  Every wave passes
     // every barrier.
-    constexpr int NREG = WR * 2 * TPW;
+    constexpr int NREG = WR * 2 * TW;
     static_assert(KG * NST * BM * 128 >= (KG / 2) * 4 * NREG * 64 * 16, "reduction slots fit");
     v4i *const red = reinterpret_cast<v4i *>(&lds[0][0][0]);
     const auto slot = [&](int gs, int mi, int nb) -> v4i * {
-      return red + ((gs * 4 + wq) * NREG + mi * 2 * TPW + nb) * 64 + lane;
+      return red + ((gs * 4 + wq) * NREG + mi * 2 * TW + nb) * 64 + lane;
     };
     const auto put_acc = [&](int gs) {
 #pragma unroll
       for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
-        for (int nb = 0; nb < 2 * TPW; ++nb) *slot(gs, mi, nb) = acc[mi][nb];
+        for (int nb = 0; nb < 2 * TW; ++nb) *slot(gs, mi, nb) = acc[mi][nb];
     };
     const auto add_acc = [&](int gs) {
 #pragma unroll
       for (int mi = 0; mi < WR; ++mi)
 #pragma unroll
-        for (int nb = 0; nb < 2 * TPW; ++nb) acc[mi][nb] += *slot(gs, mi, nb);
+        for (int nb = 0; nb < 2 * TW; ++nb) acc[mi][nb] += *slot(gs, mi, nb);
     };
     if constexpr (KG == 2) {
       if (kg == 1) put_acc(0);
@@ -455,17 +486,22 @@ __device__ __forceinline__ void gemm_body(
   // LDS table (lane l fetches row l; one division per lane), from which each
   // lane reads its four consecutive rows with one 16-byte read (the table is
   // the wave's own: a wavefront fence, no barrier).
-  __shared__ __align__(16) int e_rs[4][64];
-  __shared__ __align__(16) float e_sc[4][64];
+  constexpr int ER = 16 * WR < 64 ? 64 : 16 * WR;
+  __shared__ __align__(16) int e_rs[4][ER];
+  __shared__ __align__(16) float e_sc[4][ER];
   const int wrow0 = m0 + wm * 16 * WR;
-  if (lane < 16 * WR) {
-    const int mrow = min(wrow0 + lane, M - 1);
-    e_rs[wq][lane] = rowsum[mrow];
-    if constexpr (OUT != kOutI32) e_sc[wq][lane] = div_rn(*beta, s[mrow]);
+#pragma unroll
+  for (int r0 = 0; r0 < 16 * WR; r0 += 64) {
+    const int r = r0 + lane;
+    if (r < 16 * WR) {
+      const int mrow = min(wrow0 + r, M - 1);
+      e_rs[wq][r] = rowsum[mrow];
+      if constexpr (OUT != kOutI32) e_sc[wq][r] = div_rn(*beta, s[mrow]);
+    }
   }
   wave_lds_sync();
   const int q4 = 4 * (lane >> 4);
-  const int ncol0 = n0 + 32 * TPW * wn + (lane & 15);
+  const int ncol0 = n0 + 32 * TW * wn + (lane & 15);
   v4i rs4[WR];
   float sc4[WR][4];
 #pragma unroll
@@ -485,7 +521,7 @@ __device__ __forceinline__ void gemm_body(
   if constexpr (GLU) {
     // tiles t0 and t0 + 1 of the wave: nb = 2p holds the gated rows of tile
     // t0 + p, nb = 2p + 1 the rows they multiply; output column 16 (t0 + p) + c
-    const int t0 = (n0 >> 5) + TPW * wn;
+    const int t0 = (n0 >> 5) + TW * wn;
     const int64_t F = N >> 1;
     const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
@@ -495,7 +531,7 @@ __device__ __forceinline__ void gemm_body(
         const int m = wrow0 + 16 * mi + q4 + i;
         if (!full && m >= M) continue;
 #pragma unroll
-        for (int pr = 0; pr < TPW; ++pr) {
+        for (int pr = 0; pr < TW; ++pr) {
           if (!full && 32 * (t0 + pr) >= N) continue;
           const float yg = (float)(acc[mi][2 * pr][i] - rs4[mi][i]) * sc4[mi][i];
           const float yu = (float)(acc[mi][2 * pr + 1][i] - rs4[mi][i]) * sc4[mi][i];
@@ -554,7 +590,7 @@ __device__ __forceinline__ void gemm_body(
       for (int i = 0; i < 4; ++i) {
         const int64_t rowbase = (int64_t)(wrow0 + 16 * mi + q4 + i) * N + ncol0;
 #pragma unroll
-        for (int nb = 0; nb < 2 * TPW; ++nb) put(mi, i, nb, rowbase + 16 * nb);
+        for (int nb = 0; nb < 2 * TW; ++nb) put(mi, i, nb, rowbase + 16 * nb);
       }
   } else {
 #pragma unroll
@@ -565,7 +601,7 @@ __device__ __forceinline__ void gemm_body(
         if (m >= M) continue;
         const int64_t rowbase = (int64_t)m * N + ncol0;
 #pragma unroll
-        for (int nb = 0; nb < 2 * TPW; ++nb)
+        for (int nb = 0; nb < 2 * TW; ++nb)
           if (ncol0 + 16 * nb < N) put(mi, i, nb, rowbase + 16 * nb);
       }
   }
