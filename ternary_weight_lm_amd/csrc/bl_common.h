@@ -279,6 +279,26 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
   return r;
 }
 
+// Unpack two consecutive code words of a lane slot (the same 16 output
+// rows, both 64-wide k halves) at once: one 64-bit shift moves both words,
+// and the bits the low word takes in from the high one land outside the
+// mask, so 3 shifts and 8 masks replace 6 shifts and 8 masks.  (Written as
+// inline shifts: left to itself the compiler splits a 64-bit shift by a
+// constant into two 32-bit ones.)  The unpack is the contraction's VALU
+// work; taking a fifth of it off measured 2-4 % faster prefill launches and
+// 0.5 % faster one-token decode launches.
+__device__ __forceinline__ void unpack_pair(uint32_t x, uint32_t y, v4i &ux, v4i &uy) {
+  const uint64_t p = ((uint64_t)y << 32) | x;
+  uint64_t p2, p4, p6;
+  asm("v_lshrrev_b64 %0, 2, %1" : "=v"(p2) : "v"(p));
+  asm("v_lshrrev_b64 %0, 4, %1" : "=v"(p4) : "v"(p));
+  asm("v_lshrrev_b64 %0, 6, %1" : "=v"(p6) : "v"(p));
+  constexpr uint32_t M = 0x03030303u;
+  ux = v4i{(int)(x & M), (int)((uint32_t)p2 & M), (int)((uint32_t)p4 & M), (int)((uint32_t)p6 & M)};
+  uy = v4i{(int)(y & M), (int)((uint32_t)(p2 >> 32) & M), (int)((uint32_t)(p4 >> 32) & M),
+           (int)((uint32_t)(p6 >> 32) & M)};
+}
+
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

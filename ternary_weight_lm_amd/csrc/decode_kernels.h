@@ -332,11 +332,14 @@ __device__ __forceinline__ void decode_body(
     for (int j = 0; j < kBatch; ++j) {
       if (t0 + j >= TPW || t0 + j >= nmine) break;
       const v4i u = wt[t0 + j];
+      // word (h, s2) of a lane slot sits at dword 2h + s2
+      v4i c[2][2];
+      unpack_pair((uint32_t)u.x, (uint32_t)u.y, c[0][0], c[1][0]);
+      unpack_pair((uint32_t)u.z, (uint32_t)u.w, c[0][1], c[1][1]);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        // word (h, s2) of a lane slot sits at dword 2h + s2
-        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
-        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
+        acc0[s2] = mfma16x16x64(a[j][s2], c[s2][0], acc0[s2]);
+        acc1[s2] = mfma16x16x64(a[j][s2], c[s2][1], acc1[s2]);
       }
     }
   }
@@ -570,10 +573,13 @@ __device__ __forceinline__ void decode_rows_body(
     for (int j = 0; j < kBatch; ++j) {
       if (t0 + j >= TPW || t0 + j >= nmine) break;
       const v4i u = wt[t0 + j];
+      v4i c[2][2];
+      unpack_pair((uint32_t)u.x, (uint32_t)u.y, c[0][0], c[1][0]);
+      unpack_pair((uint32_t)u.z, (uint32_t)u.w, c[0][1], c[1][1]);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        acc0[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.y : u.x)), acc0[s2]);
-        acc1[s2] = mfma16x16x64(a[j][s2], unpack_codes((uint32_t)(s2 ? u.w : u.z)), acc1[s2]);
+        acc0[s2] = mfma16x16x64(a[j][s2], c[s2][0], acc0[s2]);
+        acc1[s2] = mfma16x16x64(a[j][s2], c[s2][1], acc1[s2]);
       }
     }
   }

@@ -219,15 +219,16 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyLaunch<MAXC> L) {
 #pragma unroll
         for (int j = 0; j < 2 * MB; ++j) an[j] = a_load(base + t + 1, j);
       }
+      // word (h, s2) of a lane slot sits at dword 2h + s2
+      v4i b[2][2];
+      unpack_pair((uint32_t)u[0], (uint32_t)u[1], b[0][0], b[1][0]);
+      unpack_pair((uint32_t)u[2], (uint32_t)u[3], b[0][1], b[1][1]);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        // word (h, s2) of a lane slot sits at dword 2h + s2
-        const v4i b0 = unpack_codes((uint32_t)u[s2]);
-        const v4i b1 = unpack_codes((uint32_t)u[2 + s2]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          acc0[mb] = mfma16x16x64(a[mb][s2], b0, acc0[mb]);
-          acc1[mb] = mfma16x16x64(a[mb][s2], b1, acc1[mb]);
+          acc0[mb] = mfma16x16x64(a[mb][s2], b[s2][0], acc0[mb]);
+          acc1[mb] = mfma16x16x64(a[mb][s2], b[s2][1], acc1[mb]);
         }
       }
     }
