@@ -69,16 +69,16 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "mlgru": ["mlgru.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; per call for -mlgru)
-    "c5-M1": ("decode", "cd86cdfcb0546931", 5255335),
-    "c5-M8": ("decode", "cd86cdfcb0546931", 5792433),
-    "c5-M64": ("skinny", "c65ec570e0cdc386", 8312541),
-    "c5-M512": ("gemm", "9dd3cdb4cda39b67", 24119058),
-    "c5-M8192": ("gemm", "9dd3cdb4cda39b67", 231755787),
-    "c2": ("decode", "cd86cdfcb0546931", 648128),
-    "c3": ("skinny", "c65ec570e0cdc386", 4662064),
-    "c4": ("gemm", "9dd3cdb4cda39b67", 87401968),
-    "c5-M8192-mlgru": ("mlgru", "4fbba9ecee82c2d9", 218206431),
-    "c5-M512-mlgru": ("mlgru", "4fbba9ecee82c2d9", 14434392),
+    "c5-M1": ("decode", "2e1f078576729423", 5255083),
+    "c5-M8": ("decode", "2e1f078576729423", 5795852),
+    "c5-M64": ("skinny", "d143c1548c36b469", 8311517),
+    "c5-M512": ("gemm", "5a6c322db053c923", 24119061),
+    "c5-M8192": ("gemm", "5a6c322db053c923", 231448469),
+    "c2": ("decode", "2e1f078576729423", 647786),
+    "c3": ("skinny", "d143c1548c36b469", 4661840),
+    "c4": ("gemm", "5a6c322db053c923", 87170674),
+    "c5-M8192-mlgru": ("mlgru", "2fee5d5152cf33d6", 218206652),
+    "c5-M512-mlgru": ("mlgru", "2fee5d5152cf33d6", 14434410),
 }
 
 
