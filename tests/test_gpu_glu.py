@@ -81,6 +81,9 @@ CASES = [
     (tw.BL_PATH_FUSED, 16, 48, 2048, "fp32", "fp32"),
     (tw.BL_PATH_FUSED, 13, 80, 2560, "bf16", "fp16"),
     (tw.BL_PATH_FUSED, 6, 16, 7040, "bf16", "bf16"),   # past the decode kernel: skinny fused
+    # the GLU gate in 128 x 256 tiles, ragged in M and in the packed rows
+    # (2 F = 8224: the last tile column holds one packed tile), every h checked
+    (tw.BL_PATH_MFMA, 3000, 4112, 128, "bf16", "bf16"),
 ]
 
 

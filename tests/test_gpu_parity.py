@@ -264,6 +264,12 @@ FWD_CASES = [
     (tw.BL_PATH_FUSED, 10, 96, 4096, "fp16", "fp16"),
     (tw.BL_PATH_AUTO, 16, 256, 1024, "fp32", "fp32"),
     (tw.BL_PATH_FUSED, 16, 64, 2560, "fp32", "fp32"),   # fp32 past K = 2048: skinny fused
+    # 128 x 256 tiles (waves side by side, two packed tiles each), ragged in
+    # both M and N: 24 x 33 = 792 such tiles, the last tile column one packed
+    # tile wide, so one wave of it holds a tile and three hold none
+    (tw.BL_PATH_MFMA, 3000, 8224, 128, "bf16", "bf16"),
+    (tw.BL_PATH_MFMA, 3001, 8224, 256, "fp16", "fp16"),
+    (tw.BL_PATH_MFMA, 3072, 8224, 128, "fp32", "fp32"),
 ]
 
 
