@@ -69,16 +69,16 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "mlgru": ["mlgru.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; per call for -mlgru)
-    "c5-M1": ("decode", "2e1f078576729423", 5255083),
-    "c5-M8": ("decode", "2e1f078576729423", 5795852),
-    "c5-M64": ("skinny", "d143c1548c36b469", 8311517),
-    "c5-M512": ("gemm", "5a6c322db053c923", 24119061),
-    "c5-M8192": ("gemm", "5a6c322db053c923", 231448469),
-    "c2": ("decode", "2e1f078576729423", 647786),
-    "c3": ("skinny", "d143c1548c36b469", 4661840),
-    "c4": ("gemm", "5a6c322db053c923", 87170674),
-    "c5-M8192-mlgru": ("mlgru", "2fee5d5152cf33d6", 218206652),
-    "c5-M512-mlgru": ("mlgru", "2fee5d5152cf33d6", 14434410),
+    "c5-M1": ("decode", "61df0d418fe5e71c", 5255079),
+    "c5-M8": ("decode", "61df0d418fe5e71c", 5795822),
+    "c5-M64": ("skinny", "7976ad7a222d303f", 8311518),
+    "c5-M512": ("gemm", "0a05717500f6b63d", 24119065),
+    "c5-M8192": ("gemm", "0a05717500f6b63d", 231322093),
+    "c2": ("decode", "61df0d418fe5e71c", 648128),
+    "c3": ("skinny", "7976ad7a222d303f", 4661626),
+    "c4": ("gemm", "0a05717500f6b63d", 87232183),
+    "c5-M8192-mlgru": ("mlgru", "9710b4206d609eee", 225843436),
+    "c5-M512-mlgru": ("mlgru", "9710b4206d609eee", 15301697),
 }
 
 
@@ -759,7 +759,8 @@ def run_mlgru(args):
             "kernel": ("bl::mlgru_apply_kernel (one chunk per sequence: one launch per scan)"
                        if nlaunch == 1 else
                        "bl::mlgru_chunk_kernel + mlgru_carry_kernel + mlgru_apply_kernel "
-                       "(chunks of 32 steps joined through their start states)"),
+                       f"(chunks of {16 if 32 < T < 1024 else 32} steps joined through their "
+                       "start states)"),
             "launches": calls * nlaunch, "avg_call_us": round(sec * 1e6 / calls, 3),
             "algorithmic_bytes_per_call": byt,
             "timed_region": f"the benchmark steps (each call: {nlaunch} launch"

@@ -301,12 +301,12 @@ int bitlinear_rmsnorm_swish_gate(const void *o, const void *g, const void *w, in
  * という層構成を読む").  This library reads that as
  *   a = 1 / (1 + e^-f[b,t,d]),  h[b,t,d] = a h[b,t-1,d] + (1 - a) i[b,t,d],
  *   h[b,-1,d] = h0[b,d]  (zero when h0 is NULL),
- * in fp32 (hardware exp2 and reciprocal), h rounded to dtype.  Chunks of 32
- * steps (64 from T = 4096) are scanned in parallel and joined through their
- * start states (three launches; one when T fits one chunk). */
+ * in fp32 (hardware exp2 and reciprocal), h rounded to dtype.  Chunks of 16
+ * steps (for 33 <= T < 1024) or 32 are scanned in parallel and joined
+ * through their start states (three launches; one when T <= 32). */
 
 /* Workspace bytes bitlinear_mlgru_scan needs for [B, T, D]: 2 B C D floats
- * for C = ceil(T / L) chunks of L = 32 steps (64 from T = 4096); 0 when
+ * for C = ceil(T / L) chunks of L = 16 steps (33 <= T < 1024) or 32; 0 when
  * T <= 32, or for an invalid shape. */
 size_t bitlinear_mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);
 

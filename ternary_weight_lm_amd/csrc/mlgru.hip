@@ -14,11 +14,13 @@
 //
 // The recurrence is linear in h, so a chunk of L steps maps a start state H
 // to P H + S (P the product of the chunk's gates, S the chunk run from
-// zero).  L = 32, or 64 from 4096 steps: shorter chunks put more waves on
-// the two streaming launches, longer ones shorten the carry's chain (2.7B
-// width, one sequence, the carry then walking the chunks in order: 8192
-// steps 55.8 / 49.1 / 52.7 us per scan at L = 32 / 64 / 128, 512 steps
-// 12.9 / 18.4 / 30.1 us).  Three launches over [B, T, D]:
+// zero).  L = 16 for 33..1023 steps, else 32 (mlgru_chunk_len): shorter
+// chunks put more independent recurrences on the two streaming launches,
+// longer ones shorten the carry (2.7B width, one sequence: 8192 steps 46.1 /
+// 44.8 / 45.2 us per scan at L = 16 / 32 / 64, 512 steps 10.4 at L = 16
+// against 12.5 at 32; before the carry composed groups of chunks in
+// parallel, 64 was the best length at 8192 steps).  Three launches over
+// [B, T, D]:
 //   1. per (sequence, chunk, 2 channels): P and S of the chunk;
 //   2. per (sequence, channel): the chunk start states (H_{c+1} = P_c H_c +
 //      S_c), written over S -- up to 32 chunks walked in order, more
@@ -318,7 +320,7 @@ hipError_t launch_l(const MlgruArgs &a, hipStream_t stream) {
 
 template <int DT>
 hipError_t launch_t(const MlgruArgs &a, hipStream_t stream) {
-  return mlgru_chunk_len(a.T) == 64 ? launch_l<DT, 64>(a, stream) : launch_l<DT, 32>(a, stream);
+  return mlgru_chunk_len(a.T) == 16 ? launch_l<DT, 16>(a, stream) : launch_l<DT, 32>(a, stream);
 }
 
 }  // namespace

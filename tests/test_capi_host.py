@@ -559,12 +559,14 @@ def test_gate_entry_points_validation():
 
 def test_mlgru_workspace_closed_form():
     L = tw.lib()
-    # 2 B C D floats with C = ceil(T / L) chunks, L = 32 (64 from 4096
-    # steps); none for one chunk
+    # 2 B C D floats with C = ceil(T / L) chunks, L = 16 for 33..1023 steps,
+    # else 32; none for one chunk (up to 32 steps)
     assert L.bitlinear_mlgru_workspace_bytes(1, 32, 2560) == 0
-    assert L.bitlinear_mlgru_workspace_bytes(1, 33, 2560) == 2 * 1 * 2 * 2560 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(1, 33, 2560) == 2 * 1 * 3 * 2560 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(2, 1023, 64) == 2 * 2 * 64 * 64 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(2, 1024, 64) == 2 * 2 * 32 * 64 * 4
     assert L.bitlinear_mlgru_workspace_bytes(4, 4095, 2048) == 2 * 4 * 128 * 2048 * 4
-    assert L.bitlinear_mlgru_workspace_bytes(4, 8192, 2048) == 2 * 4 * 128 * 2048 * 4
+    assert L.bitlinear_mlgru_workspace_bytes(4, 8192, 2048) == 2 * 4 * 256 * 2048 * 4
     assert L.bitlinear_mlgru_workspace_bytes(1, 100, 12) == 0       # D % 8 != 0: invalid
     assert L.bitlinear_mlgru_workspace_bytes(-1, 100, 16) == 0
 

@@ -56,8 +56,8 @@ def _run(i, f, h0, dt, with_h0=True, with_hT=True):
     return h.t, hT.t if hT is not None else None
 
 
-# one chunk (T <= 32) is one launch; past it three (chunks of 32, the last
-# ragged; 64 from 4096 steps), the carry in one batch up to 32 chunks, else
+# one chunk (T <= 32) is one launch; past it three (chunks of 16 below 1024
+# steps, of 32 from there, the last ragged), the carry in one batch up to 32 chunks, else
 # in groups of 32 chunks over windows of 256 (20000 steps: two windows); D
 # covers one and several 512-channel workgroups, ragged ones and the
 # 8-channel minimum
