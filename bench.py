@@ -69,14 +69,14 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "decode_kernels.h", "decode_f32.hip",
                   "skinny": ["skinny.hip", "rowquant.h", "bl_common.h", "bl_launch.h"],
                   "mlgru": ["mlgru.hip", "bl_common.h", "bl_launch.h"]}
 TRAFFIC = {  # workload: (kernel family, sources sha256[:16], bytes per launch; per call for -mlgru)
-    "c5-M1": ("decode", "61df0d418fe5e71c", 5255079),
-    "c5-M8": ("decode", "61df0d418fe5e71c", 5795822),
-    "c5-M64": ("skinny", "7976ad7a222d303f", 8311518),
-    "c5-M512": ("gemm", "0a05717500f6b63d", 24119065),
-    "c5-M8192": ("gemm", "0a05717500f6b63d", 231322093),
+    "c5-M1": ("decode", "61df0d418fe5e71c", 5255087),
+    "c5-M8": ("decode", "61df0d418fe5e71c", 5795857),
+    "c5-M64": ("skinny", "7976ad7a222d303f", 8311517),
+    "c5-M512": ("gemm", "a4312010841b3530", 24119056),
+    "c5-M8192": ("gemm", "a4312010841b3530", 231211982),
     "c2": ("decode", "61df0d418fe5e71c", 648128),
-    "c3": ("skinny", "7976ad7a222d303f", 4661626),
-    "c4": ("gemm", "0a05717500f6b63d", 87232183),
+    "c3": ("skinny", "7976ad7a222d303f", 4661509),
+    "c4": ("gemm", "a4312010841b3530", 87154001),
     "c5-M8192-mlgru": ("mlgru", "9710b4206d609eee", 225843436),
     "c5-M512-mlgru": ("mlgru", "9710b4206d609eee", 15301697),
 }

@@ -13,8 +13,8 @@
 // in blocks of 128 (one packed tile column).  4 waves, either side by side
 // over all the tile's rows, each owning one (or, in 256-wide tiles, two)
 // packed 32-row tiles -- so every code word is unpacked once per workgroup
-// -- or, for 128 x 128 tiles, as 2 x 2 waves of 16*MI rows x two packed
-// tiles each.
+// -- or, for the 96- and 128-row tiles 128 wide, as 2 x 2 waves of 16*MI
+// rows x two packed tiles each.
 //   A (xq): global -> LDS (straight, by the buffer->LDS load, or through
 //           registers), 16-byte chunks of a 128-byte row XOR-swizzled (swz)
 //           so the lanes that read one column of chunks hit distinct banks.
@@ -717,13 +717,15 @@ hipError_t launch_gemm_mfma(const int8_t *xq, const int32_t *rowsum,
   // tiles (measured at M = 512).
   const int64_t tn = (N + 127) / 128;
   const auto tiles = [&](int64_t bm) { return ((M + bm - 1) / bm) * tn; };
-  // Wide launches: 128 x 256 tiles, a wave holding 4 packed tiles, so each
-  // A operand read from LDS feeds twice the MFMAs (2 waves per SIMD: 240
-  // VGPRs).  From 768 such tiles (gate_proj at M = 4096: 87 -> 84 us, at
-  // M = 8192: 254 -> 238 us; i/f/g grouped at M = 4096: 51 -> 49 us); with
-  // fewer, the tiles do not fill the rounds (2048-wide projections at M =
-  // 4096: 20.4 -> 22.7 us, 2560-wide at M = 8192: 49 -> 52 us) and 128 x 128
-  // stays.
+  // Wide launches: 128 x 256 tiles, the waves side by side over the 128
+  // rows with two packed tiles each, so every code word is unpacked once per
+  // workgroup and feeds eight MFMAs (2 waves per SIMD: 254 VGPRs).  From 768
+  // such tiles (first built as 2 x 2 waves of four tiles: gate_proj at M =
+  // 4096 87 -> 84 us, at M = 8192 254 -> 238 us; i/f/g grouped at M = 4096
+  // 51 -> 49 us); with fewer, the tiles do not fill the rounds (2048-wide
+  // projections at M = 4096: 20.4 -> 22.7 us, 2560-wide at M = 8192: 49 ->
+  // 52 us, measured again with the side-by-side waves: no faster) and
+  // 128 x 128 stays.
   if (M > 64 && ((M + 127) / 128) * ((N + 255) / 256) >= kWideTiles)
     return launch_mi<4, 4>(xq, rowsum, s, packed, beta, M, N, K, out, out_kind, glu, stream);
   if (M > 64 && tiles(128) >= 512)
